@@ -1,0 +1,55 @@
+"""The oracle on every workload family: lossless, and within 1% of the Shannon limit.
+
+The notes report every evaluated tensor within 1% of H(X) at K = 16, L = 128
+(Shannonic talk notes, "Evaluation: compression ratio", paper section 5, Table 1);
+the synthetic tensors of each workload stand in for the unavailable real ones.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from entropy_coding_quantized_amd import datagen as D
+
+
+def _check(x, cfg, pct=1.0):
+    r = O.roundtrip(x, cfg["K"], cfg["log2_L"], cfg["chunk"], cfg["streams"])
+    assert (r["y"] == x.reshape(-1)).all()
+    st = r["stats"]
+    if st["H"] > 0:
+        assert st["pct_payload_over_H"] < pct, st
+    return st
+
+
+@pytest.mark.slow
+def test_kv_cache_every_head():
+    cfg = D.CONFIGS["kv_cache"]
+    x = D.kv_cache()
+    for a in range(x.shape[0]):
+        for h in range(x.shape[1]):
+            _check(x[a, h], cfg)
+
+
+@pytest.mark.slow
+def test_activations_slice_with_whole_tensor_table():
+    cfg = D.CONFIGS["activations"]
+    x = D.activations(batch=16)
+    h = O.histogram(x)
+    lo, f = O.build_table(h, cfg["K"], cfg["log2_L"])
+    part = x[:2].reshape(-1)                      # 16.8M of the 134M symbols
+    buf, bits = O.encode(part, lo, f, cfg["log2_L"], cfg["chunk"], cfg["streams"])
+    assert (O.decode(buf, part.size) == part).all()
+    st = O.stats(h, lo, f, cfg["log2_L"], bits, buf.size, part.size)
+    assert st["pct_payload_over_H"] < 1.0
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 8, 100, 223])
+def test_model_tensors(idx):
+    cfg = D.CONFIGS["model"]
+    x = D.model_tensor(idx)
+    name, _ = D.model_layout()[idx]
+    st = _check(x, cfg)
+    if name == "layers.0.q_proj":
+        assert st["payload_bps"] == 0.0
