@@ -1,0 +1,254 @@
+"""Python binding of libshannonic.so: the C ABI of include/shannonic.h, same names.
+
+Argument marshalling only -- every step of the codec runs in the library (HIP kernels
+on the GPU, the table build on the host in C++).  PyTorch provides device memory and
+streams.  There is no fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import build as _build
+
+SH_OK = 0
+SH_ERR_INVALID_ARG = -1
+SH_ERR_UNSUPPORTED = -2
+SH_ERR_SYMBOL_NOT_IN_TABLE = -3
+SH_ERR_CORRUPT_STREAM = -4
+SH_ERR_BUFFER_TOO_SMALL = -5
+SH_ERR_HIP = -6
+
+
+class sh_params(C.Structure):
+    _fields_ = [("K", C.c_uint32), ("log2_L", C.c_uint32), ("chunk_symbols", C.c_uint32),
+                ("streams", C.c_uint32)]
+
+
+class sh_table(C.Structure):
+    _fields_ = [("K", C.c_uint32), ("log2_L", C.c_uint32), ("lo", C.c_uint16 * 257),
+                ("freq", C.c_uint16 * 256), ("hist", C.c_uint64 * 256), ("n", C.c_uint64)]
+
+    @property
+    def lo_array(self) -> np.ndarray:
+        return np.array(self.lo[: self.K + 1], dtype=np.uint16)
+
+    @property
+    def freq_array(self) -> np.ndarray:
+        return np.array(self.freq[: self.K], dtype=np.uint16)
+
+    @property
+    def hist_array(self) -> np.ndarray:
+        return np.array(self.hist[:], dtype=np.uint64)
+
+
+STAT_FIELDS = ["H", "H_P", "D_KL", "sum_Pw", "cl_thm1", "H_p_given_P", "dkl_tans_ref",
+               "cl_tans_ref", "payload_bps", "container_bps", "csr", "pct_payload_over_H",
+               "pct_container_over_H", "pct_thm1_over_H"]
+
+
+class sh_stats_t(C.Structure):
+    _fields_ = [(f, C.c_double) for f in STAT_FIELDS]
+
+
+class sh_encode_info(C.Structure):
+    _fields_ = [("container_bytes", C.c_uint64), ("payload_bits", C.c_uint64)]
+
+
+class ShannonicError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+_EXPORTS = {
+    "sh_version": (C.c_uint32, []),
+    "sh_status_string": (C.c_char_p, [C.c_int32]),
+    "sh_histogram": (C.c_int32, [C.c_void_p, C.c_uint64, C.c_void_p, C.c_void_p]),
+    "sh_table_from_histogram": (C.c_int32, [C.c_void_p, C.POINTER(sh_params), C.POINTER(sh_table)]),
+    "sh_build_tables_workspace": (C.c_uint64, []),
+    "sh_build_tables": (C.c_int32, [C.c_void_p, C.c_uint64, C.c_int, C.POINTER(sh_params),
+                                    C.c_void_p, C.c_uint64, C.c_void_p, C.POINTER(sh_table)]),
+    "sh_encode_bound": (C.c_uint64, [C.c_uint64, C.POINTER(sh_params)]),
+    "sh_encode_workspace": (C.c_uint64, [C.c_uint64, C.POINTER(sh_params)]),
+    "sh_encode": (C.c_int32, [C.POINTER(sh_table), C.POINTER(sh_params), C.c_void_p, C.c_uint64,
+                              C.c_void_p, C.c_uint64, C.c_void_p, C.c_uint64, C.c_void_p,
+                              C.c_void_p, C.c_void_p]),
+    "sh_decode": (C.c_int32, [C.POINTER(sh_table), C.POINTER(sh_params), C.c_void_p, C.c_uint64,
+                              C.c_void_p, C.c_uint64, C.c_void_p, C.c_void_p]),
+    "sh_stats": (C.c_int32, [C.POINTER(sh_table), C.c_uint64, C.c_uint64, C.c_uint64,
+                             C.POINTER(sh_stats_t)]),
+}
+
+
+def library_path() -> str:
+    return _build.LIB
+
+
+def lib():
+    """The loaded library; raises if it has not been built (no fallback exists)."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"libshannonic.so is not built ({path}); run "
+                               "`python -m entropy_coding_quantized_amd.build`")
+        L = C.CDLL(path)
+        for name, (res, args) in _EXPORTS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(st: int) -> str:
+    return lib().sh_status_string(st).decode()
+
+
+def _check(st: int, what: str):
+    if st != SH_OK:
+        raise ShannonicError(st, what)
+
+
+@dataclass(frozen=True)
+class Params:
+    K: int = 16
+    log2_L: int = 7
+    chunk_symbols: int = 4096
+    streams: int = 32
+
+    def c(self) -> sh_params:
+        return sh_params(self.K, self.log2_L, self.chunk_symbols, self.streams)
+
+
+def _ptr(t) -> int:
+    """Device (or host) address of a torch tensor, a numpy array or an int."""
+    if t is None:
+        return 0
+    if isinstance(t, int):
+        return t
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---- the C ABI, one to one -----------------------------------------------------------
+
+def sh_version() -> int:
+    return int(lib().sh_version())
+
+
+def sh_histogram(d_x, n: int, d_hist, stream=None) -> None:
+    _check(lib().sh_histogram(_ptr(d_x), n, _ptr(d_hist), _stream(stream)), "sh_histogram")
+
+
+def sh_table_from_histogram(hist: np.ndarray, params: Params) -> sh_table:
+    h = np.ascontiguousarray(hist, dtype=np.uint64)
+    assert h.size == 256
+    t = sh_table()
+    p = params.c()
+    _check(lib().sh_table_from_histogram(h.ctypes.data, C.byref(p), C.byref(t)),
+           "sh_table_from_histogram")
+    return t
+
+
+def sh_build_tables_workspace() -> int:
+    return int(lib().sh_build_tables_workspace())
+
+
+def sh_build_tables(x, n: int, x_on_device: bool, params: Params, d_ws=None, ws_bytes: int = 0,
+                    stream=None) -> sh_table:
+    t = sh_table()
+    p = params.c()
+    st = lib().sh_build_tables(_ptr(x), n, int(bool(x_on_device)), C.byref(p), _ptr(d_ws),
+                               ws_bytes, _stream(stream) if x_on_device else 0, C.byref(t))
+    _check(st, "sh_build_tables")
+    return t
+
+
+def sh_encode_bound(n: int, params: Params) -> int:
+    p = params.c()
+    return int(lib().sh_encode_bound(n, C.byref(p)))
+
+
+def sh_encode_workspace(n: int, params: Params) -> int:
+    p = params.c()
+    return int(lib().sh_encode_workspace(n, C.byref(p)))
+
+
+def sh_encode(table: sh_table, params: Params, d_x, n: int, d_out, out_cap: int, d_ws,
+              ws_bytes: int, d_info=None, d_status=None, stream=None) -> None:
+    p = params.c()
+    st = lib().sh_encode(C.byref(table), C.byref(p), _ptr(d_x), n, _ptr(d_out), out_cap,
+                         _ptr(d_ws), ws_bytes, _ptr(d_info), _ptr(d_status), _stream(stream))
+    _check(st, "sh_encode")
+
+
+def sh_decode(table: sh_table, params: Params, d_in, in_nbytes: int, d_y, n: int,
+              d_status=None, stream=None) -> None:
+    p = params.c()
+    st = lib().sh_decode(C.byref(table), C.byref(p), _ptr(d_in), in_nbytes, _ptr(d_y), n,
+                         _ptr(d_status), _stream(stream))
+    _check(st, "sh_decode")
+
+
+def sh_stats(table: sh_table, n: int = 0, payload_bits: int = 0, container_bytes: int = 0) -> dict:
+    out = sh_stats_t()
+    _check(lib().sh_stats(C.byref(table), n, payload_bits, container_bytes, C.byref(out)),
+           "sh_stats")
+    return {f: getattr(out, f) for f in STAT_FIELDS}
+
+
+def raw_status(fn_name: str, *args) -> int:
+    """Call a C entry point and return its status without raising (for tests)."""
+    return int(getattr(lib(), fn_name)(*args))
+
+
+# ---- torch conveniences: allocate the buffers, then call the C ABI ---------------------
+
+def encode_tensor(x, table: sh_table, params: Params, stream=None):
+    """Encode a device int8 tensor.  Returns (container uint8 tensor, info, status) where
+    info and status are still on the device; call ``finish_encode`` to trim and check."""
+    import torch
+    x = x.contiguous().view(-1)
+    n = x.numel()
+    cap = sh_encode_bound(n, params)
+    wsb = sh_encode_workspace(n, params)
+    out = torch.empty(max(cap, 4), dtype=torch.uint8, device=x.device)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=x.device)
+    info = torch.zeros(2, dtype=torch.int64, device=x.device)
+    status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    sh_encode(table, params, x, n, out, cap, ws, wsb, info, status, stream)
+    return out, info, status
+
+
+def finish_encode(out, info, status):
+    """Wait for an encode, raise on a device-side error, return (container, payload_bits)."""
+    st = int(status.item())
+    if st != SH_OK:
+        raise ShannonicError(st, "sh_encode (device)")
+    nbytes, bits = (int(v) for v in info.tolist())
+    return out[:nbytes], bits
+
+
+def decode_tensor(container, n: int, table: sh_table, params: Params, stream=None):
+    """Decode a device container into a new int8 tensor; returns (y, status on device)."""
+    import torch
+    y = torch.empty(max(n, 1), dtype=torch.int8, device=container.device)
+    status = torch.zeros(1, dtype=torch.int32, device=container.device)
+    sh_decode(table, params, container, container.numel(), y, n, status, stream)
+    return y[:n], status

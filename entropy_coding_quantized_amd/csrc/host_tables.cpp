@@ -1,0 +1,216 @@
+// Host side of the offline step: histogram -> DP range split -> tANS state allocation
+// -> derived tables, plus the container header.
+//
+// Method: "Shannonic: Efficient Entropy-Optimal Compression for ML Workloads" (MLSys 2026),
+// talk notes, "Preprocessing: range selection by dynamic programming" (paper section 4.1)
+// and "Runtime encoding/decoding" (paper section 4.2).
+//
+// Everything here is integer arithmetic.  The DP cost uses a fixed-point base-2 logarithm
+// with 24 fractional bits computed by repeated squaring (a defined function, so any
+// implementation reaches the same partition, exact ties included); the pages do not fix
+// the precision of the objective.
+#include <cstring>
+#include <vector>
+
+#include "codec_internal.hpp"
+
+namespace shn {
+
+// 2^24 * log2(x), digit by digit: with x = 2^e * m, m in [1, 2) kept in Q1.63, each
+// fractional bit of log2 m is set exactly when m^2 >= 2; the square (halved when the bit
+// is set) is truncated back to 64 bits and carries on.
+uint64_t fixed_log2(uint64_t x) {
+    if (x == 0) return 0;
+    const int e = 63 - __builtin_clzll(x);
+    uint64_t m = x << (63 - e);
+    uint64_t frac = 0;
+    for (int i = 0; i < kLgFrac; ++i) {
+        const unsigned __int128 sq = (unsigned __int128)m * m;
+        const uint64_t top = (uint64_t)(sq >> 127);
+        frac = (frac << 1) | top;
+        m = (uint64_t)(sq >> (63 + top));
+    }
+    return ((uint64_t)e << kLgFrac) | frac;
+}
+
+sh_status check_table(const sh_table& t, bool allow_empty) {
+    if (t.K < 1 || t.K > 256 || t.log2_L < 1 || t.log2_L > (uint32_t)kMaxLog2LHost)
+        return SH_ERR_INVALID_ARG;
+    if (t.lo[0] != 0 || t.lo[t.K] != 256) return SH_ERR_INVALID_ARG;
+    for (uint32_t k = 0; k < t.K; ++k)
+        if (t.lo[k + 1] <= t.lo[k]) return SH_ERR_INVALID_ARG;
+    uint64_t total = 0;
+    for (uint32_t k = 0; k < t.K; ++k) total += t.freq[k];
+    if (total == (1ull << t.log2_L)) return SH_OK;
+    return (total == 0 && allow_empty) ? SH_OK : SH_ERR_INVALID_ARG;
+}
+
+// Exactly-K contiguous ranges over [0, 256) minimising the summed range cost
+//   N_R * (log2 N - log2 N_R) + N_R * ceil(log2 width)     (units of 2^-24 bit)
+// -- the ideal range-id code length plus the raw offset bits.  Recurrence
+// C[i][k] = min_{j<i} C[j][k-1] + cost[j, i); the smallest j wins ties.
+static void dp_split(const uint64_t* hist, uint32_t K, uint16_t* lo) {
+    constexpr int A = 256;
+    uint64_t prefix[A + 1];
+    prefix[0] = 0;
+    for (int v = 0; v < A; ++v) prefix[v + 1] = prefix[v] + hist[v];
+    const uint64_t N = prefix[A];
+    const uint64_t lgN = fixed_log2(N);
+
+    // cost of [j, i) for all 0 <= j < i <= 256, row i holds j = 0..i-1
+    std::vector<uint64_t> cost((size_t)(A + 1) * (A + 2) / 2);
+    auto at = [](int j, int i) { return (size_t)i * (i - 1) / 2 + (size_t)j; };
+    for (int i = 1; i <= A; ++i)
+        for (int j = 0; j < i; ++j) {
+            const uint64_t nr = prefix[i] - prefix[j];
+            cost[at(j, i)] = nr ? nr * (lgN - fixed_log2(nr)) +
+                                      nr * ((uint64_t)ceil_log2_u32((uint32_t)(i - j)) << kLgFrac)
+                                : 0;
+        }
+
+    constexpr uint64_t INF = ~0ull;
+    std::vector<uint64_t> prev(A + 1, INF), cur(A + 1, INF);
+    std::vector<int16_t> arg((size_t)(K + 1) * (A + 1), -1);
+    prev[0] = 0;
+    for (uint32_t k = 1; k <= K; ++k) {
+        std::fill(cur.begin(), cur.end(), INF);
+        for (int i = (int)k; i <= A; ++i) {
+            uint64_t best = INF;
+            int bj = -1;
+            for (int j = (int)k - 1; j < i; ++j) {
+                if (prev[j] == INF) continue;
+                const uint64_t c = prev[j] + cost[at(j, i)];
+                if (c < best) {
+                    best = c;
+                    bj = j;
+                }
+            }
+            cur[i] = best;
+            arg[(size_t)k * (A + 1) + i] = (int16_t)bj;
+        }
+        std::swap(prev, cur);
+    }
+    int i = A;
+    lo[K] = A;
+    for (uint32_t k = K; k >= 1; --k) {
+        i = arg[(size_t)k * (A + 1) + i];
+        lo[k - 1] = (uint16_t)i;
+    }
+}
+
+// State allocation: one state for each occupied range, then each remaining state to the
+// range whose N_k * (log2(f_k + 1) - log2 f_k) is largest (first k on ties) -- the
+// greedy optimum of sum_k N_k log2 f_k, i.e. the smallest D_KL(P || Q).
+sh_status allocate_states(const uint64_t* count, uint32_t K, uint32_t L, uint16_t* f) {
+    uint32_t used = 0;
+    for (uint32_t k = 0; k < K; ++k) {
+        f[k] = count[k] ? 1 : 0;
+        used += f[k];
+    }
+    if (used == 0) return SH_OK;
+    if (used > L) return SH_ERR_UNSUPPORTED;
+    std::vector<uint64_t> gain_of(L + 1, 0);  // log2(f + 1) - log2 f in fixed point
+    for (uint32_t v = 1; v <= L; ++v) gain_of[v] = fixed_log2(v + 1) - fixed_log2(v);
+    while (used < L) {
+        uint32_t best = K;
+        uint64_t bg = 0;
+        for (uint32_t k = 0; k < K; ++k) {
+            if (!count[k]) continue;
+            const uint64_t g = count[k] * gain_of[f[k]];
+            if (best == K || g > bg) {
+                best = k;
+                bg = g;
+            }
+        }
+        f[best]++;
+        used++;
+    }
+    return SH_OK;
+}
+
+sh_status table_from_histogram(const uint64_t* hist, uint32_t K, uint32_t log2_L, sh_table* out) {
+    if (!hist || !out || K < 1 || K > 256 || log2_L < 1 || log2_L > (uint32_t)kMaxLog2LHost)
+        return SH_ERR_INVALID_ARG;
+    uint64_t N = 0;
+    for (int u = 0; u < 256; ++u) N += hist[u];
+    if (N >= (1ull << 32)) return SH_ERR_UNSUPPORTED;
+    sh_table t;
+    std::memset(&t, 0, sizeof(t));
+    t.K = K;
+    t.log2_L = log2_L;
+    std::memcpy(t.hist, hist, sizeof(t.hist));
+    t.n = N;
+    dp_split(hist, K, t.lo);
+    uint64_t count[256];
+    for (uint32_t k = 0; k < K; ++k) {
+        count[k] = 0;
+        for (int u = t.lo[k]; u < t.lo[k + 1]; ++u) count[k] += hist[u];
+    }
+    const sh_status st = allocate_states(count, K, 1u << log2_L, t.freq);
+    if (st != SH_OK) return st;
+    *out = t;
+    return SH_OK;
+}
+
+// Slot spread: range k's keys (2j+1)/(2 f_k), j < f_k, merged in increasing order (exact
+// cross-multiplied comparison, smaller k first on equal keys); slot i takes the range of
+// the i-th key.  Then the tANS tables: if slot i is range s's j-th slot, decoding it
+// gives s and the sub-state x = f_s + j, reads nb = R - floor(log2 x) bits b and moves to
+// slot (x << nb) - L + b; the encoder maps (s, j) back to slot i.
+sh_status derive_slots(const sh_table& t, SlotTables* out) {
+    const sh_status st = check_table(t, false);
+    if (st != SH_OK) return st;
+    const uint32_t K = t.K, R = t.log2_L, L = 1u << R;
+    out->L = L;
+    out->cum[0] = 0;
+    for (uint32_t k = 0; k < K; ++k) out->cum[k + 1] = out->cum[k] + t.freq[k];
+    uint32_t taken[256] = {0};
+    for (uint32_t i = 0; i < L; ++i) {
+        uint32_t best = K;
+        for (uint32_t k = 0; k < K; ++k) {
+            if (taken[k] >= t.freq[k]) continue;
+            if (best == K) {
+                best = k;
+                continue;
+            }
+            // (2 taken[k] + 1) / f_k  <  (2 taken[best] + 1) / f_best ?
+            const uint64_t lhs = (uint64_t)(2 * taken[k] + 1) * t.freq[best];
+            const uint64_t rhs = (uint64_t)(2 * taken[best] + 1) * t.freq[k];
+            if (lhs < rhs) best = k;
+        }
+        const uint32_t j = taken[best]++;
+        const uint32_t x = t.freq[best] + j;
+        const uint32_t nb = R - floor_log2_u32(x);
+        out->range[i] = (uint16_t)best;
+        out->nb[i] = (uint8_t)nb;
+        out->next[i] = (uint16_t)((x << nb) - L);
+        out->enc[out->cum[best] + j] = (uint16_t)i;
+    }
+    return SH_OK;
+}
+
+void write_header(const sh_table& t, uint64_t n, uint32_t C, uint32_t S, uint64_t n_chunks,
+                  uint32_t* dwords) {
+    uint8_t b[kMaxHeaderDwords * 4];
+    std::memset(b, 0, sizeof(b));
+    auto put = [&](uint32_t at, uint64_t v, int bytes) {
+        for (int i = 0; i < bytes; ++i) b[at + i] = (uint8_t)(v >> (8 * i));
+    };
+    b[0] = 'S';
+    b[1] = 'H';
+    b[2] = 'N';
+    b[3] = '1';
+    b[4] = 1;
+    b[5] = (uint8_t)t.log2_L;
+    put(6, t.K, 2);
+    put(8, n, 8);
+    put(16, C, 4);
+    put(20, S, 4);
+    put(24, n_chunks, 4);
+    put(28, header_bytes(t.K), 4);
+    for (uint32_t k = 0; k < t.K; ++k) put(kHeaderFixed + 2 * k, t.freq[k], 2);
+    for (uint32_t k = 1; k < t.K; ++k) b[kHeaderFixed + 2 * t.K + k - 1] = (uint8_t)t.lo[k];
+    std::memcpy(dwords, b, header_bytes(t.K));
+}
+
+}  // namespace shn

@@ -1,0 +1,507 @@
+// HIP kernels of the Shannonic codec for gfx950 (CDNA4, wave64).
+//
+// Method: "Shannonic: Efficient Entropy-Optimal Compression for ML Workloads" (MLSys 2026),
+// talk notes, "Runtime encoding/decoding" (paper section 4.2, Algorithm 2): per value a
+// range id through tANS plus raw offset bits, with table lookups, shifts, masks and adds
+// only.  The chunked, lane-interleaved layout and everything about the GPU mapping are
+// this library's own design; the pages give no GPU design.
+//
+// Mapping: one chunk of C values per half wavefront (32 lanes), one tANS state machine per
+// lane.  At every step the 32 lanes of a chunk code 32 consecutive values, so their fields
+// sit back to back in the bit stream; a 32-lane DPP prefix sum of the field lengths gives
+// each lane its bit position.  Compressed words are staged through a per-chunk LDS ring
+// fed by 128-bit loads; the decode table (<= 2 KB) lives in LDS.  No MFMA: there is no
+// dense contraction.
+#include <hip/hip_runtime.h>
+
+#include "codec_internal.hpp"
+
+namespace shn {
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over [p, p + bytes): accesses past the end read 0 / are dropped.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// Inclusive prefix sum within each 32-lane half of the wavefront (DPP row shifts, then
+// the last lane of rows 0 and 2 added into rows 1 and 3).
+__device__ __forceinline__ uint32_t scan32(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false); // row_bcast:15
+    return v;
+}
+
+// Value of lane 31 of this lane's 32-lane half (ds_swizzle bit mode, or_mask = 31).
+__device__ __forceinline__ uint32_t bcast31(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x3E0);
+}
+
+typedef const __attribute__((address_space(3))) uint32_t lds_u32;
+
+// LDS byte offset of a __shared__ object
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ void report(int32_t* status, int32_t code) {
+    if (status) atomicCAS(status, 0, code);
+}
+
+// ------------------------------------------------------------------------------------
+// histogram: h[u] = #{i : x[i] + 128 == u}   (paper section 4.1)
+// ------------------------------------------------------------------------------------
+constexpr int kHistBlock = 256;
+constexpr int kHistCopies = 32;
+
+__global__ void k_zero_u64(uint64_t* p, uint32_t count) {
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count) p[i] = 0;
+}
+
+__global__ __launch_bounds__(kHistBlock) void k_histogram(const int8_t* x, uint64_t n,
+                                                          uint64_t* hist) {
+    // 32 private copies per block, copy c of bin b at b * 32 + c: the 32 lanes of a half
+    // wavefront hit 32 different banks even when every value is the same.
+    __shared__ uint32_t h[256 * kHistCopies];
+    for (int i = threadIdx.x; i < 256 * kHistCopies; i += kHistBlock) h[i] = 0;
+    __syncthreads();
+    const uint32_t copy = threadIdx.x & (kHistCopies - 1);
+    const uint64_t groups = n / 16;
+    const uint64_t stride = (uint64_t)gridDim.x * kHistBlock;
+    for (uint64_t g = (uint64_t)blockIdx.x * kHistBlock + threadIdx.x; g < groups; g += stride) {
+        const v4u w = *reinterpret_cast<const v4u*>(x + 16 * g);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const uint32_t u = ((w[q] >> (8 * b)) & 0xFF) ^ 0x80;
+                atomicAdd(&h[u * kHistCopies + copy], 1u);
+            }
+        }
+    }
+    if (blockIdx.x == 0) {  // the n % 16 tail
+        const uint64_t i = groups * 16 + threadIdx.x;
+        if (i < n) atomicAdd(&h[((uint32_t)(uint8_t)x[i] ^ 0x80) * kHistCopies + copy], 1u);
+    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < 256; b += kHistBlock) {
+        uint64_t s = 0;
+#pragma unroll 8
+        for (int c = 0; c < kHistCopies; ++c) s += h[b * kHistCopies + c];
+        if (s) atomicAdd((unsigned long long*)&hist[b], (unsigned long long)s);
+    }
+}
+
+sh_status launch_histogram(const int8_t* d_x, uint64_t n, uint64_t* d_hist, void* stream) {
+    hipStream_t s = (hipStream_t)stream;
+    hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(256), 0, s, d_hist, 256u);
+    if (n > 0) {
+        const uint64_t groups = n / 16;
+        uint64_t blocks = (groups + kHistBlock * 8 - 1) / (kHistBlock * 8);
+        if (blocks < 1) blocks = 1;
+        if (blocks > 2048) blocks = 2048;
+        hipLaunchKernelGGL(k_histogram, dim3((uint32_t)blocks), dim3(kHistBlock), 0, s, d_x, n,
+                           d_hist);
+    }
+    return hipGetLastError() == hipSuccess ? SH_OK : SH_ERR_HIP;
+}
+
+// ------------------------------------------------------------------------------------
+// decode
+// ------------------------------------------------------------------------------------
+constexpr int kDecBlock = 256;                // 4 wavefronts, 8 chunks
+constexpr uint32_t kRing = 256;               // compressed dwords resident per chunk
+// each ring starts on a 2 KB boundary (so the wrapped word address is one and-or) and is
+// followed by a copy of its dword 0, so a two-word read never wraps
+constexpr uint32_t kRingStride = 512;
+constexpr uint32_t kFill = 128;               // dwords per refill: 32 lanes x 16 bytes
+constexpr uint32_t kTabDwords = 512;
+
+// 16 bytes of the chunk starting at dword d (dwords at or past cdw read as 0).
+__device__ __forceinline__ v4u load_words(rsrc_t r, uint32_t chunk_byte, uint32_t d,
+                                          uint32_t cdw) {
+    if (d + 4 <= cdw)
+        return __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(
+                                           r, (int)(chunk_byte + 4 * d), 0, 0));
+    v4u v = {0, 0, 0, 0};
+    for (uint32_t k = 0; k < 4; ++k)
+        if (d + k < cdw)
+            v[k] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(chunk_byte + 4 * (d + k)), 0, 0);
+    return v;
+}
+
+__global__ __launch_bounds__(kDecBlock) void k_decode(const DecodeArgs a) {
+    __shared__ __align__(16) uint32_t sm[kTabDwords + 8 * kRingStride];
+    const uint32_t tid = threadIdx.x, lane = tid & 63, li = lane & 31, hw = lane >> 5;
+    // wavefront index, made visibly uniform so that per-wavefront descriptors stay scalar
+    const uint32_t wid = __builtin_amdgcn_readfirstlane(blockIdx.x * (kDecBlock / 64) + (tid >> 6));
+    const uint32_t wv = wid & (kDecBlock / 64 - 1);
+
+    for (uint32_t i = tid; i < 2 * a.L; i += kDecBlock) sm[i] = a.dec[i];
+
+    const rsrc_t rin = make_rsrc(a.in, (uint32_t)a.in_nbytes);
+    if (wid == 0) {
+        // header and index ends: the container must belong to this table and size
+        bool bad = false;
+        for (uint32_t i = lane; i < a.hdr_dwords; i += 64)
+            bad |= __builtin_amdgcn_raw_buffer_load_b32(rin, (int)(4 * i), 0, 0) != a.hdr[i];
+        if (lane == 0) {
+            const uint32_t first = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)a.index_at, 0, 0);
+            const uint32_t last = __builtin_amdgcn_raw_buffer_load_b32(
+                rin, (int)(a.index_at + 4 * a.n_chunks), 0, 0);
+            bad |= first != 0 || (uint64_t)a.payload_at + last != a.in_nbytes;
+        }
+        if (bad) report(a.status, SH_ERR_CORRUPT_STREAM);
+    }
+
+    // this half wavefront's chunk
+    const uint32_t pair = 2 * wid;
+    const uint32_t chunk = pair + hw;
+    const uint32_t ring = kTabDwords + (wv * 2 + hw) * kRingStride;
+    const uint32_t ring_byte = lds_offset(sm) + 4 * ring;
+    uint32_t nc = 0, cdw = 0, cbyte = 0, err = 0;
+    if (chunk < a.n_chunks) {
+        const uint32_t o0 = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)(a.index_at + 4 * chunk), 0, 0);
+        const uint32_t o1 = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)(a.index_at + 4 * chunk + 4), 0, 0);
+        const uint64_t first = (uint64_t)chunk * a.C;
+        const uint32_t m = (uint32_t)((a.n - first) < a.C ? (a.n - first) : a.C);
+        const bool ok = o0 <= o1 && ((o0 | o1) & 3) == 0 &&
+                        (o1 - o0) <= 4 * chunk_bound_dwords(m, a.R) &&
+                        (uint64_t)a.payload_at + o1 <= a.in_nbytes;
+        if (ok) {
+            nc = m;
+            cdw = (o1 - o0) >> 2;
+            cbyte = a.payload_at + o0;
+        } else {
+            err = 1;
+        }
+    }
+    const uint32_t lanes = nc < 32 ? nc : 32;
+
+    // first two refills, plus the third in flight
+    for (uint32_t b = 0; b < 2; ++b) {
+        const uint32_t d = b * kFill + 4 * li;
+        const v4u v = load_words(rin, cbyte, d, cdw);
+        *reinterpret_cast<v4u*>(&sm[ring + d]) = v;
+        if (b == 0 && li == 0) sm[ring + kRing] = v[0];
+    }
+    uint32_t res_hi = 2 * kFill;  // dwords [res_hi - kRing, res_hi) are in the ring
+    v4u pf = load_words(rin, cbyte, res_hi + 4 * li, cdw);
+    // the next refill is due once a step could read past res_hi: pos >> 5 >= res_hi - 17
+    uint32_t refill_at = res_hi < cdw ? (res_hi - 17) * 32 : 0xFFFFFFFFu;
+    __syncthreads();
+
+    // initial slots: lane l's R bits at l * R
+    uint32_t addr = 0;  // LDS byte address of the current slot's decode entry
+    if (li < lanes) {
+        const uint32_t p = li * a.R;
+        const uint32_t bits = __builtin_amdgcn_alignbit(sm[ring + (p >> 5) + 1], sm[ring + (p >> 5)], p);
+        addr = (bits & (a.L - 1)) << 3;
+    }
+    uint32_t pos = lanes * a.R;
+
+    // output: per-wavefront descriptor over the wavefront's two chunks
+    const uint64_t pair_first = (uint64_t)pair * a.C;
+    const uint64_t pair_len = pair_first < a.n ? a.n - pair_first : 0;
+    const rsrc_t rout = make_rsrc(a.out + (pair_first < a.n ? pair_first : 0),
+                                  (uint32_t)(pair_len < 2ull * a.C ? pair_len : 2ull * a.C));
+    const uint32_t vout = hw * a.C + li;
+
+    const uint32_t nc_lo = __builtin_amdgcn_readlane(nc, 0), nc_hi = __builtin_amdgcn_readlane(nc, 32);
+    const uint32_t full = (nc_lo < nc_hi ? nc_lo : nc_hi) >> 5;
+    const uint32_t steps = ((nc_lo > nc_hi ? nc_lo : nc_hi) + 31) >> 5;
+    uint64_t bad_offsets = 0;  // lanes that decoded an offset outside its range
+
+    auto refill = [&]() {
+        if (pos >= refill_at) {
+            const uint32_t d = (res_hi + 4 * li) & (kRing - 1);
+            *reinterpret_cast<v4u*>(&sm[ring + d]) = pf;
+            if (d == 0) sm[ring + kRing] = pf[0];
+            res_hi += kFill;
+            refill_at = res_hi < cdw ? (res_hi - 17) * 32 : 0xFFFFFFFFu;
+            pf = load_words(rin, cbyte, res_hi + 4 * li, cdw);
+        }
+    };
+
+    uint32_t t = 0;
+    for (; t < full; ++t) {
+        refill();
+        const uint2 e = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(sm) + addr);
+        const uint32_t incl = scan32(e.x);
+        const uint32_t start = pos + incl - e.x;  // only bits 0..12 matter below
+        const uint32_t rb = ((start >> 3) & (4 * kRing - 4)) | ring_byte;
+        const lds_u32* rp = (const lds_u32*)(uintptr_t)rb;
+        const uint32_t bits = __builtin_amdgcn_alignbit(rp[1], rp[0], start);
+        const uint32_t v = __builtin_amdgcn_ubfe(bits, 0, e.x);  // width = need (bits 0..4)
+        const uint32_t o = __builtin_amdgcn_ubfe(bits, 0, e.y);  // width = w_s (bits 0..4)
+        bad_offsets |= __builtin_amdgcn_ballot_w64(o > ((e.y >> 16) & 0xFF));
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(o + ((e.y >> 8) & 0xFF)), rout, (int)vout,
+                                             (int)(t * 32), 0);
+        addr = (e.x >> 16) + ((v >> (e.y & 31)) << 3);
+        pos += bcast31(incl) & 0xFFFFu;
+    }
+    for (; t < steps; ++t) {  // last, partial chunk: lanes past n_c take no bits
+        refill();
+        const bool act = t * 32 + li < nc;
+        uint2 e = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(sm) + addr);
+        if (!act) e = make_uint2(0, 0);
+        const uint32_t incl = scan32(e.x);
+        const uint32_t start = pos + incl - e.x;
+        const uint32_t d = (start >> 5) & (kRing - 1);
+        const uint32_t bits = __builtin_amdgcn_alignbit(sm[ring + d + 1], sm[ring + d], start);
+        const uint32_t v = __builtin_amdgcn_ubfe(bits, 0, e.x);
+        const uint32_t o = __builtin_amdgcn_ubfe(bits, 0, e.y);
+        if (act) {
+            err |= o > ((e.y >> 16) & 0xFF);
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(o + ((e.y >> 8) & 0xFF)), rout,
+                                                 (int)vout, (int)(t * 32), 0);
+            addr = (e.x >> 16) + ((v >> (e.y & 31)) << 3);
+        }
+        pos += bcast31(incl) & 0xFFFFu;
+    }
+
+    // a valid chunk leaves every lane in slot 0 and ends in its last word, zero-padded
+    if (nc > 0) {
+        if (li < lanes && addr != 0) err = 1;
+        if (((pos + 31) >> 5) != cdw) err = 1;
+        else if ((pos & 31) && (sm[ring + ((pos >> 5) & (kRing - 1))] >> (pos & 31)) != 0) err = 1;
+    }
+    if (err || bad_offsets) report(a.status, SH_ERR_CORRUPT_STREAM);
+}
+
+sh_status launch_decode(const DecodeArgs& a, void* stream) {
+    if (a.n_chunks == 0) return SH_OK;
+    const uint32_t blocks = (a.n_chunks + 7) / 8;
+    hipLaunchKernelGGL(k_decode, dim3(blocks), dim3(kDecBlock), 0, (hipStream_t)stream, a);
+    return hipGetLastError() == hipSuccess ? SH_OK : SH_ERR_HIP;
+}
+
+// ------------------------------------------------------------------------------------
+// encode, kernel 1: every chunk into a worst-case slot of the workspace
+// ------------------------------------------------------------------------------------
+// tANS encodes backwards.  Each lane walks its values from the last step to the first;
+// at every step the 32 fields of a chunk are placed right to left: the step's fields end
+// where the later steps' fields begin, so a 32-lane prefix sum of the lengths gives every
+// field's bit position.  Fields are OR-ed into a 256-dword LDS ring that is flushed to
+// the chunk's slot 128 dwords at a time, highest first; the chunk ends up right-aligned
+// in its slot with the lanes' final states (the decoder's initial states) in front.
+constexpr int kEncBlock = 256;
+constexpr uint32_t kERing = 256;
+constexpr uint32_t kEncHalfDwords = 256 /* input tile, 32 steps x 32 lanes bytes */ + kERing;
+constexpr uint32_t kVtDwords = 512 + 64;  // value table + encTable bytes
+
+__device__ __forceinline__ void ring_or(uint32_t* sm, uint32_t ring, uint32_t pos,
+                                        uint32_t field, uint32_t len) {
+    if (len == 0) return;
+    const uint64_t wide = (uint64_t)field << (pos & 31);
+    const uint32_t d = pos >> 5;
+    atomicOr(&sm[ring + (d & (kERing - 1))], (uint32_t)wide);
+    if ((pos & 31) + len > 32) atomicOr(&sm[ring + ((d + 1) & (kERing - 1))], (uint32_t)(wide >> 32));
+}
+
+__global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const EncodeArgs a) {
+    __shared__ __align__(16) uint32_t sm[kVtDwords + 8 * kEncHalfDwords];
+    const uint32_t tid = threadIdx.x, lane = tid & 63, li = lane & 31, hw = lane >> 5;
+    const uint32_t wv = tid >> 6;
+    for (uint32_t i = tid; i < 512; i += kEncBlock) sm[i] = a.vt[i];
+    for (uint32_t i = tid; i < 64; i += kEncBlock) {
+        sm[512 + i] = (uint32_t)a.es[4 * i] | ((uint32_t)a.es[4 * i + 1] << 8) |
+                      ((uint32_t)a.es[4 * i + 2] << 16) | ((uint32_t)a.es[4 * i + 3] << 24);
+    }
+    const uint8_t* es = reinterpret_cast<const uint8_t*>(&sm[512]);
+    const uint32_t half = kVtDwords + (wv * 2 + hw) * kEncHalfDwords;
+    const uint32_t tile = half;            // 256 dwords: bytes of 32 steps x 32 lanes
+    const uint32_t ring = half + 256;      // 256 dwords
+    for (uint32_t i = li; i < kERing; i += 32) sm[ring + i] = 0;
+
+    const uint32_t chunk = (blockIdx.x * (kEncBlock / 64) + wv) * 2 + hw;
+    const uint32_t pair = chunk & ~1u;
+    const uint64_t pair_first = (uint64_t)pair * a.C;
+    const uint64_t pair_len = pair_first < a.n ? a.n - pair_first : 0;
+    const rsrc_t rin = make_rsrc(a.x + (pair_first < a.n ? pair_first : 0),
+                                 (uint32_t)(pair_len < 2ull * a.C ? pair_len : 2ull * a.C));
+    const rsrc_t rslot = make_rsrc(a.slots + (uint64_t)(pair < a.n_chunks ? pair : 0) * a.slot_dwords,
+                                   8u * a.slot_dwords);
+    const uint32_t in_base = hw * a.C;          // byte offset of this chunk in rin
+    const uint32_t slot_base = hw * a.slot_dwords * 4;
+    uint32_t nc = 0;
+    if (chunk < a.n_chunks) {
+        const uint64_t first = (uint64_t)chunk * a.C;
+        nc = (uint32_t)((a.n - first) < a.C ? (a.n - first) : a.C);
+    }
+    const uint32_t lanes = nc < 32 ? nc : 32;
+    const uint32_t nc_lo = __builtin_amdgcn_readlane(nc, 0), nc_hi = __builtin_amdgcn_readlane(nc, 32);
+    const uint32_t steps = ((nc_lo > nc_hi ? nc_lo : nc_hi) + 31) >> 5;
+    const uint32_t L = a.L, R1 = a.R + 1;
+
+    // 32 bytes of input tile tl for this lane (32 steps x 32 lanes = 1 KB per tile)
+    auto load_tile = [&](uint32_t tl, v4u& p0, v4u& p1) {
+        const uint32_t b = tl * 1024 + 32 * li;   // chunk-relative byte
+        if (b + 32 <= nc) {
+            p0 = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rin, (int)(in_base + b), 0, 0));
+            p1 = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rin, (int)(in_base + b + 16), 0, 0));
+        } else {
+            p0 = v4u{0, 0, 0, 0};
+            p1 = v4u{0, 0, 0, 0};
+            for (uint32_t k = 0; k < 32; ++k)
+                if (b + k < nc) {
+                    const uint32_t byte = __builtin_amdgcn_raw_buffer_load_b8(rin, (int)(in_base + b + k), 0, 0);
+                    if (k < 16) p0[k >> 2] |= byte << (8 * (k & 3));
+                    else p1[(k - 16) >> 2] |= byte << (8 * (k & 3));
+                }
+        }
+    };
+    v4u p0, p1;
+    if (steps > 0) load_tile((steps - 1) >> 5, p0, p1);
+    __syncthreads();
+
+    uint32_t X = L;
+    uint32_t P = a.slot_dwords * 32;   // fields go below P, right to left
+    uint32_t fmark = a.slot_dwords;    // dwords at or above fmark are in the slot
+    uint32_t pay = 0, bad = 0;
+
+    auto flush_block = [&](uint32_t blk) {  // ring dwords [blk, blk + 128) -> slot
+        uint32_t* r = &sm[ring + ((blk + 4 * li) & (kERing - 1))];
+        const v4u v = *reinterpret_cast<v4u*>(r);
+        *reinterpret_cast<v4u*>(r) = v4u{0, 0, 0, 0};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v),
+                                               rslot, (int)(slot_base + 4 * (blk + 4 * li)), 0, 0);
+    };
+
+    for (uint32_t t = steps; t-- > 0;) {
+        if ((t & 31) == 31 || t + 1 == steps) {  // entering tile t >> 5: stage it, fetch the next
+            *reinterpret_cast<v4u*>(&sm[tile + 8 * li]) = p0;
+            *reinterpret_cast<v4u*>(&sm[tile + 8 * li + 4]) = p1;
+            if (t >= 32) load_tile((t >> 5) - 1, p0, p1);
+        }
+        const bool act = t * 32 + li < nc;
+        const uint32_t u = (uint32_t)reinterpret_cast<const uint8_t*>(&sm[tile])[(t & 31) * 32 + li] ^ 0x80;
+        const uint2 e = *reinterpret_cast<const uint2*>(&sm[2 * u]);
+        const uint32_t k = (uint32_t)((int)X + (int)e.x) >> R1;
+        const uint32_t w = (e.y >> 8) & 15;
+        const uint32_t field = (e.y & 0xFF) | (__builtin_amdgcn_ubfe(X, 0, k) << w);
+        uint32_t len = act ? w + k : 0;
+        const uint32_t Xn = L + es[((e.y >> 16) & 0x3FF) - 512 + (X >> k)];
+        if (act) {
+            bad |= e.y >> 31;
+            X = Xn;
+        }
+        const uint32_t incl = scan32(len);
+        const uint32_t total = bcast31(incl);
+        const uint32_t Pt = P - total;
+        ring_or(sm, ring, Pt + incl - len, field, len);
+        P = Pt;
+        pay += total;
+        if ((P >> 5) + 129 <= fmark) {  // dwords above P's word are final
+            fmark -= 128;
+            flush_block(fmark);
+        }
+    }
+    // the lanes' final states, the decoder's initial states, in front of the fields
+    const uint32_t Pi = P - lanes * a.R;
+    if (li < lanes) ring_or(sm, ring, Pi + li * a.R, X - L, a.R);
+    if (nc > 0) {
+        while (fmark > (Pi >> 5)) {
+            fmark -= 128;
+            flush_block(fmark);
+        }
+    }
+    if (chunk < a.n_chunks && li == 0) {
+        a.meta[2 * chunk] = Pi;
+        a.meta[2 * chunk + 1] = pay;
+    }
+    if (bad) report(a.status, SH_ERR_SYMBOL_NOT_IN_TABLE);
+}
+
+// ------------------------------------------------------------------------------------
+// encode, kernel 2: chunk index (exclusive scan of chunk sizes), header, totals
+// ------------------------------------------------------------------------------------
+constexpr int kScanBlock = 1024;
+
+__global__ __launch_bounds__(kScanBlock) void k_encode_index(const IndexArgs a) {
+    __shared__ uint32_t wsum[kScanBlock / 64];
+    __shared__ unsigned long long bits_sum;
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    uint32_t* index = reinterpret_cast<uint32_t*>(a.out + a.index_at);
+    uint32_t* hdr = reinterpret_cast<uint32_t*>(a.out);
+    for (uint32_t i = tid; i < a.hdr_dwords; i += kScanBlock) hdr[i] = a.hdr[i];
+    if (tid == 0) bits_sum = 0;
+    __syncthreads();
+    uint32_t carry = 0;
+    uint64_t my_bits = 0;
+    for (uint32_t base = 0; base < a.n_chunks; base += kScanBlock) {
+        const uint32_t c = base + tid;
+        uint32_t bytes = 0;
+        if (c < a.n_chunks) {
+            const uint32_t start = a.meta[2 * c];
+            bytes = 4 * ((a.slot_dwords * 32 - start + 31) >> 5);
+            my_bits += a.meta[2 * c + 1];
+        }
+        // wavefront inclusive scan, then across the 16 wavefronts
+        uint32_t v = bytes;
+        for (int sh = 1; sh < 64; sh <<= 1) {
+            const uint32_t o = __shfl_up(v, sh, 64);
+            if (lane >= (uint32_t)sh) v += o;
+        }
+        if (lane == 63) wsum[wv] = v;
+        __syncthreads();
+        uint32_t before = 0, all = 0;
+        for (uint32_t w = 0; w < kScanBlock / 64; ++w) {
+            before += w < wv ? wsum[w] : 0;
+            all += wsum[w];
+        }
+        if (c < a.n_chunks) index[c] = carry + before + v - bytes;
+        carry += all;
+        __syncthreads();
+    }
+    if (tid == 0) index[a.n_chunks] = carry;
+    atomicAdd(&bits_sum, (unsigned long long)my_bits);
+    __syncthreads();
+    if (tid == 0 && a.info) {
+        a.info->container_bytes = (uint64_t)a.index_at + 4ull * (a.n_chunks + 1) + carry;
+        a.info->payload_bits = bits_sum;
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// encode, kernel 3: move every chunk from its slot to its place in the payload
+// ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_encode_compact(const CompactArgs a) {
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t c = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (c >= a.n_chunks) return;
+    const uint32_t start = a.meta[2 * c];
+    const uint32_t ndw = (a.slot_dwords * 32 - start + 31) >> 5;
+    const uint32_t off = reinterpret_cast<const uint32_t*>(a.out + a.index_at)[c];
+    const uint32_t* s = a.slots + (uint64_t)c * a.slot_dwords;
+    uint32_t* d = reinterpret_cast<uint32_t*>(a.out + a.payload_at + off);
+    const uint32_t s0 = start >> 5;
+    for (uint32_t j = lane; j < ndw; j += 64) {
+        const uint32_t lo = s[s0 + j];
+        const uint32_t hi = s0 + j + 1 < a.slot_dwords ? s[s0 + j + 1] : 0;
+        d[j] = __builtin_amdgcn_alignbit(hi, lo, start);
+    }
+}
+
+sh_status launch_encode(const EncodeArgs& e, const IndexArgs& ix, const CompactArgs& cp,
+                        void* stream) {
+    hipStream_t s = (hipStream_t)stream;
+    if (e.n_chunks > 0) {
+        const uint32_t blocks = (e.n_chunks + 7) / 8;
+        hipLaunchKernelGGL(k_encode_chunks, dim3(blocks), dim3(kEncBlock), 0, s, e);
+    }
+    hipLaunchKernelGGL(k_encode_index, dim3(1), dim3(kScanBlock), 0, s, ix);
+    if (cp.n_chunks > 0) {
+        hipLaunchKernelGGL(k_encode_compact, dim3((cp.n_chunks + 3) / 4), dim3(256), 0, s, cp);
+    }
+    return hipGetLastError() == hipSuccess ? SH_OK : SH_ERR_HIP;
+}
+
+}  // namespace shn

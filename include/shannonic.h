@@ -1,0 +1,185 @@
+/*
+ * shannonic.h -- C ABI of the MI355X (gfx950) Shannonic codec library, libshannonic.so.
+ *
+ * Method: "Shannonic: Efficient Entropy-Optimal Compression for ML Workloads" (MLSys 2026),
+ * talk notes.  An offline step histograms an 8-bit tensor and splits the 256-value
+ * alphabet into K contiguous ranges by dynamic programming ("Preprocessing: range
+ * selection by dynamic programming", paper section 4.1).  Every value is then coded as
+ * (range index s, offset o): s goes through a tabled-ANS coder with L = 2^log2_L states,
+ * o is written as w_s = ceil(log2 |range s|) raw bits ("Runtime encoding/decoding", paper
+ * section 4.2, Algorithm 2).  Theorem 1 (paper section 4) gives the expected rate.
+ *
+ * Conventions shared by every call:
+ *   - Values are int8.  The coder works on u = x + 128 (offset binary, so ranges are
+ *     contiguous in value).
+ *   - Pointers named d_* are device (HBM) pointers; all others are host pointers.
+ *   - stream is a hipStream_t (0 = the null stream).  Device work is enqueued on it and
+ *     the call returns without waiting, except where a host result needs device data
+ *     (sh_build_tables with x_on_device != 0 waits for its histogram).
+ *   - The library allocates no device memory and keeps no global state: the caller owns
+ *     every buffer, and sizes of the workspaces are exported.  Calls are thread-safe.
+ *   - Argument errors are returned synchronously.  Errors found by the GPU (a corrupt
+ *     stream, a value whose range holds no tANS state) are written to *d_status with an
+ *     atomic compare-and-swap from 0, so the first error wins; the caller zeroes
+ *     *d_status beforehand and reads it back when convenient.
+ *
+ * Container (the bytes sh_encode writes and sh_decode reads), all integers little-endian:
+ *   0   "SHN1", u8 version = 1, u8 log2_L, u16 K
+ *   8   u64 n              number of values
+ *   16  u32 chunk_symbols  C
+ *   20  u32 streams        S (interleaved tANS lanes per chunk)
+ *   24  u32 n_chunks       ceil(n / C)
+ *   28  u32 index_at       header size = 4 * ceil((32 + 3K - 1) / 4)
+ *   32  u16 freq[K]        tANS state count of every range (sum L)
+ *   32+2K u8 lo[1..K-1]    first value u of ranges 1..K-1 (range 0 starts at 0, the
+ *                          last ends at 256); zero padding up to index_at
+ *   index_at: u32 off[n_chunks + 1], byte offset of every chunk from the payload start
+ *   payload: chunk c holds values [c*C, c*C + n_c).  Value i of a chunk belongs to lane
+ *   i mod S at step i div S.  The chunk is an LSB-first bit string (bit b is bit b mod 8
+ *   of byte b / 8): the initial tANS slot of each of its min(S, n_c) lanes in log2_L bits,
+ *   in lane order, then every value's field in (step, lane) order, then zero bits up to a
+ *   whole number of 32-bit words.  A field is the offset o in its low w_s bits and, above
+ *   it, the nb state bits the decoder appends to the slot's base to reach the next state.
+ *   Every lane ends in slot 0.
+ */
+#ifndef SHANNONIC_H
+#define SHANNONIC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t sh_status;
+#define SH_OK 0
+#define SH_ERR_INVALID_ARG (-1)          /* a pointer, size or parameter is out of range   */
+#define SH_ERR_UNSUPPORTED (-2)          /* valid, but outside what the GPU path handles    */
+#define SH_ERR_SYMBOL_NOT_IN_TABLE (-3)  /* a value falls in a range with no tANS state     */
+#define SH_ERR_CORRUPT_STREAM (-4)       /* the container is not a valid stream             */
+#define SH_ERR_BUFFER_TOO_SMALL (-5)     /* output or workspace capacity below the bound    */
+#define SH_ERR_HIP (-6)                  /* a HIP runtime call failed                       */
+
+/* Codec parameters.  The GPU path supports 1 <= K <= 256, 1 <= log2_L <= 8,
+ * streams == 32 and chunk_symbols a multiple of 32 in [32, 65536].
+ * The pages' configuration is K = 16, log2_L = 7 (530 B of codec state,
+ * "Codec state footprint", paper section 4.1 and Appendix A). */
+typedef struct {
+    uint32_t K;
+    uint32_t log2_L;
+    uint32_t chunk_symbols;
+    uint32_t streams;
+} sh_params;
+
+/* The canonical table of one tensor: a plain host struct, copyable and serialisable.
+ * Everything the kernels use (rangeId, base, nb, start, bias, encTable, decTable) is
+ * derived from lo[] and freq[] deterministically.  hist[] and n are kept for sh_stats. */
+typedef struct {
+    uint32_t K;
+    uint32_t log2_L;
+    uint16_t lo[257];    /* range k covers u in [lo[k], lo[k+1]); lo[0] = 0, lo[K] = 256 */
+    uint16_t freq[256];  /* f_k, sum = L (all 0 only for an empty tensor)                  */
+    uint64_t hist[256];  /* h[u] of the tensor the table was built from                    */
+    uint64_t n;          /* sum of hist                                                   */
+} sh_table;
+
+/* Theorem-1 terms and the measured rates (paper sections 4 and 5), in bits/value. */
+typedef struct {
+    double H;                    /* H(X) of the histogram                              */
+    double H_P;                  /* H(P) of the range probabilities P_k                */
+    double D_KL;                 /* D_KL(P || Q), Q_k = f_k / L                         */
+    double sum_Pw;               /* sum_k P_k w_k, offset bits                          */
+    double cl_thm1;              /* H(P) + D_KL(P || Q) + sum_k P_k w_k                  */
+    double H_p_given_P;          /* H(X) - H(P)                                         */
+    double dkl_tans_ref;         /* D_KL(p || q) of plain tANS, 256 values, L = 1024     */
+    double cl_tans_ref;          /* H(X) + dkl_tans_ref                                 */
+    double payload_bps;          /* field bits / n                                      */
+    double container_bps;        /* 8 * container bytes / n                             */
+    double csr;                  /* container bytes / n                                 */
+    double pct_payload_over_H;   /* (payload_bps - H) / H * 100                         */
+    double pct_container_over_H; /* (container_bps - H) / H * 100                       */
+    double pct_thm1_over_H;      /* (cl_thm1 - H) / H * 100                             */
+} sh_stats_t;
+
+/* What sh_encode reports, written to device memory. */
+typedef struct {
+    uint64_t container_bytes; /* bytes of the container written to d_out        */
+    uint64_t payload_bits;    /* summed field bits (initial states and padding excluded) */
+} sh_encode_info;
+
+/* Library version (major << 16 | minor). */
+uint32_t sh_version(void);
+
+/* Static text for a status code. */
+const char* sh_status_string(sh_status st);
+
+/*
+ * Histogram of n int8 values on the GPU (paper section 4.1: h[u] over [0, 255]).
+ * d_x: device, n bytes.  d_hist: device, 256 uint64, overwritten (not accumulated).
+ * Asynchronous on stream.
+ */
+sh_status sh_histogram(const int8_t* d_x, uint64_t n, uint64_t* d_hist, void* stream);
+
+/*
+ * The offline table build from a histogram, on the host (paper section 4.1): the
+ * exactly-K-range DP split minimising the summed range-id and offset cost, then the
+ * allocation of the L tANS states minimising D_KL(P || Q).  hist: host, 256 uint64 with
+ * a total below 2^32.  Supports 1 <= K <= 256 and 1 <= log2_L <= 12.  Returns
+ * SH_ERR_UNSUPPORTED when more ranges hold values than there are states.
+ */
+sh_status sh_table_from_histogram(const uint64_t* hist, const sh_params* params, sh_table* out);
+
+/*
+ * sh_histogram + sh_table_from_histogram.  x is device memory when x_on_device != 0
+ * (then d_ws must hold sh_build_tables_workspace() bytes and the call waits for the
+ * stream), else host memory (counted on the host; d_ws and stream unused).
+ */
+uint64_t sh_build_tables_workspace(void);
+sh_status sh_build_tables(const int8_t* x, uint64_t n, int x_on_device, const sh_params* params,
+                          void* d_ws, uint64_t ws_bytes, void* stream, sh_table* out);
+
+/* Largest container sh_encode can produce for n values (every field at its maximum
+ * length of 8 + log2_L bits), and the device workspace sh_encode needs.  0 on bad
+ * parameters. */
+uint64_t sh_encode_bound(uint64_t n, const sh_params* params);
+uint64_t sh_encode_workspace(uint64_t n, const sh_params* params);
+
+/*
+ * Encode n int8 values (paper section 4.2, Algorithm 2) into a container.
+ * d_x: device, n bytes.  d_out: device, out_cap >= sh_encode_bound(n, params) bytes.
+ * d_ws: device workspace of ws_bytes >= sh_encode_workspace(n, params).
+ * d_info: device sh_encode_info or NULL.  d_status: device int32 or NULL.
+ * table->K and table->log2_L must equal params->K and params->log2_L.
+ * A value in a range with f = 0 sets *d_status = SH_ERR_SYMBOL_NOT_IN_TABLE and the
+ * container is then unusable.  Asynchronous on stream.
+ */
+sh_status sh_encode(const sh_table* table, const sh_params* params, const int8_t* d_x,
+                    uint64_t n, uint8_t* d_out, uint64_t out_cap, void* d_ws, uint64_t ws_bytes,
+                    sh_encode_info* d_info, int32_t* d_status, void* stream);
+
+/*
+ * Decode a container of in_nbytes bytes (d_in, device) into n int8 values (d_y, device).
+ * The container must have been written with this table and these params; its header is
+ * checked on the GPU.  Any inconsistency -- header, chunk index, an offset outside its
+ * range, a lane not ending in slot 0, bits past a chunk's end or non-zero padding -- sets
+ * *d_status = SH_ERR_CORRUPT_STREAM (d_status may be NULL to skip reporting); d_y is
+ * then unspecified, but no access leaves d_in[0, in_nbytes) or d_y[0, n).
+ * Asynchronous on stream.
+ */
+sh_status sh_decode(const sh_table* table, const sh_params* params, const uint8_t* d_in,
+                    uint64_t in_nbytes, int8_t* d_y, uint64_t n, int32_t* d_status,
+                    void* stream);
+
+/*
+ * Theorem-1 terms of a table and the measured rates of a container of n values, on the
+ * host (paper section 4; %diff as in section 5).  The entropy terms use table->hist;
+ * payload_bits and container_bytes come from sh_encode_info (pass n = 0 to get the table
+ * terms only).
+ */
+sh_status sh_stats(const sh_table* table, uint64_t n, uint64_t payload_bits,
+                   uint64_t container_bytes, sh_stats_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
