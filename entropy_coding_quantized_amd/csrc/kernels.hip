@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const DecodeArgs a) {
 
     const rsrc_t rin = make_rsrc(a.in, (uint32_t)a.in_nbytes);
     if (wid == 0) {
-        // header and index ends: the container must belong to this table and size
+        // header and index ends: the container must belong to this table and fit in_nbytes
         bool bad = false;
         for (uint32_t i = lane; i < a.hdr_dwords; i += 64)
             bad |= __builtin_amdgcn_raw_buffer_load_b32(rin, (int)(4 * i), 0, 0) != a.hdr[i];
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const DecodeArgs a) {
             const uint32_t first = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)a.index_at, 0, 0);
             const uint32_t last = __builtin_amdgcn_raw_buffer_load_b32(
                 rin, (int)(a.index_at + 4 * a.n_chunks), 0, 0);
-            bad |= first != 0 || (uint64_t)a.payload_at + last != a.in_nbytes;
+            bad |= first != 0 || (uint64_t)a.payload_at + last > a.in_nbytes;
         }
         if (bad) report(a.status, SH_ERR_CORRUPT_STREAM);
     }

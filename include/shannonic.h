@@ -158,10 +158,13 @@ sh_status sh_encode(const sh_table* table, const sh_params* params, const int8_t
                     sh_encode_info* d_info, int32_t* d_status, void* stream);
 
 /*
- * Decode a container of in_nbytes bytes (d_in, device) into n int8 values (d_y, device).
- * The container must have been written with this table and these params; its header is
- * checked on the GPU.  Any inconsistency -- header, chunk index, an offset outside its
- * range, a lane not ending in slot 0, bits past a chunk's end or non-zero padding -- sets
+ * Decode the container at d_in (device) into n int8 values (d_y, device).  in_nbytes is
+ * the number of readable bytes at d_in: at least the container's size (its chunk index
+ * marks its end), so the output buffer of sh_encode can be passed with its capacity and
+ * no host round trip.  The container must have been written with this table and these
+ * params; its header is checked on the GPU.  Any inconsistency -- header, chunk index, an offset outside its
+ * range, a lane not ending in slot 0, bits past a chunk's end or non-zero padding, a
+ * container end past in_nbytes -- sets
  * *d_status = SH_ERR_CORRUPT_STREAM (d_status may be NULL to skip reporting); d_y is
  * then unspecified, but no access leaves d_in[0, in_nbytes) or d_y[0, n).
  * Asynchronous on stream.
