@@ -82,6 +82,21 @@ _EXPORTS = {
                               C.c_void_p, C.c_uint64, C.c_void_p, C.c_void_p]),
     "sh_stats": (C.c_int32, [C.POINTER(sh_table), C.c_uint64, C.c_uint64, C.c_uint64,
                              C.POINTER(sh_stats_t)]),
+    "sh_device_table_bytes": (C.c_uint64, []),
+    "sh_table_to_device": (C.c_int32, [C.POINTER(sh_table), C.POINTER(sh_params), C.c_void_p,
+                                       C.c_void_p]),
+    "sh_tables_from_device": (C.c_int32, [C.c_void_p, C.c_uint32, C.c_void_p, C.c_void_p,
+                                          C.c_void_p]),
+    "sh_build_tables_batch_workspace": (C.c_uint64, [C.c_uint32]),
+    "sh_build_tables_batch": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_uint32,
+                                          C.POINTER(sh_params), C.c_void_p, C.c_void_p,
+                                          C.c_uint64, C.c_void_p]),
+    "sh_encode_batch_workspace": (C.c_uint64, [C.c_void_p, C.c_uint32, C.POINTER(sh_params)]),
+    "sh_encode_batch": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_uint32,
+                                    C.POINTER(sh_params), C.c_void_p, C.c_void_p, C.c_void_p,
+                                    C.c_uint64, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "sh_decode_batch": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                    C.c_uint32, C.POINTER(sh_params), C.c_void_p, C.c_void_p]),
 }
 
 
@@ -213,6 +228,78 @@ def sh_stats(table: sh_table, n: int = 0, payload_bits: int = 0, container_bytes
     return {f: getattr(out, f) for f in STAT_FIELDS}
 
 
+def _ptrs(items) -> C.Array:
+    if isinstance(items, C.Array):
+        return items
+    return (C.c_void_p * max(len(items), 1))(*[_ptr(t) for t in items])
+
+
+def _u64s(values) -> C.Array:
+    if isinstance(values, C.Array):
+        return values
+    return (C.c_uint64 * max(len(values), 1))(*[int(v) for v in values])
+
+
+def sh_device_table_bytes() -> int:
+    return int(lib().sh_device_table_bytes())
+
+
+def sh_table_to_device(table: sh_table, params: Params, d_table, stream=None) -> None:
+    p = params.c()
+    _check(lib().sh_table_to_device(C.byref(table), C.byref(p), _ptr(d_table), _stream(stream)),
+           "sh_table_to_device")
+
+
+def sh_tables_from_device(d_tables, count: int, stream=None):
+    """([sh_table] * count, [build status] * count) of device tables."""
+    out = (sh_table * max(count, 1))()
+    st = (C.c_int32 * max(count, 1))()
+    _check(lib().sh_tables_from_device(_ptr(d_tables), count, out, st, _stream(stream)),
+           "sh_tables_from_device")
+    return [out[i] for i in range(count)], [int(st[i]) for i in range(count)]
+
+
+def table_from_device(d_table, stream=None) -> sh_table:
+    """One device table; raises with the status its build recorded, if any."""
+    (t,), (st,) = sh_tables_from_device(d_table, 1, stream)
+    _check(st, "device table")
+    return t
+
+
+def sh_build_tables_batch_workspace(nseg: int) -> int:
+    return int(lib().sh_build_tables_batch_workspace(nseg))
+
+
+def sh_build_tables_batch(d_x: list, n: list, params: Params, d_tables, d_ws, ws_bytes: int,
+                          stream=None) -> None:
+    p = params.c()
+    st = lib().sh_build_tables_batch(_ptrs(d_x), _u64s(n), len(n), C.byref(p), _ptr(d_tables),
+                                     _ptr(d_ws), ws_bytes, _stream(stream))
+    _check(st, "sh_build_tables_batch")
+
+
+def sh_encode_batch_workspace(n: list, params: Params) -> int:
+    p = params.c()
+    return int(lib().sh_encode_batch_workspace(_u64s(n), len(n), C.byref(p)))
+
+
+def sh_encode_batch(d_tables, d_x: list, n: list, params: Params, d_out: list, out_cap: list,
+                    d_ws, ws_bytes: int, d_info=None, d_status=None, stream=None) -> None:
+    p = params.c()
+    st = lib().sh_encode_batch(_ptr(d_tables), _ptrs(d_x), _u64s(n), len(n), C.byref(p),
+                               _ptrs(d_out), _u64s(out_cap), _ptr(d_ws), ws_bytes, _ptr(d_info),
+                               _ptr(d_status), _stream(stream))
+    _check(st, "sh_encode_batch")
+
+
+def sh_decode_batch(d_tables, d_in: list, in_nbytes: list, d_y: list, n: list, params: Params,
+                    d_status=None, stream=None) -> None:
+    p = params.c()
+    st = lib().sh_decode_batch(_ptr(d_tables), _ptrs(d_in), _u64s(in_nbytes), _ptrs(d_y),
+                               _u64s(n), len(n), C.byref(p), _ptr(d_status), _stream(stream))
+    _check(st, "sh_decode_batch")
+
+
 def raw_status(fn_name: str, *args) -> int:
     """Call a C entry point and return its status without raising (for tests)."""
     return int(getattr(lib(), fn_name)(*args))
@@ -252,3 +339,74 @@ def decode_tensor(container, n: int, table: sh_table, params: Params, stream=Non
     status = torch.zeros(1, dtype=torch.int32, device=container.device)
     sh_decode(table, params, container, container.numel(), y, n, status, stream)
     return y[:n], status
+
+
+# ---- batches of tensors with device tables --------------------------------------------
+
+def _round_up(v: int, a: int) -> int:
+    return (v + a - 1) // a * a
+
+
+def build_tables_tensors(xs: list, params: Params, stream=None):
+    """Device tables (one uint8 tensor, table i at i * sh_device_table_bytes()) for a list
+    of device int8 tensors, built on the GPU."""
+    import torch
+    dev = xs[0].device
+    xs = [x.contiguous().view(-1) for x in xs]
+    tables = torch.empty(len(xs) * sh_device_table_bytes(), dtype=torch.uint8, device=dev)
+    wsb = sh_build_tables_batch_workspace(len(xs))
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    sh_build_tables_batch(xs, [x.numel() for x in xs], params, tables, ws, wsb, stream)
+    return tables, ws
+
+
+def tables_to_device(tables: list, params: Params, device, stream=None):
+    """Upload host tables back to back into one device tensor."""
+    import torch
+    tb = sh_device_table_bytes()
+    d = torch.empty(len(tables) * tb, dtype=torch.uint8, device=device)
+    for i, t in enumerate(tables):
+        sh_table_to_device(t, params, d[i * tb:], stream)
+    return d
+
+
+def encode_tensors(d_tables, xs: list, params: Params, stream=None):
+    """Encode a list of device int8 tensors with their device tables.  Returns
+    (buffer, offsets, caps, info (nseg x 2 int64, device), status (device)); container i
+    starts at buffer[offsets[i]]."""
+    import torch
+    dev = xs[0].device
+    xs = [x.contiguous().view(-1) for x in xs]
+    ns = [x.numel() for x in xs]
+    caps = [max(sh_encode_bound(n, params), 4) for n in ns]
+    offs, at = [], 0
+    for c in caps:
+        offs.append(at)
+        at += _round_up(c, 256)
+    buf = torch.empty(max(at, 256), dtype=torch.uint8, device=dev)
+    wsb = sh_encode_batch_workspace(ns, params)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    info = torch.zeros((len(xs), 2), dtype=torch.int64, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    base = buf.data_ptr()
+    sh_encode_batch(d_tables, xs, ns, params, [base + o for o in offs], caps, ws, wsb, info,
+                    status, stream)
+    return buf, offs, caps, info, status
+
+
+def decode_tensors(d_tables, buf, offs: list, in_nbytes: list, ns: list, params: Params,
+                   stream=None):
+    """Decode containers buf[offs[i]:] (in_nbytes[i] readable bytes) into one int8 tensor
+    holding every output back to back (16-byte aligned starts).  Returns (y, starts,
+    status on device)."""
+    import torch
+    starts, at = [], 0
+    for n in ns:
+        starts.append(at)
+        at += _round_up(n, 256)
+    y = torch.empty(max(at, 256), dtype=torch.int8, device=buf.device)
+    status = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    base, ybase = buf.data_ptr(), y.data_ptr()
+    sh_decode_batch(d_tables, [base + o for o in offs], in_nbytes, [ybase + s for s in starts],
+                    ns, params, status, stream)
+    return y, starts, status

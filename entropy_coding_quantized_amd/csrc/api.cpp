@@ -1,7 +1,8 @@
 // C ABI of libshannonic.so (declared in include/shannonic.h): argument checks, table
-// derivation for the kernels, workspace layout and launches.
+// derivation for the kernels, workspace layout, segment grouping and launches.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -16,15 +17,25 @@ using namespace shn;
 
 namespace {
 
+constexpr uint32_t kChunksPerBlock = 8;   // decode and encode chunk kernels
+constexpr uint32_t kChunksPerBlockC = 4;  // compaction kernel
+
 bool gpu_params_ok(const sh_params* p) {
     return p && p->K >= 1 && p->K <= 256 && p->log2_L >= 1 && p->log2_L <= (uint32_t)kMaxLog2LGpu &&
            p->streams == (uint32_t)kLanes && p->chunk_symbols >= 32 &&
            p->chunk_symbols <= kMaxChunk && p->chunk_symbols % 32 == 0;
 }
 
+// INVALID_ARG for nonsense, UNSUPPORTED for valid parameters the GPU path does not take
+sh_status check_params(const sh_params* p) {
+    if (!p || p->K < 1 || p->K > 256 || p->log2_L < 1 || p->chunk_symbols == 0 || p->streams == 0)
+        return SH_ERR_INVALID_ARG;
+    return gpu_params_ok(p) ? SH_OK : SH_ERR_UNSUPPORTED;
+}
+
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-// container bytes at most, or 0 when the parameters are unusable
+// container bytes at most
 uint64_t bound_of(uint64_t n, const sh_params* p) {
     const uint64_t nch = n_chunks_of(n, p->chunk_symbols);
     uint64_t total = header_bytes(p->K) + 4 * (nch + 1);
@@ -36,27 +47,59 @@ uint64_t bound_of(uint64_t n, const sh_params* p) {
     return total;
 }
 
+uint32_t blocks_for(uint64_t nch, uint32_t per) { return (uint32_t)((nch + per - 1) / per); }
+
+// slots a segment takes in the encode workspace: its chunks rounded up to pairs
+uint64_t slots_for(uint64_t nch) { return (nch + 1) / 2 * 2; }
+
+uint64_t align256(uint64_t v) { return (v + 255) / 256 * 256; }
+
+// encode workspace for a group of segments: slots, then per-slot meta
 struct EncLayout {
-    uint64_t slots_at, meta_at, bytes;
+    uint64_t meta_at, bytes;
     uint32_t slot_dwords;
 };
-
-EncLayout enc_layout(uint64_t n, const sh_params* p) {
+EncLayout enc_layout(uint64_t total_slots, const sh_params* p) {
     EncLayout l;
-    const uint64_t nch = n_chunks_of(n, p->chunk_symbols);
-    const uint64_t pairs = (nch + 1) / 2;
     l.slot_dwords = encode_slot_dwords(p->chunk_symbols, p->log2_L);
-    l.slots_at = 0;
-    l.meta_at = (2 * pairs * l.slot_dwords * 4 + 255) / 256 * 256;
-    l.bytes = l.meta_at + (8 * nch + 255) / 256 * 256 + 256;
+    l.meta_at = align256(total_slots * l.slot_dwords * 4);
+    l.bytes = l.meta_at + align256(8 * total_slots) + 256;
     return l;
 }
+
+// groups of at most kMaxInlineSegs segments: [begin, end)
+std::vector<std::pair<uint32_t, uint32_t>> groups_of(uint32_t nseg) {
+    std::vector<std::pair<uint32_t, uint32_t>> g;
+    for (uint32_t b = 0; b < nseg; b += kMaxInlineSegs) g.push_back({b, std::min(nseg, b + kMaxInlineSegs)});
+    return g;
+}
+
+uint64_t encode_batch_ws(const uint64_t* n, uint32_t nseg, const sh_params* p) {
+    uint64_t best = 256;
+    for (auto [b, e] : groups_of(nseg)) {
+        uint64_t slots = 0;
+        for (uint32_t i = b; i < e; ++i) slots += slots_for(n_chunks_of(n[i], p->chunk_symbols));
+        best = std::max(best, enc_layout(slots, p).bytes);
+    }
+    return best;
+}
+
+void fill_codec_common(CodecArgs& a, const sh_params* p, int32_t* d_status) {
+    a.C = p->chunk_symbols;
+    a.R = p->log2_L;
+    a.L = 1u << p->log2_L;
+    a.K = p->K;
+    a.slot_dwords = encode_slot_dwords(p->chunk_symbols, p->log2_L);
+    a.status = d_status;
+}
+
+sh_status hip_ok(hipError_t e) { return e == hipSuccess ? SH_OK : SH_ERR_HIP; }
 
 }  // namespace
 
 extern "C" {
 
-uint32_t sh_version(void) { return (1u << 16) | 0u; }
+uint32_t sh_version(void) { return (1u << 16) | 1u; }
 
 const char* sh_status_string(sh_status st) {
     switch (st) {
@@ -74,7 +117,14 @@ const char* sh_status_string(sh_status st) {
 sh_status sh_histogram(const int8_t* d_x, uint64_t n, uint64_t* d_hist, void* stream) {
     if (!d_hist || (n > 0 && !d_x)) return SH_ERR_INVALID_ARG;
     if (!aligned(d_x, 16) || !aligned(d_hist, 8)) return SH_ERR_INVALID_ARG;
-    return launch_histogram(d_x, n, d_hist, stream);
+    HistArgs h;
+    std::memset(&h, 0, sizeof(h));
+    h.nseg = 1;
+    h.hist = d_hist;
+    h.segs[0].x = (uint8_t*)d_x;
+    h.segs[0].n = n;
+    h.n_blocks = (uint32_t)((n + (1u << 18) - 1) >> 18);
+    return launch_histogram(h, 1, stream);
 }
 
 sh_status sh_table_from_histogram(const uint64_t* hist, const sh_params* params, sh_table* out) {
@@ -103,6 +153,111 @@ sh_status sh_build_tables(const int8_t* x, uint64_t n, int x_on_device, const sh
     return table_from_histogram(h, params->K, params->log2_L, out);
 }
 
+// ---- device-resident tables ------------------------------------------------------------
+
+uint64_t sh_device_table_bytes(void) { return kDTBytes; }
+
+sh_status sh_table_to_device(const sh_table* table, const sh_params* params, void* d_table,
+                             void* stream) {
+    if (!table || !d_table || !aligned(d_table, 16)) return SH_ERR_INVALID_ARG;
+    sh_status st = check_params(params);
+    if (st != SH_OK) return st;
+    if (table->K != params->K || table->log2_L != params->log2_L) return SH_ERR_INVALID_ARG;
+    const bool empty = table->n == 0;
+    if (check_table(*table, empty) != SH_OK) return SH_ERR_INVALID_ARG;
+    std::vector<uint32_t> dt(kDTDwords, 0);
+    SlotTables slots;
+    if (!empty && derive_slots(*table, &slots) != SH_OK) return SH_ERR_INVALID_ARG;
+    make_device_table(*table, empty ? nullptr : &slots, params->chunk_symbols, params->streams,
+                      dt.data());
+    hipStream_t s = (hipStream_t)stream;
+    if (hipMemcpyAsync(d_table, dt.data(), kDTBytes, hipMemcpyHostToDevice, s) != hipSuccess)
+        return SH_ERR_HIP;
+    return hip_ok(hipStreamSynchronize(s));
+}
+
+sh_status sh_tables_from_device(const void* d_tables, uint32_t count, sh_table* out,
+                                int32_t* table_status, void* stream) {
+    if (count == 0) return SH_OK;
+    if (!d_tables || !out || !table_status) return SH_ERR_INVALID_ARG;
+    std::vector<uint32_t> dt((size_t)kDTDwords * count, 0);
+    hipStream_t s = (hipStream_t)stream;
+    if (hipMemcpyAsync(dt.data(), d_tables, (size_t)kDTBytes * count, hipMemcpyDeviceToHost, s) !=
+            hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return SH_ERR_HIP;
+    for (uint32_t i = 0; i < count; ++i) {
+        const uint32_t* d = dt.data() + (size_t)kDTDwords * i;
+        sh_table t;
+        std::memset(&t, 0, sizeof(t));
+        t.K = d[kDTK];
+        t.log2_L = d[kDTLog2L];
+        std::memcpy(&t.n, d + kDTN, 8);
+        std::memcpy(t.lo, d + kDTLo, sizeof(t.lo));
+        std::memcpy(t.freq, d + kDTFreq, sizeof(t.freq));
+        std::memcpy(t.hist, d + kDTHist, sizeof(t.hist));
+        table_status[i] = (int32_t)d[kDTStatus];
+        if (table_status[i] == SH_OK && check_table(t, t.n == 0) != SH_OK)
+            table_status[i] = SH_ERR_CORRUPT_STREAM;
+        out[i] = t;
+    }
+    return SH_OK;
+}
+
+uint64_t sh_build_tables_batch_workspace(uint32_t nseg) {
+    return align256(8ull * 256 * nseg) + align256(8ull * kCostEntries * nseg) +
+           align256(2ull * 257 * 257 * nseg);
+}
+
+sh_status sh_build_tables_batch(const int8_t* const* d_x, const uint64_t* n, uint32_t nseg,
+                                const sh_params* params, void* d_tables, void* d_ws,
+                                uint64_t ws_bytes, void* stream) {
+    if (nseg == 0) return SH_OK;
+    if (!d_x || !n || !d_tables || !d_ws || !aligned(d_tables, 16) || !aligned(d_ws, 256))
+        return SH_ERR_INVALID_ARG;
+    sh_status st = check_params(params);
+    if (st != SH_OK) return st;
+    if (ws_bytes < sh_build_tables_batch_workspace(nseg)) return SH_ERR_BUFFER_TOO_SMALL;
+    for (uint32_t i = 0; i < nseg; ++i) {
+        if (n[i] > 0 && (!d_x[i] || !aligned(d_x[i], 16))) return SH_ERR_INVALID_ARG;
+        if (n[i] >= (1ull << 32)) return SH_ERR_UNSUPPORTED;
+    }
+    uint8_t* ws = (uint8_t*)d_ws;
+    uint64_t* hist = (uint64_t*)ws;
+    uint64_t* cost = (uint64_t*)(ws + align256(8ull * 256 * nseg));
+    uint16_t* arg = (uint16_t*)(ws + align256(8ull * 256 * nseg) + align256(8ull * kCostEntries * nseg));
+    for (auto [b, e] : groups_of(nseg)) {
+        HistArgs h;
+        std::memset(&h, 0, sizeof(h));
+        h.nseg = e - b;
+        h.hist = hist + 256ull * b;
+        uint32_t blocks = 0;
+        for (uint32_t i = b; i < e; ++i) {
+            SegDesc& sd = h.segs[i - b];
+            sd.x = (uint8_t*)d_x[i];
+            sd.n = n[i];
+            sd.first_block = blocks;
+            blocks += (uint32_t)((n[i] + (1u << 18) - 1) >> 18);
+        }
+        h.n_blocks = blocks;
+        st = launch_histogram(h, e - b, stream);
+        if (st != SH_OK) return st;
+    }
+    BuildArgs bd;
+    bd.hist = hist;
+    bd.tables = (uint32_t*)d_tables;
+    bd.cost = cost;
+    bd.arg = arg;
+    bd.nseg = nseg;
+    bd.K = params->K;
+    bd.R = params->log2_L;
+    bd.C = params->chunk_symbols;
+    bd.S = params->streams;
+    return launch_build_tables(bd, stream);
+}
+
+// ---- encode / decode -------------------------------------------------------------------
+
 uint64_t sh_encode_bound(uint64_t n, const sh_params* params) {
     if (!gpu_params_ok(params)) return 0;
     return bound_of(n, params);
@@ -110,132 +265,177 @@ uint64_t sh_encode_bound(uint64_t n, const sh_params* params) {
 
 uint64_t sh_encode_workspace(uint64_t n, const sh_params* params) {
     if (!gpu_params_ok(params)) return 0;
-    return enc_layout(n, params).bytes;
+    return encode_batch_ws(&n, 1, params);
 }
 
 sh_status sh_encode(const sh_table* table, const sh_params* params, const int8_t* d_x,
                     uint64_t n, uint8_t* d_out, uint64_t out_cap, void* d_ws, uint64_t ws_bytes,
                     sh_encode_info* d_info, int32_t* d_status, void* stream) {
-    if (!table || !params || !d_out || (n > 0 && !d_x)) return SH_ERR_INVALID_ARG;
-    if (params->K < 1 || params->K > 256 || params->log2_L < 1) return SH_ERR_INVALID_ARG;
-    if (!gpu_params_ok(params)) return SH_ERR_UNSUPPORTED;
+    if (!table || !d_out || (n > 0 && !d_x)) return SH_ERR_INVALID_ARG;
+    sh_status st = check_params(params);
+    if (st != SH_OK) return st;
     if (table->K != params->K || table->log2_L != params->log2_L) return SH_ERR_INVALID_ARG;
     if (check_table(*table, n == 0) != SH_OK) return SH_ERR_INVALID_ARG;
     if (n >= (1ull << 32)) return SH_ERR_UNSUPPORTED;
     const uint64_t bound = bound_of(n, params);
     if (bound > 0xFFFFFFFFull) return SH_ERR_UNSUPPORTED;
     if (out_cap < bound) return SH_ERR_BUFFER_TOO_SMALL;
-    const EncLayout lay = enc_layout(n, params);
+    const uint64_t nch = n_chunks_of(n, params->chunk_symbols);
+    const EncLayout lay = enc_layout(slots_for(nch), params);
     if (!d_ws || ws_bytes < lay.bytes) return SH_ERR_BUFFER_TOO_SMALL;
     if (!aligned(d_x, 16) || !aligned(d_out, 4) || !aligned(d_ws, 256) ||
         !aligned(d_info, 8) || !aligned(d_status, 4))
         return SH_ERR_INVALID_ARG;
 
-    const uint32_t C = params->chunk_symbols, R = params->log2_L, L = 1u << R, K = params->K;
-    const uint64_t nch = n_chunks_of(n, C);
-    const uint32_t index_at = header_bytes(K);
-
-    EncodeArgs e;
-    std::memset(&e, 0, sizeof(e));
+    CodecArgs a;
+    std::memset(&a, 0, sizeof(a));
+    fill_codec_common(a, params, d_status);
+    a.nseg = 0;
+    a.slots = (uint32_t*)d_ws;
+    a.meta = (uint32_t*)((uint8_t*)d_ws + lay.meta_at);
     if (n > 0) {
-        SlotTables st;
-        if (derive_slots(*table, &st) != SH_OK) return SH_ERR_INVALID_ARG;
-        // value entries: bias_s, and o | w << 8 | (start_s + 512) << 16 | (f_s == 0) << 31
-        for (uint32_t s = 0; s < K; ++s) {
-            const uint32_t f = table->freq[s];
-            const uint32_t width = table->lo[s + 1] - table->lo[s];
-            const uint32_t w = ceil_log2_u32(width);
-            int32_t bias = 0, start = -(int32_t)L;
-            if (f > 0) {
-                const uint32_t m = floor_log2_u32(f);
-                bias = (int32_t)((R - m) << (R + 1)) - (int32_t)(f << (R - m));
-                start = (int32_t)st.cum[s] - (int32_t)f;
-            }
-            for (uint32_t u = table->lo[s]; u < table->lo[s + 1]; ++u) {
-                e.vt[2 * u] = (uint32_t)bias;
-                e.vt[2 * u + 1] = (u - table->lo[s]) | (w << 8) | ((uint32_t)(start + 512) << 16) |
-                                  (f == 0 ? 0x80000000u : 0u);
-            }
-        }
-        for (uint32_t i = 0; i < L; ++i) e.es[i] = (uint8_t)st.enc[i];
+        SlotTables slots;
+        if (derive_slots(*table, &slots) != SH_OK) return SH_ERR_INVALID_ARG;
+        derive_kernel_tables(*table, slots, nullptr, a.one.tab, a.one.es);
     }
-    e.x = d_x;
-    e.slots = (uint32_t*)((uint8_t*)d_ws + lay.slots_at);
-    e.meta = (uint32_t*)((uint8_t*)d_ws + lay.meta_at);
-    e.status = d_status;
-    e.n = n;
-    e.C = C;
-    e.R = R;
-    e.L = L;
-    e.n_chunks = (uint32_t)nch;
-    e.slot_dwords = lay.slot_dwords;
-
-    IndexArgs ix;
-    std::memset(&ix, 0, sizeof(ix));
-    ix.meta = e.meta;
-    ix.out = d_out;
-    ix.info = d_info;
-    ix.n = n;
-    ix.n_chunks = (uint32_t)nch;
-    ix.slot_dwords = lay.slot_dwords;
-    ix.index_at = index_at;
-    ix.hdr_dwords = index_at / 4;
-    write_header(*table, n, C, (uint32_t)kLanes, nch, ix.hdr);
-
-    CompactArgs cp;
-    cp.slots = e.slots;
-    cp.meta = e.meta;
-    cp.out = d_out;
-    cp.n_chunks = (uint32_t)nch;
-    cp.slot_dwords = lay.slot_dwords;
-    cp.index_at = index_at;
-    cp.payload_at = index_at + 4 * (uint32_t)(nch + 1);
-    return launch_encode(e, ix, cp, stream);
+    write_header(*table, n, params->chunk_symbols, (uint32_t)kLanes, nch, a.one.hdr);
+    SegDesc& sd = a.one.seg;
+    sd.x = (uint8_t*)d_x;
+    sd.c = d_out;
+    sd.n = n;
+    sd.c_bytes = out_cap;
+    sd.info = d_info;
+    sd.n_chunks = (uint32_t)nch;
+    return launch_encode(a, blocks_for(nch, kChunksPerBlock), blocks_for(nch, kChunksPerBlockC),
+                         stream);
 }
 
 sh_status sh_decode(const sh_table* table, const sh_params* params, const uint8_t* d_in,
                     uint64_t in_nbytes, int8_t* d_y, uint64_t n, int32_t* d_status,
                     void* stream) {
-    if (!table || !params || !d_in || (n > 0 && !d_y)) return SH_ERR_INVALID_ARG;
-    if (params->K < 1 || params->K > 256 || params->log2_L < 1) return SH_ERR_INVALID_ARG;
-    if (!gpu_params_ok(params)) return SH_ERR_UNSUPPORTED;
+    if (!table || !d_in || (n > 0 && !d_y)) return SH_ERR_INVALID_ARG;
+    sh_status st = check_params(params);
+    if (st != SH_OK) return st;
     if (table->K != params->K || table->log2_L != params->log2_L) return SH_ERR_INVALID_ARG;
     if (check_table(*table, n == 0) != SH_OK) return SH_ERR_INVALID_ARG;
     if (n >= (1ull << 32) || in_nbytes > 0xFFFFFFFFull) return SH_ERR_UNSUPPORTED;
     if (!aligned(d_in, 4) || !aligned(d_status, 4)) return SH_ERR_INVALID_ARG;
-
-    const uint32_t C = params->chunk_symbols, R = params->log2_L, L = 1u << R, K = params->K;
-    const uint64_t nch = n_chunks_of(n, C);
-    const uint32_t index_at = header_bytes(K);
-    const uint64_t payload_at = index_at + 4 * (nch + 1);
+    const uint64_t nch = n_chunks_of(n, params->chunk_symbols);
+    const uint64_t payload_at = header_bytes(params->K) + 4 * (nch + 1);
     if (in_nbytes < payload_at) return SH_ERR_CORRUPT_STREAM;
     if (n == 0) return SH_OK;
 
-    SlotTables st;
-    if (derive_slots(*table, &st) != SH_OK) return SH_ERR_INVALID_ARG;
-    DecodeArgs a;
+    CodecArgs a;
     std::memset(&a, 0, sizeof(a));
-    for (uint32_t i = 0; i < L; ++i) {
-        const uint32_t s = st.range[i];
-        const uint32_t width = table->lo[s + 1] - table->lo[s];
-        const uint32_t w = ceil_log2_u32(width);
-        a.dec[2 * i] = (w + st.nb[i]) | ((uint32_t)st.next[i] * 8u << 16);
-        a.dec[2 * i + 1] = w | (((uint32_t)(table->lo[s] - 128) & 0xFFu) << 8) | ((width - 1) << 16);
+    fill_codec_common(a, params, d_status);
+    a.nseg = 0;
+    SlotTables slots;
+    if (derive_slots(*table, &slots) != SH_OK) return SH_ERR_INVALID_ARG;
+    derive_kernel_tables(*table, slots, a.one.tab, nullptr, nullptr);
+    write_header(*table, n, params->chunk_symbols, (uint32_t)kLanes, nch, a.one.hdr);
+    SegDesc& sd = a.one.seg;
+    sd.x = (uint8_t*)d_y;
+    sd.c = (uint8_t*)d_in;
+    sd.n = n;
+    sd.c_bytes = in_nbytes;
+    sd.n_chunks = (uint32_t)nch;
+    return launch_decode(a, blocks_for(nch, kChunksPerBlock), stream);
+}
+
+uint64_t sh_encode_batch_workspace(const uint64_t* n, uint32_t nseg, const sh_params* params) {
+    if (!n || !gpu_params_ok(params)) return 0;
+    return encode_batch_ws(n, nseg, params);
+}
+
+sh_status sh_encode_batch(const void* d_tables, const int8_t* const* d_x, const uint64_t* n,
+                          uint32_t nseg, const sh_params* params, uint8_t* const* d_out,
+                          const uint64_t* out_cap, void* d_ws, uint64_t ws_bytes,
+                          sh_encode_info* d_info, int32_t* d_status, void* stream) {
+    if (nseg == 0) return SH_OK;
+    if (!d_tables || !d_x || !n || !d_out || !out_cap || !aligned(d_tables, 16))
+        return SH_ERR_INVALID_ARG;
+    sh_status st = check_params(params);
+    if (st != SH_OK) return st;
+    if (!d_ws || !aligned(d_ws, 256) || ws_bytes < encode_batch_ws(n, nseg, params))
+        return SH_ERR_BUFFER_TOO_SMALL;
+    if (!aligned(d_info, 8) || !aligned(d_status, 4)) return SH_ERR_INVALID_ARG;
+    for (uint32_t i = 0; i < nseg; ++i) {
+        if (!d_out[i] || !aligned(d_out[i], 4) || (n[i] > 0 && (!d_x[i] || !aligned(d_x[i], 16))))
+            return SH_ERR_INVALID_ARG;
+        if (n[i] >= (1ull << 32) || bound_of(n[i], params) > 0xFFFFFFFFull) return SH_ERR_UNSUPPORTED;
+        if (out_cap[i] < bound_of(n[i], params)) return SH_ERR_BUFFER_TOO_SMALL;
     }
-    write_header(*table, n, C, (uint32_t)kLanes, nch, a.hdr);
-    a.hdr_dwords = index_at / 4;
-    a.in = d_in;
-    a.out = d_y;
-    a.status = d_status;
-    a.in_nbytes = in_nbytes;
-    a.n = n;
-    a.payload_at = (uint32_t)payload_at;
-    a.index_at = index_at;
-    a.C = C;
-    a.R = R;
-    a.L = L;
-    a.n_chunks = (uint32_t)nch;
-    return launch_decode(a, stream);
+    for (auto [b, e] : groups_of(nseg)) {
+        CodecArgs a;
+        std::memset(&a, 0, sizeof(a));
+        fill_codec_common(a, params, d_status);
+        a.nseg = e - b;
+        uint64_t slots = 0;
+        uint32_t blocks = 0, blocks_c = 0;
+        for (uint32_t i = b; i < e; ++i) {
+            SegDesc& sd = a.many[i - b];
+            const uint64_t nch = n_chunks_of(n[i], params->chunk_symbols);
+            sd.x = (uint8_t*)d_x[i];
+            sd.c = d_out[i];
+            sd.n = n[i];
+            sd.c_bytes = out_cap[i];
+            sd.tab = (const uint32_t*)((const uint8_t*)d_tables + (uint64_t)i * kDTBytes);
+            sd.info = d_info ? d_info + i : nullptr;
+            sd.first_block = blocks;
+            sd.first_block_c = blocks_c;
+            sd.n_chunks = (uint32_t)nch;
+            sd.slot_base = (uint32_t)slots;
+            blocks += blocks_for(nch, kChunksPerBlock);
+            blocks_c += blocks_for(nch, kChunksPerBlockC);
+            slots += slots_for(nch);
+        }
+        const EncLayout lay = enc_layout(slots, params);
+        a.slots = (uint32_t*)d_ws;
+        a.meta = (uint32_t*)((uint8_t*)d_ws + lay.meta_at);
+        st = launch_encode(a, blocks, blocks_c, stream);
+        if (st != SH_OK) return st;
+    }
+    return SH_OK;
+}
+
+sh_status sh_decode_batch(const void* d_tables, const uint8_t* const* d_in,
+                          const uint64_t* in_nbytes, int8_t* const* d_y, const uint64_t* n,
+                          uint32_t nseg, const sh_params* params, int32_t* d_status,
+                          void* stream) {
+    if (nseg == 0) return SH_OK;
+    if (!d_tables || !d_in || !in_nbytes || !d_y || !n || !aligned(d_tables, 16))
+        return SH_ERR_INVALID_ARG;
+    sh_status st = check_params(params);
+    if (st != SH_OK) return st;
+    if (!aligned(d_status, 4)) return SH_ERR_INVALID_ARG;
+    for (uint32_t i = 0; i < nseg; ++i) {
+        if (!d_in[i] || !aligned(d_in[i], 4) || (n[i] > 0 && !d_y[i])) return SH_ERR_INVALID_ARG;
+        if (n[i] >= (1ull << 32) || in_nbytes[i] > 0xFFFFFFFFull) return SH_ERR_UNSUPPORTED;
+        const uint64_t nch = n_chunks_of(n[i], params->chunk_symbols);
+        if (in_nbytes[i] < header_bytes(params->K) + 4 * (nch + 1)) return SH_ERR_CORRUPT_STREAM;
+    }
+    for (auto [b, e] : groups_of(nseg)) {
+        CodecArgs a;
+        std::memset(&a, 0, sizeof(a));
+        fill_codec_common(a, params, d_status);
+        a.nseg = e - b;
+        uint32_t blocks = 0;
+        for (uint32_t i = b; i < e; ++i) {
+            SegDesc& sd = a.many[i - b];
+            const uint64_t nch = n_chunks_of(n[i], params->chunk_symbols);
+            sd.x = (uint8_t*)d_y[i];
+            sd.c = (uint8_t*)d_in[i];
+            sd.n = n[i];
+            sd.c_bytes = in_nbytes[i];
+            sd.tab = (const uint32_t*)((const uint8_t*)d_tables + (uint64_t)i * kDTBytes);
+            sd.first_block = blocks;
+            sd.n_chunks = (uint32_t)nch;
+            blocks += blocks_for(nch, kChunksPerBlock);
+        }
+        st = launch_decode(a, blocks, stream);
+        if (st != SH_OK) return st;
+    }
+    return SH_OK;
 }
 
 sh_status sh_stats(const sh_table* table, uint64_t n, uint64_t payload_bits,

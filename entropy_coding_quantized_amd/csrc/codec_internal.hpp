@@ -63,72 +63,93 @@ SHN_HD inline uint32_t chunk_bound_dwords(uint32_t nc, uint32_t R) {
 void write_header(const sh_table& t, uint64_t n, uint32_t C, uint32_t S, uint64_t n_chunks,
                   uint32_t* dwords /* kMaxHeaderDwords */);
 
-// ---- kernel argument blocks (kernels.hip) ------------------------------------------
-// Decode entry of a slot, two dwords:
-//   e0 = need | (byte address of the next slot's entry) << 16, need = w_s + nb <= 16
+// ---- device-resident table --------------------------------------------------------------
+// Everything the kernels need for one tensor, in device memory (dword offsets below).
+// Written by the GPU table builder or uploaded from a host sh_table.
+constexpr uint32_t kDTK = 0, kDTLog2L = 1, kDTL = 2, kDTStatus = 3, kDTN = 4 /* u64 */;
+constexpr uint32_t kDTHdrDwords = 6;
+constexpr uint32_t kDTHdr = 8;        // 200 dwords: container header with n = n_chunks = 0
+constexpr uint32_t kDTDec = 208;      // 512 dwords: decode entries, two per slot
+constexpr uint32_t kDTVt = 720;       // 512 dwords: encode entries, two per value
+constexpr uint32_t kDTEs = 1232;      // 64 dwords: encode slot bytes
+constexpr uint32_t kDTLo = 1296;      // 129 dwords: lo[257] as u16
+constexpr uint32_t kDTFreq = 1426;    // 128 dwords: freq[256] as u16
+constexpr uint32_t kDTHist = 1554;    // 512 dwords: hist[256] as u64
+constexpr uint32_t kDTDwords = 2112;  // 8448 bytes
+constexpr uint32_t kDTBytes = 4 * kDTDwords;
+
+// header dwords that depend on the segment, not on the table: n (2, 3) and n_chunks (6)
+SHN_HD inline uint32_t header_dword(const uint32_t* tmpl, uint32_t i, uint64_t n, uint32_t nch) {
+    return i == 2 ? (uint32_t)n : i == 3 ? (uint32_t)(n >> 32) : i == 6 ? nch : tmpl[i];
+}
+
+// Decode entry of a slot (kernel-argument / device-table form), two dwords:
+//   e0 = need | (next slot * 8) << 16, need = w_s + nb <= 16
 //   e1 = w_s | (int8 bits of the range base) << 8 | (|range| - 1) << 16
 // Encode entry of a value u, two dwords:
 //   v0 = bias_s (int32): the state-bit count is (X + bias_s) >> (R + 1)
 //   v1 = o | w_s << 8 | (start_s + 512) << 16 | (f_s == 0) << 31, start_s = cum_s - f_s
-struct DecodeArgs {
-    const uint8_t* in;
-    int8_t* out;
+void derive_kernel_tables(const sh_table& t, const SlotTables& st, uint32_t* dec,
+                          uint32_t* vt, uint8_t* es);
+// st is null for a table built from no values
+void make_device_table(const sh_table& t, const SlotTables* st, uint32_t C, uint32_t S,
+                       uint32_t* dt /* kDTDwords */);
+
+// ---- kernel arguments (kernels.hip) ------------------------------------------------------
+// One tensor of a launch.
+struct SegDesc {
+    uint8_t* x;             // int8 values: encode input, decode output
+    uint8_t* c;             // container: encode output, decode input
+    uint64_t n;             // values
+    uint64_t c_bytes;       // decode: readable bytes at c
+    const uint32_t* tab;    // device table, or null: the tables inside CodecArgs
+    sh_encode_info* info;   // encode: where to report (may be null)
+    uint32_t first_block;   // this segment's first block in the chunk kernels
+    uint32_t first_block_c; // ... and in the compaction kernel
+    uint32_t n_chunks;
+    uint32_t slot_base;     // encode: first workspace slot
+};
+
+constexpr uint32_t kMaxInlineSegs = 48;  // descriptors carried in one launch's arguments
+
+struct CodecArgs {
+    uint32_t nseg;          // 0: a single segment with host-built tables (one), else many
+    uint32_t C, R, L, K;
+    uint32_t slot_dwords;   // encode: dwords per slot, a multiple of 128
     int32_t* status;
-    uint64_t in_nbytes;
-    uint64_t n;
-    uint32_t payload_at;    // byte offset of the payload in the container
-    uint32_t index_at;      // byte offset of the chunk index
-    uint32_t C;
-    uint32_t R;
-    uint32_t L;
-    uint32_t n_chunks;
-    uint32_t hdr_dwords;
-    uint32_t pad_;
-    uint32_t hdr[kMaxHeaderDwords];
-    uint32_t dec[2 * 256];
+    uint32_t* slots;        // encode workspace
+    uint32_t* meta;         // encode workspace: per slot {start bit, field bits}
+    union {
+        struct {
+            SegDesc seg;
+            uint32_t hdr[kMaxHeaderDwords];
+            uint32_t tab[2 * 256];  // decode entries (decode) or value entries (encode)
+            uint8_t es[256];        // encode slot bytes
+        } one;
+        SegDesc many[kMaxInlineSegs];  // each with a device table
+    };
 };
 
-struct EncodeArgs {
-    const int8_t* x;
-    uint32_t* slots;        // workspace: n_chunks slots of slot_dwords
-    uint32_t* meta;         // workspace: per chunk {start bit in slot, field bits}
-    int32_t* status;
-    uint64_t n;
-    uint32_t C;
-    uint32_t R;
-    uint32_t L;
-    uint32_t n_chunks;
-    uint32_t slot_dwords;   // multiple of 128
-    uint32_t pad_;
-    uint32_t vt[2 * 256];
-    uint8_t es[256];
+struct HistArgs {
+    uint32_t nseg;
+    uint32_t n_blocks;
+    uint64_t* hist;         // nseg x 256
+    SegDesc segs[kMaxInlineSegs];  // x, n and first_block of each segment
 };
 
-struct IndexArgs {
-    const uint32_t* meta;
-    uint8_t* out;
-    sh_encode_info* info;
-    uint64_t n;
-    uint32_t n_chunks;
-    uint32_t slot_dwords;
-    uint32_t index_at;
-    uint32_t hdr_dwords;
-    uint32_t hdr[kMaxHeaderDwords];
+struct BuildArgs {
+    const uint64_t* hist;   // nseg x 256
+    uint32_t* tables;       // nseg x kDTDwords
+    uint64_t* cost;         // workspace: nseg x kCostEntries
+    uint16_t* arg;          // workspace: nseg x 257 x 257
+    uint32_t nseg, K, R, C, S;
 };
+constexpr uint32_t kCostEntries = 257 * 256 / 2;  // [j, i) for 0 <= j < i <= 256
 
-struct CompactArgs {
-    const uint32_t* slots;
-    const uint32_t* meta;
-    uint8_t* out;
-    uint32_t n_chunks;
-    uint32_t slot_dwords;
-    uint32_t index_at;
-    uint32_t payload_at;
-};
-
-sh_status launch_histogram(const int8_t* d_x, uint64_t n, uint64_t* d_hist, void* stream);
-sh_status launch_decode(const DecodeArgs& a, void* stream);
-sh_status launch_encode(const EncodeArgs& e, const IndexArgs& ix, const CompactArgs& cp,
+sh_status launch_histogram(const HistArgs& h, uint32_t nseg_zero, void* stream);
+sh_status launch_build_tables(const BuildArgs& b, void* stream);
+sh_status launch_decode(const CodecArgs& a, uint32_t total_blocks, void* stream);
+sh_status launch_encode(const CodecArgs& a, uint32_t total_blocks, uint32_t total_blocks_c,
                         void* stream);
 
 // encode workspace layout

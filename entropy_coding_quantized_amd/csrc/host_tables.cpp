@@ -214,3 +214,60 @@ void write_header(const sh_table& t, uint64_t n, uint32_t C, uint32_t S, uint64_
 }
 
 }  // namespace shn
+
+namespace shn {
+
+// The kernels' forms of a table (see codec_internal.hpp for the packing).
+void derive_kernel_tables(const sh_table& t, const SlotTables& st, uint32_t* dec, uint32_t* vt,
+                          uint8_t* es) {
+    const uint32_t K = t.K, R = t.log2_L, L = 1u << R;
+    if (dec) {
+        for (uint32_t i = 0; i < L; ++i) {
+            const uint32_t s = st.range[i];
+            const uint32_t width = t.lo[s + 1] - t.lo[s];
+            const uint32_t w = ceil_log2_u32(width);
+            dec[2 * i] = (w + st.nb[i]) | ((uint32_t)st.next[i] * 8u << 16);
+            dec[2 * i + 1] = w | (((uint32_t)(t.lo[s] - 128) & 0xFFu) << 8) | ((width - 1) << 16);
+        }
+    }
+    if (vt) {
+        for (uint32_t s = 0; s < K; ++s) {
+            const uint32_t f = t.freq[s];
+            const uint32_t w = ceil_log2_u32(t.lo[s + 1] - t.lo[s]);
+            int32_t bias = 0, start = -(int32_t)L;
+            if (f > 0) {
+                const uint32_t m = floor_log2_u32(f);
+                bias = (int32_t)((R - m) << (R + 1)) - (int32_t)(f << (R - m));
+                start = (int32_t)st.cum[s] - (int32_t)f;
+            }
+            for (uint32_t u = t.lo[s]; u < t.lo[s + 1]; ++u) {
+                vt[2 * u] = (uint32_t)bias;
+                vt[2 * u + 1] = (u - t.lo[s]) | (w << 8) | ((uint32_t)(start + 512) << 16) |
+                                (f == 0 ? 0x80000000u : 0u);
+            }
+        }
+    }
+    if (es)
+        for (uint32_t i = 0; i < L; ++i) es[i] = (uint8_t)st.enc[i];
+}
+
+void make_device_table(const sh_table& t, const SlotTables* st, uint32_t C, uint32_t S,
+                       uint32_t* dt) {
+    std::memset(dt, 0, kDTBytes);
+    dt[kDTK] = t.K;
+    dt[kDTLog2L] = t.log2_L;
+    dt[kDTL] = 1u << t.log2_L;
+    dt[kDTStatus] = 0;
+    std::memcpy(dt + kDTN, &t.n, 8);
+    dt[kDTHdrDwords] = header_bytes(t.K) / 4;
+    write_header(t, 0, C, S, 0, dt + kDTHdr);
+    if (st)
+        derive_kernel_tables(t, *st, dt + kDTDec, dt + kDTVt, reinterpret_cast<uint8_t*>(dt + kDTEs));
+    else  // a table built from no values: every value is outside it
+        for (uint32_t u = 0; u < 256; ++u) dt[kDTVt + 2 * u + 1] = 0x80000000u;
+    std::memcpy(dt + kDTLo, t.lo, sizeof(t.lo));
+    std::memcpy(dt + kDTFreq, t.freq, sizeof(t.freq));
+    std::memcpy(dt + kDTHist, t.hist, sizeof(t.hist));
+}
+
+}  // namespace shn

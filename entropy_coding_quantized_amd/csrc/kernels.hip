@@ -61,27 +61,54 @@ __device__ __forceinline__ void report(int32_t* status, int32_t code, bool mine 
 }
 
 // ------------------------------------------------------------------------------------
+// segments: every launch covers one or more tensors; a block finds its tensor by a binary
+// search over the descriptors' first blocks (uniform, so it runs on the scalar unit)
+// ------------------------------------------------------------------------------------
+__device__ __forceinline__ const SegDesc* find_seg(const SegDesc* segs, uint32_t nseg,
+                                                    uint32_t block, bool compaction) {
+    uint32_t lo = 0, hi = nseg;  // the last segment whose first block <= block
+    while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) >> 1;
+        const uint32_t fb = compaction ? segs[mid].first_block_c : segs[mid].first_block;
+        if (fb <= block) lo = mid;
+        else hi = mid;
+    }
+    return &segs[lo];
+}
+__device__ __forceinline__ const SegDesc* codec_seg(const CodecArgs& a, uint32_t block,
+                                                     bool compaction) {
+    return a.nseg == 0 ? &a.one.seg : find_seg(a.many, a.nseg, block, compaction);
+}
+
+// ------------------------------------------------------------------------------------
 // histogram: h[u] = #{i : x[i] + 128 == u}   (paper section 4.1)
 // ------------------------------------------------------------------------------------
 constexpr int kHistBlock = 256;
 constexpr int kHistCopies = 32;
+constexpr uint32_t kHistBytesPerBlock = 1u << 18;  // 256 KiB of values per block
 
 __global__ void k_zero_u64(uint64_t* p, uint32_t count) {
     const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < count) p[i] = 0;
 }
 
-__global__ __launch_bounds__(kHistBlock) void k_histogram(const int8_t* x, uint64_t n,
-                                                          uint64_t* hist) {
+__global__ __launch_bounds__(kHistBlock) void k_histogram(const HistArgs a) {
     // 32 private copies per block, copy c of bin b at b * 32 + c: the 32 lanes of a half
     // wavefront hit 32 different banks even when every value is the same.
     __shared__ uint32_t h[256 * kHistCopies];
     for (int i = threadIdx.x; i < 256 * kHistCopies; i += kHistBlock) h[i] = 0;
     __syncthreads();
+    const uint32_t block = blockIdx.x;
+    const SegDesc* sg = find_seg(a.segs, a.nseg, block, false);
+    const uint32_t seg = (uint32_t)(sg - a.segs);
+    const uint8_t* x = sg->x;
+    const uint64_t n = sg->n;
+    const uint64_t lo = (uint64_t)(block - sg->first_block) * kHistBytesPerBlock;
+    const uint64_t hi = lo + kHistBytesPerBlock < n ? lo + kHistBytesPerBlock : n;
     const uint32_t copy = threadIdx.x & (kHistCopies - 1);
-    const uint64_t groups = n / 16;
-    const uint64_t stride = (uint64_t)gridDim.x * kHistBlock;
-    for (uint64_t g = (uint64_t)blockIdx.x * kHistBlock + threadIdx.x; g < groups; g += stride) {
+    // 16-byte groups fully inside [lo, hi); x is 16-byte aligned and lo a multiple of 16
+    const uint64_t g0 = lo / 16, g1 = hi / 16;
+    for (uint64_t g = g0 + threadIdx.x; g < g1; g += kHistBlock) {
         const v4u w = *reinterpret_cast<const v4u*>(x + 16 * g);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -92,30 +119,252 @@ __global__ __launch_bounds__(kHistBlock) void k_histogram(const int8_t* x, uint6
             }
         }
     }
-    if (blockIdx.x == 0) {  // the n % 16 tail
-        const uint64_t i = groups * 16 + threadIdx.x;
-        if (i < n) atomicAdd(&h[((uint32_t)(uint8_t)x[i] ^ 0x80) * kHistCopies + copy], 1u);
-    }
+    for (uint64_t i = g1 * 16 + threadIdx.x; i < hi; i += kHistBlock)  // tail < 16 values
+        atomicAdd(&h[((uint32_t)x[i] ^ 0x80) * kHistCopies + copy], 1u);
     __syncthreads();
     for (int b = threadIdx.x; b < 256; b += kHistBlock) {
         uint64_t s = 0;
 #pragma unroll 8
         for (int c = 0; c < kHistCopies; ++c) s += h[b * kHistCopies + c];
-        if (s) atomicAdd((unsigned long long*)&hist[b], (unsigned long long)s);
+        if (s) atomicAdd((unsigned long long*)&a.hist[256 * seg + b], (unsigned long long)s);
     }
 }
 
-sh_status launch_histogram(const int8_t* d_x, uint64_t n, uint64_t* d_hist, void* stream) {
+sh_status launch_histogram(const HistArgs& h, uint32_t nseg_zero, void* stream) {
     hipStream_t s = (hipStream_t)stream;
-    hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(256), 0, s, d_hist, 256u);
-    if (n > 0) {
-        const uint64_t groups = n / 16;
-        uint64_t blocks = (groups + kHistBlock * 8 - 1) / (kHistBlock * 8);
-        if (blocks < 1) blocks = 1;
-        if (blocks > 2048) blocks = 2048;
-        hipLaunchKernelGGL(k_histogram, dim3((uint32_t)blocks), dim3(kHistBlock), 0, s, d_x, n,
-                           d_hist);
+    const uint32_t words = 256 * nseg_zero;
+    hipLaunchKernelGGL(k_zero_u64, dim3((words + 255) / 256), dim3(256), 0, s, h.hist, words);
+    if (h.n_blocks > 0)
+        hipLaunchKernelGGL(k_histogram, dim3(h.n_blocks), dim3(kHistBlock), 0, s, h);
+    return hipGetLastError() == hipSuccess ? SH_OK : SH_ERR_HIP;
+}
+
+// ------------------------------------------------------------------------------------
+// table build on the GPU (paper section 4.1): one block per tensor
+// ------------------------------------------------------------------------------------
+// 2^24 * log2(x), digit by digit: with x = 2^e * m, m in [1, 2) kept in Q1.63, each
+// fractional bit of log2 m is set exactly when m^2 >= 2; the square (halved when the bit
+// is set) is truncated back to 64 bits and carries on.  The same function as the host's.
+__device__ uint64_t dev_fixed_log2(uint64_t x) {
+    if (x == 0) return 0;
+    const int e = 63 - __builtin_clzll(x);
+    uint64_t m = x << (63 - e);
+    uint64_t frac = 0;
+    for (int i = 0; i < kLgFrac; ++i) {
+        const uint64_t hi = __umul64hi(m, m);
+        const uint64_t lo = m * m;
+        const uint64_t top = hi >> 63;
+        frac = (frac << 1) | top;
+        m = top ? hi : (hi << 1) | (lo >> 63);
     }
+    return ((uint64_t)e << kLgFrac) | frac;
+}
+
+__device__ __forceinline__ uint32_t header_bytes_dev(uint32_t K) { return (kHeaderFixed + 3 * K - 1 + 3) / 4 * 4; }
+__device__ __forceinline__ uint32_t dev_ceil_log2(uint32_t m) { return m <= 1 ? 0 : 32 - __builtin_clz(m - 1); }
+__device__ __forceinline__ uint32_t dev_floor_log2(uint32_t x) { return 31 - __builtin_clz(x); }
+
+constexpr int kBuildBlock = 256;
+
+__global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a) {
+    __shared__ uint64_t prefix[257];
+    __shared__ uint64_t cprev[257], ccur[257];
+    __shared__ uint64_t gain[257];
+    __shared__ uint32_t lo_s[257], freq_s[256], cum_s[257], range_of_u[256];
+    __shared__ uint64_t count_s[256];
+    __shared__ uint64_t lgN_s;
+    __shared__ uint32_t status_s;
+    const uint32_t tid = threadIdx.x, seg = blockIdx.x;
+    const uint64_t* hist = a.hist + 256 * (uint64_t)seg;
+    uint32_t* dt = a.tables + (uint64_t)seg * kDTDwords;
+    uint64_t* cost = a.cost + (uint64_t)seg * kCostEntries;
+    uint16_t* arg = a.arg + (uint64_t)seg * 257 * 257;
+    const uint32_t K = a.K, R = a.R, L = 1u << R;
+    constexpr uint64_t INF = ~0ull;
+
+    for (uint32_t i = tid; i < kDTDwords; i += kBuildBlock) dt[i] = 0;  // unused parts read 0
+    if (tid == 0) {
+        uint64_t acc = 0;
+        prefix[0] = 0;
+        for (int v = 0; v < 256; ++v) prefix[v + 1] = (acc += hist[v]);
+        status_s = acc >= (1ull << 32) ? (uint32_t)SH_ERR_UNSUPPORTED : 0u;
+        lgN_s = dev_fixed_log2(acc);
+    }
+    __syncthreads();
+    const uint64_t lgN = lgN_s;
+
+    // cost of [j, i) for every 0 <= j < i <= 256, row i holding j = 0..i-1:
+    // N_R * (log2 N - log2 N_R) + N_R * ceil(log2 (i - j)), in units of 2^-24 bit
+    for (uint32_t idx = tid; idx < kCostEntries; idx += kBuildBlock) {
+        uint32_t i = (uint32_t)((1.0 + sqrt(1.0 + 8.0 * (double)idx)) * 0.5);
+        while ((uint64_t)i * (i - 1) / 2 > idx) --i;
+        while ((uint64_t)(i + 1) * i / 2 <= idx) ++i;
+        const uint32_t j = idx - i * (i - 1) / 2;
+        const uint64_t nr = prefix[i] - prefix[j];
+        cost[idx] = nr ? nr * (lgN - dev_fixed_log2(nr)) + nr * ((uint64_t)dev_ceil_log2(i - j) << kLgFrac)
+                       : 0;
+    }
+    for (uint32_t i = tid; i <= 256; i += kBuildBlock) cprev[i] = i == 0 ? 0 : INF;
+    __syncthreads();
+
+    // C[i][k] = min over j < i of C[j][k-1] + cost[j, i): the smallest j wins ties
+    for (uint32_t k = 1; k <= K; ++k) {
+        for (uint32_t i = tid; i <= 256; i += kBuildBlock) {
+            uint64_t best = INF;
+            uint32_t bj = 0;
+            if (i >= k) {
+                const uint64_t* row = cost + (uint64_t)i * (i - 1) / 2;
+                for (uint32_t j = k - 1; j < i; ++j) {
+                    if (cprev[j] == INF) continue;
+                    const uint64_t c = cprev[j] + row[j];
+                    if (c < best) {
+                        best = c;
+                        bj = j;
+                    }
+                }
+            }
+            ccur[i] = best;
+            arg[k * 257 + i] = (uint16_t)bj;
+        }
+        __syncthreads();
+        for (uint32_t i = tid; i <= 256; i += kBuildBlock) cprev[i] = ccur[i];
+        __syncthreads();
+    }
+
+    if (tid == 0) {
+        uint32_t i = 256;
+        lo_s[K] = 256;
+        for (uint32_t k = K; k >= 1; --k) {
+            i = arg[k * 257 + i];
+            lo_s[k - 1] = i;
+        }
+    }
+    __syncthreads();
+    for (uint32_t k = tid; k < K; k += kBuildBlock) count_s[k] = prefix[lo_s[k + 1]] - prefix[lo_s[k]];
+    for (uint32_t f = tid; f <= L; f += kBuildBlock)
+        gain[f] = f == 0 ? 0 : dev_fixed_log2(f + 1) - dev_fixed_log2(f);
+    __syncthreads();
+
+    // state allocation: one state per occupied range, then every remaining state to the
+    // range with the largest N_k * (log2(f_k + 1) - log2 f_k), first k on ties
+    if (tid == 0) {
+        uint32_t used = 0;
+        for (uint32_t k = 0; k < K; ++k) {
+            freq_s[k] = count_s[k] ? 1 : 0;
+            used += freq_s[k];
+        }
+        if (used > L) status_s = (uint32_t)SH_ERR_UNSUPPORTED;
+        if (used > 0 && status_s == 0) {
+            for (; used < L; ++used) {
+                uint32_t best = K;
+                uint64_t bg = 0;
+                for (uint32_t k = 0; k < K; ++k) {
+                    if (!count_s[k]) continue;
+                    const uint64_t g = count_s[k] * gain[freq_s[k]];
+                    if (best == K || g > bg) {
+                        best = k;
+                        bg = g;
+                    }
+                }
+                freq_s[best]++;
+            }
+        }
+        uint32_t c = 0;
+        for (uint32_t k = 0; k < K; ++k) {
+            cum_s[k] = c;
+            c += freq_s[k];
+        }
+        cum_s[K] = c;
+    }
+    __syncthreads();
+    const bool ok = status_s == 0 && cum_s[K] == L;
+
+    // slot spread: pair (k, j), j < f_k, goes to the slot equal to the number of pairs with
+    // a smaller key (2j'+1)/(2 f_k'), or an equal key and a smaller range; then the tANS
+    // tables of that slot: sub-state x = f_k + j, nb = R - floor(log2 x), next (x << nb) - L
+    if (!ok)  // no usable table: every value is outside it
+        for (uint32_t u = tid; u < 256; u += kBuildBlock) dt[kDTVt + 2 * u + 1] = 0x80000000u;
+    for (uint32_t p = tid; ok && p < L; p += kBuildBlock) {
+        uint32_t k = 0;
+        while (cum_s[k + 1] <= p) ++k;
+        const uint32_t j = p - cum_s[k], f = freq_s[k];
+        uint32_t rank = 0;
+        for (uint32_t k2 = 0; k2 < K; ++k2) {
+            const uint32_t f2 = freq_s[k2];
+            if (!f2) continue;
+            const uint32_t A = (2 * j + 1) * f2;
+            const uint32_t odd_max = k2 < k ? A / f : (A - 1) / f;  // largest usable 2j'+1
+            const uint32_t c = (odd_max + 1) >> 1;
+            rank += c < f2 ? c : f2;
+        }
+        const uint32_t x = f + j;
+        const uint32_t nb = R - dev_floor_log2(x);
+        const uint32_t next = (x << nb) - L;
+        const uint32_t width = lo_s[k + 1] - lo_s[k];
+        const uint32_t w = dev_ceil_log2(width);
+        dt[kDTDec + 2 * rank] = (w + nb) | ((next * 8u) << 16);
+        dt[kDTDec + 2 * rank + 1] = w | (((lo_s[k] - 128u) & 0xFFu) << 8) | ((width - 1) << 16);
+        reinterpret_cast<uint8_t*>(dt + kDTEs)[cum_s[k] + j] = (uint8_t)rank;
+    }
+    for (uint32_t k = tid; k < K; k += kBuildBlock)
+        for (uint32_t u = lo_s[k]; u < lo_s[k + 1]; ++u) range_of_u[u] = k;
+    __syncthreads();
+    // encode entry of every value u
+    for (uint32_t u = tid; ok && u < 256; u += kBuildBlock) {
+        const uint32_t s = range_of_u[u];
+        const uint32_t f = freq_s[s];
+        const uint32_t w = dev_ceil_log2(lo_s[s + 1] - lo_s[s]);
+        int32_t bias = 0, start = -(int32_t)L;
+        if (f > 0) {
+            const uint32_t m = dev_floor_log2(f);
+            bias = (int32_t)((R - m) << (R + 1)) - (int32_t)(f << (R - m));
+            start = (int32_t)cum_s[s] - (int32_t)f;
+        }
+        dt[kDTVt + 2 * u] = (uint32_t)bias;
+        dt[kDTVt + 2 * u + 1] = (u - lo_s[s]) | (w << 8) | ((uint32_t)(start + 512) << 16) |
+                                (f == 0 ? 0x80000000u : 0u);
+    }
+    // canonical table, histogram and the header template (n and n_chunks left 0)
+    uint16_t* lo16 = reinterpret_cast<uint16_t*>(dt + kDTLo);
+    uint16_t* f16 = reinterpret_cast<uint16_t*>(dt + kDTFreq);
+    for (uint32_t k = tid; k <= 256; k += kBuildBlock) lo16[k] = k <= K ? (uint16_t)lo_s[k] : 0;
+    for (uint32_t k = tid; k < 256; k += kBuildBlock) f16[k] = k < K ? (uint16_t)freq_s[k] : 0;
+    for (uint32_t u = tid; u < 256; u += kBuildBlock)
+        reinterpret_cast<uint64_t*>(dt + kDTHist)[u] = hist[u];
+    const uint32_t hbytes = (kHeaderFixed + 3 * K - 1 + 3) / 4 * 4;
+    for (uint32_t d = tid; d < kMaxHeaderDwords; d += kBuildBlock) {
+        uint32_t word = 0;
+        for (uint32_t b = 0; b < 4; ++b) {
+            const uint32_t at = 4 * d + b;
+            uint32_t byte = 0;
+            if (at < 4) byte = (uint32_t)"SHN1"[at];
+            else if (at == 4) byte = 1;
+            else if (at == 5) byte = R;
+            else if (at < 8) byte = (K >> (8 * (at - 6))) & 0xFF;
+            else if (at < 16) byte = 0;                                   // n
+            else if (at < 20) byte = (a.C >> (8 * (at - 16))) & 0xFF;
+            else if (at < 24) byte = (a.S >> (8 * (at - 20))) & 0xFF;
+            else if (at < 28) byte = 0;                                   // n_chunks
+            else if (at < 32) byte = (hbytes >> (8 * (at - 28))) & 0xFF;
+            else if (at < kHeaderFixed + 2 * K) byte = (freq_s[(at - kHeaderFixed) >> 1] >> (8 * ((at - kHeaderFixed) & 1))) & 0xFF;
+            else if (at < kHeaderFixed + 3 * K - 1) byte = lo_s[at - kHeaderFixed - 2 * K + 1] & 0xFF;
+            word |= byte << (8 * b);
+        }
+        dt[kDTHdr + d] = 4 * d < hbytes ? word : 0;
+    }
+    if (tid == 0) {
+        dt[kDTK] = K;
+        dt[kDTLog2L] = R;
+        dt[kDTL] = L;
+        dt[kDTStatus] = ok || prefix[256] == 0 ? status_s : (uint32_t)SH_ERR_UNSUPPORTED;
+        reinterpret_cast<uint64_t*>(dt + kDTN)[0] = prefix[256];
+        dt[kDTHdrDwords] = hbytes / 4;
+    }
+}
+
+sh_status launch_build_tables(const BuildArgs& b, void* stream) {
+    if (b.nseg == 0) return SH_OK;
+    hipLaunchKernelGGL(k_build_tables, dim3(b.nseg), dim3(kBuildBlock), 0, (hipStream_t)stream, b);
     return hipGetLastError() == hipSuccess ? SH_OK : SH_ERR_HIP;
 }
 
@@ -161,33 +410,47 @@ constexpr int kDecBlock = 256;  // 4 wavefronts
 // 2k + h (k < ILP) of the wavefront's group.  ILP = 1 is the one launched: measured on
 // MI355X, two independent chains per lane ran slower than twice as many wavefronts.
 template <int ILP>
-__global__ __launch_bounds__(kDecBlock) void k_decode(const DecodeArgs a) {
+__global__ __launch_bounds__(kDecBlock) void k_decode(const CodecArgs a) {
     constexpr uint32_t kChunksPerWave = 2 * ILP;
-    __shared__ __align__(16) uint32_t sm[kTabDwords + kDecBlock / 64 * kChunksPerWave * kRingStride];
+    constexpr uint32_t kChunksPerBlock = kDecBlock / 64 * kChunksPerWave;
+    __shared__ __align__(16) uint32_t sm[kTabDwords + kChunksPerBlock * kRingStride];
     const uint32_t tid = threadIdx.x, lane = tid & 63, li = lane & 31, hw = lane >> 5;
-    // wavefront index, made visibly uniform so that per-wavefront descriptors stay scalar
-    const uint32_t wid = __builtin_amdgcn_readfirstlane(blockIdx.x * (kDecBlock / 64) + (tid >> 6));
+    const uint32_t block = __builtin_amdgcn_readfirstlane(blockIdx.x);
+    const SegDesc* sg = codec_seg(a, block, false);
+    const uint32_t bseg = block - sg->first_block;  // block within its segment
+    // wavefront index within the segment, uniform so that descriptors stay scalar
+    const uint32_t wid = __builtin_amdgcn_readfirstlane(bseg * (kDecBlock / 64) + (tid >> 6));
     const uint32_t wv = wid & (kDecBlock / 64 - 1);
     const uint32_t tab_byte = lds_offset(sm);
+    const uint32_t* dec = sg->tab ? sg->tab + kDTDec : a.one.tab;
+    const uint32_t* hdr = sg->tab ? sg->tab + kDTHdr : a.one.hdr;
+    const uint32_t n_chunks = sg->n_chunks;
+    const uint64_t n = sg->n;
+    const uint32_t index_at = header_bytes_dev(a.K);
+    const uint32_t payload_at = index_at + 4 * (n_chunks + 1);
+    const uint64_t in_nbytes = sg->c_bytes;
 
-    // rearrange the kernel-argument entries into the LDS form
+    // rearrange the table's entries into the LDS form
     for (uint32_t i = tid; i < a.L; i += kDecBlock) {
-        const uint32_t e0 = a.dec[2 * i], e1 = a.dec[2 * i + 1];
+        const uint32_t e0 = dec[2 * i], e1 = dec[2 * i + 1];
         sm[2 * i] = (e0 & 0xFFFF) | (e1 & 0x00FF0000u) | ((e1 & 0xFF00u) << 16);
         sm[2 * i + 1] = (e1 & 31) | ((tab_byte + (e0 >> 16)) << 16);
     }
 
-    const rsrc_t rin = make_rsrc(a.in, (uint32_t)a.in_nbytes);
+    const rsrc_t rin = make_rsrc(sg->c, (uint32_t)in_nbytes);
     if (wid == 0) {
         // header and index ends: the container must belong to this table and fit in_nbytes
-        bool bad = false;
-        for (uint32_t i = lane; i < a.hdr_dwords; i += 64)
-            bad |= __builtin_amdgcn_raw_buffer_load_b32(rin, (int)(4 * i), 0, 0) != a.hdr[i];
+        // a device table that failed to build, or was built from no values, decodes nothing
+        bool bad = sg->tab && (sg->tab[kDTStatus] != 0 ||
+                               (n > 0 && (sg->tab[kDTN] | sg->tab[kDTN + 1]) == 0));
+        for (uint32_t i = lane; i < index_at / 4; i += 64)
+            bad |= __builtin_amdgcn_raw_buffer_load_b32(rin, (int)(4 * i), 0, 0) !=
+                   header_dword(hdr, i, n, n_chunks);
         if (lane == 0) {
-            const uint32_t first = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)a.index_at, 0, 0);
+            const uint32_t first = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)index_at, 0, 0);
             const uint32_t last = __builtin_amdgcn_raw_buffer_load_b32(
-                rin, (int)(a.index_at + 4 * a.n_chunks), 0, 0);
-            bad |= first != 0 || (uint64_t)a.payload_at + last > a.in_nbytes;
+                rin, (int)(index_at + 4 * n_chunks), 0, 0);
+            bad |= first != 0 || (uint64_t)payload_at + last > in_nbytes;
         }
         report(a.status, SH_ERR_CORRUPT_STREAM, bad);
     }
@@ -195,9 +458,9 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const DecodeArgs a) {
     // output: per-wavefront descriptor over the wavefront's chunks
     const uint32_t group = kChunksPerWave * wid;
     const uint64_t grp_first = (uint64_t)group * a.C;
-    const uint64_t grp_len = grp_first < a.n ? a.n - grp_first : 0;
+    const uint64_t grp_len = grp_first < n ? n - grp_first : 0;
     const uint64_t grp_cap = (uint64_t)kChunksPerWave * a.C;
-    const rsrc_t rout = make_rsrc(a.out + (grp_first < a.n ? grp_first : 0),
+    const rsrc_t rout = make_rsrc(sg->x + (grp_first < n ? grp_first : 0),
                                   (uint32_t)(grp_len < grp_cap ? grp_len : grp_cap));
 
     DecChain ch[ILP];
@@ -213,18 +476,18 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const DecodeArgs a) {
         c.cdw = 0;
         c.cbyte = 0;
         c.err = 0;
-        if (chunk < a.n_chunks) {
-            const uint32_t o0 = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)(a.index_at + 4 * chunk), 0, 0);
-            const uint32_t o1 = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)(a.index_at + 4 * chunk + 4), 0, 0);
+        if (chunk < n_chunks) {
+            const uint32_t o0 = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)(index_at + 4 * chunk), 0, 0);
+            const uint32_t o1 = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)(index_at + 4 * chunk + 4), 0, 0);
             const uint64_t first = (uint64_t)chunk * a.C;
-            const uint32_t m = (uint32_t)((a.n - first) < a.C ? (a.n - first) : a.C);
+            const uint32_t m = (uint32_t)((n - first) < a.C ? (n - first) : a.C);
             const bool ok = o0 <= o1 && ((o0 | o1) & 3) == 0 &&
                             (o1 - o0) <= 4 * chunk_bound_dwords(m, a.R) &&
-                            (uint64_t)a.payload_at + o1 <= a.in_nbytes;
+                            (uint64_t)payload_at + o1 <= in_nbytes;
             if (ok) {
                 c.nc = m;
                 c.cdw = (o1 - o0) >> 2;
-                c.cbyte = a.payload_at + o0;
+                c.cbyte = payload_at + o0;
             } else {
                 c.err = 1;
             }
@@ -373,10 +636,9 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const DecodeArgs a) {
     report(a.status, SH_ERR_CORRUPT_STREAM, err != 0 || bad_offsets != 0);
 }
 
-sh_status launch_decode(const DecodeArgs& a, void* stream) {
-    if (a.n_chunks == 0) return SH_OK;
-    hipLaunchKernelGGL(k_decode<1>, dim3((a.n_chunks + 7) / 8), dim3(kDecBlock), 0,
-                       (hipStream_t)stream, a);
+sh_status launch_decode(const CodecArgs& a, uint32_t total_blocks, void* stream) {
+    if (total_blocks == 0) return SH_OK;
+    hipLaunchKernelGGL(k_decode<1>, dim3(total_blocks), dim3(kDecBlock), 0, (hipStream_t)stream, a);
     return hipGetLastError() == hipSuccess ? SH_OK : SH_ERR_HIP;
 }
 
@@ -403,14 +665,22 @@ __device__ __forceinline__ void ring_or(uint32_t* sm, uint32_t ring, uint32_t po
     if ((pos & 31) + len > 32) atomicOr(&sm[ring + ((d + 1) & (kERing - 1))], (uint32_t)(wide >> 32));
 }
 
-__global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const EncodeArgs a) {
+__global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const CodecArgs a) {
     __shared__ __align__(16) uint32_t sm[kVtDwords + 8 * kEncHalfDwords];
     const uint32_t tid = threadIdx.x, lane = tid & 63, li = lane & 31, hw = lane >> 5;
-    const uint32_t wv = tid >> 6;
-    for (uint32_t i = tid; i < 512; i += kEncBlock) sm[i] = a.vt[i];
+    const uint32_t block = __builtin_amdgcn_readfirstlane(blockIdx.x);
+    const SegDesc* sg = codec_seg(a, block, false);
+    const uint32_t bseg = block - sg->first_block;
+    const uint32_t wid = __builtin_amdgcn_readfirstlane(bseg * (kEncBlock / 64) + (tid >> 6));
+    const uint32_t wv = wid & (kEncBlock / 64 - 1);
+    const uint32_t* vt = sg->tab ? sg->tab + kDTVt : a.one.tab;
+    const uint8_t* es_src = sg->tab ? reinterpret_cast<const uint8_t*>(sg->tab + kDTEs) : a.one.es;
+    const uint32_t n_chunks = sg->n_chunks;
+    const uint64_t n = sg->n;
+    for (uint32_t i = tid; i < 512; i += kEncBlock) sm[i] = vt[i];
     for (uint32_t i = tid; i < 64; i += kEncBlock) {
-        sm[512 + i] = (uint32_t)a.es[4 * i] | ((uint32_t)a.es[4 * i + 1] << 8) |
-                      ((uint32_t)a.es[4 * i + 2] << 16) | ((uint32_t)a.es[4 * i + 3] << 24);
+        sm[512 + i] = (uint32_t)es_src[4 * i] | ((uint32_t)es_src[4 * i + 1] << 8) |
+                      ((uint32_t)es_src[4 * i + 2] << 16) | ((uint32_t)es_src[4 * i + 3] << 24);
     }
     const uint8_t* es = reinterpret_cast<const uint8_t*>(&sm[512]);
     const uint32_t half = kVtDwords + (wv * 2 + hw) * kEncHalfDwords;
@@ -418,20 +688,20 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const EncodeArgs a)
     const uint32_t ring = half + 256;      // 256 dwords
     for (uint32_t i = li; i < kERing; i += 32) sm[ring + i] = 0;
 
-    const uint32_t chunk = (blockIdx.x * (kEncBlock / 64) + wv) * 2 + hw;
-    const uint32_t pair = chunk & ~1u;
+    const uint32_t pair = 2 * wid;
+    const uint32_t chunk = pair + hw;
     const uint64_t pair_first = (uint64_t)pair * a.C;
-    const uint64_t pair_len = pair_first < a.n ? a.n - pair_first : 0;
-    const rsrc_t rin = make_rsrc(a.x + (pair_first < a.n ? pair_first : 0),
+    const uint64_t pair_len = pair_first < n ? n - pair_first : 0;
+    const rsrc_t rin = make_rsrc(sg->x + (pair_first < n ? pair_first : 0),
                                  (uint32_t)(pair_len < 2ull * a.C ? pair_len : 2ull * a.C));
-    const rsrc_t rslot = make_rsrc(a.slots + (uint64_t)(pair < a.n_chunks ? pair : 0) * a.slot_dwords,
-                                   8u * a.slot_dwords);
+    const uint32_t slot0 = sg->slot_base + (pair < n_chunks ? pair : 0);
+    const rsrc_t rslot = make_rsrc(a.slots + (uint64_t)slot0 * a.slot_dwords, 8u * a.slot_dwords);
     const uint32_t in_base = hw * a.C;          // byte offset of this chunk in rin
     const uint32_t slot_base = hw * a.slot_dwords * 4;
     uint32_t nc = 0;
-    if (chunk < a.n_chunks) {
+    if (chunk < n_chunks) {
         const uint64_t first = (uint64_t)chunk * a.C;
-        nc = (uint32_t)((a.n - first) < a.C ? (a.n - first) : a.C);
+        nc = (uint32_t)((n - first) < a.C ? (n - first) : a.C);
     }
     const uint32_t lanes = nc < 32 ? nc : 32;
     const uint32_t nc_lo = __builtin_amdgcn_readlane(nc, 0), nc_hi = __builtin_amdgcn_readlane(nc, 32);
@@ -462,14 +732,13 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const EncodeArgs a)
     uint32_t X = L;
     uint32_t P = a.slot_dwords * 32;   // fields go below P, right to left
     uint32_t fmark = a.slot_dwords;    // dwords at or above fmark are in the slot
-    uint32_t pay = 0, bad = 0;
+    uint32_t pay = 0, bad = sg->tab && sg->tab[kDTStatus] != 0 && nc > 0;
 
     auto flush_block = [&](uint32_t blk) {  // ring dwords [blk, blk + 128) -> slot
         uint32_t* r = &sm[ring + ((blk + 4 * li) & (kERing - 1))];
         const v4u v = *reinterpret_cast<v4u*>(r);
         *reinterpret_cast<v4u*>(r) = v4u{0, 0, 0, 0};
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v),
-                                               rslot, (int)(slot_base + 4 * (blk + 4 * li)), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v, rslot, (int)(slot_base + 4 * (blk + 4 * li)), 0, 0);
     };
 
     for (uint32_t t = steps; t-- > 0;) {
@@ -510,11 +779,13 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const EncodeArgs a)
             flush_block(fmark);
         }
     }
-    if (chunk < a.n_chunks && li == 0) {
-        a.meta[2 * chunk] = Pi;
-        a.meta[2 * chunk + 1] = pay;
+    if (chunk < n_chunks && li == 0) {
+        a.meta[2 * (sg->slot_base + chunk)] = Pi;
+        a.meta[2 * (sg->slot_base + chunk) + 1] = pay;
     }
-    report(a.status, SH_ERR_SYMBOL_NOT_IN_TABLE, bad != 0);
+    report(a.status, bad && sg->tab && sg->tab[kDTStatus] != 0 ? SH_ERR_UNSUPPORTED
+                                                              : SH_ERR_SYMBOL_NOT_IN_TABLE,
+           bad != 0);
 }
 
 // ------------------------------------------------------------------------------------
@@ -522,24 +793,29 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const EncodeArgs a)
 // ------------------------------------------------------------------------------------
 constexpr int kScanBlock = 1024;
 
-__global__ __launch_bounds__(kScanBlock) void k_encode_index(const IndexArgs a) {
+__global__ __launch_bounds__(kScanBlock) void k_encode_index(const CodecArgs a) {
     __shared__ uint32_t wsum[kScanBlock / 64];
     __shared__ unsigned long long bits_sum;
     const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    uint32_t* index = reinterpret_cast<uint32_t*>(a.out + a.index_at);
-    uint32_t* hdr = reinterpret_cast<uint32_t*>(a.out);
-    for (uint32_t i = tid; i < a.hdr_dwords; i += kScanBlock) hdr[i] = a.hdr[i];
+    const SegDesc* sg = a.nseg == 0 ? &a.one.seg : &a.many[blockIdx.x];
+    const uint32_t n_chunks = sg->n_chunks;
+    const uint32_t index_at = header_bytes_dev(a.K);
+    const uint32_t* tmpl = sg->tab ? sg->tab + kDTHdr : a.one.hdr;
+    const uint32_t* meta = a.meta + 2ull * sg->slot_base;
+    uint32_t* index = reinterpret_cast<uint32_t*>(sg->c + index_at);
+    uint32_t* hdr = reinterpret_cast<uint32_t*>(sg->c);
+    for (uint32_t i = tid; i < index_at / 4; i += kScanBlock) hdr[i] = header_dword(tmpl, i, sg->n, n_chunks);
     if (tid == 0) bits_sum = 0;
     __syncthreads();
     uint32_t carry = 0;
     uint64_t my_bits = 0;
-    for (uint32_t base = 0; base < a.n_chunks; base += kScanBlock) {
+    for (uint32_t base = 0; base < n_chunks; base += kScanBlock) {
         const uint32_t c = base + tid;
         uint32_t bytes = 0;
-        if (c < a.n_chunks) {
-            const uint32_t start = a.meta[2 * c];
+        if (c < n_chunks) {
+            const uint32_t start = meta[2 * c];
             bytes = 4 * ((a.slot_dwords * 32 - start + 31) >> 5);
-            my_bits += a.meta[2 * c + 1];
+            my_bits += meta[2 * c + 1];
         }
         // wavefront inclusive scan, then across the 16 wavefronts
         uint32_t v = bytes;
@@ -554,31 +830,36 @@ __global__ __launch_bounds__(kScanBlock) void k_encode_index(const IndexArgs a) 
             before += w < wv ? wsum[w] : 0;
             all += wsum[w];
         }
-        if (c < a.n_chunks) index[c] = carry + before + v - bytes;
+        if (c < n_chunks) index[c] = carry + before + v - bytes;
         carry += all;
         __syncthreads();
     }
-    if (tid == 0) index[a.n_chunks] = carry;
+    if (tid == 0) index[n_chunks] = carry;
     atomicAdd(&bits_sum, (unsigned long long)my_bits);
     __syncthreads();
-    if (tid == 0 && a.info) {
-        a.info->container_bytes = (uint64_t)a.index_at + 4ull * (a.n_chunks + 1) + carry;
-        a.info->payload_bits = bits_sum;
+    if (tid == 0 && sg->info) {
+        sg->info->container_bytes = (uint64_t)index_at + 4ull * (n_chunks + 1) + carry;
+        sg->info->payload_bits = bits_sum;
     }
 }
 
 // ------------------------------------------------------------------------------------
 // encode, kernel 3: move every chunk from its slot to its place in the payload
 // ------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_encode_compact(const CompactArgs a) {
+__global__ __launch_bounds__(256) void k_encode_compact(const CodecArgs a) {
     const uint32_t lane = threadIdx.x & 63;
-    const uint32_t c = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (c >= a.n_chunks) return;
-    const uint32_t start = a.meta[2 * c];
+    const uint32_t block = __builtin_amdgcn_readfirstlane(blockIdx.x);
+    const SegDesc* sg = codec_seg(a, block, true);
+    const uint32_t c = (block - sg->first_block_c) * 4 + (threadIdx.x >> 6);
+    if (c >= sg->n_chunks) return;
+    const uint32_t index_at = header_bytes_dev(a.K);
+    const uint32_t payload_at = index_at + 4 * (sg->n_chunks + 1);
+    const uint32_t slot = sg->slot_base + c;
+    const uint32_t start = a.meta[2 * slot];
     const uint32_t ndw = (a.slot_dwords * 32 - start + 31) >> 5;
-    const uint32_t off = reinterpret_cast<const uint32_t*>(a.out + a.index_at)[c];
-    const uint32_t* s = a.slots + (uint64_t)c * a.slot_dwords;
-    uint32_t* d = reinterpret_cast<uint32_t*>(a.out + a.payload_at + off);
+    const uint32_t off = reinterpret_cast<const uint32_t*>(sg->c + index_at)[c];
+    const uint32_t* s = a.slots + (uint64_t)slot * a.slot_dwords;
+    uint32_t* d = reinterpret_cast<uint32_t*>(sg->c + payload_at + off);
     const uint32_t s0 = start >> 5;
     for (uint32_t j = lane; j < ndw; j += 64) {
         const uint32_t lo = s[s0 + j];
@@ -587,17 +868,14 @@ __global__ __launch_bounds__(256) void k_encode_compact(const CompactArgs a) {
     }
 }
 
-sh_status launch_encode(const EncodeArgs& e, const IndexArgs& ix, const CompactArgs& cp,
+sh_status launch_encode(const CodecArgs& a, uint32_t total_blocks, uint32_t total_blocks_c,
                         void* stream) {
     hipStream_t s = (hipStream_t)stream;
-    if (e.n_chunks > 0) {
-        const uint32_t blocks = (e.n_chunks + 7) / 8;
-        hipLaunchKernelGGL(k_encode_chunks, dim3(blocks), dim3(kEncBlock), 0, s, e);
-    }
-    hipLaunchKernelGGL(k_encode_index, dim3(1), dim3(kScanBlock), 0, s, ix);
-    if (cp.n_chunks > 0) {
-        hipLaunchKernelGGL(k_encode_compact, dim3((cp.n_chunks + 3) / 4), dim3(256), 0, s, cp);
-    }
+    if (total_blocks > 0)
+        hipLaunchKernelGGL(k_encode_chunks, dim3(total_blocks), dim3(kEncBlock), 0, s, a);
+    hipLaunchKernelGGL(k_encode_index, dim3(a.nseg ? a.nseg : 1), dim3(kScanBlock), 0, s, a);
+    if (total_blocks_c > 0)
+        hipLaunchKernelGGL(k_encode_compact, dim3(total_blocks_c), dim3(256), 0, s, a);
     return hipGetLastError() == hipSuccess ? SH_OK : SH_ERR_HIP;
 }
 

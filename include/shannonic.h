@@ -15,7 +15,8 @@
  *   - Pointers named d_* are device (HBM) pointers; all others are host pointers.
  *   - stream is a hipStream_t (0 = the null stream).  Device work is enqueued on it and
  *     the call returns without waiting, except where a host result needs device data
- *     (sh_build_tables with x_on_device != 0 waits for its histogram).
+ *     or a host buffer is copied (sh_build_tables with x_on_device != 0,
+ *     sh_table_to_device and sh_tables_from_device wait for the stream).
  *   - The library allocates no device memory and keeps no global state: the caller owns
  *     every buffer, and sizes of the workspaces are exported.  Calls are thread-safe.
  *   - Argument errors are returned synchronously.  Errors found by the GPU (a corrupt
@@ -172,6 +173,81 @@ sh_status sh_encode(const sh_table* table, const sh_params* params, const int8_t
 sh_status sh_decode(const sh_table* table, const sh_params* params, const uint8_t* d_in,
                     uint64_t in_nbytes, int8_t* d_y, uint64_t n, int32_t* d_status,
                     void* stream);
+
+/* ---- device-resident tables and batches ---------------------------------------------
+ *
+ * A device table is the per-tensor state the kernels read, in device memory: the canonical
+ * table (lo, freq, hist, n), its decode and encode entries and the container header that
+ * goes with it.  It is sh_device_table_bytes() bytes, 16-byte aligned, and is written by
+ * sh_build_tables_batch (on the GPU, nothing returns to the host) or by sh_table_to_device
+ * (from a host sh_table).  Tables of a batch sit back to back: table i at
+ * d_tables + i * sh_device_table_bytes().
+ *
+ * The batch calls take host arrays of nseg device pointers and sizes and cover all the
+ * tensors in a few launches (tensors are grouped 48 to a launch), so a model's worth of
+ * small tensors costs no more launches than one large one.
+ */
+uint64_t sh_device_table_bytes(void);
+
+/*
+ * Upload a host table for params (K and log2_L must match) to d_table.  Waits for the
+ * copy.  An empty table (n = 0) is accepted: it encodes and decodes only empty tensors.
+ */
+sh_status sh_table_to_device(const sh_table* table, const sh_params* params, void* d_table,
+                             void* stream);
+
+/*
+ * Read count device tables (back to back at d_tables) into out[count] with one copy; waits
+ * for the stream.  table_status[i] (host) gets the status the GPU table build recorded
+ * for table i: SH_OK, or SH_ERR_UNSUPPORTED when more ranges hold values than there are
+ * states or the tensor has 2^32 values or more (out[i] is then not a usable table), or
+ * SH_ERR_CORRUPT_STREAM for bytes that do not form a table.  The call itself returns
+ * SH_ERR_HIP if the copy fails, else SH_OK.
+ */
+sh_status sh_tables_from_device(const void* d_tables, uint32_t count, sh_table* out,
+                                int32_t* table_status, void* stream);
+
+/*
+ * The offline table build of paper section 4.1, on the GPU, for nseg tensors: histogram,
+ * the exactly-K-range DP split (same integer cost and tie rule as sh_table_from_histogram,
+ * so the tables are identical), the state allocation, the spread and every derived entry.
+ * d_x[i] (device, 16-byte aligned when n[i] > 0) holds n[i] < 2^32 values.  d_tables:
+ * nseg device tables.  d_ws: device workspace, 256-byte aligned, of
+ * sh_build_tables_batch_workspace(nseg) bytes.  Asynchronous on stream; a tensor whose
+ * table cannot be built gets a status inside its table (see sh_tables_from_device), which
+ * the batch encode and decode turn into errors.
+ */
+uint64_t sh_build_tables_batch_workspace(uint32_t nseg);
+sh_status sh_build_tables_batch(const int8_t* const* d_x, const uint64_t* n, uint32_t nseg,
+                                const sh_params* params, void* d_tables, void* d_ws,
+                                uint64_t ws_bytes, void* stream);
+
+/*
+ * sh_encode for nseg tensors with device tables: tensor i (d_x[i], n[i] values) is
+ * encoded with table i into d_out[i] (out_cap[i] >= sh_encode_bound(n[i]) bytes, 4-byte
+ * aligned), and its sh_encode_info goes to d_info[i] (d_info may be NULL).  d_ws: device
+ * workspace, 256-byte aligned, of sh_encode_batch_workspace(n, nseg, params) bytes, reused
+ * by every launch of the batch.  Errors of any tensor go to the one *d_status: a value
+ * outside its table (SH_ERR_SYMBOL_NOT_IN_TABLE) or a table whose build failed
+ * (SH_ERR_UNSUPPORTED).  Asynchronous on stream.
+ */
+uint64_t sh_encode_batch_workspace(const uint64_t* n, uint32_t nseg, const sh_params* params);
+sh_status sh_encode_batch(const void* d_tables, const int8_t* const* d_x, const uint64_t* n,
+                          uint32_t nseg, const sh_params* params, uint8_t* const* d_out,
+                          const uint64_t* out_cap, void* d_ws, uint64_t ws_bytes,
+                          sh_encode_info* d_info, int32_t* d_status, void* stream);
+
+/*
+ * sh_decode for nseg containers with device tables: container i (d_in[i], in_nbytes[i]
+ * readable bytes) decodes into d_y[i] (n[i] values) with table i.  Every check of
+ * sh_decode applies to every container; the first error of any goes to *d_status.
+ * A table that failed to build, or was built from no values, decodes no values.
+ * Asynchronous on stream.
+ */
+sh_status sh_decode_batch(const void* d_tables, const uint8_t* const* d_in,
+                          const uint64_t* in_nbytes, int8_t* const* d_y, const uint64_t* n,
+                          uint32_t nseg, const sh_params* params, int32_t* d_status,
+                          void* stream);
 
 /*
  * Theorem-1 terms of a table and the measured rates of a container of n values, on the

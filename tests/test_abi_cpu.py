@@ -131,3 +131,47 @@ def test_argument_checks_are_synchronous():
 def test_status_strings():
     for st in range(-6, 1):
         assert codec.status_string(st) and "unknown" not in codec.status_string(st)
+
+
+def test_batch_argument_checks_are_synchronous():
+    lib = codec.lib()
+    p = codec.Params()
+    pc = p.c()
+    fake = 1 << 20  # never dereferenced
+    ns = [100000, 0, 4097]
+    ptrs = codec._ptrs([fake] * 3)
+    n_arr = codec._u64s(ns)
+    caps = codec._u64s([codec.sh_encode_bound(n, p) for n in ns])
+    ws = codec.sh_encode_batch_workspace(ns, p)
+    assert ws >= max(codec.sh_encode_workspace(n, p) for n in ns)
+    # nothing to do
+    assert lib.sh_encode_batch(fake, ptrs, n_arr, 0, C.byref(pc), ptrs, caps, fake, 0, None,
+                               None, None) == codec.SH_OK
+    # workspace, capacity, alignment
+    assert lib.sh_encode_batch(fake, ptrs, n_arr, 3, C.byref(pc), ptrs, caps, fake, ws - 1,
+                               None, None, None) == codec.SH_ERR_BUFFER_TOO_SMALL
+    small = codec._u64s([codec.sh_encode_bound(n, p) - (i == 2) for i, n in enumerate(ns)])
+    assert lib.sh_encode_batch(fake, ptrs, n_arr, 3, C.byref(pc), ptrs, small, fake, ws,
+                               None, None, None) == codec.SH_ERR_BUFFER_TOO_SMALL
+    assert lib.sh_encode_batch(fake + 4, ptrs, n_arr, 3, C.byref(pc), ptrs, caps, fake, ws,
+                               None, None, None) == codec.SH_ERR_INVALID_ARG
+    bad = codec.Params(streams=16).c()
+    assert lib.sh_encode_batch(fake, ptrs, n_arr, 3, C.byref(bad), ptrs, caps, fake, ws,
+                               None, None, None) == codec.SH_ERR_UNSUPPORTED
+    # a container shorter than its own index
+    short = codec._u64s([codec.sh_encode_bound(n, p) for n in ns[:2]] + [40])
+    assert lib.sh_decode_batch(fake, ptrs, short, ptrs, n_arr, 3, C.byref(pc), None,
+                               None) == codec.SH_ERR_CORRUPT_STREAM
+    # table build: workspace and parameters
+    need = codec.sh_build_tables_batch_workspace(3)
+    assert need > codec.sh_build_tables_batch_workspace(1) > 0
+    assert lib.sh_build_tables_batch(ptrs, n_arr, 3, C.byref(pc), fake, fake, need - 1,
+                                     None) == codec.SH_ERR_BUFFER_TOO_SMALL
+    big = codec.Params(log2_L=10).c()
+    assert lib.sh_build_tables_batch(ptrs, n_arr, 3, C.byref(big), fake, fake, need,
+                                     None) == codec.SH_ERR_UNSUPPORTED
+    # host table upload: K mismatch is found before any copy
+    t = codec.sh_table_from_histogram(O.histogram(D.tiny()), p)
+    p8 = codec.Params(K=8).c()
+    assert lib.sh_table_to_device(C.byref(t), C.byref(p8), fake, None) == codec.SH_ERR_INVALID_ARG
+    assert codec.sh_device_table_bytes() % 16 == 0
