@@ -1,6 +1,6 @@
 """Build libshannonic.so in-tree with hipcc for gfx950.
 
-The library is the product path: HIP kernels (csrc/kernels.hip), the host table builder
+The library is the product path: HIP kernels (csrc/k_*.hip), the host table builder
 (csrc/host_tables.cpp) and the C ABI (csrc/api.cpp, declared in include/shannonic.h).
 """
 from __future__ import annotations
@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libshannonic.so")
-SOURCES = ["kernels.hip", "host_tables.cpp", "api.cpp"]
+SOURCES = ["k_build.hip", "k_encode.hip", "k_decode.hip", "host_tables.cpp", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -123,7 +123,7 @@ sh_status sh_histogram(const int8_t* d_x, uint64_t n, uint64_t* d_hist, void* st
     h.hist = d_hist;
     h.segs[0].x = (uint8_t*)d_x;
     h.segs[0].n = n;
-    h.n_blocks = (uint32_t)((n + (1u << 18) - 1) >> 18);
+    h.n_blocks = (uint32_t)((n + kHistBytesPerBlock - 1) / kHistBytesPerBlock);
     return launch_histogram(h, 1, stream);
 }
 
@@ -132,25 +132,30 @@ sh_status sh_table_from_histogram(const uint64_t* hist, const sh_params* params,
     return table_from_histogram(hist, params->K, params->log2_L, out);
 }
 
-uint64_t sh_build_tables_workspace(void) { return 256 * sizeof(uint64_t); }
+uint64_t sh_build_tables_workspace(void) {
+    return align256(kDTBytes) + sh_build_tables_batch_workspace(1);
+}
 
 sh_status sh_build_tables(const int8_t* x, uint64_t n, int x_on_device, const sh_params* params,
                           void* d_ws, uint64_t ws_bytes, void* stream, sh_table* out) {
     if (!params || !out || (n > 0 && !x)) return SH_ERR_INVALID_ARG;
-    uint64_t h[256] = {0};
-    if (x_on_device) {
-        if (!d_ws || ws_bytes < sh_build_tables_workspace()) return SH_ERR_BUFFER_TOO_SMALL;
-        uint64_t* d_hist = (uint64_t*)d_ws;
-        sh_status st = sh_histogram(x, n, d_hist, stream);
-        if (st != SH_OK) return st;
-        if (hipMemcpyAsync(h, d_hist, sizeof(h), hipMemcpyDeviceToHost, (hipStream_t)stream) !=
-                hipSuccess ||
-            hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
-            return SH_ERR_HIP;
-    } else {
+    if (!x_on_device) {
+        uint64_t h[256] = {0};
         for (uint64_t i = 0; i < n; ++i) h[(uint8_t)x[i] ^ 0x80]++;
+        return table_from_histogram(h, params->K, params->log2_L, out);
     }
-    return table_from_histogram(h, params->K, params->log2_L, out);
+    // on the GPU: histogram and the whole table build, then one copy back
+    sh_status st = check_params(params);
+    if (st != SH_OK) return st;
+    if (!d_ws || !aligned(d_ws, 256)) return SH_ERR_INVALID_ARG;
+    if (ws_bytes < sh_build_tables_workspace()) return SH_ERR_BUFFER_TOO_SMALL;
+    uint8_t* dt = (uint8_t*)d_ws;
+    uint8_t* ws = dt + align256(kDTBytes);
+    st = sh_build_tables_batch(&x, &n, 1, params, dt, ws, sh_build_tables_batch_workspace(1), stream);
+    if (st != SH_OK) return st;
+    int32_t table_status = SH_OK;
+    st = sh_tables_from_device(dt, 1, out, &table_status, stream);
+    return st != SH_OK ? st : table_status;
 }
 
 // ---- device-resident tables ------------------------------------------------------------
@@ -205,8 +210,8 @@ sh_status sh_tables_from_device(const void* d_tables, uint32_t count, sh_table* 
 }
 
 uint64_t sh_build_tables_batch_workspace(uint32_t nseg) {
-    return align256(8ull * 256 * nseg) + align256(8ull * kCostEntries * nseg) +
-           align256(2ull * 257 * 257 * nseg);
+    return align256(8ull * 256 * nseg) + align256(4ull * kCostEntries * nseg) +
+           align256((uint64_t)kArgBytes * nseg);
 }
 
 sh_status sh_build_tables_batch(const int8_t* const* d_x, const uint64_t* n, uint32_t nseg,
@@ -224,8 +229,8 @@ sh_status sh_build_tables_batch(const int8_t* const* d_x, const uint64_t* n, uin
     }
     uint8_t* ws = (uint8_t*)d_ws;
     uint64_t* hist = (uint64_t*)ws;
-    uint64_t* cost = (uint64_t*)(ws + align256(8ull * 256 * nseg));
-    uint16_t* arg = (uint16_t*)(ws + align256(8ull * 256 * nseg) + align256(8ull * kCostEntries * nseg));
+    uint32_t* scost = (uint32_t*)(ws + align256(8ull * 256 * nseg));
+    uint8_t* arg = ws + align256(8ull * 256 * nseg) + align256(4ull * kCostEntries * nseg);
     for (auto [b, e] : groups_of(nseg)) {
         HistArgs h;
         std::memset(&h, 0, sizeof(h));
@@ -237,7 +242,7 @@ sh_status sh_build_tables_batch(const int8_t* const* d_x, const uint64_t* n, uin
             sd.x = (uint8_t*)d_x[i];
             sd.n = n[i];
             sd.first_block = blocks;
-            blocks += (uint32_t)((n[i] + (1u << 18) - 1) >> 18);
+            blocks += (uint32_t)((n[i] + kHistBytesPerBlock - 1) / kHistBytesPerBlock);
         }
         h.n_blocks = blocks;
         st = launch_histogram(h, e - b, stream);
@@ -246,7 +251,7 @@ sh_status sh_build_tables_batch(const int8_t* const* d_x, const uint64_t* n, uin
     BuildArgs bd;
     bd.hist = hist;
     bd.tables = (uint32_t*)d_tables;
-    bd.cost = cost;
+    bd.scost = scost;
     bd.arg = arg;
     bd.nseg = nseg;
     bd.K = params->K;

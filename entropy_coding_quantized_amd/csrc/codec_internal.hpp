@@ -130,6 +130,8 @@ struct CodecArgs {
     };
 };
 
+constexpr uint32_t kHistBytesPerBlock = 1u << 16;  // values per histogram block
+
 struct HistArgs {
     uint32_t nseg;
     uint32_t n_blocks;
@@ -140,11 +142,12 @@ struct HistArgs {
 struct BuildArgs {
     const uint64_t* hist;   // nseg x 256
     uint32_t* tables;       // nseg x kDTDwords
-    uint64_t* cost;         // workspace: nseg x kCostEntries
-    uint16_t* arg;          // workspace: nseg x 257 x 257
+    uint32_t* scost;        // workspace: nseg x kCostEntries cost factors
+    uint8_t* arg;           // workspace: nseg x kArgBytes, the DP's choice per (k, i < 256)
     uint32_t nseg, K, R, C, S;
 };
 constexpr uint32_t kCostEntries = 257 * 256 / 2;  // [j, i) for 0 <= j < i <= 256
+constexpr uint32_t kArgBytes = 257 * 256;
 
 sh_status launch_histogram(const HistArgs& h, uint32_t nseg_zero, void* stream);
 sh_status launch_build_tables(const BuildArgs& b, void* stream);

@@ -1,0 +1,81 @@
+// Device helpers shared by the HIP kernels of the Shannonic codec (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "codec_internal.hpp"
+
+namespace shn {
+
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over [p, p + bytes): accesses past the end read 0 / are dropped.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// Inclusive prefix sum within each 32-lane half of the wavefront (DPP row shifts, then
+// the last lane of rows 0 and 2 added into rows 1 and 3).
+__device__ __forceinline__ uint32_t scan32(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false); // row_bcast:15
+    return v;
+}
+
+// Value of lane 31 of this lane's 32-lane half (ds_swizzle bit mode, or_mask = 31).
+__device__ __forceinline__ uint32_t bcast31(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x3E0);
+}
+
+typedef const __attribute__((address_space(3))) uint32_t lds_u32;
+
+// LDS byte offset of a __shared__ object
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Record an error for the whole wavefront: one atomic from the first lane that has one,
+// skipped when an error is already recorded (the first error wins).
+__device__ __forceinline__ void report(int32_t* status, int32_t code, bool mine = true) {
+    const uint64_t who = __builtin_amdgcn_ballot_w64(mine);
+    if (!status || who == 0) return;
+    const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    if (lane == (uint32_t)__builtin_ctzll(who) && __atomic_load_n(status, __ATOMIC_RELAXED) == 0)
+        atomicCAS(status, 0, code);
+}
+
+// ------------------------------------------------------------------------------------
+// segments: every launch covers one or more tensors; a block finds its tensor by a binary
+// search over the descriptors' first blocks (uniform, so it runs on the scalar unit)
+// ------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t find_seg_index(const SegDesc* segs, uint32_t nseg,
+                                                    uint32_t block, bool compaction) {
+    uint32_t lo = 0, hi = nseg;  // the last segment whose first block <= block
+    while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) >> 1;
+        const uint32_t fb = compaction ? segs[mid].first_block_c : segs[mid].first_block;
+        if (fb <= block) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+__device__ __forceinline__ const SegDesc* find_seg(const SegDesc* segs, uint32_t nseg,
+                                                    uint32_t block, bool compaction) {
+    return &segs[find_seg_index(segs, nseg, block, compaction)];
+}
+__device__ __forceinline__ const SegDesc* codec_seg(const CodecArgs& a, uint32_t block,
+                                                     bool compaction) {
+    return a.nseg == 0 ? &a.one.seg : find_seg(a.many, a.nseg, block, compaction);
+}
+
+__device__ __forceinline__ uint32_t header_bytes_dev(uint32_t K) {
+    return (kHeaderFixed + 3 * K - 1 + 3) / 4 * 4;
+}
+
+}  // namespace shn

@@ -10,6 +10,7 @@
 // implementation reaches the same partition, exact ties included); the pages do not fix
 // the precision of the objective.
 #include <cstring>
+#include <queue>
 #include <vector>
 
 #include "codec_internal.hpp"
@@ -109,21 +110,28 @@ sh_status allocate_states(const uint64_t* count, uint32_t K, uint32_t L, uint16_
     }
     if (used == 0) return SH_OK;
     if (used > L) return SH_ERR_UNSUPPORTED;
-    std::vector<uint64_t> gain_of(L + 1, 0);  // log2(f + 1) - log2 f in fixed point
-    for (uint32_t v = 1; v <= L; ++v) gain_of[v] = fixed_log2(v + 1) - fixed_log2(v);
-    while (used < L) {
-        uint32_t best = K;
-        uint64_t bg = 0;
-        for (uint32_t k = 0; k < K; ++k) {
-            if (!count[k]) continue;
-            const uint64_t g = count[k] * gain_of[f[k]];
-            if (best == K || g > bg) {
-                best = k;
-                bg = g;
-            }
-        }
-        f[best]++;
-        used++;
+    // log2(f + 1) - log2 f in fixed point, for every f up to the largest L: built once
+    static const std::vector<uint64_t> gain_of = [] {
+        std::vector<uint64_t> g((1u << kMaxLog2LHost) + 1, 0);
+        for (uint32_t v = 1; v < g.size(); ++v) g[v] = fixed_log2(v + 1) - fixed_log2(v);
+        return g;
+    }();
+    if (L > (1u << kMaxLog2LHost)) return SH_ERR_UNSUPPORTED;
+    // a max-heap of each occupied range's next gain; on equal gains the smaller k is on top
+    struct Item {
+        uint64_t g;
+        uint32_t k;
+        bool operator<(const Item& o) const { return g < o.g || (g == o.g && k > o.k); }
+    };
+    std::priority_queue<Item> heap;
+    for (uint32_t k = 0; k < K; ++k)
+        if (count[k]) heap.push({count[k] * gain_of[1], k});
+    for (; used < L; ++used) {
+        const Item top = heap.top();
+        heap.pop();
+        const uint32_t k = top.k;
+        f[k]++;
+        heap.push({count[k] * gain_of[f[k]], k});
     }
     return SH_OK;
 }

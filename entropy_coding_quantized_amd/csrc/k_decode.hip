@@ -1,0 +1,293 @@
+// Decode kernel of the Shannonic codec for gfx950 (CDNA4, wave64).
+//
+// Method: "Shannonic: Efficient Entropy-Optimal Compression for ML Workloads" (MLSys 2026),
+// talk notes, "Runtime encoding/decoding" (paper section 4.2, Algorithm 2): per value a
+// range id through tANS plus raw offset bits, with table lookups, shifts, masks and adds
+// only.  The chunked, lane-interleaved layout and everything about the GPU mapping are
+// this library's own design; the pages give no GPU design.
+//
+// Mapping: one chunk of C values per half wavefront (32 lanes), one tANS state machine per
+// lane.  At every step the 32 lanes of a chunk code 32 consecutive values, so their fields
+// sit back to back in the bit stream; a 32-lane DPP prefix sum of the field lengths gives
+// each lane its bit position.  Compressed words are staged through a per-chunk LDS ring
+// fed by 128-bit loads; the decode table (<= 2 KB) lives in LDS.  No MFMA: there is no
+// dense contraction.
+#include "device_common.hpp"
+
+namespace shn {
+
+// ------------------------------------------------------------------------------------
+// decode
+// ------------------------------------------------------------------------------------
+constexpr uint32_t kRing = 256;               // compressed dwords resident per chunk
+// each ring starts on a 2 KB boundary (so the wrapped word address is one and-or) and is
+// followed by a copy of its dword 0, so a two-word read never wraps
+constexpr uint32_t kRingStride = 512;
+constexpr uint32_t kFill = 128;               // dwords per refill: 32 lanes x 16 bytes
+// decode table in LDS, 8 bytes per slot (a random 8-byte LDS read costs less than half of
+// a 16-byte one): e0 = need | maxo << 16 | base << 24, e1 = w | next << 16, where need =
+// w_s + nb, maxo = |range| - 1, base = the range's first value as int8 bits and next = the
+// LDS byte address of the entry reached with zero state bits
+constexpr uint32_t kTabDwords = 512;
+
+// 16 bytes of the chunk starting at dword d (dwords at or past cdw read as 0).
+__device__ __forceinline__ v4u load_words(rsrc_t r, uint32_t chunk_byte, uint32_t d,
+                                          uint32_t cdw) {
+    if (d + 4 <= cdw)
+        return __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(
+                                           r, (int)(chunk_byte + 4 * d), 0, 0));
+    v4u v = {0, 0, 0, 0};
+    for (uint32_t k = 0; k < 4; ++k)
+        if (d + k < cdw)
+            v[k] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(chunk_byte + 4 * (d + k)), 0, 0);
+    return v;
+}
+
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+
+typedef const __attribute__((address_space(3))) v2u lds_v2u;
+
+// Per-chunk decoder state of one half wavefront.
+struct DecChain {
+    uint32_t nc, cdw, cbyte, ring, ring_byte, lanes, pos, addr, res_hi, refill_at, err, vout;
+    v4u pf;
+};
+
+constexpr int kDecBlock = 256;  // 4 wavefronts
+// ILP chunks per lane: a wavefront decodes 2 * ILP chunks, lanes 32h..32h+31 take chunks
+// 2k + h (k < ILP) of the wavefront's group.  ILP = 1 is the one launched: measured on
+// MI355X, two independent chains per lane ran slower than twice as many wavefronts.
+template <int ILP>
+__global__ __launch_bounds__(kDecBlock) void k_decode(const CodecArgs a) {
+    constexpr uint32_t kChunksPerWave = 2 * ILP;
+    constexpr uint32_t kChunksPerBlock = kDecBlock / 64 * kChunksPerWave;
+    __shared__ __align__(16) uint32_t sm[kTabDwords + kChunksPerBlock * kRingStride];
+    const uint32_t tid = threadIdx.x, lane = tid & 63, li = lane & 31, hw = lane >> 5;
+    const uint32_t block = __builtin_amdgcn_readfirstlane(blockIdx.x);
+    const SegDesc* sg = codec_seg(a, block, false);
+    const uint32_t bseg = block - sg->first_block;  // block within its segment
+    // wavefront index within the segment, uniform so that descriptors stay scalar
+    const uint32_t wid = __builtin_amdgcn_readfirstlane(bseg * (kDecBlock / 64) + (tid >> 6));
+    const uint32_t wv = wid & (kDecBlock / 64 - 1);
+    const uint32_t tab_byte = lds_offset(sm);
+    const uint32_t* dec = sg->tab ? sg->tab + kDTDec : a.one.tab;
+    const uint32_t* hdr = sg->tab ? sg->tab + kDTHdr : a.one.hdr;
+    const uint32_t n_chunks = sg->n_chunks;
+    const uint64_t n = sg->n;
+    const uint32_t index_at = header_bytes_dev(a.K);
+    const uint32_t payload_at = index_at + 4 * (n_chunks + 1);
+    const uint64_t in_nbytes = sg->c_bytes;
+
+    // rearrange the table's entries into the LDS form
+    for (uint32_t i = tid; i < a.L; i += kDecBlock) {
+        const uint32_t e0 = dec[2 * i], e1 = dec[2 * i + 1];
+        sm[2 * i] = (e0 & 0xFFFF) | (e1 & 0x00FF0000u) | ((e1 & 0xFF00u) << 16);
+        sm[2 * i + 1] = (e1 & 31) | ((tab_byte + (e0 >> 16)) << 16);
+    }
+
+    const rsrc_t rin = make_rsrc(sg->c, (uint32_t)in_nbytes);
+    if (wid == 0) {
+        // header and index ends: the container must belong to this table and fit in_nbytes
+        // a device table that failed to build, or was built from no values, decodes nothing
+        bool bad = sg->tab && (sg->tab[kDTStatus] != 0 ||
+                               (n > 0 && (sg->tab[kDTN] | sg->tab[kDTN + 1]) == 0));
+        for (uint32_t i = lane; i < index_at / 4; i += 64)
+            bad |= __builtin_amdgcn_raw_buffer_load_b32(rin, (int)(4 * i), 0, 0) !=
+                   header_dword(hdr, i, n, n_chunks);
+        if (lane == 0) {
+            const uint32_t first = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)index_at, 0, 0);
+            const uint32_t last = __builtin_amdgcn_raw_buffer_load_b32(
+                rin, (int)(index_at + 4 * n_chunks), 0, 0);
+            bad |= first != 0 || (uint64_t)payload_at + last > in_nbytes;
+        }
+        report(a.status, SH_ERR_CORRUPT_STREAM, bad);
+    }
+
+    // output: per-wavefront descriptor over the wavefront's chunks
+    const uint32_t group = kChunksPerWave * wid;
+    const uint64_t grp_first = (uint64_t)group * a.C;
+    const uint64_t grp_len = grp_first < n ? n - grp_first : 0;
+    const uint64_t grp_cap = (uint64_t)kChunksPerWave * a.C;
+    const rsrc_t rout = make_rsrc(sg->x + (grp_first < n ? grp_first : 0),
+                                  (uint32_t)(grp_len < grp_cap ? grp_len : grp_cap));
+
+    DecChain ch[ILP];
+#pragma unroll
+    for (int k = 0; k < ILP; ++k) {
+        DecChain& c = ch[k];
+        const uint32_t slot = 2 * k + hw;
+        const uint32_t chunk = group + slot;
+        c.ring = kTabDwords + (wv * kChunksPerWave + slot) * kRingStride;
+        c.ring_byte = tab_byte + 4 * c.ring;
+        c.vout = slot * a.C + li;
+        c.nc = 0;
+        c.cdw = 0;
+        c.cbyte = 0;
+        c.err = 0;
+        if (chunk < n_chunks) {
+            const uint32_t o0 = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)(index_at + 4 * chunk), 0, 0);
+            const uint32_t o1 = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)(index_at + 4 * chunk + 4), 0, 0);
+            const uint64_t first = (uint64_t)chunk * a.C;
+            const uint32_t m = (uint32_t)((n - first) < a.C ? (n - first) : a.C);
+            const bool ok = o0 <= o1 && ((o0 | o1) & 3) == 0 &&
+                            (o1 - o0) <= 4 * chunk_bound_dwords(m, a.R) &&
+                            (uint64_t)payload_at + o1 <= in_nbytes;
+            if (ok) {
+                c.nc = m;
+                c.cdw = (o1 - o0) >> 2;
+                c.cbyte = payload_at + o0;
+            } else {
+                c.err = 1;
+            }
+        }
+        c.lanes = c.nc < 32 ? c.nc : 32;
+        // first two refills, plus the third in flight
+        for (uint32_t b = 0; b < 2; ++b) {
+            const uint32_t d = b * kFill + 4 * li;
+            const v4u v = load_words(rin, c.cbyte, d, c.cdw);
+            *reinterpret_cast<v4u*>(&sm[c.ring + d]) = v;
+            if (b == 0 && li == 0) sm[c.ring + kRing] = v[0];
+        }
+        c.res_hi = 2 * kFill;  // dwords [res_hi - kRing, res_hi) are in the ring
+        c.pf = load_words(rin, c.cbyte, c.res_hi + 4 * li, c.cdw);
+        // refills are checked every other step; one is due once the next two steps could
+        // read past res_hi (each advances at most 16 dwords): pos >> 5 >= res_hi - 33
+        c.refill_at = c.res_hi < c.cdw ? (c.res_hi - 33) * 32 : 0xFFFFFFFFu;
+    }
+    __syncthreads();
+
+    uint32_t nc_min = 0xFFFFFFFFu, nc_max = 0;
+#pragma unroll
+    for (int k = 0; k < ILP; ++k) {
+        DecChain& c = ch[k];
+        // initial slots: lane l's R bits at l * R
+        c.addr = tab_byte;  // LDS byte address of the current slot's decode entry
+        if (li < c.lanes) {
+            const uint32_t p = li * a.R;
+            const uint32_t bits = __builtin_amdgcn_alignbit(sm[c.ring + (p >> 5) + 1], sm[c.ring + (p >> 5)], p);
+            c.addr = tab_byte + ((bits & (a.L - 1)) << 3);
+        }
+        c.pos = c.lanes * a.R;
+        const uint32_t lo = __builtin_amdgcn_readlane(c.nc, 0), hi = __builtin_amdgcn_readlane(c.nc, 32);
+        nc_min = nc_min < lo ? nc_min : lo;
+        nc_min = nc_min < hi ? nc_min : hi;
+        nc_max = nc_max > lo ? nc_max : lo;
+        nc_max = nc_max > hi ? nc_max : hi;
+    }
+    const uint32_t full = nc_min >> 5;
+    const uint32_t steps = (nc_max + 31) >> 5;
+    uint64_t bad_offsets = 0;  // lanes that decoded an offset outside its range
+
+    auto refill = [&](DecChain& c) {
+        if (c.pos >= c.refill_at) {
+            const uint32_t d = (c.res_hi + 4 * li) & (kRing - 1);
+            *reinterpret_cast<v4u*>(&sm[c.ring + d]) = c.pf;
+            if (d == 0) sm[c.ring + kRing] = c.pf[0];
+            c.res_hi += kFill;
+            c.refill_at = c.res_hi < c.cdw ? (c.res_hi - 33) * 32 : 0xFFFFFFFFu;
+            c.pf = load_words(rin, c.cbyte, c.res_hi + 4 * li, c.cdw);
+        }
+    };
+
+    // One step of every chain: each lane decodes one value per chain.  The entries for the
+    // step were read at the end of the previous one, so the serial path per chain is
+    // scan -> ring read -> bit extract -> next entry read; the chains go through these
+    // phases side by side so that one chain's LDS waits overlap the other's work.
+    auto full_step = [&](const v2u (&e)[ILP], v2u (&en)[ILP], uint32_t t) {
+        uint32_t incl[ILP], start[ILP], w0[ILP], w1[ILP];
+#pragma unroll
+        for (int k = 0; k < ILP; ++k) {
+            const uint32_t posm = ch[k].pos - e[k][0];   // bits 16.. of e0 and sums ignored
+            incl[k] = scan32(e[k][0]);
+            start[k] = posm + incl[k];                   // only bits 0..12 matter below
+        }
+#pragma unroll
+        for (int k = 0; k < ILP; ++k) {
+            const uint32_t rb = ((start[k] >> 3) & (4 * kRing - 4)) | ch[k].ring_byte;
+            const lds_u32* rp = (const lds_u32*)(uintptr_t)rb;
+            w0[k] = rp[0];
+            w1[k] = rp[1];
+        }
+#pragma unroll
+        for (int k = 0; k < ILP; ++k) {
+            const uint32_t bits = __builtin_amdgcn_alignbit(w1[k], w0[k], start[k]);
+            const uint32_t v = __builtin_amdgcn_ubfe(bits, 0, e[k][0]);   // the field (need bits)
+            const uint32_t o = __builtin_amdgcn_ubfe(bits, 0, e[k][1]);   // its low w_s bits
+            ch[k].addr = ((v >> (e[k][1] & 31)) << 3) + (e[k][1] >> 16);
+            en[k] = *(lds_v2u*)(uintptr_t)ch[k].addr;
+            bad_offsets |= __builtin_amdgcn_ballot_w64(o > ((e[k][0] >> 16) & 0xFF));
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(o + (e[k][0] >> 24)), rout,
+                                                 (int)ch[k].vout, (int)(t * 32), 0);
+        }
+#pragma unroll
+        for (int k = 0; k < ILP; ++k) ch[k].pos += bcast31(incl[k]) & 0xFFFFu;
+    };
+
+    v2u e[ILP], e2[ILP];
+#pragma unroll
+    for (int k = 0; k < ILP; ++k) e[k] = *(lds_v2u*)(uintptr_t)ch[k].addr;
+    uint32_t t = 0;
+    for (; t + 2 <= full; t += 2) {  // two steps per trip, so the entries alternate registers
+        full_step(e, e2, t);
+        full_step(e2, e, t + 1);
+#pragma unroll
+        for (int k = 0; k < ILP; ++k) refill(ch[k]);
+    }
+    if (t < full) {
+        full_step(e, e2, t);
+#pragma unroll
+        for (int k = 0; k < ILP; ++k) {
+            e[k] = e2[k];
+            refill(ch[k]);
+        }
+        ++t;
+    }
+    for (; t < steps; ++t) {  // chunks shorter than the others: lanes past n_c take no bits
+#pragma unroll
+        for (int k = 0; k < ILP; ++k) {
+            DecChain& c = ch[k];
+            const bool act = t * 32 + li < c.nc;
+            v2u ek = e[k];
+            if (!act) ek = v2u{0, 0};
+            const uint32_t incl = scan32(ek[0]);
+            const uint32_t start = c.pos - ek[0] + incl;
+            const uint32_t rb = ((start >> 3) & (4 * kRing - 4)) | c.ring_byte;
+            const lds_u32* rp = (const lds_u32*)(uintptr_t)rb;
+            const uint32_t bits = __builtin_amdgcn_alignbit(rp[1], rp[0], start);
+            const uint32_t v = __builtin_amdgcn_ubfe(bits, 0, ek[0]);
+            const uint32_t o = __builtin_amdgcn_ubfe(bits, 0, ek[1]);
+            if (act) {
+                c.err |= o > ((ek[0] >> 16) & 0xFF);
+                __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(o + (ek[0] >> 24)), rout,
+                                                     (int)c.vout, (int)(t * 32), 0);
+                c.addr = ((v >> (ek[1] & 31)) << 3) + (ek[1] >> 16);
+            }
+            c.pos += bcast31(incl) & 0xFFFFu;
+            e[k] = *(lds_v2u*)(uintptr_t)c.addr;
+            refill(c);
+        }
+    }
+
+    // a valid chunk leaves every lane in slot 0 and ends in its last word, zero-padded
+    uint32_t err = 0;
+#pragma unroll
+    for (int k = 0; k < ILP; ++k) {
+        DecChain& c = ch[k];
+        err |= c.err;
+        if (c.nc > 0) {
+            if (li < c.lanes && c.addr != tab_byte) err = 1;
+            if (((c.pos + 31) >> 5) != c.cdw) err = 1;
+            else if ((c.pos & 31) && (sm[c.ring + ((c.pos >> 5) & (kRing - 1))] >> (c.pos & 31)) != 0)
+                err = 1;
+        }
+    }
+    report(a.status, SH_ERR_CORRUPT_STREAM, err != 0 || bad_offsets != 0);
+}
+
+sh_status launch_decode(const CodecArgs& a, uint32_t total_blocks, void* stream) {
+    if (total_blocks == 0) return SH_OK;
+    hipLaunchKernelGGL(k_decode<1>, dim3(total_blocks), dim3(kDecBlock), 0, (hipStream_t)stream, a);
+    return hipGetLastError() == hipSuccess ? SH_OK : SH_ERR_HIP;
+}
+
+}  // namespace shn

@@ -1,0 +1,245 @@
+// Encode kernels of the Shannonic codec for gfx950 (CDNA4, wave64): the inverse of the
+// decode mapping ("Runtime encoding/decoding", paper section 4.2, Algorithm 2, of the
+// Shannonic talk notes), run backwards per lane, then a chunk index and a compaction pass.
+#include "device_common.hpp"
+
+namespace shn {
+
+// ------------------------------------------------------------------------------------
+// encode, kernel 1: every chunk into a worst-case slot of the workspace
+// ------------------------------------------------------------------------------------
+// tANS encodes backwards.  Each lane walks its values from the last step to the first;
+// at every step the 32 fields of a chunk are placed right to left: the step's fields end
+// where the later steps' fields begin, so a 32-lane prefix sum of the lengths gives every
+// field's bit position.  Fields are OR-ed into a 256-dword LDS ring that is flushed to
+// the chunk's slot 128 dwords at a time, highest first; the chunk ends up right-aligned
+// in its slot with the lanes' final states (the decoder's initial states) in front.
+constexpr int kEncBlock = 256;
+constexpr uint32_t kERing = 256;
+constexpr uint32_t kEncHalfDwords = 256 /* input tile, 32 steps x 32 lanes bytes */ + kERing;
+constexpr uint32_t kVtDwords = 512 + 64;  // value table + encTable bytes
+
+__device__ __forceinline__ void ring_or(uint32_t* sm, uint32_t ring, uint32_t pos,
+                                        uint32_t field, uint32_t len) {
+    if (len == 0) return;
+    const uint64_t wide = (uint64_t)field << (pos & 31);
+    const uint32_t d = pos >> 5;
+    atomicOr(&sm[ring + (d & (kERing - 1))], (uint32_t)wide);
+    if ((pos & 31) + len > 32) atomicOr(&sm[ring + ((d + 1) & (kERing - 1))], (uint32_t)(wide >> 32));
+}
+
+__global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const CodecArgs a) {
+    __shared__ __align__(16) uint32_t sm[kVtDwords + 8 * kEncHalfDwords];
+    const uint32_t tid = threadIdx.x, lane = tid & 63, li = lane & 31, hw = lane >> 5;
+    const uint32_t block = __builtin_amdgcn_readfirstlane(blockIdx.x);
+    const SegDesc* sg = codec_seg(a, block, false);
+    const uint32_t bseg = block - sg->first_block;
+    const uint32_t wid = __builtin_amdgcn_readfirstlane(bseg * (kEncBlock / 64) + (tid >> 6));
+    const uint32_t wv = wid & (kEncBlock / 64 - 1);
+    const uint32_t* vt = sg->tab ? sg->tab + kDTVt : a.one.tab;
+    const uint8_t* es_src = sg->tab ? reinterpret_cast<const uint8_t*>(sg->tab + kDTEs) : a.one.es;
+    const uint32_t n_chunks = sg->n_chunks;
+    const uint64_t n = sg->n;
+    for (uint32_t i = tid; i < 512; i += kEncBlock) sm[i] = vt[i];
+    for (uint32_t i = tid; i < 64; i += kEncBlock) {
+        sm[512 + i] = (uint32_t)es_src[4 * i] | ((uint32_t)es_src[4 * i + 1] << 8) |
+                      ((uint32_t)es_src[4 * i + 2] << 16) | ((uint32_t)es_src[4 * i + 3] << 24);
+    }
+    const uint8_t* es = reinterpret_cast<const uint8_t*>(&sm[512]);
+    const uint32_t half = kVtDwords + (wv * 2 + hw) * kEncHalfDwords;
+    const uint32_t tile = half;            // 256 dwords: bytes of 32 steps x 32 lanes
+    const uint32_t ring = half + 256;      // 256 dwords
+    for (uint32_t i = li; i < kERing; i += 32) sm[ring + i] = 0;
+
+    const uint32_t pair = 2 * wid;
+    const uint32_t chunk = pair + hw;
+    const uint64_t pair_first = (uint64_t)pair * a.C;
+    const uint64_t pair_len = pair_first < n ? n - pair_first : 0;
+    const rsrc_t rin = make_rsrc(sg->x + (pair_first < n ? pair_first : 0),
+                                 (uint32_t)(pair_len < 2ull * a.C ? pair_len : 2ull * a.C));
+    const uint32_t slot0 = sg->slot_base + (pair < n_chunks ? pair : 0);
+    const rsrc_t rslot = make_rsrc(a.slots + (uint64_t)slot0 * a.slot_dwords, 8u * a.slot_dwords);
+    const uint32_t in_base = hw * a.C;          // byte offset of this chunk in rin
+    const uint32_t slot_base = hw * a.slot_dwords * 4;
+    uint32_t nc = 0;
+    if (chunk < n_chunks) {
+        const uint64_t first = (uint64_t)chunk * a.C;
+        nc = (uint32_t)((n - first) < a.C ? (n - first) : a.C);
+    }
+    const uint32_t lanes = nc < 32 ? nc : 32;
+    const uint32_t nc_lo = __builtin_amdgcn_readlane(nc, 0), nc_hi = __builtin_amdgcn_readlane(nc, 32);
+    const uint32_t steps = ((nc_lo > nc_hi ? nc_lo : nc_hi) + 31) >> 5;
+    const uint32_t L = a.L, R1 = a.R + 1;
+
+    // 32 bytes of input tile tl for this lane (32 steps x 32 lanes = 1 KB per tile)
+    auto load_tile = [&](uint32_t tl, v4u& p0, v4u& p1) {
+        const uint32_t b = tl * 1024 + 32 * li;   // chunk-relative byte
+        if (b + 32 <= nc) {
+            p0 = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rin, (int)(in_base + b), 0, 0));
+            p1 = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rin, (int)(in_base + b + 16), 0, 0));
+        } else {
+            p0 = v4u{0, 0, 0, 0};
+            p1 = v4u{0, 0, 0, 0};
+            for (uint32_t k = 0; k < 32; ++k)
+                if (b + k < nc) {
+                    const uint32_t byte = __builtin_amdgcn_raw_buffer_load_b8(rin, (int)(in_base + b + k), 0, 0);
+                    if (k < 16) p0[k >> 2] |= byte << (8 * (k & 3));
+                    else p1[(k - 16) >> 2] |= byte << (8 * (k & 3));
+                }
+        }
+    };
+    v4u p0, p1;
+    if (steps > 0) load_tile((steps - 1) >> 5, p0, p1);
+    __syncthreads();
+
+    uint32_t X = L;
+    uint32_t P = a.slot_dwords * 32;   // fields go below P, right to left
+    uint32_t fmark = a.slot_dwords;    // dwords at or above fmark are in the slot
+    uint32_t pay = 0, bad = sg->tab && sg->tab[kDTStatus] != 0 && nc > 0;
+
+    auto flush_block = [&](uint32_t blk) {  // ring dwords [blk, blk + 128) -> slot
+        uint32_t* r = &sm[ring + ((blk + 4 * li) & (kERing - 1))];
+        const v4u v = *reinterpret_cast<v4u*>(r);
+        *reinterpret_cast<v4u*>(r) = v4u{0, 0, 0, 0};
+        __builtin_amdgcn_raw_buffer_store_b128(v, rslot, (int)(slot_base + 4 * (blk + 4 * li)), 0, 0);
+    };
+
+    for (uint32_t t = steps; t-- > 0;) {
+        if ((t & 31) == 31 || t + 1 == steps) {  // entering tile t >> 5: stage it, fetch the next
+            *reinterpret_cast<v4u*>(&sm[tile + 8 * li]) = p0;
+            *reinterpret_cast<v4u*>(&sm[tile + 8 * li + 4]) = p1;
+            if (t >= 32) load_tile((t >> 5) - 1, p0, p1);
+        }
+        const bool act = t * 32 + li < nc;
+        const uint32_t u = (uint32_t)reinterpret_cast<const uint8_t*>(&sm[tile])[(t & 31) * 32 + li] ^ 0x80;
+        const uint2 e = *reinterpret_cast<const uint2*>(&sm[2 * u]);
+        const uint32_t k = (uint32_t)((int)X + (int)e.x) >> R1;
+        const uint32_t w = (e.y >> 8) & 15;
+        const uint32_t field = (e.y & 0xFF) | (__builtin_amdgcn_ubfe(X, 0, k) << w);
+        uint32_t len = act ? w + k : 0;
+        const uint32_t Xn = L + es[((e.y >> 16) & 0x3FF) - 512 + (X >> k)];
+        if (act) {
+            bad |= e.y >> 31;
+            X = Xn;
+        }
+        const uint32_t incl = scan32(len);
+        const uint32_t total = bcast31(incl);
+        const uint32_t Pt = P - total;
+        ring_or(sm, ring, Pt + incl - len, field, len);
+        P = Pt;
+        pay += total;
+        if ((P >> 5) + 129 <= fmark) {  // dwords above P's word are final
+            fmark -= 128;
+            flush_block(fmark);
+        }
+    }
+    // the lanes' final states, the decoder's initial states, in front of the fields
+    const uint32_t Pi = P - lanes * a.R;
+    if (li < lanes) ring_or(sm, ring, Pi + li * a.R, X - L, a.R);
+    if (nc > 0) {
+        while (fmark > (Pi >> 5)) {
+            fmark -= 128;
+            flush_block(fmark);
+        }
+    }
+    if (chunk < n_chunks && li == 0) {
+        a.meta[2 * (sg->slot_base + chunk)] = Pi;
+        a.meta[2 * (sg->slot_base + chunk) + 1] = pay;
+    }
+    report(a.status, bad && sg->tab && sg->tab[kDTStatus] != 0 ? SH_ERR_UNSUPPORTED
+                                                              : SH_ERR_SYMBOL_NOT_IN_TABLE,
+           bad != 0);
+}
+
+// ------------------------------------------------------------------------------------
+// encode, kernel 2: chunk index (exclusive scan of chunk sizes), header, totals
+// ------------------------------------------------------------------------------------
+constexpr int kScanBlock = 1024;
+
+__global__ __launch_bounds__(kScanBlock) void k_encode_index(const CodecArgs a) {
+    __shared__ uint32_t wsum[kScanBlock / 64];
+    __shared__ unsigned long long bits_sum;
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const SegDesc* sg = a.nseg == 0 ? &a.one.seg : &a.many[blockIdx.x];
+    const uint32_t n_chunks = sg->n_chunks;
+    const uint32_t index_at = header_bytes_dev(a.K);
+    const uint32_t* tmpl = sg->tab ? sg->tab + kDTHdr : a.one.hdr;
+    const uint32_t* meta = a.meta + 2ull * sg->slot_base;
+    uint32_t* index = reinterpret_cast<uint32_t*>(sg->c + index_at);
+    uint32_t* hdr = reinterpret_cast<uint32_t*>(sg->c);
+    for (uint32_t i = tid; i < index_at / 4; i += kScanBlock) hdr[i] = header_dword(tmpl, i, sg->n, n_chunks);
+    if (tid == 0) bits_sum = 0;
+    __syncthreads();
+    uint32_t carry = 0;
+    uint64_t my_bits = 0;
+    for (uint32_t base = 0; base < n_chunks; base += kScanBlock) {
+        const uint32_t c = base + tid;
+        uint32_t bytes = 0;
+        if (c < n_chunks) {
+            const uint32_t start = meta[2 * c];
+            bytes = 4 * ((a.slot_dwords * 32 - start + 31) >> 5);
+            my_bits += meta[2 * c + 1];
+        }
+        // wavefront inclusive scan, then across the 16 wavefronts
+        uint32_t v = bytes;
+        for (int sh = 1; sh < 64; sh <<= 1) {
+            const uint32_t o = __shfl_up(v, sh, 64);
+            if (lane >= (uint32_t)sh) v += o;
+        }
+        if (lane == 63) wsum[wv] = v;
+        __syncthreads();
+        uint32_t before = 0, all = 0;
+        for (uint32_t w = 0; w < kScanBlock / 64; ++w) {
+            before += w < wv ? wsum[w] : 0;
+            all += wsum[w];
+        }
+        if (c < n_chunks) index[c] = carry + before + v - bytes;
+        carry += all;
+        __syncthreads();
+    }
+    if (tid == 0) index[n_chunks] = carry;
+    atomicAdd(&bits_sum, (unsigned long long)my_bits);
+    __syncthreads();
+    if (tid == 0 && sg->info) {
+        sg->info->container_bytes = (uint64_t)index_at + 4ull * (n_chunks + 1) + carry;
+        sg->info->payload_bits = bits_sum;
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// encode, kernel 3: move every chunk from its slot to its place in the payload
+// ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_encode_compact(const CodecArgs a) {
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t block = __builtin_amdgcn_readfirstlane(blockIdx.x);
+    const SegDesc* sg = codec_seg(a, block, true);
+    const uint32_t c = (block - sg->first_block_c) * 4 + (threadIdx.x >> 6);
+    if (c >= sg->n_chunks) return;
+    const uint32_t index_at = header_bytes_dev(a.K);
+    const uint32_t payload_at = index_at + 4 * (sg->n_chunks + 1);
+    const uint32_t slot = sg->slot_base + c;
+    const uint32_t start = a.meta[2 * slot];
+    const uint32_t ndw = (a.slot_dwords * 32 - start + 31) >> 5;
+    const uint32_t off = reinterpret_cast<const uint32_t*>(sg->c + index_at)[c];
+    const uint32_t* s = a.slots + (uint64_t)slot * a.slot_dwords;
+    uint32_t* d = reinterpret_cast<uint32_t*>(sg->c + payload_at + off);
+    const uint32_t s0 = start >> 5;
+    for (uint32_t j = lane; j < ndw; j += 64) {
+        const uint32_t lo = s[s0 + j];
+        const uint32_t hi = s0 + j + 1 < a.slot_dwords ? s[s0 + j + 1] : 0;
+        d[j] = __builtin_amdgcn_alignbit(hi, lo, start);
+    }
+}
+
+sh_status launch_encode(const CodecArgs& a, uint32_t total_blocks, uint32_t total_blocks_c,
+                        void* stream) {
+    hipStream_t s = (hipStream_t)stream;
+    if (total_blocks > 0)
+        hipLaunchKernelGGL(k_encode_chunks, dim3(total_blocks), dim3(kEncBlock), 0, s, a);
+    hipLaunchKernelGGL(k_encode_index, dim3(a.nseg ? a.nseg : 1), dim3(kScanBlock), 0, s, a);
+    if (total_blocks_c > 0)
+        hipLaunchKernelGGL(k_encode_compact, dim3(total_blocks_c), dim3(256), 0, s, a);
+    return hipGetLastError() == hipSuccess ? SH_OK : SH_ERR_HIP;
+}
+
+}  // namespace shn

@@ -131,9 +131,12 @@ sh_status sh_histogram(const int8_t* d_x, uint64_t n, uint64_t* d_hist, void* st
 sh_status sh_table_from_histogram(const uint64_t* hist, const sh_params* params, sh_table* out);
 
 /*
- * sh_histogram + sh_table_from_histogram.  x is device memory when x_on_device != 0
- * (then d_ws must hold sh_build_tables_workspace() bytes and the call waits for the
- * stream), else host memory (counted on the host; d_ws and stream unused).
+ * The table of one tensor.  x is device memory when x_on_device != 0: the histogram and the
+ * whole table build run on the GPU (sh_build_tables_batch with one tensor; the table is
+ * identical to sh_table_from_histogram's), x must be 16-byte aligned, params must be ones
+ * the GPU path supports, d_ws must hold sh_build_tables_workspace() bytes (256-byte
+ * aligned) and the call waits for the stream.  Otherwise x is host memory, counted and
+ * built on the host (d_ws and stream unused).
  */
 uint64_t sh_build_tables_workspace(void);
 sh_status sh_build_tables(const int8_t* x, uint64_t n, int x_on_device, const sh_params* params,
