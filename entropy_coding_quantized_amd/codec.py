@@ -87,6 +87,7 @@ _EXPORTS = {
                                        C.c_void_p]),
     "sh_tables_from_device": (C.c_int32, [C.c_void_p, C.c_uint32, C.c_void_p, C.c_void_p,
                                           C.c_void_p]),
+    "sh_tables_from_bytes": (C.c_int32, [C.c_void_p, C.c_uint32, C.c_void_p, C.c_void_p]),
     "sh_build_tables_batch_workspace": (C.c_uint64, [C.c_uint32]),
     "sh_build_tables_batch": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_uint32,
                                           C.POINTER(sh_params), C.c_void_p, C.c_void_p,
@@ -256,6 +257,14 @@ def sh_tables_from_device(d_tables, count: int, stream=None):
     st = (C.c_int32 * max(count, 1))()
     _check(lib().sh_tables_from_device(_ptr(d_tables), count, out, st, _stream(stream)),
            "sh_tables_from_device")
+    return [out[i] for i in range(count)], [int(st[i]) for i in range(count)]
+
+
+def sh_tables_from_bytes(tables, count: int):
+    """sh_tables_from_device for device-table images already in host memory."""
+    out = (sh_table * max(count, 1))()
+    st = (C.c_int32 * max(count, 1))()
+    _check(lib().sh_tables_from_bytes(_ptr(tables), count, out, st), "sh_tables_from_bytes")
     return [out[i] for i in range(count)], [int(st[i]) for i in range(count)]
 
 

@@ -181,18 +181,12 @@ sh_status sh_table_to_device(const sh_table* table, const sh_params* params, voi
     return hip_ok(hipStreamSynchronize(s));
 }
 
-sh_status sh_tables_from_device(const void* d_tables, uint32_t count, sh_table* out,
-                                int32_t* table_status, void* stream) {
+sh_status sh_tables_from_bytes(const void* tables, uint32_t count, sh_table* out,
+                               int32_t* table_status) {
     if (count == 0) return SH_OK;
-    if (!d_tables || !out || !table_status) return SH_ERR_INVALID_ARG;
-    std::vector<uint32_t> dt((size_t)kDTDwords * count, 0);
-    hipStream_t s = (hipStream_t)stream;
-    if (hipMemcpyAsync(dt.data(), d_tables, (size_t)kDTBytes * count, hipMemcpyDeviceToHost, s) !=
-            hipSuccess ||
-        hipStreamSynchronize(s) != hipSuccess)
-        return SH_ERR_HIP;
+    if (!tables || !out || !table_status || !aligned(tables, 4)) return SH_ERR_INVALID_ARG;
     for (uint32_t i = 0; i < count; ++i) {
-        const uint32_t* d = dt.data() + (size_t)kDTDwords * i;
+        const uint32_t* d = (const uint32_t*)tables + (size_t)kDTDwords * i;
         sh_table t;
         std::memset(&t, 0, sizeof(t));
         t.K = d[kDTK];
@@ -207,6 +201,19 @@ sh_status sh_tables_from_device(const void* d_tables, uint32_t count, sh_table* 
         out[i] = t;
     }
     return SH_OK;
+}
+
+sh_status sh_tables_from_device(const void* d_tables, uint32_t count, sh_table* out,
+                                int32_t* table_status, void* stream) {
+    if (count == 0) return SH_OK;
+    if (!d_tables || !out || !table_status) return SH_ERR_INVALID_ARG;
+    std::vector<uint32_t> dt((size_t)kDTDwords * count, 0);
+    hipStream_t s = (hipStream_t)stream;
+    if (hipMemcpyAsync(dt.data(), d_tables, (size_t)kDTBytes * count, hipMemcpyDeviceToHost, s) !=
+            hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return SH_ERR_HIP;
+    return sh_tables_from_bytes(dt.data(), count, out, table_status);
 }
 
 uint64_t sh_build_tables_batch_workspace(uint32_t nseg) {

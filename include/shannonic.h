@@ -211,6 +211,14 @@ sh_status sh_tables_from_device(const void* d_tables, uint32_t count, sh_table* 
                                 int32_t* table_status, void* stream);
 
 /*
+ * sh_tables_from_device for tables the caller has already copied to host memory (for
+ * example with an asynchronous copy into pinned memory): tables points to count device-
+ * table images, back to back, 4-byte aligned.  Host only; statuses as above.
+ */
+sh_status sh_tables_from_bytes(const void* tables, uint32_t count, sh_table* out,
+                               int32_t* table_status);
+
+/*
  * The offline table build of paper section 4.1, on the GPU, for nseg tensors: histogram,
  * the exactly-K-range DP split (same integer cost and tie rule as sh_table_from_histogram,
  * so the tables are identical), the state allocation, the spread and every derived entry.

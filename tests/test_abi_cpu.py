@@ -175,3 +175,16 @@ def test_batch_argument_checks_are_synchronous():
     p8 = codec.Params(K=8).c()
     assert lib.sh_table_to_device(C.byref(t), C.byref(p8), fake, None) == codec.SH_ERR_INVALID_ARG
     assert codec.sh_device_table_bytes() % 16 == 0
+
+
+def test_tables_from_bytes_rejects_garbage():
+    """Device-table images that do not form a table are reported per table, not raised."""
+    words = codec.sh_device_table_bytes() // 4
+    img = np.zeros(3 * words, dtype=np.uint32)
+    img[words + 0], img[words + 1] = 16, 7        # K and log2 L, but no ranges
+    img[2 * words + 3] = np.uint32(2**32 - 2)      # a recorded build status (-2)
+    img[2 * words + 0], img[2 * words + 1] = 16, 7
+    _, st = codec.sh_tables_from_bytes(img, 3)
+    assert st == [codec.SH_ERR_CORRUPT_STREAM, codec.SH_ERR_CORRUPT_STREAM,
+                  codec.SH_ERR_UNSUPPORTED]
+    assert codec.raw_status("sh_tables_from_bytes", None, 1, None, None) == codec.SH_ERR_INVALID_ARG

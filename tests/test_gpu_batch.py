@@ -61,6 +61,12 @@ def test_gpu_table_build_matches_oracle(torch_cuda, K, log2_L):
     torch.cuda.synchronize()
     tb = codec.sh_device_table_bytes()
     host = tables.cpu().numpy()
+    # parsing a host copy gives what the device read-back gives
+    t_dev, st_dev = codec.sh_tables_from_device(tables, len(xs))
+    t_host, st_host = codec.sh_tables_from_bytes(host, len(xs))
+    assert st_dev == st_host
+    for a_, b_ in zip(t_dev, t_host):
+        assert bytes(a_) == bytes(b_)
     for i, x in enumerate(xs):
         h = O.histogram(x)
         part = tables[i * tb:(i + 1) * tb]
