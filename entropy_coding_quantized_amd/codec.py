@@ -98,6 +98,10 @@ _EXPORTS = {
                                     C.c_uint64, C.c_void_p, C.c_void_p, C.c_void_p]),
     "sh_decode_batch": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                     C.c_uint32, C.POINTER(sh_params), C.c_void_p, C.c_void_p]),
+    "sh_decode_stream_staging": (C.c_uint64, [C.c_void_p, C.c_uint32, C.c_uint32]),
+    "sh_decode_stream": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                     C.c_uint32, C.POINTER(sh_params), C.c_void_p, C.c_uint64,
+                                     C.c_uint32, C.c_void_p, C.c_void_p, C.c_void_p]),
 }
 
 
@@ -307,6 +311,20 @@ def sh_decode_batch(d_tables, d_in: list, in_nbytes: list, d_y: list, n: list, p
     st = lib().sh_decode_batch(_ptr(d_tables), _ptrs(d_in), _u64s(in_nbytes), _ptrs(d_y),
                                _u64s(n), len(n), C.byref(p), _ptr(d_status), _stream(stream))
     _check(st, "sh_decode_batch")
+
+
+def sh_decode_stream_staging(in_nbytes: list, depth: int) -> int:
+    return int(lib().sh_decode_stream_staging(_u64s(in_nbytes), len(in_nbytes), depth))
+
+
+def sh_decode_stream(d_tables, h_in: list, in_nbytes: list, d_y: list, n: list, params: Params,
+                     d_staging, staging_bytes: int, depth: int, d_status=None, copy_stream=None,
+                     stream=None) -> None:
+    p = params.c()
+    st = lib().sh_decode_stream(_ptr(d_tables), _ptrs(h_in), _u64s(in_nbytes), _ptrs(d_y),
+                                _u64s(n), len(n), C.byref(p), _ptr(d_staging), staging_bytes,
+                                depth, _ptr(d_status), _stream(copy_stream), _stream(stream))
+    _check(st, "sh_decode_stream")
 
 
 def raw_status(fn_name: str, *args) -> int:

@@ -450,6 +450,86 @@ sh_status sh_decode_batch(const void* d_tables, const uint8_t* const* d_in,
     return SH_OK;
 }
 
+uint64_t sh_decode_stream_staging(const uint64_t* in_nbytes, uint32_t nseg, uint32_t depth) {
+    if (!in_nbytes || depth == 0) return 0;
+    uint64_t most = 0;
+    for (uint32_t i = 0; i < nseg; ++i) most = std::max(most, in_nbytes[i]);
+    return (uint64_t)depth * align256(std::max<uint64_t>(most, 1));
+}
+
+sh_status sh_decode_stream(const void* d_tables, const uint8_t* const* h_in,
+                           const uint64_t* in_nbytes, int8_t* const* d_y, const uint64_t* n,
+                           uint32_t nseg, const sh_params* params, void* d_staging,
+                           uint64_t staging_bytes, uint32_t depth, int32_t* d_status,
+                           void* copy_stream, void* stream) {
+    if (nseg == 0) return SH_OK;
+    if (!d_tables || !h_in || !in_nbytes || !d_y || !n || !d_staging || depth == 0 ||
+        !aligned(d_tables, 16) || !aligned(d_staging, 256) || !aligned(d_status, 4))
+        return SH_ERR_INVALID_ARG;
+    sh_status st = check_params(params);
+    if (st != SH_OK) return st;
+    const uint64_t slot_bytes = staging_bytes / depth / 256 * 256;
+    for (uint32_t i = 0; i < nseg; ++i) {
+        if (!h_in[i] || (n[i] > 0 && !d_y[i])) return SH_ERR_INVALID_ARG;
+        if (n[i] >= (1ull << 32) || in_nbytes[i] > 0xFFFFFFFFull) return SH_ERR_UNSUPPORTED;
+        if (in_nbytes[i] > slot_bytes) return SH_ERR_BUFFER_TOO_SMALL;
+        const uint64_t nch = n_chunks_of(n[i], params->chunk_symbols);
+        if (in_nbytes[i] < header_bytes(params->K) + 4 * (nch + 1)) return SH_ERR_CORRUPT_STREAM;
+    }
+    hipStream_t cs = (hipStream_t)copy_stream, ds = (hipStream_t)stream;
+    std::vector<hipEvent_t> copied(depth, nullptr), freed(depth, nullptr);
+    hipEvent_t start = nullptr;
+    auto release = [&]() {
+        for (hipEvent_t e : copied)
+            if (e) (void)hipEventDestroy(e);
+        for (hipEvent_t e : freed)
+            if (e) (void)hipEventDestroy(e);
+        if (start) (void)hipEventDestroy(start);
+    };
+    bool ok = hipEventCreateWithFlags(&start, hipEventDisableTiming) == hipSuccess;
+    for (uint32_t s = 0; s < depth && ok; ++s)
+        ok = hipEventCreateWithFlags(&copied[s], hipEventDisableTiming) == hipSuccess &&
+             hipEventCreateWithFlags(&freed[s], hipEventDisableTiming) == hipSuccess;
+    // the first copies wait for everything already queued on stream, which may still read
+    // the staging area (an earlier call)
+    ok = ok && hipEventRecord(start, ds) == hipSuccess && hipStreamWaitEvent(cs, start, 0) == hipSuccess;
+    if (!ok) {
+        release();
+        return SH_ERR_HIP;
+    }
+    // groups of consecutive containers that fit one staging slot go up together and are
+    // decoded by one launch; slot g % depth is reused once the decode that read it is done
+    std::vector<const uint8_t*> ins;
+    uint32_t i = 0;
+    for (uint32_t g = 0; i < nseg && st == SH_OK; ++g) {
+        const uint32_t slot = g % depth;
+        uint8_t* base = (uint8_t*)d_staging + (uint64_t)slot * slot_bytes;
+        uint32_t j = i;
+        uint64_t used = 0;
+        ins.clear();
+        while (j < nseg && j - i < kMaxInlineSegs && align256(used) + in_nbytes[j] <= slot_bytes) {
+            ins.push_back(base + align256(used));
+            used = align256(used) + in_nbytes[j];
+            ++j;
+        }
+        if (g >= depth && hipStreamWaitEvent(cs, freed[slot], 0) != hipSuccess) st = SH_ERR_HIP;
+        for (uint32_t k = i; k < j && st == SH_OK; ++k)
+            if (hipMemcpyAsync((void*)ins[k - i], h_in[k], in_nbytes[k], hipMemcpyHostToDevice, cs) !=
+                hipSuccess)
+                st = SH_ERR_HIP;
+        if (st == SH_OK && (hipEventRecord(copied[slot], cs) != hipSuccess ||
+                            hipStreamWaitEvent(ds, copied[slot], 0) != hipSuccess))
+            st = SH_ERR_HIP;
+        if (st == SH_OK)
+            st = sh_decode_batch((const uint8_t*)d_tables + (uint64_t)i * kDTBytes, ins.data(),
+                                 in_nbytes + i, d_y + i, n + i, j - i, params, d_status, stream);
+        if (st == SH_OK && hipEventRecord(freed[slot], ds) != hipSuccess) st = SH_ERR_HIP;
+        i = j;
+    }
+    release();  // events still pending are released once they complete
+    return st;
+}
+
 sh_status sh_stats(const sh_table* table, uint64_t n, uint64_t payload_bits,
                    uint64_t container_bytes, sh_stats_t* out) {
     if (!table || !out) return SH_ERR_INVALID_ARG;

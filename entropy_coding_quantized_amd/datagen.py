@@ -30,6 +30,7 @@ __all__ = [
     "activations",
     "model_layout",
     "model_tensor",
+    "model_tensor_torch",
     "uniform_exact",
     "CONFIGS",
 ]
@@ -126,3 +127,24 @@ CONFIGS = {
     "activations": dict(K=16, log2_L=7, chunk=16384, streams=32),
     "model": dict(K=16, log2_L=7, chunk=4096, streams=32),
 }
+
+
+def model_tensor_torch(idx: int, device, seed: int = 5, **layout):
+    """Tensor ``idx`` of ``model_layout`` drawn on ``device`` with torch's seeded generator,
+    the same recipe as ``model_tensor`` (Laplace(0, b), b ~ U(6, 20) from the same numpy
+    seed; layer 0's q_proj all zero, o_proj uniform) but other draws: a model's 7e9 values
+    are generated on the GPU in about a second instead of minutes on the host.  Laplace by
+    inversion: x = -b sign(v) log(1 - 2|v|), v uniform on [-1/2, 1/2)."""
+    import torch
+    name, shape = model_layout(**layout)[idx]
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 1_000_003 + idx)
+    if name == "layers.0.q_proj":
+        return torch.zeros(shape, dtype=torch.int8, device=device)
+    if name == "layers.0.o_proj":
+        return torch.randint(-128, 128, shape, generator=g, device=device,
+                             dtype=torch.int16).to(torch.int8)
+    b = float(_rng(seed + idx).uniform(6.0, 20.0))
+    v = torch.rand(shape, generator=g, device=device, dtype=torch.float32) - 0.5
+    x = -b * torch.sign(v) * torch.log1p(-2.0 * v.abs())
+    return torch.clamp(torch.round(x), -128, 127).to(torch.int8)

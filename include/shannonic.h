@@ -261,6 +261,28 @@ sh_status sh_decode_batch(const void* d_tables, const uint8_t* const* d_in,
                           void* stream);
 
 /*
+ * Streaming decode, for tensors parked compressed in host memory (the model-scale case:
+ * a model's tensors streamed from host memory into HBM).  Container i (h_in[i], host,
+ * in_nbytes[i] bytes, pinned for the copies to be asynchronous) is decoded with device
+ * table i into d_y[i] (n[i] values).  Containers are copied to the device on copy_stream
+ * into d_staging (256-byte aligned, staging_bytes), split into depth slots: groups of
+ * consecutive containers that fit one slot go up together and are decoded by one launch
+ * on stream, and a slot is refilled only after the decode that read it has finished, so
+ * copies overlap decodes.  Every container must fit one slot (else
+ * SH_ERR_BUFFER_TOO_SMALL); sh_decode_stream_staging gives the smallest staging size for
+ * a depth.  The first copy waits for the work already queued on stream, so a staging area
+ * may be reused by consecutive calls.  Checks and errors are sh_decode_batch's.
+ * Asynchronous: the call only queues work on both streams (it creates and releases its own
+ * events); synchronise stream.
+ */
+uint64_t sh_decode_stream_staging(const uint64_t* in_nbytes, uint32_t nseg, uint32_t depth);
+sh_status sh_decode_stream(const void* d_tables, const uint8_t* const* h_in,
+                           const uint64_t* in_nbytes, int8_t* const* d_y, const uint64_t* n,
+                           uint32_t nseg, const sh_params* params, void* d_staging,
+                           uint64_t staging_bytes, uint32_t depth, int32_t* d_status,
+                           void* copy_stream, void* stream);
+
+/*
  * Theorem-1 terms of a table and the measured rates of a container of n values, on the
  * host (paper section 4; %diff as in section 5).  The entropy terms use table->hist;
  * payload_bits and container_bytes come from sh_encode_info (pass n = 0 to get the table
