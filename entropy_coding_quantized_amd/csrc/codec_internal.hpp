@@ -88,7 +88,7 @@ SHN_HD inline uint32_t header_dword(const uint32_t* tmpl, uint32_t i, uint64_t n
 //   e1 = w_s | (int8 bits of the range base) << 8 | (|range| - 1) << 16
 // Encode entry of a value u, two dwords:
 //   v0 = bias_s (int32): the state-bit count is (X + bias_s) >> (R + 1)
-//   v1 = o | w_s << 8 | (start_s + 512) << 16 | (f_s == 0) << 31, start_s = cum_s - f_s
+//   v1 = o | w_s << 8 | (f_s == 0) << 15 | (start_s + 512) << 16, start_s = cum_s - f_s
 void derive_kernel_tables(const sh_table& t, const SlotTables& st, uint32_t* dec,
                           uint32_t* vt, uint8_t* es);
 // st is null for a table built from no values

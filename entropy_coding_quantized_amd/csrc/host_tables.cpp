@@ -251,7 +251,7 @@ void derive_kernel_tables(const sh_table& t, const SlotTables& st, uint32_t* dec
             for (uint32_t u = t.lo[s]; u < t.lo[s + 1]; ++u) {
                 vt[2 * u] = (uint32_t)bias;
                 vt[2 * u + 1] = (u - t.lo[s]) | (w << 8) | ((uint32_t)(start + 512) << 16) |
-                                (f == 0 ? 0x80000000u : 0u);
+                                (f == 0 ? 0x8000u : 0u);
             }
         }
     }
@@ -272,7 +272,7 @@ void make_device_table(const sh_table& t, const SlotTables* st, uint32_t C, uint
     if (st)
         derive_kernel_tables(t, *st, dt + kDTDec, dt + kDTVt, reinterpret_cast<uint8_t*>(dt + kDTEs));
     else  // a table built from no values: every value is outside it
-        for (uint32_t u = 0; u < 256; ++u) dt[kDTVt + 2 * u + 1] = 0x80000000u;
+        for (uint32_t u = 0; u < 256; ++u) dt[kDTVt + 2 * u + 1] = 0x8000u;
     std::memcpy(dt + kDTLo, t.lo, sizeof(t.lo));
     std::memcpy(dt + kDTFreq, t.freq, sizeof(t.freq));
     std::memcpy(dt + kDTHist, t.hist, sizeof(t.hist));

@@ -167,10 +167,12 @@ __device__ __forceinline__ uint32_t small_div(uint32_t A, uint32_t f) {
 }
 
 // DP work split of one layer: the i < 256 form four groups of 64 (one per lane), group g
-// needing the j below 64 g + 64.  Wavefront w takes group g = floor(sqrt(w)) and chunk
-// c = w - g^2 of it: chunks c < 2g are the 32 j at 32c (all below every i of the group),
+// needing the j below 64 g + 64.  Work unit u (0..15) is group g = floor(sqrt(u)) and
+// chunk c = u - g^2 of it: chunks c < 2g are the 32 j at 32c (all below every i of the group),
 // chunk 2g the 64 j at 64g, where j < i per lane (a triangle, the same work as 32 full j).
-// So all sixteen wavefronts get the same work.
+// So all sixteen wavefronts get the same useful work; a diagonal chunk takes 64 passes
+// for it, so the four of them are spread over the four SIMDs (wave w runs on SIMD w % 4).
+__constant__ uint8_t kDpUnit[16] = {0, 3, 8, 15, 1, 2, 4, 5, 6, 7, 9, 10, 11, 12, 13, 14};
 __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a) {
     __shared__ __align__(16) uint32_t sc[kCostEntries];  // cost factors; the DP's choices after it
     __shared__ uint32_t prefix[257];
@@ -237,8 +239,11 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
         for (uint32_t i = tid; i < 256; i += kBuildBlock)
             cbuf[1][i] = i >= 1 ? (uint64_t)prefix[i] * sc[i * (i - 1) / 2] : kInf;
         __syncthreads();
-        const uint32_t g = wave >= 9 ? 3 : wave >= 4 ? 2 : wave >= 1 ? 1 : 0;
-        const uint32_t chunk = wave - g * g;
+        // work unit of this wavefront: the four diagonal units (0, 3, 8, 15) go to waves
+        // 0-3, one per SIMD, the twelve others to waves 4-15
+        const uint32_t unit = kDpUnit[wave];
+        const uint32_t g = unit >= 9 ? 3 : unit >= 4 ? 2 : unit >= 1 ? 1 : 0;
+        const uint32_t chunk = unit - g * g;
         const bool diag = chunk == 2 * g;
         const uint32_t ja = diag ? 64 * g : 32 * chunk, jb = diag ? 64 * g + 64 : 32 * chunk + 32;
         const uint32_t i = 64 * g + lane;
@@ -456,7 +461,7 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
     // a smaller key (2j'+1)/(2 f_k'), or an equal key and a smaller range; then the tANS
     // tables of that slot: sub-state x = f_k + j, nb = R - floor(log2 x), next (x << nb) - L
     if (!ok)  // no usable table: every value is outside it
-        for (uint32_t u = tid; u < 256; u += kBuildBlock) dt[kDTVt + 2 * u + 1] = 0x80000000u;
+        for (uint32_t u = tid; u < 256; u += kBuildBlock) dt[kDTVt + 2 * u + 1] = 0x8000u;
     for (uint32_t p = tid; ok && p < L; p += kBuildBlock) {
         uint32_t k = 0;
         while (cum_s[k + 1] <= p) ++k;
@@ -495,7 +500,7 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
         }
         dt[kDTVt + 2 * u] = (uint32_t)bias;
         dt[kDTVt + 2 * u + 1] = (u - lo_s[s]) | (w << 8) | ((uint32_t)(start + 512) << 16) |
-                                (f == 0 ? 0x80000000u : 0u);
+                                (f == 0 ? 0x8000u : 0u);
     }
     // canonical table, histogram and the header template (n and n_chunks left 0)
     uint16_t* lo16 = reinterpret_cast<uint16_t*>(dt + kDTLo);

@@ -1,6 +1,8 @@
 // Encode kernels of the Shannonic codec for gfx950 (CDNA4, wave64): the inverse of the
 // decode mapping ("Runtime encoding/decoding", paper section 4.2, Algorithm 2, of the
 // Shannonic talk notes), run backwards per lane, then a chunk index and a compaction pass.
+#include <type_traits>
+
 #include "device_common.hpp"
 
 namespace shn {
@@ -16,20 +18,31 @@ namespace shn {
 // in its slot with the lanes' final states (the decoder's initial states) in front.
 constexpr int kEncBlock = 256;
 constexpr uint32_t kERing = 256;
-constexpr uint32_t kEncHalfDwords = 256 /* input tile, 32 steps x 32 lanes bytes */ + kERing;
-constexpr uint32_t kVtDwords = 512 + 64;  // value table + encTable bytes
+// LDS: eight 1 KB rings (one per half wavefront, 1 KB aligned), eight 1 KB input tiles
+// (bytes of 32 steps x 32 lanes), then the value table and the encTable bytes
+constexpr uint32_t kTileBase = 8 * kERing;
+constexpr uint32_t kVtBase = kTileBase + 8 * 256;
+constexpr uint32_t kVtDwords = 512 + 64;
 
-__device__ __forceinline__ void ring_or(uint32_t* sm, uint32_t ring, uint32_t pos,
-                                        uint32_t field, uint32_t len) {
-    if (len == 0) return;
+// OR a field (zero above its length) into a ring at bit pos; ring_byte is the ring's LDS
+// byte offset, a multiple of its 1 KB size.  Both dwords the field may touch are OR-ed
+// unconditionally: a field that stays in one dword ORs zero into the next, which is
+// harmless even when that ring slot has been flushed and reused.
+__device__ __forceinline__ void ring_or(uint32_t* sm, uint32_t ring_byte, uint32_t pos,
+                                        uint32_t field) {
+    typedef __attribute__((address_space(3))) uint32_t lds_word;
     const uint64_t wide = (uint64_t)field << (pos & 31);
-    const uint32_t d = pos >> 5;
-    atomicOr(&sm[ring + (d & (kERing - 1))], (uint32_t)wide);
-    if ((pos & 31) + len > 32) atomicOr(&sm[ring + ((d + 1) & (kERing - 1))], (uint32_t)(wide >> 32));
+    const uint32_t b = pos >> 3;
+    const uint32_t a0 = (b & 0x3FC) | ring_byte, a1 = ((b + 4) & 0x3FC) | ring_byte;
+    (void)sm;  // the rings sit at LDS byte 0 of the block's only __shared__ array
+    __hip_atomic_fetch_or((lds_word*)(uintptr_t)a0, (uint32_t)wide, __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_fetch_or((lds_word*)(uintptr_t)a1, (uint32_t)(wide >> 32), __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const CodecArgs a) {
-    __shared__ __align__(16) uint32_t sm[kVtDwords + 8 * kEncHalfDwords];
+    __shared__ __align__(1024) uint32_t sm[kVtBase + kVtDwords];
     const uint32_t tid = threadIdx.x, lane = tid & 63, li = lane & 31, hw = lane >> 5;
     const uint32_t block = __builtin_amdgcn_readfirstlane(blockIdx.x);
     const SegDesc* sg = codec_seg(a, block, false);
@@ -40,15 +53,17 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const CodecArgs a) 
     const uint8_t* es_src = sg->tab ? reinterpret_cast<const uint8_t*>(sg->tab + kDTEs) : a.one.es;
     const uint32_t n_chunks = sg->n_chunks;
     const uint64_t n = sg->n;
-    for (uint32_t i = tid; i < 512; i += kEncBlock) sm[i] = vt[i];
+    for (uint32_t i = tid; i < 512; i += kEncBlock) sm[kVtBase + i] = vt[i];
     for (uint32_t i = tid; i < 64; i += kEncBlock) {
-        sm[512 + i] = (uint32_t)es_src[4 * i] | ((uint32_t)es_src[4 * i + 1] << 8) |
-                      ((uint32_t)es_src[4 * i + 2] << 16) | ((uint32_t)es_src[4 * i + 3] << 24);
+        sm[kVtBase + 512 + i] = (uint32_t)es_src[4 * i] | ((uint32_t)es_src[4 * i + 1] << 8) |
+                                ((uint32_t)es_src[4 * i + 2] << 16) |
+                                ((uint32_t)es_src[4 * i + 3] << 24);
     }
-    const uint8_t* es = reinterpret_cast<const uint8_t*>(&sm[512]);
-    const uint32_t half = kVtDwords + (wv * 2 + hw) * kEncHalfDwords;
-    const uint32_t tile = half;            // 256 dwords: bytes of 32 steps x 32 lanes
-    const uint32_t ring = half + 256;      // 256 dwords
+    const uint8_t* es = reinterpret_cast<const uint8_t*>(&sm[kVtBase + 512]);
+    const uint32_t hi = wv * 2 + hw;       // this half wavefront's ring and tile
+    const uint32_t tile = kTileBase + hi * 256;
+    const uint32_t ring = hi * kERing;
+    const uint32_t ring_byte = lds_offset(sm) + 4 * ring;  // 1 KB aligned
     for (uint32_t i = li; i < kERing; i += 32) sm[ring + i] = 0;
 
     const uint32_t pair = 2 * wid;
@@ -95,7 +110,9 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const CodecArgs a) 
     uint32_t X = L;
     uint32_t P = a.slot_dwords * 32;   // fields go below P, right to left
     uint32_t fmark = a.slot_dwords;    // dwords at or above fmark are in the slot
-    uint32_t pay = 0, bad = sg->tab && sg->tab[kDTStatus] != 0 && nc > 0;
+    uint32_t flush_at = (fmark - 128) * 32;  // once P is below this, flush a block
+    // every encode entry is OR-ed in; its bit 15 marks a value in a range without states
+    uint32_t bad = sg->tab && sg->tab[kDTStatus] != 0 && nc > 0 ? 0x8000u : 0u;
 
     auto flush_block = [&](uint32_t blk) {  // ring dwords [blk, blk + 128) -> slot
         uint32_t* r = &sm[ring + ((blk + 4 * li) & (kERing - 1))];
@@ -104,38 +121,82 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const CodecArgs a) 
         __builtin_amdgcn_raw_buffer_store_b128(v, rslot, (int)(slot_base + 4 * (blk + 4 * li)), 0, 0);
     };
 
-    for (uint32_t t = steps; t-- > 0;) {
-        if ((t & 31) == 31 || t + 1 == steps) {  // entering tile t >> 5: stage it, fetch the next
-            *reinterpret_cast<v4u*>(&sm[tile + 8 * li]) = p0;
-            *reinterpret_cast<v4u*>(&sm[tile + 8 * li + 4]) = p1;
-            if (t >= 32) load_tile((t >> 5) - 1, p0, p1);
+    // Values are read two steps ahead and table entries one step ahead, so the only LDS
+    // read on the chain from one step to the next is the state-dependent encTable read,
+    // and no read waits for the previous step's ring writes.
+    auto stage = [&]() {  // the tile in p0/p1 into LDS, as u = x + 128
+        const v4u flip = {0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};
+        *reinterpret_cast<v4u*>(&sm[tile + 8 * li]) = p0 ^ flip;
+        *reinterpret_cast<v4u*>(&sm[tile + 8 * li + 4]) = p1 ^ flip;
+    };
+    auto value_at = [&](uint32_t t) {  // u of step t, from the staged tile t >> 5
+        return (uint32_t)reinterpret_cast<const uint8_t*>(&sm[tile])[(t & 31) * 32 + li];
+    };
+    auto entry = [&](uint32_t u) {  // encode entry of value u
+        return *reinterpret_cast<const uint2*>(&sm[kVtBase + 2 * u]);
+    };
+    // step t2's value, staging its tile first when t2 is the first step of a tile; the tile it
+    // replaces is no longer read (the values of later steps are in registers)
+    auto fetch = [&](uint32_t t2) {
+        if ((t2 & 31) == 31) {
+            stage();
+            if (t2 >= 32) load_tile((t2 >> 5) - 1, p0, p1);
         }
-        const bool act = t * 32 + li < nc;
-        const uint32_t u = (uint32_t)reinterpret_cast<const uint8_t*>(&sm[tile])[(t & 31) * 32 + li] ^ 0x80;
-        const uint2 e = *reinterpret_cast<const uint2*>(&sm[2 * u]);
-        const uint32_t k = (uint32_t)((int)X + (int)e.x) >> R1;
-        const uint32_t w = (e.y >> 8) & 15;
-        const uint32_t field = (e.y & 0xFF) | (__builtin_amdgcn_ubfe(X, 0, k) << w);
-        uint32_t len = act ? w + k : 0;
-        const uint32_t Xn = L + es[((e.y >> 16) & 0x3FF) - 512 + (X >> k)];
-        if (act) {
-            bad |= e.y >> 31;
+        return value_at(t2);
+    };
+    uint2 e_c = {0, 0};
+    uint32_t u_n = 0;
+    if (steps > 0) {
+        stage();
+        if (steps - 1 >= 32) load_tile(((steps - 1) >> 5) - 1, p0, p1);
+        const uint32_t u_c = value_at(steps - 1);
+        if (steps >= 2) u_n = fetch(steps - 2);
+        e_c = entry(u_c);
+    }
+    auto step = [&](uint32_t t, auto partial) {
+        const uint32_t u_nn = t >= 2 ? fetch(t - 2) : 0u;
+        const uint2 e_n = entry(u_n);
+        const uint32_t k = (uint32_t)((int)X + (int)e_c.x) >> R1;
+        const uint32_t Xn = L + es[(e_c.y >> 16) - 512 + (X >> k)];
+        const uint32_t w = (e_c.y >> 8) & 15;
+        uint32_t field = (e_c.y & 0xFF) | (__builtin_amdgcn_ubfe(X, 0, k) << w);
+        uint32_t len = w + k;
+        uint32_t flag = e_c.y;
+        if constexpr (decltype(partial)::value) {
+            const bool act = t * 32 + li < nc;
+            field = act ? field : 0u;
+            len = act ? len : 0u;
+            flag = act ? flag : 0u;
+            X = act ? Xn : X;
+        } else {
             X = Xn;
         }
+        bad |= flag;
         const uint32_t incl = scan32(len);
         const uint32_t total = bcast31(incl);
-        const uint32_t Pt = P - total;
-        ring_or(sm, ring, Pt + incl - len, field, len);
-        P = Pt;
-        pay += total;
-        if ((P >> 5) + 129 <= fmark) {  // dwords above P's word are final
+        P -= total;
+        ring_or(sm, ring_byte, P + incl - len, field);
+        if (P < flush_at) {  // dwords from P's word + 129 up are final
             fmark -= 128;
+            flush_at -= 128 * 32;
             flush_block(fmark);
         }
+        e_c = e_n;
+        u_n = u_nn;
+    };
+    // steps where a lane of either half has no value (the tail of a short chunk) first
+    const uint32_t t_full = (nc_lo < nc_hi ? nc_lo : nc_hi) >> 5;
+    uint32_t t = steps;
+    while (t > t_full) step(--t, std::true_type{});
+    if (t & 1) step(--t, std::false_type{});
+    while (t > 0) {  // two steps per iteration: the carried values need no copies
+        step(--t, std::false_type{});
+        step(--t, std::false_type{});
     }
+    const uint32_t pay = a.slot_dwords * 32 - P;  // field bits
     // the lanes' final states, the decoder's initial states, in front of the fields
     const uint32_t Pi = P - lanes * a.R;
-    if (li < lanes) ring_or(sm, ring, Pi + li * a.R, X - L, a.R);
+    ring_or(sm, ring_byte, Pi + li * a.R, li < lanes ? X - L : 0u);
     if (nc > 0) {
         while (fmark > (Pi >> 5)) {
             fmark -= 128;
@@ -146,6 +207,7 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const CodecArgs a) 
         a.meta[2 * (sg->slot_base + chunk)] = Pi;
         a.meta[2 * (sg->slot_base + chunk) + 1] = pay;
     }
+    bad &= 0x8000u;
     report(a.status, bad && sg->tab && sg->tab[kDTStatus] != 0 ? SH_ERR_UNSUPPORTED
                                                               : SH_ERR_SYMBOL_NOT_IN_TABLE,
            bad != 0);
