@@ -112,6 +112,9 @@ struct SegDesc {
 
 constexpr uint32_t kMaxInlineSegs = 48;  // descriptors carried in one launch's arguments
 
+// A launch as the C ABI describes it (host side).  The launch functions pass the kernels
+// the smallest argument block that holds it (KOne or KSegs<N> below): the cost of a
+// launch on the host grows with the size of its arguments.
 struct CodecArgs {
     uint32_t nseg;          // 0: a single segment with host-built tables (one), else many
     uint32_t C, R, L, K;
@@ -130,14 +133,37 @@ struct CodecArgs {
     };
 };
 
+// ---- kernel argument blocks ----
+struct KHead {
+    uint32_t nseg, C, R, L, K;
+    uint32_t slot_dwords;
+    int32_t* status;
+    uint32_t* slots;
+    uint32_t* meta;
+};
+template <int N>
+struct KSegs {  // N segments with device tables
+    KHead h;
+    SegDesc segs[N];
+};
+struct KOne {  // one segment with the tables in the arguments
+    KHead h;
+    SegDesc segs[1];
+    uint32_t hdr[kMaxHeaderDwords];
+    uint32_t tab[2 * 256];
+    uint8_t es[256];
+};
+
 constexpr uint32_t kHistBytesPerBlock = 1u << 16;  // values per histogram block
 
-struct HistArgs {
+template <int N>
+struct HistArgsN {
     uint32_t nseg;
     uint32_t n_blocks;
     uint64_t* hist;         // nseg x 256
-    SegDesc segs[kMaxInlineSegs];  // x, n and first_block of each segment
+    SegDesc segs[N];        // x, n and first_block of each segment
 };
+using HistArgs = HistArgsN<kMaxInlineSegs>;  // host side; launches pass the smallest N
 
 struct BuildArgs {
     const uint64_t* hist;   // nseg x 256

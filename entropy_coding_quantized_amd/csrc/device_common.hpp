@@ -3,6 +3,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstring>
+
 #include "codec_internal.hpp"
 
 namespace shn {
@@ -69,9 +71,60 @@ __device__ __forceinline__ const SegDesc* find_seg(const SegDesc* segs, uint32_t
                                                     uint32_t block, bool compaction) {
     return &segs[find_seg_index(segs, nseg, block, compaction)];
 }
-__device__ __forceinline__ const SegDesc* codec_seg(const CodecArgs& a, uint32_t block,
-                                                     bool compaction) {
-    return a.nseg == 0 ? &a.one.seg : find_seg(a.many, a.nseg, block, compaction);
+template <class A>
+__device__ __forceinline__ const SegDesc* codec_seg(const A& a, uint32_t block, bool compaction) {
+    return find_seg(a.segs, a.h.nseg, block, compaction);
+}
+
+// the tables carried in the arguments (KOne), or none (KSegs: every segment has a device
+// table); which a segment uses is decided by its tab pointer
+__device__ __forceinline__ const uint32_t* inline_tab(const KOne& a) { return a.tab; }
+__device__ __forceinline__ const uint32_t* inline_hdr(const KOne& a) { return a.hdr; }
+__device__ __forceinline__ const uint8_t* inline_es(const KOne& a) { return a.es; }
+template <int N>
+__device__ __forceinline__ const uint32_t* inline_tab(const KSegs<N>&) { return nullptr; }
+template <int N>
+__device__ __forceinline__ const uint32_t* inline_hdr(const KSegs<N>&) { return nullptr; }
+template <int N>
+__device__ __forceinline__ const uint8_t* inline_es(const KSegs<N>&) { return nullptr; }
+
+// ---- host side: the smallest argument block for a launch ----
+inline KHead kernel_head(const CodecArgs& a) {
+    return KHead{a.nseg ? a.nseg : 1, a.C, a.R, a.L, a.K, a.slot_dwords, a.status, a.slots, a.meta};
+}
+inline KOne kernel_one(const CodecArgs& a) {
+    KOne k;
+    k.h = kernel_head(a);
+    k.segs[0] = a.one.seg;
+    std::memcpy(k.hdr, a.one.hdr, sizeof(k.hdr));
+    std::memcpy(k.tab, a.one.tab, sizeof(k.tab));
+    std::memcpy(k.es, a.one.es, sizeof(k.es));
+    return k;
+}
+template <int N>
+inline KSegs<N> kernel_segs(const CodecArgs& a) {
+    KSegs<N> k;
+    k.h = kernel_head(a);
+    std::memcpy(k.segs, a.many, sizeof(SegDesc) * a.nseg);
+    return k;
+}
+// Calls f(args) with the smallest argument block that holds a.
+template <class F>
+inline void with_kernel_args(const CodecArgs& a, F&& f) {
+    if (a.nseg == 0) f(kernel_one(a));
+    else if (a.nseg <= 1) f(kernel_segs<1>(a));
+    else if (a.nseg <= 4) f(kernel_segs<4>(a));
+    else if (a.nseg <= 16) f(kernel_segs<16>(a));
+    else f(kernel_segs<kMaxInlineSegs>(a));
+}
+template <int N>
+inline HistArgsN<N> hist_args(const HistArgs& h) {
+    HistArgsN<N> k;
+    k.nseg = h.nseg;
+    k.n_blocks = h.n_blocks;
+    k.hist = h.hist;
+    std::memcpy(k.segs, h.segs, sizeof(SegDesc) * h.nseg);
+    return k;
 }
 
 __device__ __forceinline__ uint32_t header_bytes_dev(uint32_t K) {

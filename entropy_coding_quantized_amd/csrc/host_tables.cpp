@@ -117,21 +117,58 @@ sh_status allocate_states(const uint64_t* count, uint32_t K, uint32_t L, uint16_
         return g;
     }();
     if (L > (1u << kMaxLog2LHost)) return SH_ERR_UNSUPPORTED;
-    // a max-heap of each occupied range's next gain; on equal gains the smaller k is on top
+    // The greedy steps take the L - used largest increments N_k * gain(f), f >= 1, in the
+    // order (gain down, k up); a range's increments fall strictly with f.  So a start
+    // close to the result can be finished greedily and then checked: the allocation is
+    // the greedy one exactly when the last increment taken precedes the first one left.
     struct Item {
         uint64_t g;
         uint32_t k;
         bool operator<(const Item& o) const { return g < o.g || (g == o.g && k > o.k); }
     };
-    std::priority_queue<Item> heap;
-    for (uint32_t k = 0; k < K; ++k)
-        if (count[k]) heap.push({count[k] * gain_of[1], k});
-    for (; used < L; ++used) {
-        const Item top = heap.top();
-        heap.pop();
-        const uint32_t k = top.k;
-        f[k]++;
-        heap.push({count[k] * gain_of[f[k]], k});
+    auto finish = [&](uint32_t total) {  // greedy increments from f up to L
+        std::priority_queue<Item> heap;
+        for (uint32_t k = 0; k < K; ++k)
+            if (count[k]) heap.push({count[k] * gain_of[f[k]], k});
+        for (; total < L; ++total) {
+            const Item top = heap.top();
+            heap.pop();
+            f[top.k]++;
+            heap.push({count[top.k] * gain_of[f[top.k]], top.k});
+        }
+    };
+    uint64_t N = 0;
+    for (uint32_t k = 0; k < K; ++k) N += count[k];
+    uint32_t total = 0;
+    for (uint32_t k = 0; k < K; ++k)  // the proportional share, less one: rarely above the result
+        if (count[k]) {
+            const uint64_t share = (uint64_t)(L - used) * count[k] / N;
+            f[k] = (uint16_t)(share > 1 ? share : 1);
+            total += f[k];
+        }
+    if (total > L) {
+        for (uint32_t k = 0; k < K; ++k) f[k] = count[k] ? 1 : 0;
+        total = used;
+    }
+    finish(total);
+    bool have_last = false, have_next = false;
+    Item last{0, 0}, next{0, 0};  // last increment taken, first increment left
+    for (uint32_t k = 0; k < K; ++k) {
+        if (!count[k]) continue;
+        if (f[k] >= 2) {
+            const Item t{count[k] * gain_of[f[k] - 1], k};
+            if (!have_last || t < last) last = t;  // later in the order
+            have_last = true;
+        }
+        if (f[k] < L) {
+            const Item t{count[k] * gain_of[f[k]], k};
+            if (!have_next || next < t) next = t;  // earlier in the order
+            have_next = true;
+        }
+    }
+    if (have_last && have_next && last < next) {  // the start overshot: greedy from one each
+        for (uint32_t k = 0; k < K; ++k) f[k] = count[k] ? 1 : 0;
+        finish(used);
     }
     return SH_OK;
 }

@@ -16,7 +16,8 @@ __global__ void k_zero_u64(uint64_t* p, uint32_t count) {
     if (i < count) p[i] = 0;
 }
 
-__global__ __launch_bounds__(kHistBlock) void k_histogram(const HistArgs a) {
+template <class H>
+__global__ __launch_bounds__(kHistBlock) void k_histogram(const H a) {
     // 32 private copies per block, copy c of bin b at b * 32 + c: the 32 lanes of a half
     // wavefront hit 32 different banks even when every value is the same.
     __shared__ uint32_t h[256 * kHistCopies];
@@ -57,8 +58,16 @@ sh_status launch_histogram(const HistArgs& h, uint32_t nseg_zero, void* stream) 
     hipStream_t s = (hipStream_t)stream;
     const uint32_t words = 256 * nseg_zero;
     hipLaunchKernelGGL(k_zero_u64, dim3((words + 255) / 256), dim3(256), 0, s, h.hist, words);
-    if (h.n_blocks > 0)
-        hipLaunchKernelGGL(k_histogram, dim3(h.n_blocks), dim3(kHistBlock), 0, s, h);
+    if (h.n_blocks > 0) {
+        if (h.nseg <= 1)
+            hipLaunchKernelGGL(k_histogram<HistArgsN<1>>, dim3(h.n_blocks), dim3(kHistBlock), 0, s,
+                               hist_args<1>(h));
+        else if (h.nseg <= 16)
+            hipLaunchKernelGGL(k_histogram<HistArgsN<16>>, dim3(h.n_blocks), dim3(kHistBlock), 0,
+                               s, hist_args<16>(h));
+        else
+            hipLaunchKernelGGL(k_histogram<HistArgs>, dim3(h.n_blocks), dim3(kHistBlock), 0, s, h);
+    }
     return hipGetLastError() == hipSuccess ? SH_OK : SH_ERR_HIP;
 }
 

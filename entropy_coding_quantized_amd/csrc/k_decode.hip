@@ -12,6 +12,8 @@
 // each lane its bit position.  Compressed words are staged through a per-chunk LDS ring
 // fed by 128-bit loads; the decode table (<= 2 KB) lives in LDS.  No MFMA: there is no
 // dense contraction.
+#include <type_traits>
+
 #include "device_common.hpp"
 
 namespace shn {
@@ -57,8 +59,8 @@ constexpr int kDecBlock = 256;  // 4 wavefronts
 // ILP chunks per lane: a wavefront decodes 2 * ILP chunks, lanes 32h..32h+31 take chunks
 // 2k + h (k < ILP) of the wavefront's group.  ILP = 1 is the one launched: measured on
 // MI355X, two independent chains per lane ran slower than twice as many wavefronts.
-template <int ILP>
-__global__ __launch_bounds__(kDecBlock) void k_decode(const CodecArgs a) {
+template <int ILP, class A>
+__global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
     constexpr uint32_t kChunksPerWave = 2 * ILP;
     constexpr uint32_t kChunksPerBlock = kDecBlock / 64 * kChunksPerWave;
     __shared__ __align__(16) uint32_t sm[kTabDwords + kChunksPerBlock * kRingStride];
@@ -70,16 +72,16 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const CodecArgs a) {
     const uint32_t wid = __builtin_amdgcn_readfirstlane(bseg * (kDecBlock / 64) + (tid >> 6));
     const uint32_t wv = wid & (kDecBlock / 64 - 1);
     const uint32_t tab_byte = lds_offset(sm);
-    const uint32_t* dec = sg->tab ? sg->tab + kDTDec : a.one.tab;
-    const uint32_t* hdr = sg->tab ? sg->tab + kDTHdr : a.one.hdr;
+    const uint32_t* dec = sg->tab ? sg->tab + kDTDec : inline_tab(a);
+    const uint32_t* hdr = sg->tab ? sg->tab + kDTHdr : inline_hdr(a);
     const uint32_t n_chunks = sg->n_chunks;
     const uint64_t n = sg->n;
-    const uint32_t index_at = header_bytes_dev(a.K);
+    const uint32_t index_at = header_bytes_dev(a.h.K);
     const uint32_t payload_at = index_at + 4 * (n_chunks + 1);
     const uint64_t in_nbytes = sg->c_bytes;
 
     // rearrange the table's entries into the LDS form
-    for (uint32_t i = tid; i < a.L; i += kDecBlock) {
+    for (uint32_t i = tid; i < a.h.L; i += kDecBlock) {
         const uint32_t e0 = dec[2 * i], e1 = dec[2 * i + 1];
         sm[2 * i] = (e0 & 0xFFFF) | (e1 & 0x00FF0000u) | ((e1 & 0xFF00u) << 16);
         sm[2 * i + 1] = (e1 & 31) | ((tab_byte + (e0 >> 16)) << 16);
@@ -100,14 +102,14 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const CodecArgs a) {
                 rin, (int)(index_at + 4 * n_chunks), 0, 0);
             bad |= first != 0 || (uint64_t)payload_at + last > in_nbytes;
         }
-        report(a.status, SH_ERR_CORRUPT_STREAM, bad);
+        report(a.h.status, SH_ERR_CORRUPT_STREAM, bad);
     }
 
     // output: per-wavefront descriptor over the wavefront's chunks
     const uint32_t group = kChunksPerWave * wid;
-    const uint64_t grp_first = (uint64_t)group * a.C;
+    const uint64_t grp_first = (uint64_t)group * a.h.C;
     const uint64_t grp_len = grp_first < n ? n - grp_first : 0;
-    const uint64_t grp_cap = (uint64_t)kChunksPerWave * a.C;
+    const uint64_t grp_cap = (uint64_t)kChunksPerWave * a.h.C;
     const rsrc_t rout = make_rsrc(sg->x + (grp_first < n ? grp_first : 0),
                                   (uint32_t)(grp_len < grp_cap ? grp_len : grp_cap));
 
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const CodecArgs a) {
         const uint32_t chunk = group + slot;
         c.ring = kTabDwords + (wv * kChunksPerWave + slot) * kRingStride;
         c.ring_byte = tab_byte + 4 * c.ring;
-        c.vout = slot * a.C + li;
+        c.vout = slot * a.h.C + li;
         c.nc = 0;
         c.cdw = 0;
         c.cbyte = 0;
@@ -127,10 +129,10 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const CodecArgs a) {
         if (chunk < n_chunks) {
             const uint32_t o0 = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)(index_at + 4 * chunk), 0, 0);
             const uint32_t o1 = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)(index_at + 4 * chunk + 4), 0, 0);
-            const uint64_t first = (uint64_t)chunk * a.C;
-            const uint32_t m = (uint32_t)((n - first) < a.C ? (n - first) : a.C);
+            const uint64_t first = (uint64_t)chunk * a.h.C;
+            const uint32_t m = (uint32_t)((n - first) < a.h.C ? (n - first) : a.h.C);
             const bool ok = o0 <= o1 && ((o0 | o1) & 3) == 0 &&
-                            (o1 - o0) <= 4 * chunk_bound_dwords(m, a.R) &&
+                            (o1 - o0) <= 4 * chunk_bound_dwords(m, a.h.R) &&
                             (uint64_t)payload_at + o1 <= in_nbytes;
             if (ok) {
                 c.nc = m;
@@ -163,11 +165,11 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const CodecArgs a) {
         // initial slots: lane l's R bits at l * R
         c.addr = tab_byte;  // LDS byte address of the current slot's decode entry
         if (li < c.lanes) {
-            const uint32_t p = li * a.R;
+            const uint32_t p = li * a.h.R;
             const uint32_t bits = __builtin_amdgcn_alignbit(sm[c.ring + (p >> 5) + 1], sm[c.ring + (p >> 5)], p);
-            c.addr = tab_byte + ((bits & (a.L - 1)) << 3);
+            c.addr = tab_byte + ((bits & (a.h.L - 1)) << 3);
         }
-        c.pos = c.lanes * a.R;
+        c.pos = c.lanes * a.h.R;
         const uint32_t lo = __builtin_amdgcn_readlane(c.nc, 0), hi = __builtin_amdgcn_readlane(c.nc, 32);
         nc_min = nc_min < lo ? nc_min : lo;
         nc_min = nc_min < hi ? nc_min : hi;
@@ -281,12 +283,15 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const CodecArgs a) {
                 err = 1;
         }
     }
-    report(a.status, SH_ERR_CORRUPT_STREAM, err != 0 || bad_offsets != 0);
+    report(a.h.status, SH_ERR_CORRUPT_STREAM, err != 0 || bad_offsets != 0);
 }
 
 sh_status launch_decode(const CodecArgs& a, uint32_t total_blocks, void* stream) {
     if (total_blocks == 0) return SH_OK;
-    hipLaunchKernelGGL(k_decode<1>, dim3(total_blocks), dim3(kDecBlock), 0, (hipStream_t)stream, a);
+    with_kernel_args(a, [&](const auto& k) {
+        hipLaunchKernelGGL((k_decode<1, std::decay_t<decltype(k)>>), dim3(total_blocks),
+                           dim3(kDecBlock), 0, (hipStream_t)stream, k);
+    });
     return hipGetLastError() == hipSuccess ? SH_OK : SH_ERR_HIP;
 }
 

@@ -41,7 +41,8 @@ __device__ __forceinline__ void ring_or(uint32_t* sm, uint32_t ring_byte, uint32
                           __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-__global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const CodecArgs a) {
+template <class A>
+__global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
     __shared__ __align__(1024) uint32_t sm[kVtBase + kVtDwords];
     const uint32_t tid = threadIdx.x, lane = tid & 63, li = lane & 31, hw = lane >> 5;
     const uint32_t block = __builtin_amdgcn_readfirstlane(blockIdx.x);
@@ -49,8 +50,9 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const CodecArgs a) 
     const uint32_t bseg = block - sg->first_block;
     const uint32_t wid = __builtin_amdgcn_readfirstlane(bseg * (kEncBlock / 64) + (tid >> 6));
     const uint32_t wv = wid & (kEncBlock / 64 - 1);
-    const uint32_t* vt = sg->tab ? sg->tab + kDTVt : a.one.tab;
-    const uint8_t* es_src = sg->tab ? reinterpret_cast<const uint8_t*>(sg->tab + kDTEs) : a.one.es;
+    const uint32_t* vt = sg->tab ? sg->tab + kDTVt : inline_tab(a);
+    const uint8_t* es_src = sg->tab ? reinterpret_cast<const uint8_t*>(sg->tab + kDTEs)
+                                   : inline_es(a);
     const uint32_t n_chunks = sg->n_chunks;
     const uint64_t n = sg->n;
     for (uint32_t i = tid; i < 512; i += kEncBlock) sm[kVtBase + i] = vt[i];
@@ -68,23 +70,23 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const CodecArgs a) 
 
     const uint32_t pair = 2 * wid;
     const uint32_t chunk = pair + hw;
-    const uint64_t pair_first = (uint64_t)pair * a.C;
+    const uint64_t pair_first = (uint64_t)pair * a.h.C;
     const uint64_t pair_len = pair_first < n ? n - pair_first : 0;
     const rsrc_t rin = make_rsrc(sg->x + (pair_first < n ? pair_first : 0),
-                                 (uint32_t)(pair_len < 2ull * a.C ? pair_len : 2ull * a.C));
+                                 (uint32_t)(pair_len < 2ull * a.h.C ? pair_len : 2ull * a.h.C));
     const uint32_t slot0 = sg->slot_base + (pair < n_chunks ? pair : 0);
-    const rsrc_t rslot = make_rsrc(a.slots + (uint64_t)slot0 * a.slot_dwords, 8u * a.slot_dwords);
-    const uint32_t in_base = hw * a.C;          // byte offset of this chunk in rin
-    const uint32_t slot_base = hw * a.slot_dwords * 4;
+    const rsrc_t rslot = make_rsrc(a.h.slots + (uint64_t)slot0 * a.h.slot_dwords, 8u * a.h.slot_dwords);
+    const uint32_t in_base = hw * a.h.C;          // byte offset of this chunk in rin
+    const uint32_t slot_base = hw * a.h.slot_dwords * 4;
     uint32_t nc = 0;
     if (chunk < n_chunks) {
-        const uint64_t first = (uint64_t)chunk * a.C;
-        nc = (uint32_t)((n - first) < a.C ? (n - first) : a.C);
+        const uint64_t first = (uint64_t)chunk * a.h.C;
+        nc = (uint32_t)((n - first) < a.h.C ? (n - first) : a.h.C);
     }
     const uint32_t lanes = nc < 32 ? nc : 32;
     const uint32_t nc_lo = __builtin_amdgcn_readlane(nc, 0), nc_hi = __builtin_amdgcn_readlane(nc, 32);
     const uint32_t steps = ((nc_lo > nc_hi ? nc_lo : nc_hi) + 31) >> 5;
-    const uint32_t L = a.L, R1 = a.R + 1;
+    const uint32_t L = a.h.L, R1 = a.h.R + 1;
 
     // 32 bytes of input tile tl for this lane (32 steps x 32 lanes = 1 KB per tile)
     auto load_tile = [&](uint32_t tl, v4u& p0, v4u& p1) {
@@ -108,8 +110,8 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const CodecArgs a) 
     __syncthreads();
 
     uint32_t X = L;
-    uint32_t P = a.slot_dwords * 32;   // fields go below P, right to left
-    uint32_t fmark = a.slot_dwords;    // dwords at or above fmark are in the slot
+    uint32_t P = a.h.slot_dwords * 32;   // fields go below P, right to left
+    uint32_t fmark = a.h.slot_dwords;    // dwords at or above fmark are in the slot
     uint32_t flush_at = (fmark - 128) * 32;  // once P is below this, flush a block
     // every encode entry is OR-ed in; its bit 15 marks a value in a range without states
     uint32_t bad = sg->tab && sg->tab[kDTStatus] != 0 && nc > 0 ? 0x8000u : 0u;
@@ -193,10 +195,10 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const CodecArgs a) 
         step(--t, std::false_type{});
         step(--t, std::false_type{});
     }
-    const uint32_t pay = a.slot_dwords * 32 - P;  // field bits
+    const uint32_t pay = a.h.slot_dwords * 32 - P;  // field bits
     // the lanes' final states, the decoder's initial states, in front of the fields
-    const uint32_t Pi = P - lanes * a.R;
-    ring_or(sm, ring_byte, Pi + li * a.R, li < lanes ? X - L : 0u);
+    const uint32_t Pi = P - lanes * a.h.R;
+    ring_or(sm, ring_byte, Pi + li * a.h.R, li < lanes ? X - L : 0u);
     if (nc > 0) {
         while (fmark > (Pi >> 5)) {
             fmark -= 128;
@@ -204,11 +206,11 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const CodecArgs a) 
         }
     }
     if (chunk < n_chunks && li == 0) {
-        a.meta[2 * (sg->slot_base + chunk)] = Pi;
-        a.meta[2 * (sg->slot_base + chunk) + 1] = pay;
+        a.h.meta[2 * (sg->slot_base + chunk)] = Pi;
+        a.h.meta[2 * (sg->slot_base + chunk) + 1] = pay;
     }
     bad &= 0x8000u;
-    report(a.status, bad && sg->tab && sg->tab[kDTStatus] != 0 ? SH_ERR_UNSUPPORTED
+    report(a.h.status, bad && sg->tab && sg->tab[kDTStatus] != 0 ? SH_ERR_UNSUPPORTED
                                                               : SH_ERR_SYMBOL_NOT_IN_TABLE,
            bad != 0);
 }
@@ -218,15 +220,16 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const CodecArgs a) 
 // ------------------------------------------------------------------------------------
 constexpr int kScanBlock = 1024;
 
-__global__ __launch_bounds__(kScanBlock) void k_encode_index(const CodecArgs a) {
+template <class A>
+__global__ __launch_bounds__(kScanBlock) void k_encode_index(const A a) {
     __shared__ uint32_t wsum[kScanBlock / 64];
     __shared__ unsigned long long bits_sum;
     const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const SegDesc* sg = a.nseg == 0 ? &a.one.seg : &a.many[blockIdx.x];
+    const SegDesc* sg = &a.segs[blockIdx.x];
     const uint32_t n_chunks = sg->n_chunks;
-    const uint32_t index_at = header_bytes_dev(a.K);
-    const uint32_t* tmpl = sg->tab ? sg->tab + kDTHdr : a.one.hdr;
-    const uint32_t* meta = a.meta + 2ull * sg->slot_base;
+    const uint32_t index_at = header_bytes_dev(a.h.K);
+    const uint32_t* tmpl = sg->tab ? sg->tab + kDTHdr : inline_hdr(a);
+    const uint32_t* meta = a.h.meta + 2ull * sg->slot_base;
     uint32_t* index = reinterpret_cast<uint32_t*>(sg->c + index_at);
     uint32_t* hdr = reinterpret_cast<uint32_t*>(sg->c);
     for (uint32_t i = tid; i < index_at / 4; i += kScanBlock) hdr[i] = header_dword(tmpl, i, sg->n, n_chunks);
@@ -239,7 +242,7 @@ __global__ __launch_bounds__(kScanBlock) void k_encode_index(const CodecArgs a) 
         uint32_t bytes = 0;
         if (c < n_chunks) {
             const uint32_t start = meta[2 * c];
-            bytes = 4 * ((a.slot_dwords * 32 - start + 31) >> 5);
+            bytes = 4 * ((a.h.slot_dwords * 32 - start + 31) >> 5);
             my_bits += meta[2 * c + 1];
         }
         // wavefront inclusive scan, then across the 16 wavefronts
@@ -271,24 +274,25 @@ __global__ __launch_bounds__(kScanBlock) void k_encode_index(const CodecArgs a) 
 // ------------------------------------------------------------------------------------
 // encode, kernel 3: move every chunk from its slot to its place in the payload
 // ------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_encode_compact(const CodecArgs a) {
+template <class A>
+__global__ __launch_bounds__(256) void k_encode_compact(const A a) {
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t block = __builtin_amdgcn_readfirstlane(blockIdx.x);
     const SegDesc* sg = codec_seg(a, block, true);
     const uint32_t c = (block - sg->first_block_c) * 4 + (threadIdx.x >> 6);
     if (c >= sg->n_chunks) return;
-    const uint32_t index_at = header_bytes_dev(a.K);
+    const uint32_t index_at = header_bytes_dev(a.h.K);
     const uint32_t payload_at = index_at + 4 * (sg->n_chunks + 1);
     const uint32_t slot = sg->slot_base + c;
-    const uint32_t start = a.meta[2 * slot];
-    const uint32_t ndw = (a.slot_dwords * 32 - start + 31) >> 5;
+    const uint32_t start = a.h.meta[2 * slot];
+    const uint32_t ndw = (a.h.slot_dwords * 32 - start + 31) >> 5;
     const uint32_t off = reinterpret_cast<const uint32_t*>(sg->c + index_at)[c];
-    const uint32_t* s = a.slots + (uint64_t)slot * a.slot_dwords;
+    const uint32_t* s = a.h.slots + (uint64_t)slot * a.h.slot_dwords;
     uint32_t* d = reinterpret_cast<uint32_t*>(sg->c + payload_at + off);
     const uint32_t s0 = start >> 5;
     for (uint32_t j = lane; j < ndw; j += 64) {
         const uint32_t lo = s[s0 + j];
-        const uint32_t hi = s0 + j + 1 < a.slot_dwords ? s[s0 + j + 1] : 0;
+        const uint32_t hi = s0 + j + 1 < a.h.slot_dwords ? s[s0 + j + 1] : 0;
         d[j] = __builtin_amdgcn_alignbit(hi, lo, start);
     }
 }
@@ -296,11 +300,14 @@ __global__ __launch_bounds__(256) void k_encode_compact(const CodecArgs a) {
 sh_status launch_encode(const CodecArgs& a, uint32_t total_blocks, uint32_t total_blocks_c,
                         void* stream) {
     hipStream_t s = (hipStream_t)stream;
-    if (total_blocks > 0)
-        hipLaunchKernelGGL(k_encode_chunks, dim3(total_blocks), dim3(kEncBlock), 0, s, a);
-    hipLaunchKernelGGL(k_encode_index, dim3(a.nseg ? a.nseg : 1), dim3(kScanBlock), 0, s, a);
-    if (total_blocks_c > 0)
-        hipLaunchKernelGGL(k_encode_compact, dim3(total_blocks_c), dim3(256), 0, s, a);
+    with_kernel_args(a, [&](const auto& k) {
+        using K = std::decay_t<decltype(k)>;
+        if (total_blocks > 0)
+            hipLaunchKernelGGL(k_encode_chunks<K>, dim3(total_blocks), dim3(kEncBlock), 0, s, k);
+        hipLaunchKernelGGL(k_encode_index<K>, dim3(k.h.nseg), dim3(kScanBlock), 0, s, k);
+        if (total_blocks_c > 0)
+            hipLaunchKernelGGL(k_encode_compact<K>, dim3(total_blocks_c), dim3(256), 0, s, k);
+    });
     return hipGetLastError() == hipSuccess ? SH_OK : SH_ERR_HIP;
 }
 
