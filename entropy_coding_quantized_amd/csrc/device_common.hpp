@@ -42,6 +42,14 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+// Workgroup barrier that orders LDS accesses only: global stores issued before it may still
+// be in flight (__syncthreads would wait for them).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Record an error for the whole wavefront: one atomic from the first lane that has one,
 // skipped when an error is already recorded (the first error wins).
 __device__ __forceinline__ void report(int32_t* status, int32_t code, bool mine = true) {

@@ -1,6 +1,8 @@
 // Histogram and table-build kernels of the Shannonic codec for gfx950 (CDNA4, wave64):
 // the offline step of the Shannonic talk notes ("Preprocessing: range selection by dynamic
 // programming", paper section 4.1) run on the GPU, so that tables never leave HBM.
+#include <type_traits>
+
 #include "device_common.hpp"
 
 namespace shn {
@@ -153,20 +155,6 @@ __global__ __launch_bounds__(256) void k_build_cost(const BuildArgs a) {
 constexpr int kBuildBlock = 1024;
 constexpr uint64_t kInf = ~0ull;
 
-// c_k(T) = #{f in [1, L) : N_k * gain(f) >= T}; gain(f) = log2(f+1) - log2(f) strictly
-// decreases in f for f <= 256, so the count is a binary search.
-__device__ __forceinline__ uint32_t items_at_least(uint32_t count, const uint32_t* gain,
-                                                   uint32_t L, uint64_t T) {
-    if (count == 0) return 0;
-    uint32_t lo = 0, hi = L - 1;
-    while (lo < hi) {
-        const uint32_t mid = (lo + hi + 1) >> 1;
-        if ((uint64_t)count * gain[mid] >= T) lo = mid;
-        else hi = mid - 1;
-    }
-    return lo;
-}
-
 // floor(A / f) for A < 2^24, f >= 1: a correctly rounded float quotient, then corrected
 __device__ __forceinline__ uint32_t small_div(uint32_t A, uint32_t f) {
     uint32_t q = (uint32_t)((float)A / (float)f);
@@ -175,25 +163,29 @@ __device__ __forceinline__ uint32_t small_div(uint32_t A, uint32_t f) {
     return q;
 }
 
-// DP work split of one layer: the i < 256 form four groups of 64 (one per lane), group g
-// needing the j below 64 g + 64.  Work unit u (0..15) is group g = floor(sqrt(u)) and
-// chunk c = u - g^2 of it: chunks c < 2g are the 32 j at 32c (all below every i of the group),
-// chunk 2g the 64 j at 64g, where j < i per lane (a triangle, the same work as 32 full j).
-// So all sixteen wavefronts get the same useful work; a diagonal chunk takes 64 passes
-// for it, so the four of them are spread over the four SIMDs (wave w runs on SIMD w % 4).
-__constant__ uint8_t kDpUnit[16] = {0, 3, 8, 15, 1, 2, 4, 5, 6, 7, 9, 10, 11, 12, 13, 14};
+// DP work split: lane q < 1008 owns value i and the 37 j in [37 p, 37 p + 37), for the
+// pieces p = 0 .. ceil(i / 37) - 1 of every i in [1, 256) (piece-major, so a wavefront
+// mostly shares p and its reads of C[j] are broadcasts).  The lane keeps the 37 candidate
+// costs N_[j,i) * s(j, i), which do not change between layers, in registers; slots with
+// j >= i hold kInfCost.  Infeasible C entries hold kInfC.  s(j, i) < 40 * 2^24, so every
+// real cost and every real C value (a sum of costs over a partition of at most N values) is
+// below N * 2^29.33 <= 2^61.33: no sum wraps and every sum with an infinite part stays above
+// every real one.  When N <= 2^27 the values also fit in 57 bits, and the DP runs on keys
+// value << 6 | u (u = the slot of j): the smallest key is the smallest value with the
+// smallest j, one 64-bit compare per candidate.
+constexpr uint32_t kPiece = 37, kPieces = 7, kDpLanes = 1008;
+constexpr uint64_t kInfC = 1ull << 63, kInfCost = 3ull << 61;
 __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a) {
     __shared__ __align__(16) uint32_t sc[kCostEntries];  // cost factors; the DP's choices after it
     __shared__ uint32_t prefix[257];
-    __shared__ uint64_t cbuf[2][256];              // C[i][k-1] and C[i][k], i < 256
-    __shared__ uint64_t qbest[7][256];             // per j-chunk minima of a layer
-    __shared__ uint8_t qarg[7][256];
+    __shared__ uint64_t cbuf[2][kPiece * kPieces];  // C[j][k-1] and C[j][k], kInfC past 255
+    __shared__ uint64_t qbest[kPieces][256];        // per-piece minima of a layer
+    __shared__ uint8_t qarg[kPieces][256];
     __shared__ uint64_t red_c[kBuildBlock / 64];
     __shared__ uint32_t red_j[kBuildBlock / 64];
     __shared__ uint32_t lo_s[257], freq_s[256], cum_s[257], range_of_u[256], count_s[256];
-    __shared__ uint32_t lg_s[257], gain_s[256];
-    __shared__ uint32_t g_at[64];                  // state allocation: G at the probes
-    __shared__ uint64_t t_lo_s, t_hi_s;
+    __shared__ uint32_t lg_s[258], gain_s[257];
+    __shared__ uint32_t f0_s[256], add_s[256], alloc_s[2];  // state allocation: start, taken, total and check
     __shared__ uint32_t status_s;
     const uint32_t tid = threadIdx.x, lane = tid & 63, seg = blockIdx.x;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -209,7 +201,7 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
 #pragma unroll 3
         for (uint32_t i = tid; i < kCostEntries / 4; i += kBuildBlock) dst[i] = src[i];
     }
-    if (tid < 257) lg_s[tid] = (uint32_t)dev_fixed_log2(tid);
+    if (tid < 258) lg_s[tid] = (uint32_t)dev_fixed_log2(tid);
 
     // prefix sums of the histogram, 64-bit to check that the total fits 32 bits
     uint64_t incl = 0;
@@ -228,6 +220,7 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
         prefix[tid + 1] = (uint32_t)(before + incl);
         gain_s[tid] = tid == 0 ? 0u : lg_s[tid + 1] - lg_s[tid];
     }
+    if (tid == 256) gain_s[256] = lg_s[257] - lg_s[256];
     if (tid == 0) {
         prefix[0] = 0;
         const uint64_t total = red_c[0] + red_c[1] + red_c[2] + red_c[3];
@@ -245,82 +238,88 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
             lo_s[1] = 256;
         }
     } else {
-        for (uint32_t i = tid; i < 256; i += kBuildBlock)
-            cbuf[1][i] = i >= 1 ? (uint64_t)prefix[i] * sc[i * (i - 1) / 2] : kInf;
-        __syncthreads();
-        // work unit of this wavefront: the four diagonal units (0, 3, 8, 15) go to waves
-        // 0-3, one per SIMD, the twelve others to waves 4-15
-        const uint32_t unit = kDpUnit[wave];
-        const uint32_t g = unit >= 9 ? 3 : unit >= 4 ? 2 : unit >= 1 ? 1 : 0;
-        const uint32_t chunk = unit - g * g;
-        const bool diag = chunk == 2 * g;
-        const uint32_t ja = diag ? 64 * g : 32 * chunk, jb = diag ? 64 * g + 64 : 32 * chunk + 32;
-        const uint32_t i = 64 * g + lane;
-        const uint32_t row = i * (i - 1) / 2, pi = prefix[i];
-        for (uint32_t k = 2; k < K; ++k) {
-            const uint64_t* cp = cbuf[(k - 1) & 1];
-            uint64_t best = kInf;
-            uint32_t bj = 0;
-            uint32_t j = max(k - 1, ja);
-            if (!diag) {  // every j of the chunk lies below every i of the group
-                for (; j + 4 <= jb; j += 4) {
+        const bool packed = prefix[256] <= (1u << 27);  // uniform
+        for (uint32_t i = tid; i < kPiece * kPieces; i += kBuildBlock) {
+            const uint64_t c1 = i >= 1 && i < 256 ? (uint64_t)prefix[i] * sc[i * (i - 1) / 2] : kInfC;
+            cbuf[1][i] = packed && c1 != kInfC ? c1 << 6 : c1;
+            cbuf[0][i] = kInfC;
+        }
+        // this lane's piece: p, then i = 37 p + 1 + (q - first lane of p)
+        uint32_t p = 0, first = 0;
+        while (p + 1 < kPieces && tid >= first + (255 - kPiece * p)) {
+            first += 255 - kPiece * p;
+            ++p;
+        }
+        const bool dp_lane = tid < kDpLanes;
+        const uint32_t i = dp_lane ? kPiece * p + 1 + (tid - first) : 1;  // idle lanes: no j < i
+        const uint32_t j0 = kPiece * p;
+        uint64_t cost[kPiece];
+        {
+            const uint32_t row = i * (i - 1) / 2, pi = dp_lane ? prefix[i] : 0;
 #pragma unroll
-                    for (uint32_t u = 0; u < 4; ++u) {
-                        const uint64_t c = (uint64_t)(pi - prefix[j + u]) * sc[row + j + u] + cp[j + u];
+            for (uint32_t u = 0; u < kPiece; ++u) {
+                const uint32_t j = j0 + u;
+                const uint64_t c = dp_lane && j < i ? (uint64_t)(pi - prefix[j]) * sc[row + j] : kInfCost;
+                cost[u] = packed ? (c == kInfCost ? c : c << 6) | u : c;
+            }
+        }
+        __syncthreads();
+        auto layers = [&](auto packed_tag) {
+            constexpr bool kPacked = decltype(packed_tag)::value;
+            for (uint32_t k = 2; k < K; ++k) {
+                const uint64_t* cp = cbuf[(k - 1) & 1] + j0;
+                uint64_t best = ~0ull;
+                uint32_t bu = 0;
+                if constexpr (kPacked) {  // keys are distinct: any order, four running minima
+                    uint64_t m[4] = {~0ull, ~0ull, ~0ull, ~0ull};
+#pragma unroll
+                    for (uint32_t u = 0; u < kPiece; ++u) {
+                        const uint64_t c = cp[u] + cost[u];
+                        m[u & 3] = c < m[u & 3] ? c : m[u & 3];
+                    }
+                    m[0] = m[1] < m[0] ? m[1] : m[0];
+                    m[2] = m[3] < m[2] ? m[3] : m[2];
+                    best = m[2] < m[0] ? m[2] : m[0];
+                } else {
+#pragma unroll
+                    for (uint32_t u = 0; u < kPiece; ++u) {
+                        const uint64_t c = cp[u] + cost[u];
                         if (c < best) {
                             best = c;
-                            bj = j + u;
+                            bu = u;
                         }
                     }
                 }
-                for (; j < jb; ++j) {
-                    const uint64_t c = (uint64_t)(pi - prefix[j]) * sc[row + j] + cp[j];
-                    if (c < best) {
-                        best = c;
-                        bj = j;
-                    }
+                if (dp_lane) {
+                    qbest[p][i] = kPacked ? best >> 6 : best;
+                    qarg[p][i] = (uint8_t)(j0 + (kPacked ? (uint32_t)best & 63 : bu));
                 }
-            } else {  // j < i per lane
-                for (; j + 4 <= jb; j += 4) {
-#pragma unroll
-                    for (uint32_t u = 0; u < 4; ++u) {
-                        const uint64_t c = (uint64_t)(pi - prefix[j + u]) * sc[row + j + u] + cp[j + u];
-                        if (j + u < i && c < best) {
-                            best = c;
-                            bj = j + u;
+                lds_barrier();  // the choices go to global memory, read after a full barrier
+                if (tid < 256) {  // pieces in increasing j: the first minimum keeps the smallest j
+                    const uint64_t inf = kPacked ? kInfC >> 6 : kInfC;
+                    uint64_t bb = inf;
+                    uint32_t jj = 0;
+                    for (uint32_t pp = 0; kPiece * pp < tid; ++pp)
+                        if (qbest[pp][tid] < bb || pp == 0) {
+                            bb = qbest[pp][tid];
+                            jj = qarg[pp][tid];
                         }
-                    }
+                    bb = bb < inf ? bb : inf;
+                    cbuf[k & 1][tid] = kPacked && bb != inf ? bb << 6 : (bb == inf ? kInfC : bb);
+                    arg[k * 256 + tid] = (uint8_t)jj;
                 }
-                for (; j < jb; ++j) {
-                    const uint64_t c = (uint64_t)(pi - prefix[j]) * sc[row + j] + cp[j];
-                    if (j < i && c < best) {
-                        best = c;
-                        bj = j;
-                    }
-                }
+                lds_barrier();  // the choices go to global memory, read after a full barrier
             }
-            qbest[chunk][i] = best;
-            qarg[chunk][i] = (uint8_t)bj;
-            __syncthreads();
-            if (tid < 256) {  // chunks in increasing j: the first minimum keeps the smallest j
-                uint64_t b = qbest[0][tid];
-                uint32_t jj = qarg[0][tid];
-                for (uint32_t cc = 1; cc <= 2 * (tid >> 6); ++cc)
-                    if (qbest[cc][tid] < b) {
-                        b = qbest[cc][tid];
-                        jj = qarg[cc][tid];
-                    }
-                cbuf[k & 1][tid] = b;
-                arg[k * 256 + tid] = (uint8_t)jj;
-            }
-            __syncthreads();
-        }
+        };
+        if (packed) layers(std::true_type{});
+        else layers(std::false_type{});
         // layer K at i = 256
         {
             const uint64_t* cp = cbuf[(K - 1) & 1];
             const uint32_t j = K - 1 + tid;
-            uint64_t c = kInf;
-            if (j < 256) c = (uint64_t)(prefix[256] - prefix[j]) * sc[256 * 255 / 2 + j] + cp[j];
+            uint64_t c = ~0ull;
+            if (j < 256) c = (uint64_t)(prefix[256] - prefix[j]) * sc[256 * 255 / 2 + j] +
+                             (packed && cp[j] != kInfC ? cp[j] >> 6 : cp[j]);
             uint32_t bj = j;
             for (int d = 1; d < 64; d <<= 1) {  // lexicographic (cost, j) minimum
                 const uint64_t oc = __shfl_xor(c, d, 64);
@@ -366,83 +365,119 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
         used = wave_sum(used);
         if (lane == 0) {
             if (used > L) status_s = (uint32_t)SH_ERR_UNSUPPORTED;
-            t_lo_s = 0;
-            t_hi_s = 1ull << 57;  // above every N_k * gain(f)
             red_j[0] = used;
+            alloc_s[0] = 0;
         }
-        g_at[lane] = 0;
     }
     __syncthreads();
 
     // ---- state allocation ----
-    // One state per occupied range, then the remaining M = L - used states one at a time to
-    // the range with the largest N_k * gain(f_k), the smallest k on ties.  Each range's
-    // gains fall strictly with f, so those M steps take the M largest items N_k * gain(f)
-    // (f >= 1) in the order (value down, k up): find the value T of the M-th item, give
-    // every range its items above T, and the items equal to T (at most one per range) to
-    // the first ranges in k order.  T is found by a multiway search: per round, every
-    // thread counts one range's items at or above one of nt probes, so the bracket
-    // [t_lo, t_hi) with G(t_lo) >= M > G(t_hi) shrinks (nt + 1)-fold.
+    // One state per occupied range, then the remaining L - used states one at a time to
+    // the range with the largest N_k * gain(f_k), the smallest k on ties; gain(f) =
+    // log2(f + 1) - log2 f falls strictly with f.  Start from the proportional share (at
+    // least one per occupied range); the greedy from there takes the L - total largest of
+    // the increments N_k * gain(f), f >= f_start, in the order (gain down, k up), so every
+    // candidate increment counts, by one binary search per other range, the increments
+    // before it, and is taken when fewer than L - total are.  The result is the greedy
+    // from one state per range when the last increment taken comes before the first one
+    // left; otherwise the selection runs again from one state per range.
     const uint32_t used = red_j[0];
     const bool alloc_ok = used <= L && status_s == 0;
-    const uint32_t M = alloc_ok && used > 0 ? L - used : 0;
-    if (M > 0) {
-        uint32_t kp = 16;
-        while (kp < K) kp <<= 1;
-        const uint32_t nt = kBuildBlock / kp;  // probes per round, at most 64
-        const uint32_t kk = tid % kp, probe = tid / kp;
-        while (true) {
-            const uint64_t t_lo = t_lo_s, t_hi = t_hi_s;
-            if (t_hi - t_lo <= 1) break;
-            const uint64_t span = t_hi - t_lo;
-            const uint64_t step = span / (nt + 1) + 1;
-            if (tid < 64) g_at[tid] = 0;
-            __syncthreads();
-            const uint64_t T = t_lo + step * (probe + 1);
-            if (kk < K && T < t_hi) {
-                const uint32_t c = items_at_least(count_s[kk], gain_s, L, T);
-                if (c) atomicAdd(&g_at[probe], c);
+    if (tid < 256) {
+        uint32_t f0 = 0;
+        if (tid < K && count_s[tid] && alloc_ok) {
+            const uint64_t share = (uint64_t)(L - used) * count_s[tid] / prefix[256];
+            f0 = share > 1 ? (uint32_t)share : 1u;
+        }
+        f0_s[tid] = f0;
+        add_s[tid] = 0;
+        const uint32_t ws = wave_sum(f0);
+        if (lane == 0) atomicAdd(&alloc_s[0], ws);
+    }
+    lds_barrier();
+    uint32_t total = alloc_s[0];
+    if (total > L) {  // the start overshot L: one state per range
+        if (tid < 256) f0_s[tid] = tid < K && count_s[tid] && alloc_ok ? 1u : 0u;
+        total = used;
+        lds_barrier();
+    }
+    auto take = [&](uint32_t from) {  // the L - from largest increments, counted in add_s
+        const uint32_t Mp = L - from;
+        for (uint32_t c = tid; alloc_ok && c < K * Mp; c += kBuildBlock) {
+            const uint32_t k = c / Mp, t = c - k * Mp;
+            const uint32_t fk = f0_s[k];
+            if (!count_s[k] || fk + t >= L) continue;
+            const uint64_t g = (uint64_t)count_s[k] * gain_s[fk + t];
+            uint32_t rank = t;
+            for (uint32_t k2 = 0; k2 < K && rank < Mp; ++k2) {
+                if (k2 == k || !count_s[k2]) continue;
+                const uint64_t c2 = count_s[k2];
+                const uint32_t f2 = f0_s[k2];
+                uint32_t lo = 0, hi = min(Mp, L - f2);  // increments of k2 before (g, k)
+                while (lo < hi) {
+                    const uint32_t mid = (lo + hi) >> 1;
+                    const uint64_t g2 = c2 * gain_s[f2 + mid];
+                    if (g2 > g || (g2 == g && k2 < k)) lo = mid + 1;
+                    else hi = mid;
+                }
+                rank += lo;
             }
-            __syncthreads();
-            if (wave == 0) {
-                const uint64_t Tl = t_lo + step * (lane + 1);
-                const bool probe_ok = lane < nt && Tl < t_hi;
-                const uint64_t ge = __ballot(probe_ok && g_at[lane] >= M);
-                const uint64_t lt = __ballot(probe_ok && g_at[lane] < M);
-                if (lane == 0) {
-                    // G falls with T: the probes at or above M form a prefix
-                    if (ge) t_lo_s = t_lo + step * (63 - __builtin_clzll(ge) + 1);
-                    if (lt) t_hi_s = t_lo + step * (__builtin_ctzll(lt) + 1);
+            if (rank < Mp) atomicAdd(&add_s[k], 1u);
+        }
+        lds_barrier();
+    };
+    take(total);
+    if (wave == 0) {  // the check: lane l looks at ranges l, l + 64, l + 128, l + 192
+        // is (g, k) later in the order than (g2, k2)?
+        auto later = [](uint64_t g, uint32_t k, uint64_t g2, uint32_t k2) {
+            return g < g2 || (g == g2 && k > k2);
+        };
+        uint64_t lg = 0, ng = 0;  // last increment taken, first one left
+        uint32_t lk = 0xFFFFFFFFu, nk = 0xFFFFFFFFu;
+        for (uint32_t k = lane; k < K; k += 64) {
+            if (!count_s[k]) continue;
+            const uint32_t f = f0_s[k] + add_s[k];
+            if (f >= 2) {
+                const uint64_t g = (uint64_t)count_s[k] * gain_s[f - 1];
+                if (lk == 0xFFFFFFFFu || later(g, k, lg, lk)) {
+                    lg = g;
+                    lk = k;
                 }
             }
-            __syncthreads();
-        }
-    }
-    if (wave == 0) {
-        const uint64_t T = t_lo_s;
-        uint32_t above = 0;
-        for (uint32_t k = lane; k < K; k += 64) above += M ? items_at_least(count_s[k], gain_s, L, T + 1) : 0;
-        const uint32_t r = M - wave_sum(above);  // items equal to T still to give
-        uint32_t given = 0;                       // ties given to ranges below k
-        for (uint32_t k0 = 0; k0 < K; k0 += 64) {
-            const uint32_t k = k0 + lane;
-            uint32_t f = 0;
-            bool tie = false;
-            if (k < K && count_s[k] && alloc_ok) {
-                const uint32_t gt = M ? items_at_least(count_s[k], gain_s, L, T + 1) : 0;
-                tie = M && items_at_least(count_s[k], gain_s, L, T) > gt;
-                f = 1 + gt;
+            if (f < L) {
+                const uint64_t g = (uint64_t)count_s[k] * gain_s[f];
+                if (nk == 0xFFFFFFFFu || later(ng, nk, g, k)) {
+                    ng = g;
+                    nk = k;
+                }
             }
-            const uint64_t ties = __ballot(tie);
-            const uint32_t rank = given + __builtin_amdgcn_mbcnt_hi(
-                                              (uint32_t)(ties >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ties, 0u));
-            if (tie && rank < r) ++f;
-            if (k < K) freq_s[k] = f;
-            given += (uint32_t)__builtin_popcountll(ties);
         }
-        if (!alloc_ok && lane == 0) status_s = (uint32_t)SH_ERR_UNSUPPORTED;
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint64_t olg = __shfl_xor(lg, d, 64), ong = __shfl_xor(ng, d, 64);
+            const uint32_t olk = __shfl_xor(lk, d, 64), onk = __shfl_xor(nk, d, 64);
+            if (olk != 0xFFFFFFFFu && (lk == 0xFFFFFFFFu || later(olg, olk, lg, lk))) {
+                lg = olg;
+                lk = olk;
+            }
+            if (onk != 0xFFFFFFFFu && (nk == 0xFFFFFFFFu || later(ng, nk, ong, onk))) {
+                ng = ong;
+                nk = onk;
+            }
+        }
+        if (lane == 0) alloc_s[1] = lk != 0xFFFFFFFFu && nk != 0xFFFFFFFFu && later(lg, lk, ng, nk);
     }
-    __syncthreads();
+    lds_barrier();
+    if (alloc_s[1]) {  // uniform
+        if (tid < 256) {
+            f0_s[tid] = tid < K && count_s[tid] && alloc_ok ? 1u : 0u;
+            add_s[tid] = 0;
+        }
+        lds_barrier();
+        take(used);
+    }
+    if (tid < K) freq_s[tid] = alloc_ok ? f0_s[tid] + add_s[tid] : 0u;
+    if (!alloc_ok && tid == 0) status_s = (uint32_t)SH_ERR_UNSUPPORTED;
+    lds_barrier();
     if (wave == 0) {  // cum_k = f_0 + ... + f_{k-1}; lane l sums ranges 4l .. 4l+3
         uint32_t v[4], sum = 0;
         for (uint32_t r = 0; r < 4; ++r) {
