@@ -82,6 +82,8 @@ _EXPORTS = {
                               C.c_void_p, C.c_uint64, C.c_void_p, C.c_void_p]),
     "sh_stats": (C.c_int32, [C.POINTER(sh_table), C.c_uint64, C.c_uint64, C.c_uint64,
                              C.POINTER(sh_stats_t)]),
+    "sh_stats_batch": (C.c_int32, [C.c_void_p, C.c_uint32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                   C.c_void_p]),
     "sh_device_table_bytes": (C.c_uint64, []),
     "sh_table_to_device": (C.c_int32, [C.POINTER(sh_table), C.POINTER(sh_params), C.c_void_p,
                                        C.c_void_p]),
@@ -233,6 +235,20 @@ def sh_stats(table: sh_table, n: int = 0, payload_bits: int = 0, container_bytes
     return {f: getattr(out, f) for f in STAT_FIELDS}
 
 
+def sh_stats_batch(tables, n=None, payload_bits=None, container_bytes=None) -> list:
+    """sh_stats of every table in one call; tables: a list of sh_table or a ctypes array of
+    them.  Returns one dict per table."""
+    if not isinstance(tables, C.Array):
+        tables = (sh_table * max(len(tables), 1))(*tables)
+    k = len(tables)
+    out = (sh_stats_t * max(k, 1))()
+    arrs = [None if a is None else _u64s(a) for a in (n, payload_bits, container_bytes)]
+    _check(lib().sh_stats_batch(C.addressof(tables), k, *[None if a is None else C.addressof(a)
+                                                          for a in arrs], C.addressof(out)),
+           "sh_stats_batch")
+    return [{f: getattr(out[i], f) for f in STAT_FIELDS} for i in range(k)]
+
+
 def _ptrs(items) -> C.Array:
     if isinstance(items, C.Array):
         return items
@@ -264,12 +280,13 @@ def sh_tables_from_device(d_tables, count: int, stream=None):
     return [out[i] for i in range(count)], [int(st[i]) for i in range(count)]
 
 
-def sh_tables_from_bytes(tables, count: int):
-    """sh_tables_from_device for device-table images already in host memory."""
+def sh_tables_from_bytes(tables, count: int, as_array: bool = False):
+    """sh_tables_from_device for device-table images already in host memory.  With
+    as_array, the tables come back as one ctypes array (for sh_stats_batch)."""
     out = (sh_table * max(count, 1))()
     st = (C.c_int32 * max(count, 1))()
     _check(lib().sh_tables_from_bytes(_ptr(tables), count, out, st), "sh_tables_from_bytes")
-    return [out[i] for i in range(count)], [int(st[i]) for i in range(count)]
+    return (out if as_array else [out[i] for i in range(count)]), [int(st[i]) for i in range(count)]
 
 
 def table_from_device(d_table, stream=None) -> sh_table:

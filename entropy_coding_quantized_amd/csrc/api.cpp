@@ -584,4 +584,18 @@ sh_status sh_stats(const sh_table* table, uint64_t n, uint64_t payload_bits,
     return SH_OK;
 }
 
+sh_status sh_stats_batch(const sh_table* tables, uint32_t nseg, const uint64_t* n,
+                         const uint64_t* payload_bits, const uint64_t* container_bytes,
+                         sh_stats_t* out) {
+    if (nseg == 0) return SH_OK;
+    if (!tables || !out) return SH_ERR_INVALID_ARG;
+    sh_status first = SH_OK;
+    for (uint32_t i = 0; i < nseg; ++i) {
+        const sh_status st = sh_stats(&tables[i], n ? n[i] : 0, payload_bits ? payload_bits[i] : 0,
+                                      container_bytes ? container_bytes[i] : 0, &out[i]);
+        if (st != SH_OK && first == SH_OK) first = st;
+    }
+    return first;
+}
+
 }  // extern "C"

@@ -10,7 +10,8 @@
 // implementation reaches the same partition, exact ties included); the pages do not fix
 // the precision of the objective.
 #include <cstring>
-#include <queue>
+#include <algorithm>
+#include <cmath>
 #include <vector>
 
 #include "codec_internal.hpp"
@@ -126,23 +127,38 @@ sh_status allocate_states(const uint64_t* count, uint32_t K, uint32_t L, uint16_
         uint32_t k;
         bool operator<(const Item& o) const { return g < o.g || (g == o.g && k > o.k); }
     };
-    auto finish = [&](uint32_t total) {  // greedy increments from f up to L
-        std::priority_queue<Item> heap;
+    // greedy increments from f up to L: a binary max-heap whose top is replaced in place
+    Item heap[256];
+    auto finish = [&](uint32_t total) {
+        uint32_t n = 0;
         for (uint32_t k = 0; k < K; ++k)
-            if (count[k]) heap.push({count[k] * gain_of[f[k]], k});
+            if (count[k]) heap[n++] = {count[k] * gain_of[f[k]], k};
+        std::make_heap(heap, heap + n);
         for (; total < L; ++total) {
-            const Item top = heap.top();
-            heap.pop();
-            f[top.k]++;
-            heap.push({count[top.k] * gain_of[f[top.k]], top.k});
+            const uint32_t k = heap[0].k;
+            f[k]++;
+            const Item v{count[k] * gain_of[f[k]], k};
+            uint32_t i = 0;  // sift v down from the root
+            while (true) {
+                uint32_t c = 2 * i + 1;
+                if (c >= n) break;
+                if (c + 1 < n && heap[c] < heap[c + 1]) ++c;
+                if (!(v < heap[c])) break;
+                heap[i] = heap[c];
+                i = c;
+            }
+            heap[i] = v;
         }
     };
     uint64_t N = 0;
     for (uint32_t k = 0; k < K; ++k) N += count[k];
     uint32_t total = 0;
-    for (uint32_t k = 0; k < K; ++k)  // the proportional share, less one: rarely above the result
+    // the proportional share (at least one): rarely above the result.  Any start gives the
+    // greedy result once the check below passes, so it is computed in floating point.
+    const double scale = (double)(L - used) / (double)N;
+    for (uint32_t k = 0; k < K; ++k)
         if (count[k]) {
-            const uint64_t share = (uint64_t)(L - used) * count[k] / N;
+            const double share = std::floor(scale * (double)count[k]);
             f[k] = (uint16_t)(share > 1 ? share : 1);
             total += f[k];
         }

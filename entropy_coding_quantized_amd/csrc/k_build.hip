@@ -174,6 +174,8 @@ __device__ __forceinline__ uint32_t small_div(uint32_t A, uint32_t f) {
 // value << 6 | u (u = the slot of j): the smallest key is the smallest value with the
 // smallest j, one 64-bit compare per candidate.
 constexpr uint32_t kPiece = 37, kPieces = 7, kDpLanes = 1008;
+// state allocation in LDS: at most kIncMax increments (8 bytes each) and their ranks
+constexpr uint32_t kIncMax = 8192;
 constexpr uint64_t kInfC = 1ull << 63, kInfCost = 3ull << 61;
 __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a) {
     __shared__ __align__(16) uint32_t sc[kCostEntries];  // cost factors; the DP's choices after it
@@ -191,7 +193,6 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint64_t* hist = a.hist + 256ull * seg;
     uint32_t* dt = a.tables + (uint64_t)seg * kDTDwords;
-    uint8_t* arg = a.arg + (uint64_t)seg * kArgBytes;
     const uint32_t K = a.K, R = a.R, L = 1u << R;
 
     for (uint32_t i = tid; i < kDTDwords; i += kBuildBlock) dt[i] = 0;  // unused parts read 0
@@ -213,7 +214,7 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
         }
         if (lane == 63) red_c[wave] = incl;
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < 256) {
         uint64_t before = 0;
         for (uint32_t w = 0; w < wave; ++w) before += red_c[w];
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
         const uint64_t total = red_c[0] + red_c[1] + red_c[2] + red_c[3];
         status_s = total >= (1ull << 32) ? (uint32_t)SH_ERR_UNSUPPORTED : 0u;
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- the DP: C[i][k] = min over k-1 <= j < i of C[j][k-1] + N_[j,i) * s(j, i) ----
     // Ties keep the smallest j.  C[j][k-1] is finite for every j >= k-1 once k >= 2.
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
                 cost[u] = packed ? (c == kInfCost ? c : c << 6) | u : c;
             }
         }
-        __syncthreads();
+        lds_barrier();  // from here the cost factors' LDS holds the DP's choices
         auto layers = [&](auto packed_tag) {
             constexpr bool kPacked = decltype(packed_tag)::value;
             for (uint32_t k = 2; k < K; ++k) {
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
                     qbest[p][i] = kPacked ? best >> 6 : best;
                     qarg[p][i] = (uint8_t)(j0 + (kPacked ? (uint32_t)best & 63 : bu));
                 }
-                lds_barrier();  // the choices go to global memory, read after a full barrier
+                lds_barrier();
                 if (tid < 256) {  // pieces in increasing j: the first minimum keeps the smallest j
                     const uint64_t inf = kPacked ? kInfC >> 6 : kInfC;
                     uint64_t bb = inf;
@@ -306,9 +307,9 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
                         }
                     bb = bb < inf ? bb : inf;
                     cbuf[k & 1][tid] = kPacked && bb != inf ? bb << 6 : (bb == inf ? kInfC : bb);
-                    arg[k * 256 + tid] = (uint8_t)jj;
+                    reinterpret_cast<uint8_t*>(sc)[k * 256 + tid] = (uint8_t)jj;
                 }
-                lds_barrier();  // the choices go to global memory, read after a full barrier
+                lds_barrier();
             }
         };
         if (packed) layers(std::true_type{});
@@ -334,12 +335,8 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
                 red_j[wave] = bj;
             }
         }
-        __syncthreads();
-        // the choices of layers 2 .. K-1 back from global memory (written by this block)
-        uint8_t* argl = reinterpret_cast<uint8_t*>(sc);
-        for (uint32_t d = 2 * 64 + tid; d < K * 64; d += kBuildBlock)
-            reinterpret_cast<uint32_t*>(argl)[d] = reinterpret_cast<const uint32_t*>(arg)[d];
-        __syncthreads();
+        lds_barrier();
+        const uint8_t* argl = reinterpret_cast<const uint8_t*>(sc);  // choices of layers 2 .. K-1
         if (tid == 0) {
             uint64_t c = red_c[0];
             uint32_t i = red_j[0];
@@ -357,7 +354,7 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
             lo_s[0] = 0;
         }
     }
-    __syncthreads();
+    lds_barrier();
     for (uint32_t k = tid; k < K; k += kBuildBlock) count_s[k] = prefix[lo_s[k + 1]] - prefix[lo_s[k]];
     if (wave == 0) {
         uint32_t used = 0;
@@ -369,7 +366,7 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
             alloc_s[0] = 0;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- state allocation ----
     // One state per occupied range, then the remaining L - used states one at a time to
@@ -401,28 +398,70 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
         total = used;
         lds_barrier();
     }
-    auto take = [&](uint32_t from) {  // the L - from largest increments, counted in add_s
-        const uint32_t Mp = L - from;
-        for (uint32_t c = tid; alloc_ok && c < K * Mp; c += kBuildBlock) {
-            const uint32_t k = c / Mp, t = c - k * Mp;
-            const uint32_t fk = f0_s[k];
-            if (!count_s[k] || fk + t >= L) continue;
-            const uint64_t g = (uint64_t)count_s[k] * gain_s[fk + t];
-            uint32_t rank = t;
-            for (uint32_t k2 = 0; k2 < K && rank < Mp; ++k2) {
-                if (k2 == k || !count_s[k2]) continue;
-                const uint64_t c2 = count_s[k2];
-                const uint32_t f2 = f0_s[k2];
-                uint32_t lo = 0, hi = min(Mp, L - f2);  // increments of k2 before (g, k)
+    // the L - from largest increments beyond f0_s, counted in add_s.  Small cases hold the
+    // increments and their ranks in LDS (over the cost factors, no longer needed) and split
+    // the work per (increment, other range); others search the gain table per increment.
+    uint64_t* inc = reinterpret_cast<uint64_t*>(sc);
+    uint32_t* rank_of = reinterpret_cast<uint32_t*>(inc + kIncMax);
+    auto take = [&](uint32_t from) {
+        const uint32_t Mp = L - from, n_inc = K * Mp;
+        if (!alloc_ok || Mp == 0) return;
+        // power-of-two strides: increment c = k << lm | t, pair q = c << lk | k2
+        uint32_t lm = 0, lk = 0;
+        while ((1u << lm) < Mp) ++lm;
+        while ((1u << lk) < K) ++lk;
+        const uint32_t n_slots = K << lm;
+        if (n_slots <= kIncMax && (n_slots << lk) <= 64 * kBuildBlock) {
+            for (uint32_t c = tid; c < n_slots; c += kBuildBlock) {
+                const uint32_t k = c >> lm, t = c & ((1u << lm) - 1);
+                const uint32_t fk = f0_s[k];
+                inc[c] = count_s[k] && t < Mp && fk + t < L ? (uint64_t)count_s[k] * gain_s[fk + t] : 0;
+                rank_of[c] = t;
+            }
+            lds_barrier();
+            for (uint32_t q = tid; q < (n_slots << lk); q += kBuildBlock) {
+                const uint32_t c = q >> lk, k2 = q & ((1u << lk) - 1);
+                const uint32_t k = c >> lm, t = c & ((1u << lm) - 1);
+                if (k2 >= K || k2 == k || t >= Mp || !count_s[k2] || !count_s[k] || f0_s[k] + t >= L)
+                    continue;
+                const uint64_t g = inc[c];
+                const uint64_t* row = inc + (k2 << lm);
+                uint32_t lo = 0, hi = min(Mp, L - f0_s[k2]);  // increments of k2 before (g, k)
                 while (lo < hi) {
                     const uint32_t mid = (lo + hi) >> 1;
-                    const uint64_t g2 = c2 * gain_s[f2 + mid];
+                    const uint64_t g2 = row[mid];
                     if (g2 > g || (g2 == g && k2 < k)) lo = mid + 1;
                     else hi = mid;
                 }
-                rank += lo;
+                if (lo) atomicAdd(&rank_of[c], lo);
             }
-            if (rank < Mp) atomicAdd(&add_s[k], 1u);
+            lds_barrier();
+            for (uint32_t c = tid; c < n_slots; c += kBuildBlock) {
+                const uint32_t k = c >> lm, t = c & ((1u << lm) - 1);
+                if (t < Mp && count_s[k] && f0_s[k] + t < L && rank_of[c] < Mp) atomicAdd(&add_s[k], 1u);
+            }
+        } else {
+            for (uint32_t c = tid; c < n_inc; c += kBuildBlock) {
+                const uint32_t k = c / Mp, t = c - k * Mp;
+                const uint32_t fk = f0_s[k];
+                if (!count_s[k] || fk + t >= L) continue;
+                const uint64_t g = (uint64_t)count_s[k] * gain_s[fk + t];
+                uint32_t rank = t;
+                for (uint32_t k2 = 0; k2 < K && rank < Mp; ++k2) {
+                    if (k2 == k || !count_s[k2]) continue;
+                    const uint64_t c2 = count_s[k2];
+                    const uint32_t f2 = f0_s[k2];
+                    uint32_t lo = 0, hi = min(Mp, L - f2);  // increments of k2 before (g, k)
+                    while (lo < hi) {
+                        const uint32_t mid = (lo + hi) >> 1;
+                        const uint64_t g2 = c2 * gain_s[f2 + mid];
+                        if (g2 > g || (g2 == g && k2 < k)) lo = mid + 1;
+                        else hi = mid;
+                    }
+                    rank += lo;
+                }
+                if (rank < Mp) atomicAdd(&add_s[k], 1u);
+            }
         }
         lds_barrier();
     };
@@ -498,7 +537,7 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
         }
         if (lane == 63) cum_s[K] = incl;
     }
-    __syncthreads();
+    __syncthreads();  // also orders the zeroing of the table before the writes below
     const bool ok = status_s == 0 && cum_s[K] == L;
 
     // slot spread: pair (k, j), j < f_k, goes to the slot equal to the number of pairs with
@@ -528,9 +567,16 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
         dt[kDTDec + 2 * rank + 1] = w | (((lo_s[k] - 128u) & 0xFFu) << 8) | ((width - 1) << 16);
         reinterpret_cast<uint8_t*>(dt + kDTEs)[cum_s[k] + j] = (uint8_t)rank;
     }
-    for (uint32_t k = tid; k < K; k += kBuildBlock)
-        for (uint32_t u = lo_s[k]; u < lo_s[k + 1]; ++u) range_of_u[u] = k;
-    __syncthreads();
+    for (uint32_t u = tid; u < 256; u += kBuildBlock) {  // the range of value u: lo_s[k] <= u < lo_s[k+1]
+        uint32_t lo = 0, hi = K - 1;
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi + 1) >> 1;
+            if (lo_s[mid] <= u) lo = mid;
+            else hi = mid - 1;
+        }
+        range_of_u[u] = lo;
+    }
+    lds_barrier();
     // encode entry of every value u
     for (uint32_t u = tid; ok && u < 256; u += kBuildBlock) {
         const uint32_t s = range_of_u[u];

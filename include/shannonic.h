@@ -291,6 +291,16 @@ sh_status sh_decode_stream(const void* d_tables, const uint8_t* const* h_in,
 sh_status sh_stats(const sh_table* table, uint64_t n, uint64_t payload_bits,
                    uint64_t container_bytes, sh_stats_t* out);
 
+/*
+ * sh_stats for nseg tables in one call (a tensor with several tables, e.g. one per KV head).
+ * tables: host array of nseg sh_table.  n, payload_bits, container_bytes: host arrays of
+ * nseg values, or NULL for zeros.  out: host array of nseg sh_stats_t.  Returns the status
+ * of the first table (in index order) that fails; every other entry is still filled.
+ */
+sh_status sh_stats_batch(const sh_table* tables, uint32_t nseg, const uint64_t* n,
+                         const uint64_t* payload_bits, const uint64_t* container_bytes,
+                         sh_stats_t* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -86,6 +86,21 @@ def test_stats_match_oracle():
         assert abs(mine[k] - v) <= 1e-12 * max(1.0, abs(v)), k
 
 
+def test_stats_batch_matches_single_calls():
+    xs = [D.tiny(), D.weight(seed=4)[:100000], np.zeros(0, np.int8)]
+    p = codec.Params()
+    tabs = [codec.sh_build_tables(x, x.size, False, p) for x in xs]
+    ns = [x.size for x in xs]
+    bits = [5 * n + 3 for n in ns]
+    nbytes = [n + 77 for n in ns]
+    single = [codec.sh_stats(t, n, b, c) for t, n, b, c in zip(tabs, ns, bits, nbytes)]
+    assert codec.sh_stats_batch(tabs, ns, bits, nbytes) == single
+    # NULL count arrays mean zeros: the table terms only
+    assert codec.sh_stats_batch(tabs) == [codec.sh_stats(t) for t in tabs]
+    assert codec.lib().sh_stats_batch(None, 2, None, None, None, None) == codec.SH_ERR_INVALID_ARG
+    assert codec.lib().sh_stats_batch(None, 0, None, None, None, None) == codec.SH_OK
+
+
 @pytest.mark.parametrize("n", [0, 1, 31, 32, 4095, 4096, 4097, 123457, 4194304])
 @pytest.mark.parametrize("C_,R", [(4096, 7), (32, 1), (8192, 8), (16384, 7)])
 def test_encode_bound_matches_oracle(n, C_, R):
