@@ -123,7 +123,8 @@ sh_status sh_histogram(const int8_t* d_x, uint64_t n, uint64_t* d_hist, void* st
     h.hist = d_hist;
     h.segs[0].x = (uint8_t*)d_x;
     h.segs[0].n = n;
-    h.n_blocks = (uint32_t)((n + kHistBytesPerBlock - 1) / kHistBytesPerBlock);
+    h.block_bytes = hist_block_bytes(n);
+    h.n_blocks = (uint32_t)((n + h.block_bytes - 1) / h.block_bytes);
     return launch_histogram(h, 1, stream);
 }
 
@@ -243,13 +244,16 @@ sh_status sh_build_tables_batch(const int8_t* const* d_x, const uint64_t* n, uin
         std::memset(&h, 0, sizeof(h));
         h.nseg = e - b;
         h.hist = hist + 256ull * b;
+        uint64_t total = 0;
+        for (uint32_t i = b; i < e; ++i) total += n[i];
+        h.block_bytes = hist_block_bytes(total);
         uint32_t blocks = 0;
         for (uint32_t i = b; i < e; ++i) {
             SegDesc& sd = h.segs[i - b];
             sd.x = (uint8_t*)d_x[i];
             sd.n = n[i];
             sd.first_block = blocks;
-            blocks += (uint32_t)((n[i] + kHistBytesPerBlock - 1) / kHistBytesPerBlock);
+            blocks += (uint32_t)((n[i] + h.block_bytes - 1) / h.block_bytes);
         }
         h.n_blocks = blocks;
         st = launch_histogram(h, e - b, stream);

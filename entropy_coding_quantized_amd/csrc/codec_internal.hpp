@@ -154,12 +154,19 @@ struct KOne {  // one segment with the tables in the arguments
     uint8_t es[256];
 };
 
-constexpr uint32_t kHistBytesPerBlock = 1u << 16;  // values per histogram block
+// values per histogram block: a power of two from 16 KB to 64 KB, so that a launch has about
+// 2048 blocks when it can
+inline uint32_t hist_block_bytes(uint64_t total) {
+    uint32_t b = 1u << 14;
+    while (b < (1u << 16) && (uint64_t)b * 2048 < total) b <<= 1;
+    return b;
+}
 
 template <int N>
 struct HistArgsN {
     uint32_t nseg;
     uint32_t n_blocks;
+    uint32_t block_bytes;   // values per block (hist_block_bytes)
     uint64_t* hist;         // nseg x 256
     SegDesc segs[N];        // x, n and first_block of each segment
 };

@@ -130,6 +130,7 @@ inline HistArgsN<N> hist_args(const HistArgs& h) {
     HistArgsN<N> k;
     k.nseg = h.nseg;
     k.n_blocks = h.n_blocks;
+    k.block_bytes = h.block_bytes;
     k.hist = h.hist;
     std::memcpy(k.segs, h.segs, sizeof(SegDesc) * h.nseg);
     return k;

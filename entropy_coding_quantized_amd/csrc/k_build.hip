@@ -29,13 +29,10 @@ __global__ __launch_bounds__(kHistBlock) void k_histogram(const H a) {
     const uint32_t seg = __builtin_amdgcn_readfirstlane(find_seg_index(a.segs, a.nseg, block, false));
     const uint8_t* x = a.segs[seg].x;
     const uint64_t n = a.segs[seg].n;
-    const uint64_t lo = (uint64_t)(block - a.segs[seg].first_block) * kHistBytesPerBlock;
-    const uint64_t hi = lo + kHistBytesPerBlock < n ? lo + kHistBytesPerBlock : n;
+    const uint64_t lo = (uint64_t)(block - a.segs[seg].first_block) * a.block_bytes;
+    const uint64_t hi = lo + a.block_bytes < n ? lo + a.block_bytes : n;
     const uint32_t copy = threadIdx.x & (kHistCopies - 1);
-    // 16-byte groups fully inside [lo, hi); x is 16-byte aligned and lo a multiple of 16
-    const uint64_t g0 = lo / 16, g1 = hi / 16;
-    for (uint64_t g = g0 + threadIdx.x; g < g1; g += kHistBlock) {
-        const v4u w = *reinterpret_cast<const v4u*>(x + 16 * g);
+    auto count16 = [&](const v4u w) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
 #pragma unroll
@@ -44,7 +41,19 @@ __global__ __launch_bounds__(kHistBlock) void k_histogram(const H a) {
                 atomicAdd(&h[u * kHistCopies + copy], 1u);
             }
         }
+    };
+    // 16-byte groups fully inside [lo, hi); x is 16-byte aligned and lo a multiple of 16.
+    // Four loads per thread are in flight before their counts.
+    const uint64_t g0 = lo / 16, g1 = hi / 16;
+    uint64_t g = g0 + threadIdx.x;
+    for (; g + 3 * kHistBlock < g1; g += 4 * kHistBlock) {
+        v4u w[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = *reinterpret_cast<const v4u*>(x + 16 * (g + r * kHistBlock));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) count16(w[r]);
     }
+    for (; g < g1; g += kHistBlock) count16(*reinterpret_cast<const v4u*>(x + 16 * g));
     for (uint64_t i = g1 * 16 + threadIdx.x; i < hi; i += kHistBlock)  // tail < 16 values
         atomicAdd(&h[((uint32_t)x[i] ^ 0x80) * kHistCopies + copy], 1u);
     __syncthreads();

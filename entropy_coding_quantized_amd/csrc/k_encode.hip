@@ -25,9 +25,9 @@ constexpr uint32_t kVtBase = kTileBase + 8 * 256;
 constexpr uint32_t kVtDwords = 512 + 64;
 
 // OR a field (zero above its length) into a ring at bit pos; ring_byte is the ring's LDS
-// byte offset, a multiple of its 1 KB size.  Both dwords the field may touch are OR-ed
-// unconditionally: a field that stays in one dword ORs zero into the next, which is
-// harmless even when that ring slot has been flushed and reused.
+// byte offset, a multiple of its 1 KB size.  The second dword is OR-ed only by the lanes
+// whose field reaches into it: the 32 fields of a step share a few dwords, and same-address
+// LDS atomics serialise.
 __device__ __forceinline__ void ring_or(uint32_t* sm, uint32_t ring_byte, uint32_t pos,
                                         uint32_t field) {
     typedef __attribute__((address_space(3))) uint32_t lds_word;
@@ -37,8 +37,9 @@ __device__ __forceinline__ void ring_or(uint32_t* sm, uint32_t ring_byte, uint32
     (void)sm;  // the rings sit at LDS byte 0 of the block's only __shared__ array
     __hip_atomic_fetch_or((lds_word*)(uintptr_t)a0, (uint32_t)wide, __ATOMIC_RELAXED,
                           __HIP_MEMORY_SCOPE_WORKGROUP);
-    __hip_atomic_fetch_or((lds_word*)(uintptr_t)a1, (uint32_t)(wide >> 32), __ATOMIC_RELAXED,
-                          __HIP_MEMORY_SCOPE_WORKGROUP);
+    if ((uint32_t)(wide >> 32))
+        __hip_atomic_fetch_or((lds_word*)(uintptr_t)a1, (uint32_t)(wide >> 32), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 template <class A>
