@@ -79,8 +79,12 @@ constexpr uint32_t kDTDwords = 2112;  // 8448 bytes
 constexpr uint32_t kDTBytes = 4 * kDTDwords;
 
 // header dwords that depend on the segment, not on the table: n (2, 3) and n_chunks (6)
+// (template dword ti already read)
+SHN_HD inline uint32_t header_dword_of(uint32_t ti, uint32_t i, uint64_t n, uint32_t nch) {
+    return i == 2 ? (uint32_t)n : i == 3 ? (uint32_t)(n >> 32) : i == 6 ? nch : ti;
+}
 SHN_HD inline uint32_t header_dword(const uint32_t* tmpl, uint32_t i, uint64_t n, uint32_t nch) {
-    return i == 2 ? (uint32_t)n : i == 3 ? (uint32_t)(n >> 32) : i == 6 ? nch : tmpl[i];
+    return header_dword_of(tmpl[i], i, n, nch);
 }
 
 // Decode entry of a slot (kernel-argument / device-table form), two dwords:

@@ -31,18 +31,24 @@ constexpr uint32_t kFill = 128;               // dwords per refill: 32 lanes x 1
 // w_s + nb, maxo = |range| - 1, base = the range's first value as int8 bits and next = the
 // LDS byte address of the entry reached with zero state bits
 constexpr uint32_t kTabDwords = 512;
+constexpr uint32_t kRot = 32;  // ring turn of the odd half wavefront, dwords
 
-// 16 bytes of the chunk starting at dword d (dwords at or past cdw read as 0).
+// 16 bytes of the chunk starting at dword d (dwords at or past cdw read as 0).  The whole
+// load is issued by every lane (from offset 0 where it would leave the chunk) and the rare
+// lanes at the chunk's end fetch their dwords one by one into other registers, so nothing
+// waits for the load here.
 __device__ __forceinline__ v4u load_words(rsrc_t r, uint32_t chunk_byte, uint32_t d,
                                           uint32_t cdw) {
-    if (d + 4 <= cdw)
-        return __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(
-                                           r, (int)(chunk_byte + 4 * d), 0, 0));
-    v4u v = {0, 0, 0, 0};
-    for (uint32_t k = 0; k < 4; ++k)
-        if (d + k < cdw)
-            v[k] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(chunk_byte + 4 * (d + k)), 0, 0);
-    return v;
+    const bool whole = d + 4 <= cdw;
+    const v4u full = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 r, whole ? (int)(chunk_byte + 4 * d) : 0, 0, 0));
+    v4u part = {0, 0, 0, 0};
+    if (!whole && d < cdw) {
+        for (uint32_t k = 0; k < 4; ++k)
+            if (d + k < cdw)
+                part[k] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(chunk_byte + 4 * (d + k)), 0, 0);
+    }
+    return whole ? full : part;
 }
 
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
@@ -51,7 +57,7 @@ typedef const __attribute__((address_space(3))) v2u lds_v2u;
 
 // Per-chunk decoder state of one half wavefront.
 struct DecChain {
-    uint32_t nc, cdw, cbyte, ring, ring_byte, lanes, pos, addr, res_hi, refill_at, err, vout;
+    uint32_t nc, cdw, cbyte, ring, ring_byte, rot, lanes, pos, addr, res_hi, refill_at, err, vout;
     v4u pf;
 };
 
@@ -80,33 +86,23 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
     const uint32_t payload_at = index_at + 4 * (n_chunks + 1);
     const uint64_t in_nbytes = sg->c_bytes;
 
-    // rearrange the table's entries into the LDS form
-    for (uint32_t i = tid; i < a.h.L; i += kDecBlock) {
-        const uint32_t e0 = dec[2 * i], e1 = dec[2 * i + 1];
-        sm[2 * i] = (e0 & 0xFFFF) | (e1 & 0x00FF0000u) | ((e1 & 0xFF00u) << 16);
-        sm[2 * i + 1] = (e1 & 31) | ((tab_byte + (e0 >> 16)) << 16);
-    }
-
+    // The prologue's loads go out in two waves: first everything that needs nothing else
+    // (each lane's pair of chunk-index entries and its table slot), then, once the index is
+    // in, the chunk's first payload words; LDS is written only after both waves are issued.
     const rsrc_t rin = make_rsrc(sg->c, (uint32_t)in_nbytes);
-    if (wid == 0) {
-        // header and index ends: the container must belong to this table and fit in_nbytes
-        // a device table that failed to build, or was built from no values, decodes nothing
-        bool bad = sg->tab && (sg->tab[kDTStatus] != 0 ||
-                               (n > 0 && (sg->tab[kDTN] | sg->tab[kDTN + 1]) == 0));
-        for (uint32_t i = lane; i < index_at / 4; i += 64)
-            bad |= __builtin_amdgcn_raw_buffer_load_b32(rin, (int)(4 * i), 0, 0) !=
-                   header_dword(hdr, i, n, n_chunks);
-        if (lane == 0) {
-            const uint32_t first = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)index_at, 0, 0);
-            const uint32_t last = __builtin_amdgcn_raw_buffer_load_b32(
-                rin, (int)(index_at + 4 * n_chunks), 0, 0);
-            bad |= first != 0 || (uint64_t)payload_at + last > in_nbytes;
-        }
-        report(a.h.status, SH_ERR_CORRUPT_STREAM, bad);
+    const uint32_t group = kChunksPerWave * wid;
+    v2u idx[ILP];
+#pragma unroll
+    for (int k = 0; k < ILP; ++k) {
+        const uint32_t chunk = group + 2 * k + hw;
+        idx[k] = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(
+                                             rin, (int)(index_at + 4 * (chunk < n_chunks ? chunk : 0)), 0, 0));
     }
+    // L <= 256 = kDecBlock: one slot per thread; threads past L repeat the last slot
+    const uint32_t ts = tid < a.h.L ? tid : a.h.L - 1;
+    const uint32_t te0 = dec[2 * ts], te1 = dec[2 * ts + 1];
 
     // output: per-wavefront descriptor over the wavefront's chunks
-    const uint32_t group = kChunksPerWave * wid;
     const uint64_t grp_first = (uint64_t)group * a.h.C;
     const uint64_t grp_len = grp_first < n ? n - grp_first : 0;
     const uint64_t grp_cap = (uint64_t)kChunksPerWave * a.h.C;
@@ -114,6 +110,7 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
                                   (uint32_t)(grp_len < grp_cap ? grp_len : grp_cap));
 
     DecChain ch[ILP];
+    v4u fill0[ILP], fill1[ILP];
 #pragma unroll
     for (int k = 0; k < ILP; ++k) {
         DecChain& c = ch[k];
@@ -121,14 +118,16 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
         const uint32_t chunk = group + slot;
         c.ring = kTabDwords + (wv * kChunksPerWave + slot) * kRingStride;
         c.ring_byte = tab_byte + 4 * c.ring;
+        // the odd half wavefront's ring is turned by kRot dwords, so that the two halves,
+        // which read at similar offsets, do not read the same LDS banks
+        c.rot = hw * kRot;
         c.vout = slot * a.h.C + li;
         c.nc = 0;
         c.cdw = 0;
         c.cbyte = 0;
         c.err = 0;
         if (chunk < n_chunks) {
-            const uint32_t o0 = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)(index_at + 4 * chunk), 0, 0);
-            const uint32_t o1 = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)(index_at + 4 * chunk + 4), 0, 0);
+            const uint32_t o0 = idx[k][0], o1 = idx[k][1];
             const uint64_t first = (uint64_t)chunk * a.h.C;
             const uint32_t m = (uint32_t)((n - first) < a.h.C ? (n - first) : a.h.C);
             const bool ok = o0 <= o1 && ((o0 | o1) & 3) == 0 &&
@@ -143,18 +142,54 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
             }
         }
         c.lanes = c.nc < 32 ? c.nc : 32;
-        // first two refills, plus the third in flight
-        for (uint32_t b = 0; b < 2; ++b) {
-            const uint32_t d = b * kFill + 4 * li;
-            const v4u v = load_words(rin, c.cbyte, d, c.cdw);
-            *reinterpret_cast<v4u*>(&sm[c.ring + d]) = v;
-            if (b == 0 && li == 0) sm[c.ring + kRing] = v[0];
-        }
+        // the first two refills, plus the third in flight
+        fill0[k] = load_words(rin, c.cbyte, 4 * li, c.cdw);
+        fill1[k] = load_words(rin, c.cbyte, kFill + 4 * li, c.cdw);
         c.res_hi = 2 * kFill;  // dwords [res_hi - kRing, res_hi) are in the ring
         c.pf = load_words(rin, c.cbyte, c.res_hi + 4 * li, c.cdw);
         // refills are checked every other step; one is due once the next two steps could
-        // read past res_hi (each advances at most 16 dwords): pos >> 5 >= res_hi - 33
-        c.refill_at = c.res_hi < c.cdw ? (c.res_hi - 33) * 32 : 0xFFFFFFFFu;
+        // read past res_hi (each advances at most 16 dwords): pos >> 5 >= res_hi - 33 + rot
+        c.refill_at = c.res_hi < c.cdw ? (c.res_hi - 33 + c.rot) * 32 : 0xFFFFFFFFu;
+    }
+
+    if (wid == 0) {
+        // header and index ends: the container must belong to this table and fit in_nbytes
+        // a device table that failed to build, or was built from no values, decodes nothing
+        // every load first (at most 200 header dwords: four per lane), then the compares
+        constexpr int kHdrPerLane = (kMaxHeaderDwords + 63) / 64;
+        const uint32_t hd = index_at / 4;
+        uint32_t hv[kHdrPerLane], tv[kHdrPerLane];
+#pragma unroll
+        for (int r = 0; r < kHdrPerLane; ++r) {
+            const uint32_t i = lane + 64 * r, j = i < hd ? i : 0;
+            hv[r] = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)(4 * j), 0, 0);
+            tv[r] = hdr[j];
+        }
+        const uint32_t first = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)index_at, 0, 0);
+        const uint32_t last = __builtin_amdgcn_raw_buffer_load_b32(
+            rin, (int)(index_at + 4 * n_chunks), 0, 0);
+        bool bad = sg->tab && (sg->tab[kDTStatus] != 0 ||
+                               (n > 0 && (sg->tab[kDTN] | sg->tab[kDTN + 1]) == 0));
+#pragma unroll
+        for (int r = 0; r < kHdrPerLane; ++r) {
+            const uint32_t i = lane + 64 * r;
+            if (i < hd) bad |= hv[r] != header_dword_of(tv[r], i, n, n_chunks);
+        }
+        bad |= first != 0 || (uint64_t)payload_at + last > in_nbytes;
+        report(a.h.status, SH_ERR_CORRUPT_STREAM, bad);
+    }
+
+    // the table's entries in the LDS form
+    sm[2 * ts] = (te0 & 0xFFFF) | (te1 & 0x00FF0000u) | ((te1 & 0xFF00u) << 16);
+    sm[2 * ts + 1] = (te1 & 31) | ((tab_byte + (te0 >> 16)) << 16);
+#pragma unroll
+    for (int k = 0; k < ILP; ++k) {
+        const DecChain& c = ch[k];
+        const uint32_t d0 = (4 * li + c.rot) & (kRing - 1), d1 = (kFill + 4 * li + c.rot) & (kRing - 1);
+        *reinterpret_cast<v4u*>(&sm[c.ring + d0]) = fill0[k];
+        *reinterpret_cast<v4u*>(&sm[c.ring + d1]) = fill1[k];
+        if (d0 == 0) sm[c.ring + kRing] = fill0[k][0];
+        if (d1 == 0) sm[c.ring + kRing] = fill1[k][0];
     }
     __syncthreads();
 
@@ -165,11 +200,12 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
         // initial slots: lane l's R bits at l * R
         c.addr = tab_byte;  // LDS byte address of the current slot's decode entry
         if (li < c.lanes) {
-            const uint32_t p = li * a.h.R;
-            const uint32_t bits = __builtin_amdgcn_alignbit(sm[c.ring + (p >> 5) + 1], sm[c.ring + (p >> 5)], p);
+            const uint32_t p = li * a.h.R;  // below 32 * 8 bits: no wrap
+            const uint32_t bits = __builtin_amdgcn_alignbit(sm[c.ring + (p >> 5) + c.rot + 1],
+                                                            sm[c.ring + (p >> 5) + c.rot], p);
             c.addr = tab_byte + ((bits & (a.h.L - 1)) << 3);
         }
-        c.pos = c.lanes * a.h.R;
+        c.pos = c.lanes * a.h.R + 32 * c.rot;  // ring bit position
         const uint32_t lo = __builtin_amdgcn_readlane(c.nc, 0), hi = __builtin_amdgcn_readlane(c.nc, 32);
         nc_min = nc_min < lo ? nc_min : lo;
         nc_min = nc_min < hi ? nc_min : hi;
@@ -182,11 +218,11 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
 
     auto refill = [&](DecChain& c) {
         if (c.pos >= c.refill_at) {
-            const uint32_t d = (c.res_hi + 4 * li) & (kRing - 1);
+            const uint32_t d = (c.res_hi + 4 * li + c.rot) & (kRing - 1);
             *reinterpret_cast<v4u*>(&sm[c.ring + d]) = c.pf;
             if (d == 0) sm[c.ring + kRing] = c.pf[0];
             c.res_hi += kFill;
-            c.refill_at = c.res_hi < c.cdw ? (c.res_hi - 33) * 32 : 0xFFFFFFFFu;
+            c.refill_at = c.res_hi < c.cdw ? (c.res_hi - 33 + c.rot) * 32 : 0xFFFFFFFFu;
             c.pf = load_words(rin, c.cbyte, c.res_hi + 4 * li, c.cdw);
         }
     };
@@ -213,9 +249,10 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
 #pragma unroll
         for (int k = 0; k < ILP; ++k) {
             const uint32_t bits = __builtin_amdgcn_alignbit(w1[k], w0[k], start[k]);
-            const uint32_t v = __builtin_amdgcn_ubfe(bits, 0, e[k][0]);   // the field (need bits)
-            const uint32_t o = __builtin_amdgcn_ubfe(bits, 0, e[k][1]);   // its low w_s bits
-            ch[k].addr = ((v >> (e[k][1] & 31)) << 3) + (e[k][1] >> 16);
+            const uint32_t o = __builtin_amdgcn_ubfe(bits, 0, e[k][1]);   // the low w_s bits
+            // the nb = need - w_s state bits above them
+            const uint32_t sb = __builtin_amdgcn_ubfe(bits, e[k][1], e[k][0] - e[k][1]);
+            ch[k].addr = (sb << 3) + (e[k][1] >> 16);
             en[k] = *(lds_v2u*)(uintptr_t)ch[k].addr;
             bad_offsets |= __builtin_amdgcn_ballot_w64(o > ((e[k][0] >> 16) & 0xFF));
             __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(o + (e[k][0] >> 24)), rout,
@@ -256,13 +293,13 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
             const uint32_t rb = ((start >> 3) & (4 * kRing - 4)) | c.ring_byte;
             const lds_u32* rp = (const lds_u32*)(uintptr_t)rb;
             const uint32_t bits = __builtin_amdgcn_alignbit(rp[1], rp[0], start);
-            const uint32_t v = __builtin_amdgcn_ubfe(bits, 0, ek[0]);
             const uint32_t o = __builtin_amdgcn_ubfe(bits, 0, ek[1]);
+            const uint32_t sb = __builtin_amdgcn_ubfe(bits, ek[1], ek[0] - ek[1]);
             if (act) {
                 c.err |= o > ((ek[0] >> 16) & 0xFF);
                 __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(o + (ek[0] >> 24)), rout,
                                                      (int)c.vout, (int)(t * 32), 0);
-                c.addr = ((v >> (ek[1] & 31)) << 3) + (ek[1] >> 16);
+                c.addr = (sb << 3) + (ek[1] >> 16);
             }
             c.pos += bcast31(incl) & 0xFFFFu;
             e[k] = *(lds_v2u*)(uintptr_t)c.addr;
@@ -278,7 +315,7 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
         err |= c.err;
         if (c.nc > 0) {
             if (li < c.lanes && c.addr != tab_byte) err = 1;
-            if (((c.pos + 31) >> 5) != c.cdw) err = 1;
+            if (((c.pos - 32 * c.rot + 31) >> 5) != c.cdw) err = 1;
             else if ((c.pos & 31) && (sm[c.ring + ((c.pos >> 5) & (kRing - 1))] >> (c.pos & 31)) != 0)
                 err = 1;
         }
