@@ -50,6 +50,22 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Waves that share a SIMD are issued oldest first, which over hundreds of dependent steps
+// lets the oldest wave finish far ahead of the youngest while the launch waits for the
+// youngest.  Kernels with long step loops let their waves take turns at the highest
+// priority: in period p a wave's priority is set from (p + its slot on the SIMD) mod 4.
+constexpr uint32_t kPrioSteps = 16;  // steps per period (even)
+__device__ __forceinline__ uint32_t wave_slot() {
+    return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 4);  // HW_ID bits 0..3
+}
+__device__ __forceinline__ void take_turn(uint32_t period, uint32_t slot) {
+    const uint32_t turn = (period + slot) & 3;
+    if (turn == 0) __builtin_amdgcn_s_setprio(3);
+    else if (turn == 1) __builtin_amdgcn_s_setprio(2);
+    else if (turn == 2) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+}
+
 // Record an error for the whole wavefront: one atomic from the first lane that has one,
 // skipped when an error is already recorded (the first error wins).
 __device__ __forceinline__ void report(int32_t* status, int32_t code, bool mine = true) {

@@ -32,9 +32,6 @@ constexpr uint32_t kFill = 128;               // dwords per refill: 32 lanes x 1
 // LDS byte address of the entry reached with zero state bits
 constexpr uint32_t kTabDwords = 512;
 constexpr uint32_t kRot = 32;  // ring turn of the odd half wavefront, dwords
-constexpr uint32_t kPrioSteps = 16;  // steps per turn at the top wave priority (even)
-// s_getreg operand for the wave's slot on its SIMD: HW_ID bits 0..3
-constexpr int kHwIdWaveSlot = (3 << 11) | (0 << 6) | 4;
 
 // 16 bytes of the chunk starting at dword d (dwords at or past cdw read as 0).  The whole
 // load is issued by every lane (from offset 0 where it would leave the chunk) and the rare
@@ -269,18 +266,11 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
 #pragma unroll
     for (int k = 0; k < ILP; ++k) e[k] = *(lds_v2u*)(uintptr_t)ch[k].addr;
     uint32_t t = 0;
-    // Waves that share a SIMD are issued oldest first, which over hundreds of steps lets the
-    // oldest finish far ahead of the youngest while the launch waits for the youngest.  So
-    // the waves take turns at the highest priority, one period of kPrioSteps steps each,
-    // by their slot on the SIMD.
-    const uint32_t slot_id = __builtin_amdgcn_s_getreg(kHwIdWaveSlot);
+    // the waves on a SIMD take turns at the highest priority (take_turn)
+    const uint32_t slot_id = wave_slot();
     const uint32_t full2 = full & ~1u;
     while (t < full2) {
-        const uint32_t turn = ((t / kPrioSteps) + slot_id) & 3;
-        if (turn == 0) __builtin_amdgcn_s_setprio(3);
-        else if (turn == 1) __builtin_amdgcn_s_setprio(2);
-        else if (turn == 2) __builtin_amdgcn_s_setprio(1);
-        else __builtin_amdgcn_s_setprio(0);
+        take_turn(t / kPrioSteps, slot_id);
         const uint32_t stop = full2 - t < kPrioSteps ? full2 : t + kPrioSteps;
         for (; t < stop; t += 2) {  // two steps per trip, so the entries alternate registers
             full_step(e, e2, t);

@@ -192,10 +192,17 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
     uint32_t t = steps;
     while (t > t_full) step(--t, std::true_type{});
     if (t & 1) step(--t, std::false_type{});
-    while (t > 0) {  // two steps per iteration: the carried values need no copies
-        step(--t, std::false_type{});
-        step(--t, std::false_type{});
+    // the waves on a SIMD take turns at the highest priority (take_turn)
+    const uint32_t slot_id = wave_slot();
+    while (t > 0) {
+        take_turn(t / kPrioSteps, slot_id);
+        const uint32_t stop = t > kPrioSteps ? t - kPrioSteps : 0;  // t and kPrioSteps even
+        while (t > stop) {  // two steps per iteration: the carried values need no copies
+            step(--t, std::false_type{});
+            step(--t, std::false_type{});
+        }
     }
+    __builtin_amdgcn_s_setprio(0);
     const uint32_t pay = a.h.slot_dwords * 32 - P;  // field bits
     // the lanes' final states, the decoder's initial states, in front of the fields
     const uint32_t Pi = P - lanes * a.h.R;
