@@ -156,11 +156,28 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
         if (steps >= 2) u_n = fetch(steps - 2);
         e_c = entry(u_c);
     }
+    // A step's fields are placed one step late, so that the state update of step t, whose
+    // encTable read is in flight, overlaps the placement of step t + 1's fields.
+    uint32_t len_p = 0, field_p = 0;  // nothing to place before the first step
+    auto place = [&]() {  // the carried fields, right to left below P
+        const uint32_t incl = scan32(len_p);
+        P -= bcast31_valu(incl);
+        ring_or(sm, ring_byte, P + incl - len_p, field_p);
+    };
+    // Checked every other step: P then falls at most 48 dwords past flush_at before the
+    // flush (two steps and the final placement), and the ring keeps 256.
+    auto flush_due = [&]() {
+        if (P < flush_at) {  // dwords from P's word + 129 up are final
+            fmark -= 128;
+            flush_at -= 128 * 32;
+            flush_block(fmark);
+        }
+    };
     auto step = [&](uint32_t t, auto partial) {
         const uint32_t u_nn = t >= 2 ? fetch(t - 2) : 0u;
         const uint2 e_n = entry(u_n);
         const uint32_t k = (uint32_t)((int)X + (int)e_c.x) >> R1;
-        const uint32_t Xn = L + es[(e_c.y >> 16) - 512 + (X >> k)];
+        const uint32_t sx = es[(e_c.y >> 16) - 512 + (X >> k)];
         const uint32_t w = (e_c.y >> 8) & 15;
         uint32_t field = (e_c.y & 0xFF) | (__builtin_amdgcn_ubfe(X, 0, k) << w);
         uint32_t len = w + k;
@@ -170,28 +187,30 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
             field = act ? field : 0u;
             len = act ? len : 0u;
             flag = act ? flag : 0u;
-            X = act ? Xn : X;
-        } else {
-            X = Xn;
         }
         bad |= flag;
-        const uint32_t incl = scan32(len);
-        const uint32_t total = bcast31(incl);
-        P -= total;
-        ring_or(sm, ring_byte, P + incl - len, field);
-        if (P < flush_at) {  // dwords from P's word + 129 up are final
-            fmark -= 128;
-            flush_at -= 128 * 32;
-            flush_block(fmark);
+        place();
+        if constexpr (decltype(partial)::value) {
+            X = t * 32 + li < nc ? L + sx : X;
+        } else {
+            X = L + sx;
         }
+        len_p = len;
+        field_p = field;
         e_c = e_n;
         u_n = u_nn;
     };
     // steps where a lane of either half has no value (the tail of a short chunk) first
     const uint32_t t_full = (nc_lo < nc_hi ? nc_lo : nc_hi) >> 5;
     uint32_t t = steps;
-    while (t > t_full) step(--t, std::true_type{});
-    if (t & 1) step(--t, std::false_type{});
+    while (t > t_full) {
+        step(--t, std::true_type{});
+        flush_due();
+    }
+    if (t & 1) {
+        step(--t, std::false_type{});
+        flush_due();
+    }
     // the waves on a SIMD take turns at the highest priority (take_turn)
     const uint32_t slot_id = wave_slot();
     while (t > 0) {
@@ -200,8 +219,10 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
         while (t > stop) {  // two steps per iteration: the carried values need no copies
             step(--t, std::false_type{});
             step(--t, std::false_type{});
+            flush_due();
         }
     }
+    place();  // the first step's fields
     __builtin_amdgcn_s_setprio(0);
     const uint32_t pay = a.h.slot_dwords * 32 - P;  // field bits
     // the lanes' final states, the decoder's initial states, in front of the fields
