@@ -307,14 +307,25 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
                 lds_barrier();
                 if (tid < 256) {  // pieces in increasing j: the first minimum keeps the smallest j
                     const uint64_t inf = kPacked ? kInfC >> 6 : kInfC;
-                    uint64_t bb = inf;
-                    uint32_t jj = 0;
-                    for (uint32_t pp = 0; kPiece * pp < tid; ++pp)
-                        if (qbest[pp][tid] < bb || pp == 0) {
-                            bb = qbest[pp][tid];
-                            jj = qarg[pp][tid];
+                    // every piece's entry is read at once; pieces past i (never written for
+                    // this i) are left out by the predicate
+                    uint64_t qb[kPieces];
+                    uint32_t qa[kPieces];
+#pragma unroll
+                    for (uint32_t pp = 0; pp < kPieces; ++pp) {
+                        qb[pp] = qbest[pp][tid];
+                        qa[pp] = qarg[pp][tid];
+                    }
+                    uint64_t bb = qb[0];
+                    uint32_t jj = qa[0];
+#pragma unroll
+                    for (uint32_t pp = 1; pp < kPieces; ++pp)
+                        if (kPiece * pp < tid && qb[pp] < bb) {
+                            bb = qb[pp];
+                            jj = qa[pp];
                         }
-                    bb = bb < inf ? bb : inf;
+                    bb = tid == 0 ? inf : (bb < inf ? bb : inf);
+                    jj = tid == 0 ? 0u : jj;
                     cbuf[k & 1][tid] = kPacked && bb != inf ? bb << 6 : (bb == inf ? kInfC : bb);
                     reinterpret_cast<uint8_t*>(sc)[k * 256 + tid] = (uint8_t)jj;
                 }
