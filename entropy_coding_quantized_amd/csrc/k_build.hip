@@ -205,11 +205,22 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
     const uint32_t K = a.K, R = a.R, L = 1u << R;
 
     for (uint32_t i = tid; i < kDTDwords; i += kBuildBlock) dt[i] = 0;  // unused parts read 0
-    {
+    {  // the cost factors into LDS: every thread's loads in flight together
+        static_assert(kCostEntries % 4 == 0, "16-byte groups");
+        constexpr uint32_t kGroups = kCostEntries / 4, kPer = (kGroups + kBuildBlock - 1) / kBuildBlock;
         const v4u* src = reinterpret_cast<const v4u*>(a.scost + (uint64_t)seg * kCostEntries);
         v4u* dst = reinterpret_cast<v4u*>(sc);
-#pragma unroll 3
-        for (uint32_t i = tid; i < kCostEntries / 4; i += kBuildBlock) dst[i] = src[i];
+        v4u v[kPer];
+#pragma unroll
+        for (uint32_t r = 0; r < kPer; ++r) {
+            const uint32_t i = tid + r * kBuildBlock;
+            if (i < kGroups) v[r] = src[i];
+        }
+#pragma unroll
+        for (uint32_t r = 0; r < kPer; ++r) {
+            const uint32_t i = tid + r * kBuildBlock;
+            if (i < kGroups) dst[i] = v[r];
+        }
     }
     if (tid < 258) lg_s[tid] = (uint32_t)dev_fixed_log2(tid);
 
@@ -534,6 +545,8 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
         lds_barrier();
         take(used);
     }
+    // the histogram's copy for the table, loaded here so that its latency overlaps the spread
+    const uint64_t h_mine = tid < 256 ? hist[tid] : 0;
     if (tid < K) freq_s[tid] = alloc_ok ? f0_s[tid] + add_s[tid] : 0u;
     if (!alloc_ok && tid == 0) status_s = (uint32_t)SH_ERR_UNSUPPORTED;
     lds_barrier();
@@ -566,8 +579,12 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
     if (!ok)  // no usable table: every value is outside it
         for (uint32_t u = tid; u < 256; u += kBuildBlock) dt[kDTVt + 2 * u + 1] = 0x8000u;
     for (uint32_t p = tid; ok && p < L; p += kBuildBlock) {
-        uint32_t k = 0;
-        while (cum_s[k + 1] <= p) ++k;
+        uint32_t k = 0, khi = K - 1;  // the range of slot p: the first k with cum_s[k + 1] > p
+        while (k < khi) {
+            const uint32_t mid = (k + khi) >> 1;
+            if (cum_s[mid + 1] > p) khi = mid;
+            else k = mid + 1;
+        }
         const uint32_t j = p - cum_s[k], f = freq_s[k];
         uint32_t rank = 0;
         for (uint32_t k2 = 0; k2 < K; ++k2) {
@@ -617,8 +634,7 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
     uint16_t* f16 = reinterpret_cast<uint16_t*>(dt + kDTFreq);
     for (uint32_t k = tid; k <= 256; k += kBuildBlock) lo16[k] = k <= K ? (uint16_t)lo_s[k] : 0;
     for (uint32_t k = tid; k < 256; k += kBuildBlock) f16[k] = k < K ? (uint16_t)freq_s[k] : 0;
-    for (uint32_t u = tid; u < 256; u += kBuildBlock)
-        reinterpret_cast<uint64_t*>(dt + kDTHist)[u] = hist[u];
+    if (tid < 256) reinterpret_cast<uint64_t*>(dt + kDTHist)[tid] = h_mine;
     const uint32_t hbytes = (kHeaderFixed + 3 * K - 1 + 3) / 4 * 4;
     for (uint32_t d = tid; d < kMaxHeaderDwords; d += kBuildBlock) {
         uint32_t word = 0;
