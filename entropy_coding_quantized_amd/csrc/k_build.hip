@@ -442,7 +442,35 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
         while ((1u << lm) < Mp) ++lm;
         while ((1u << lk) < K) ++lk;
         const uint32_t n_slots = K << lm;
-        if (n_slots <= kIncMax && (n_slots << lk) <= 64 * kBuildBlock) {
+        if (n_inc <= kBuildBlock && K <= 256) {
+            // one candidate per thread, c = k * Mp + t, keyed (g << 8) | (255 - k): g < 2^56
+            // (counts < 2^32, gains <= 2^24), and a range's increments fall strictly, so
+            // the keys are distinct and a larger key comes first in the order (g down, k up).
+            // A candidate's rank is the number of larger keys; every lane reads the same
+            // key in each round.
+            const uint32_t c = tid, k = c < n_inc ? c / Mp : 0, t = c - k * Mp;
+            bool valid = false;
+            if (c < n_inc) {
+                const uint32_t fk = f0_s[k];
+                valid = count_s[k] && fk + t < L;
+                inc[c] = valid ? ((uint64_t)count_s[k] * gain_s[fk + t]) << 8 | (255u - k) : 0ull;
+            }
+            lds_barrier();
+            if (valid) {
+                const uint64_t key = inc[c];
+                uint32_t before = 0;
+                uint32_t d = 0;
+                for (; d + 8 <= n_inc; d += 8) {  // eight reads in flight
+                    uint64_t v[8];
+#pragma unroll
+                    for (uint32_t r = 0; r < 8; ++r) v[r] = inc[d + r];
+#pragma unroll
+                    for (uint32_t r = 0; r < 8; ++r) before += v[r] > key ? 1u : 0u;
+                }
+                for (; d < n_inc; ++d) before += inc[d] > key ? 1u : 0u;
+                if (before < Mp) atomicAdd(&add_s[k], 1u);
+            }
+        } else if (n_slots <= kIncMax && (n_slots << lk) <= 64 * kBuildBlock) {
             for (uint32_t c = tid; c < n_slots; c += kBuildBlock) {
                 const uint32_t k = c >> lm, t = c & ((1u << lm) - 1);
                 const uint32_t fk = f0_s[k];
