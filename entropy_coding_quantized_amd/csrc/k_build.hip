@@ -164,9 +164,10 @@ __global__ __launch_bounds__(256) void k_build_cost(const BuildArgs a) {
 constexpr int kBuildBlock = 1024;
 constexpr uint64_t kInf = ~0ull;
 
-// floor(A / f) for A < 2^24, f >= 1: a correctly rounded float quotient, then corrected
+// floor(A / f) for A < 2^20, f >= 1: a float quotient through the hardware reciprocal
+// (relative error below 2^-21, so below 1/2 in absolute terms), then corrected by one
 __device__ __forceinline__ uint32_t small_div(uint32_t A, uint32_t f) {
-    uint32_t q = (uint32_t)((float)A / (float)f);
+    uint32_t q = (uint32_t)((float)A * __builtin_amdgcn_rcpf((float)f));
     if (q * f > A) --q;
     else if ((q + 1) * f <= A) ++q;
     return q;
@@ -399,6 +400,10 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
     }
     lds_barrier();
 
+    // the histogram's copy for the table, loaded here so that it has arrived by the
+    // barrier before the spread, which waits for every outstanding memory access
+    const uint64_t h_mine = tid < 256 ? hist[tid] : 0;
+
     // ---- state allocation ----
     // One state per occupied range, then the remaining L - used states one at a time to
     // the range with the largest N_k * gain(f_k), the smallest k on ties; gain(f) =
@@ -573,8 +578,6 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
         lds_barrier();
         take(used);
     }
-    // the histogram's copy for the table, loaded here so that its latency overlaps the spread
-    const uint64_t h_mine = tid < 256 ? hist[tid] : 0;
     if (tid < K) freq_s[tid] = alloc_ok ? f0_s[tid] + add_s[tid] : 0u;
     if (!alloc_ok && tid == 0) status_s = (uint32_t)SH_ERR_UNSUPPORTED;
     lds_barrier();
@@ -614,14 +617,19 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
             else k = mid + 1;
         }
         const uint32_t j = p - cum_s[k], f = freq_s[k];
-        uint32_t rank = 0;
-        for (uint32_t k2 = 0; k2 < K; ++k2) {
-            const uint32_t f2 = freq_s[k2];
-            if (!f2) continue;
-            const uint32_t A = (2 * j + 1) * f2;
-            const uint32_t odd_max = small_div(k2 < k ? A : A - 1, f);  // largest usable 2j'+1
-            const uint32_t c = (odd_max + 1) >> 1;
-            rank += c < f2 ? c : f2;
+        uint32_t rank = 0;  // A = (2j + 1) f2 < 2L * L <= 2^17
+        for (uint32_t k0 = 0; k0 < K; k0 += 4) {  // four ranges at a time, reads together
+            uint32_t f2v[4];
+#pragma unroll
+            for (uint32_t r = 0; r < 4; ++r) f2v[r] = k0 + r < K ? freq_s[k0 + r] : 0u;
+#pragma unroll
+            for (uint32_t r = 0; r < 4; ++r) {
+                const uint32_t k2 = k0 + r, f2 = f2v[r];
+                const uint32_t A = (2 * j + 1) * f2;
+                const uint32_t odd_max = small_div(k2 < k ? A : A - 1, f);  // largest usable 2j'+1
+                const uint32_t c = (odd_max + 1) >> 1;
+                rank += f2 == 0 ? 0u : (c < f2 ? c : f2);
+            }
         }
         const uint32_t x = f + j;
         const uint32_t nb = R - dev_floor_log2(x);
@@ -664,23 +672,25 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
     for (uint32_t k = tid; k < 256; k += kBuildBlock) f16[k] = k < K ? (uint16_t)freq_s[k] : 0;
     if (tid < 256) reinterpret_cast<uint64_t*>(dt + kDTHist)[tid] = h_mine;
     const uint32_t hbytes = (kHeaderFixed + 3 * K - 1 + 3) / 4 * 4;
+    // header template: the fixed 32 bytes ("SHN1", version 1, log2 L, K, n = 0, C, S,
+    // n_chunks = 0, header bytes), then freq[k] as u16 and lo[1..K-1] as bytes.  Every byte
+    // is computed without branches (both table reads are made, one is kept), so that the
+    // lanes of a wavefront do not serialise over the cases.
     for (uint32_t d = tid; d < kMaxHeaderDwords; d += kBuildBlock) {
         uint32_t word = 0;
-        for (uint32_t b = 0; b < 4; ++b) {
-            const uint32_t at = 4 * d + b;
-            uint32_t byte = 0;
-            if (at < 4) byte = (uint32_t)"SHN1"[at];
-            else if (at == 4) byte = 1;
-            else if (at == 5) byte = R;
-            else if (at < 8) byte = (K >> (8 * (at - 6))) & 0xFF;
-            else if (at < 16) byte = 0;                                   // n
-            else if (at < 20) byte = (a.C >> (8 * (at - 16))) & 0xFF;
-            else if (at < 24) byte = (a.S >> (8 * (at - 20))) & 0xFF;
-            else if (at < 28) byte = 0;                                   // n_chunks
-            else if (at < 32) byte = (hbytes >> (8 * (at - 28))) & 0xFF;
-            else if (at < kHeaderFixed + 2 * K) byte = (freq_s[(at - kHeaderFixed) >> 1] >> (8 * ((at - kHeaderFixed) & 1))) & 0xFF;
-            else if (at < kHeaderFixed + 3 * K - 1) byte = lo_s[at - kHeaderFixed - 2 * K + 1] & 0xFF;
-            word |= byte << (8 * b);
+        if (d < kHeaderFixed / 4) {
+            word = d == 0 ? 0x314E4853u : d == 1 ? 1u | (R << 8) | ((K & 0xFFFFu) << 16)
+                 : d == 4 ? a.C : d == 5 ? a.S : d == 7 ? hbytes : 0u;
+        } else {
+#pragma unroll
+            for (uint32_t b = 0; b < 4; ++b) {
+                const uint32_t at = 4 * d + b - kHeaderFixed;  // byte after the fixed part
+                const uint32_t fi = (at >> 1) < 255 ? at >> 1 : 255u;
+                const uint32_t li = at - 2 * K + 1 < 256 ? at - 2 * K + 1 : 0u;
+                const uint32_t fv = (freq_s[fi] >> (8 * (at & 1))) & 0xFF, lv = lo_s[li] & 0xFF;
+                const uint32_t byte = at < 2 * K ? fv : at < 3 * K - 1 ? lv : 0u;
+                word |= byte << (8 * b);
+            }
         }
         dt[kDTHdr + d] = 4 * d < hbytes ? word : 0;
     }
