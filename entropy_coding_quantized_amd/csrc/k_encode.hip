@@ -173,8 +173,12 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
             flush_block(fmark);
         }
     };
-    auto step = [&](uint32_t t, auto partial) {
-        const uint32_t u_nn = t >= 2 ? fetch(t - 2) : 0u;
+    // may_stage: false for a step whose t is known even (t - 2 is then never a tile's first
+    // step, and for t = 0 the value read is a harmless, unused byte of the tile)
+    auto step = [&](uint32_t t, auto partial, auto may_stage) {
+        uint32_t u_nn;
+        if constexpr (decltype(may_stage)::value) u_nn = t >= 2 ? fetch(t - 2) : 0u;
+        else u_nn = value_at(t - 2);
         const uint2 e_n = entry(u_n);
         const uint32_t k = (uint32_t)((int)X + (int)e_c.x) >> R1;
         const uint32_t sx = es[(e_c.y >> 16) - 512 + (X >> k)];
@@ -204,11 +208,11 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
     const uint32_t t_full = (nc_lo < nc_hi ? nc_lo : nc_hi) >> 5;
     uint32_t t = steps;
     while (t > t_full) {
-        step(--t, std::true_type{});
+        step(--t, std::true_type{}, std::true_type{});
         flush_due();
     }
     if (t & 1) {
-        step(--t, std::false_type{});
+        step(--t, std::false_type{}, std::true_type{});
         flush_due();
     }
     // the waves on a SIMD take turns at the highest priority (take_turn)
@@ -217,8 +221,8 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
         take_turn(t / kPrioSteps, slot_id);
         const uint32_t stop = t > kPrioSteps ? t - kPrioSteps : 0;  // t and kPrioSteps even
         while (t > stop) {  // two steps per iteration: the carried values need no copies
-            step(--t, std::false_type{});
-            step(--t, std::false_type{});
+            step(--t, std::false_type{}, std::true_type{});   // odd t
+            step(--t, std::false_type{}, std::false_type{});  // even t
             flush_due();
         }
     }
