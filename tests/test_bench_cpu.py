@@ -1,0 +1,84 @@
+"""bench.py's host-side pieces, on the CPU: the counter summary (scaling by the calibration
+copy, instruction counts per symbol), stale-profile detection, and the one-GPU guard."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+pytestmark = pytest.mark.filterwarnings("ignore")
+
+
+def _write_counters(path, workload, rows):
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, f"{workload}_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def test_summarize_counters_scales_by_the_calibration_copy(tmp_path):
+    wl = "tiny"
+    prof = tmp_path / "prof"
+    copy_grid = (256 << 20) // 2048
+    # FETCH_SIZE reads half of the copy's 256 MiB, WRITE_SIZE all of it
+    _write_counters(prof / f"pmc_FETCH_SIZE_{wl}", wl, [
+        {"Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": copy_grid,
+         "Counter_Name": "FETCH_SIZE", "Counter_Value": 131072.0},
+        {"Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": 64,  # another copy: ignored
+         "Counter_Name": "FETCH_SIZE", "Counter_Value": 9.0},
+        {"Kernel_Name": "void shn::k_decode<1>(x)", "Grid_Size": 1024,
+         "Counter_Name": "FETCH_SIZE", "Counter_Value": 100.0},
+        {"Kernel_Name": "void shn::k_decode<1>(x)", "Grid_Size": 1024,
+         "Counter_Name": "FETCH_SIZE", "Counter_Value": 300.0}])
+    _write_counters(prof / f"pmc_WRITE_SIZE_{wl}", wl, [
+        {"Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": copy_grid,
+         "Counter_Name": "WRITE_SIZE", "Counter_Value": 262144.0},
+        {"Kernel_Name": "void shn::k_decode<1>(x)", "Grid_Size": 1024,
+         "Counter_Name": "WRITE_SIZE", "Counter_Value": 64.0}])
+    n = sum(x.size for x in bench.make_segments(wl))
+    _write_counters(prof / f"pmc_SQ_{wl}", wl, [
+        {"Kernel_Name": "void shn::k_decode<1>(x)", "Grid_Size": 1024,
+         "Counter_Name": "SQ_INSTS_VALU", "Counter_Value": float(n)},
+        {"Kernel_Name": "void shn::k_encode_chunks<1>(x)", "Grid_Size": 1024,
+         "Counter_Name": "SQ_INSTS_VALU", "Counter_Value": float(2 * n)}])
+    out = tmp_path / "out"
+    os.makedirs(out)
+    bench.summarize_counters(wl, str(prof), str(out))
+    rec = json.load(open(out / f"decode_traffic_{wl}.json"))
+    assert rec["FETCH_SIZE"]["scale"] == pytest.approx(2.0)
+    assert rec["WRITE_SIZE"]["scale"] == pytest.approx(1.0)
+    # (mean 200 KiB x 2 + 64 KiB x 1) in bytes
+    assert rec["hbm_bytes_per_launch"] == pytest.approx((200.0 * 2 + 64.0) * 1024)
+    assert rec["instructions"]["k_decode"]["valu_per_symbol"] == pytest.approx(64.0)
+    assert rec["instructions"]["k_encode_chunks"]["valu_per_symbol"] == pytest.approx(128.0)
+    assert rec["kernels_sha256_16"] == bench.kernels_hash()
+
+
+def test_profiles_taken_from_other_sources_are_ignored(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    os.makedirs(tmp_path / "profiles")
+    with open(tmp_path / "profiles" / "decode_traffic_weight.json", "w") as f:
+        json.dump({"kernels_sha256_16": "not-this-source", "hbm_bytes_per_launch": 1.0}, f)
+    monkeypatch.setattr(bench, "kernels_hash", lambda: "this-source")
+    assert bench.traffic_from_profile("weight") is None
+    with open(tmp_path / "profiles" / "decode_traffic_weight.json", "w") as f:
+        json.dump({"kernels_sha256_16": "this-source", "hbm_bytes_per_launch": 5.0,
+                   "instructions": {"k_decode": {"valu_per_symbol": 19.5}}}, f)
+    assert bench.traffic_from_profile("weight") == 5.0
+    assert bench.valu_per_symbol_from_profile("weight") == 19.5
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["n_gpus"] == 2 and "one GPU" in line["error"]
