@@ -38,7 +38,7 @@ __device__ __forceinline__ uint32_t bcast31(uint32_t v) {
 // The same in VALU only: DPP row_newbcast:15 gives every row its own lane 15, then
 // v_permlane16_swap moves rows 1 and 3 into rows 0 and 2.
 __device__ __forceinline__ uint32_t bcast31_valu(uint32_t v) {
-    const uint32_t r = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x15F, 0xF, 0xF, false);
+    const uint32_t r = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x15F, 0xF, 0xF, true);
     return __builtin_amdgcn_permlane16_swap(r, r, false, false)[1];
 }
 
