@@ -235,18 +235,28 @@ def sh_stats(table: sh_table, n: int = 0, payload_bits: int = 0, container_bytes
     return {f: getattr(out, f) for f in STAT_FIELDS}
 
 
-def sh_stats_batch(tables, n=None, payload_bits=None, container_bytes=None) -> list:
+def sh_stats_batch(tables, n=None, payload_bits=None, container_bytes=None, out=None):
     """sh_stats of every table in one call; tables: a list of sh_table or a ctypes array of
-    them.  Returns one dict per table."""
+    them.  Returns one dict per table, or, given out (a ctypes array of at least as many
+    sh_stats_t), fills out and returns it."""
     if not isinstance(tables, C.Array):
         tables = (sh_table * max(len(tables), 1))(*tables)
     k = len(tables)
-    out = (sh_stats_t * max(k, 1))()
+    raw = out is not None
+    if raw and len(out) < k:
+        raise ValueError("sh_stats_batch: out holds fewer records than tables")
+    if not raw:
+        out = (sh_stats_t * max(k, 1))()
     arrs = [None if a is None else _u64s(a) for a in (n, payload_bits, container_bytes)]
     _check(lib().sh_stats_batch(C.addressof(tables), k, *[None if a is None else C.addressof(a)
                                                           for a in arrs], C.addressof(out)),
            "sh_stats_batch")
-    return [{f: getattr(out[i], f) for f in STAT_FIELDS} for i in range(k)]
+    return out if raw else stats_dicts(out, k)
+
+
+def stats_dicts(records, count: int) -> list:
+    """sh_stats_t records as one dict per record."""
+    return [{f: getattr(records[i], f) for f in STAT_FIELDS} for i in range(count)]
 
 
 def _ptrs(items) -> C.Array:
