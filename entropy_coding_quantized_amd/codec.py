@@ -100,6 +100,9 @@ _EXPORTS = {
                                     C.c_uint64, C.c_void_p, C.c_void_p, C.c_void_p]),
     "sh_decode_batch": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                     C.c_uint32, C.POINTER(sh_params), C.c_void_p, C.c_void_p]),
+    "sh_decode_matvec_batch": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                           C.c_void_p, C.c_void_p, C.c_uint32, C.c_uint32,
+                                           C.POINTER(sh_params), C.c_void_p, C.c_void_p]),
     "sh_decode_stream_staging": (C.c_uint64, [C.c_void_p, C.c_uint32, C.c_uint32]),
     "sh_decode_stream": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                      C.c_uint32, C.POINTER(sh_params), C.c_void_p, C.c_uint64,
@@ -338,6 +341,18 @@ def sh_decode_batch(d_tables, d_in: list, in_nbytes: list, d_y: list, n: list, p
     st = lib().sh_decode_batch(_ptr(d_tables), _ptrs(d_in), _u64s(in_nbytes), _ptrs(d_y),
                                _u64s(n), len(n), C.byref(p), _ptr(d_status), _stream(stream))
     _check(st, "sh_decode_batch")
+
+
+def sh_decode_matvec_batch(d_tables, d_in: list, in_nbytes: list, d_a: list, d_y: list,
+                           n: list, cols: int, params: Params, d_status=None,
+                           stream=None) -> None:
+    """y[i] += W_i a[i] for the int8 matrices W_i (rows of cols values) held by the
+    containers, without writing W_i; d_a[i]: int8 vectors, d_y[i]: int32 outputs."""
+    p = params.c()
+    st = lib().sh_decode_matvec_batch(_ptr(d_tables), _ptrs(d_in), _u64s(in_nbytes), _ptrs(d_a),
+                                      _ptrs(d_y), _u64s(n), cols, len(n), C.byref(p),
+                                      _ptr(d_status), _stream(stream))
+    _check(st, "sh_decode_matvec_batch")
 
 
 def sh_decode_stream_staging(in_nbytes: list, depth: int) -> int:

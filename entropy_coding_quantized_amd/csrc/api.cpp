@@ -454,6 +454,53 @@ sh_status sh_decode_batch(const void* d_tables, const uint8_t* const* d_in,
     return SH_OK;
 }
 
+sh_status sh_decode_matvec_batch(const void* d_tables, const uint8_t* const* d_in,
+                                 const uint64_t* in_nbytes, const int8_t* const* d_a,
+                                 int32_t* const* d_y, const uint64_t* n, uint32_t cols,
+                                 uint32_t nseg, const sh_params* params, int32_t* d_status,
+                                 void* stream) {
+    if (nseg == 0) return SH_OK;
+    if (!d_tables || !d_in || !in_nbytes || !d_a || !d_y || !n || !aligned(d_tables, 16) ||
+        cols == 0)
+        return SH_ERR_INVALID_ARG;
+    sh_status st = check_params(params);
+    if (st != SH_OK) return st;
+    if (cols % 32 != 0 || cols > kMaxMatvecCols) return SH_ERR_UNSUPPORTED;
+    if (!aligned(d_status, 4)) return SH_ERR_INVALID_ARG;
+    for (uint32_t i = 0; i < nseg; ++i) {
+        if (!d_in[i] || !aligned(d_in[i], 4) || n[i] % cols != 0) return SH_ERR_INVALID_ARG;
+        if (n[i] > 0 && (!d_a[i] || !d_y[i] || !aligned(d_a[i], 16) || !aligned(d_y[i], 4)))
+            return SH_ERR_INVALID_ARG;
+        if (n[i] >= (1ull << 32) || in_nbytes[i] > 0xFFFFFFFFull) return SH_ERR_UNSUPPORTED;
+        const uint64_t nch = n_chunks_of(n[i], params->chunk_symbols);
+        if (in_nbytes[i] < header_bytes(params->K) + 4 * (nch + 1)) return SH_ERR_CORRUPT_STREAM;
+    }
+    for (auto [b, e] : groups_of(nseg)) {
+        CodecArgs a;
+        std::memset(&a, 0, sizeof(a));
+        fill_codec_common(a, params, d_status);
+        a.cols = cols;
+        a.nseg = e - b;
+        uint32_t blocks = 0;
+        for (uint32_t i = b; i < e; ++i) {
+            SegDesc& sd = a.many[i - b];
+            const uint64_t nch = n_chunks_of(n[i], params->chunk_symbols);
+            sd.x = (uint8_t*)d_y[i];
+            sd.vec = d_a[i];
+            sd.c = (uint8_t*)d_in[i];
+            sd.n = n[i];
+            sd.c_bytes = in_nbytes[i];
+            sd.tab = (const uint32_t*)((const uint8_t*)d_tables + (uint64_t)i * kDTBytes);
+            sd.first_block = blocks;
+            sd.n_chunks = (uint32_t)nch;
+            blocks += blocks_for(nch, kChunksPerBlock);
+        }
+        st = launch_decode_matvec(a, blocks, stream);
+        if (st != SH_OK) return st;
+    }
+    return SH_OK;
+}
+
 uint64_t sh_decode_stream_staging(const uint64_t* in_nbytes, uint32_t nseg, uint32_t depth) {
     if (!in_nbytes || depth == 0) return 0;
     uint64_t most = 0;

@@ -107,7 +107,10 @@ struct SegDesc {
     uint64_t n;             // values
     uint64_t c_bytes;       // decode: readable bytes at c
     const uint32_t* tab;    // device table, or null: the tables inside CodecArgs
-    sh_encode_info* info;   // encode: where to report (may be null)
+    union {
+        sh_encode_info* info;   // encode: where to report (may be null)
+        const int8_t* vec;      // decode into a matrix-vector product: the vector
+    };
     uint32_t first_block;   // this segment's first block in the chunk kernels
     uint32_t first_block_c; // ... and in the compaction kernel
     uint32_t n_chunks;
@@ -122,7 +125,10 @@ constexpr uint32_t kMaxInlineSegs = 48;  // descriptors carried in one launch's 
 struct CodecArgs {
     uint32_t nseg;          // 0: a single segment with host-built tables (one), else many
     uint32_t C, R, L, K;
-    uint32_t slot_dwords;   // encode: dwords per slot, a multiple of 128
+    union {
+        uint32_t slot_dwords;   // encode: dwords per slot, a multiple of 128
+        uint32_t cols;          // decode into a matrix-vector product: values per row
+    };
     int32_t* status;
     uint32_t* slots;        // encode workspace
     uint32_t* meta;         // encode workspace: per slot {start bit, field bits}
@@ -140,7 +146,10 @@ struct CodecArgs {
 // ---- kernel argument blocks ----
 struct KHead {
     uint32_t nseg, C, R, L, K;
-    uint32_t slot_dwords;
+    union {
+        uint32_t slot_dwords;
+        uint32_t cols;
+    };
     int32_t* status;
     uint32_t* slots;
     uint32_t* meta;
@@ -191,6 +200,10 @@ constexpr uint32_t kArgBytes = 257 * 256;
 sh_status launch_histogram(const HistArgs& h, uint32_t nseg_zero, void* stream);
 sh_status launch_build_tables(const BuildArgs& b, void* stream);
 sh_status launch_decode(const CodecArgs& a, uint32_t total_blocks, void* stream);
+// decode into a matrix-vector product: the vector is staged in LDS, so rows are at most
+// this many values long
+constexpr uint32_t kMaxMatvecCols = 16384;
+sh_status launch_decode_matvec(const CodecArgs& a, uint32_t total_blocks, void* stream);
 sh_status launch_encode(const CodecArgs& a, uint32_t total_blocks, uint32_t total_blocks_c,
                         void* stream);
 

@@ -162,7 +162,6 @@ __global__ __launch_bounds__(256) void k_build_cost(const BuildArgs a) {
 // Build, step 2 (one block per tensor): the DP over the cost factors held in LDS, the
 // state allocation, the spread and every derived table.
 constexpr int kBuildBlock = 1024;
-constexpr uint64_t kInf = ~0ull;
 
 // floor(A / f) for A < 2^20, f >= 1: a float quotient through the hardware reciprocal
 // (relative error below 2^-21, so below 1/2 in absolute terms), then corrected by one

@@ -62,14 +62,133 @@ struct DecChain {
 };
 
 constexpr int kDecBlock = 256;  // 4 wavefronts
+
+// Where the decoded values go.  Bytes: the decoded tensor, one byte per value
+// (sh_decode); the kernel stores them itself.  Any other sink takes one value per lane,
+// step and chain (put, or put_if in the steps where a chunk may already have ended);
+// step_done follows every step and finish the last one.
+struct Bytes {
+    static constexpr bool kBytes = true;
+    static constexpr uint32_t kLdsDwords = 0;
+};
+
+// MatvecSink: y[r] += sum_c W[r][c] a[c] over the decoded matrix W (row-major, cols values
+// a row, cols a multiple of 32) without writing W (sh_decode_matvec_batch).  The 32 values
+// of a chunk's step lie in one row; every lane keeps the products of its values in an int32
+// and, where a row ends within the chunk or the chunk ends, the half wavefront's 32 sums go
+// into y[r] with one atomic add, so rows split across chunks are summed exactly too.  The
+// vector a (int8, at most kMaxMatvecCols values) is held in LDS.
+// a * b + c for a, b sign-extended bytes: one 24-bit multiply-add (the compiler would
+// otherwise pick a 64-bit multiply-add for the wrapping 32-bit sum)
+__device__ __forceinline__ int32_t mad24(int32_t a, int32_t b, int32_t c) {
+    int32_t d;
+    asm volatile("v_mad_i32_i24 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
+
+struct MatvecSink {
+    static constexpr bool kBytes = false;
+    static constexpr uint32_t kLdsDwords = kMaxMatvecCols / 4;
+    int32_t acc;
+    int32_t xp, ap;           // the last step's value and vector entry, multiplied one step
+                              // later so that nothing waits for the vector's LDS read
+    uint32_t abyte;           // LDS byte address of a[c] for this lane's value of the step
+    uint32_t cols;
+    int32_t* y;
+    // per half wavefront (wave-uniform copies of both): the step that ends the current row
+    // (~0 once past the chunk), the row, and the chunk's steps; next = the earlier end
+    uint32_t wrap[2], row[2], steps[2], next;
+    template <class A>
+    __device__ __forceinline__ void init(const A& a, const SegDesc* sg, uint32_t group,
+                                         uint32_t li, uint32_t hw, uint32_t n_chunks,
+                                         uint32_t vec_byte) {
+        cols = a.h.cols;
+        y = reinterpret_cast<int32_t*>(sg->x);
+        acc = 0;
+        xp = 0;
+        ap = 0;
+        uint32_t col_mine = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t chunk = group + h;
+            const uint32_t first = chunk * a.h.C;  // below 2^32: n is
+            const uint32_t col0 = first % cols;
+            steps[h] = 0;
+            if (chunk < n_chunks) {
+                const uint32_t m = (uint32_t)(sg->n - first) < a.h.C ? (uint32_t)(sg->n - first) : a.h.C;
+                steps[h] = m / 32;
+            }
+            wrap[h] = (cols - col0) / 32 - 1;
+            if (wrap[h] >= steps[h]) wrap[h] = ~0u;
+            row[h] = first / cols;
+            if (h == (int)hw) col_mine = col0;
+        }
+        next = wrap[0] < wrap[1] ? wrap[0] : wrap[1];
+        abyte = vec_byte + col_mine + li;
+    }
+    // v: the value's int8 bits in its low byte
+    __device__ __forceinline__ void put(int, uint32_t v, uint32_t) {
+        typedef const __attribute__((address_space(3))) int8_t lds_i8;
+        acc = mad24(xp, ap, acc);
+        xp = (int32_t)(int8_t)(uint8_t)v;
+        ap = *(lds_i8*)(uintptr_t)abyte;
+    }
+    __device__ __forceinline__ void put_if(int k, uint32_t v, uint32_t t, bool act) {
+        acc = mad24(xp, ap, acc);
+        xp = 0;
+        ap = 0;
+        if (act) put(k, v, t);
+    }
+    // the sums of the half wavefronts whose row ended with step t go to y
+    __device__ __forceinline__ void flush(bool end0, bool end1, uint32_t li, uint32_t hw) {
+        acc = mad24(xp, ap, acc);
+        xp = 0;
+        const uint32_t tot = scan32((uint32_t)acc);  // lane 31 of a half: its sum
+        if (hw ? end1 : end0) {
+            if (li == 31 && tot != 0) atomicAdd(y + (hw ? row[1] : row[0]), (int32_t)tot);
+            acc = 0;
+        }
+    }
+    __device__ __forceinline__ void step_done(uint32_t t) {
+        abyte += 32;
+        if (__builtin_expect(t == next, 0)) {  // one scalar compare a step; the rest once a row
+            const bool end0 = t == wrap[0], end1 = t == wrap[1];
+            const uint32_t lane = __lane_id(), li = lane & 31, hw = lane >> 5;
+            flush(end0, end1, li, hw);
+            if (hw ? end1 : end0) abyte -= cols;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                if (h == 0 ? end0 : end1) {
+                    wrap[h] += cols / 32;
+                    if (wrap[h] >= steps[h]) wrap[h] = ~0u;
+                    ++row[h];
+                }
+            next = wrap[0] < wrap[1] ? wrap[0] : wrap[1];
+        }
+    }
+    // a chunk that ends inside a row leaves a partial sum (the sums of ended rows are 0)
+    __device__ __forceinline__ void finish() {
+        const uint32_t lane = __lane_id();
+        flush(true, true, lane & 31, lane >> 5);
+    }
+    // the vector into LDS at vec_byte (cols values, 16-byte aligned, a multiple of 32)
+    template <class A>
+    __device__ __forceinline__ static void stage(const A& a, const SegDesc* sg, uint32_t* vec,
+                                                 uint32_t tid) {
+        const uint32_t groups = a.h.cols / 16;
+        const v4u* src = reinterpret_cast<const v4u*>(sg->vec);
+        for (uint32_t i = tid; i < groups; i += kDecBlock) reinterpret_cast<v4u*>(vec)[i] = src[i];
+    }
+};
 // ILP chunks per lane: a wavefront decodes 2 * ILP chunks, lanes 32h..32h+31 take chunks
 // 2k + h (k < ILP) of the wavefront's group.  ILP = 1 is the one launched: measured on
 // MI355X, two independent chains per lane ran slower than twice as many wavefronts.
-template <int ILP, class A>
+template <int ILP, class Sink, class A>
 __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
     constexpr uint32_t kChunksPerWave = 2 * ILP;
     constexpr uint32_t kChunksPerBlock = kDecBlock / 64 * kChunksPerWave;
-    __shared__ __align__(16) uint32_t sm[kTabDwords + kChunksPerBlock * kRingStride];
+    constexpr uint32_t kVecAt = kTabDwords + kChunksPerBlock * kRingStride;
+    __shared__ __align__(16) uint32_t sm[kVecAt + Sink::kLdsDwords];
     const uint32_t tid = threadIdx.x, lane = tid & 63, li = lane & 31, hw = lane >> 5;
     const uint32_t block = __builtin_amdgcn_readfirstlane(blockIdx.x);
     const SegDesc* sg = codec_seg(a, block, false);
@@ -108,6 +227,11 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
     const uint64_t grp_cap = (uint64_t)kChunksPerWave * a.h.C;
     const rsrc_t rout = make_rsrc(sg->x + (grp_first < n ? grp_first : 0),
                                   (uint32_t)(grp_len < grp_cap ? grp_len : grp_cap));
+    Sink sink;
+    if constexpr (!Sink::kBytes) {
+        sink.init(a, sg, group, li, hw, n_chunks, tab_byte + 4 * kVecAt);
+        Sink::stage(a, sg, sm + kVecAt, tid);
+    }
 
     DecChain ch[ILP];
     v4u fill0[ILP], fill1[ILP];
@@ -254,12 +378,18 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
             const uint32_t sb = __builtin_amdgcn_ubfe(bits, e[k][1], e[k][0] - e[k][1]);
             ch[k].addr = (sb << 3) + (e[k][1] >> 16);
             en[k] = *(lds_v2u*)(uintptr_t)ch[k].addr;
+            // the sink's own LDS reads must not go out ahead of the chain's entry read
+            if constexpr (!Sink::kBytes) __builtin_amdgcn_sched_barrier(0);
             bad_offsets |= __builtin_amdgcn_ballot_w64(o > ((e[k][0] >> 16) & 0xFF));
-            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(o + (e[k][0] >> 24)), rout,
-                                                 (int)ch[k].vout, (int)(t * 32), 0);
+            if constexpr (Sink::kBytes)
+                __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(o + (e[k][0] >> 24)), rout,
+                                                     (int)ch[k].vout, (int)(t * 32), 0);
+            else
+                sink.put(k, o + (e[k][0] >> 24), t);
         }
 #pragma unroll
         for (int k = 0; k < ILP; ++k) ch[k].pos += bcast31(incl[k]) & 0xFFFFu;
+        if constexpr (!Sink::kBytes) sink.step_done(t);
     };
 
     v2u e[ILP], e2[ILP];
@@ -303,17 +433,21 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
             const uint32_t bits = __builtin_amdgcn_alignbit(rp[1], rp[0], start);
             const uint32_t o = __builtin_amdgcn_ubfe(bits, 0, ek[1]);
             const uint32_t sb = __builtin_amdgcn_ubfe(bits, ek[1], ek[0] - ek[1]);
+            if constexpr (!Sink::kBytes) sink.put_if(k, o + (ek[0] >> 24), t, act);
             if (act) {
                 c.err |= o > ((ek[0] >> 16) & 0xFF);
-                __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(o + (ek[0] >> 24)), rout,
-                                                     (int)c.vout, (int)(t * 32), 0);
+                if constexpr (Sink::kBytes)
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(o + (ek[0] >> 24)), rout,
+                                                         (int)c.vout, (int)(t * 32), 0);
                 c.addr = (sb << 3) + (ek[1] >> 16);
             }
             c.pos += bcast31(incl) & 0xFFFFu;
             e[k] = *(lds_v2u*)(uintptr_t)c.addr;
             refill(c);
         }
+        if constexpr (!Sink::kBytes) sink.step_done(t);
     }
+    if constexpr (!Sink::kBytes) sink.finish();
 
     // a valid chunk leaves every lane in slot 0 and ends in its last word, zero-padded
     uint32_t err = 0;
@@ -334,8 +468,20 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
 sh_status launch_decode(const CodecArgs& a, uint32_t total_blocks, void* stream) {
     if (total_blocks == 0) return SH_OK;
     with_kernel_args(a, [&](const auto& k) {
-        hipLaunchKernelGGL((k_decode<1, std::decay_t<decltype(k)>>), dim3(total_blocks),
-                           dim3(kDecBlock), 0, (hipStream_t)stream, k);
+        hipLaunchKernelGGL((k_decode<1, Bytes, std::decay_t<decltype(k)>>),
+                           dim3(total_blocks), dim3(kDecBlock), 0, (hipStream_t)stream, k);
+    });
+    return hipGetLastError() == hipSuccess ? SH_OK : SH_ERR_HIP;
+}
+
+sh_status launch_decode_matvec(const CodecArgs& a, uint32_t total_blocks, void* stream) {
+    if (total_blocks == 0) return SH_OK;
+    if (a.nseg == 0) return SH_ERR_INVALID_ARG;  // device tables only
+    with_kernel_args(a, [&](const auto& k) {
+        using K = std::decay_t<decltype(k)>;
+        if constexpr (!std::is_same_v<K, KOne>)
+            hipLaunchKernelGGL((k_decode<1, MatvecSink, K>), dim3(total_blocks),
+                               dim3(kDecBlock), 0, (hipStream_t)stream, k);
     });
     return hipGetLastError() == hipSuccess ? SH_OK : SH_ERR_HIP;
 }

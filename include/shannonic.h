@@ -261,6 +261,30 @@ sh_status sh_decode_batch(const void* d_tables, const uint8_t* const* d_in,
                           void* stream);
 
 /*
+ * Decode fused into its consumer: container i (as for sh_decode_batch, table i) holds a
+ * row-major int8 matrix W of n[i] / cols rows and cols values a row, and the call adds
+ * y[i][r] += sum_c W[r][c] * d_a[i][c] (int32, wrapping like int32 addition) for every
+ * row r, without writing W anywhere: the decoded values go from the decoder's registers
+ * into the products.  This is the use the Ecco summary page (section 3, the core technique,
+ * and its discussion of GPU decoding pipelines) describes for entropy-coded caches,
+ * decompression inside the kernels that consume the data, applied to this container with
+ * a matrix-vector product as the consumer (an int8 weight matrix times an int8 activation
+ * vector, or int8 keys times a query).
+ * cols: a multiple of 32, at most 16384 (SH_ERR_UNSUPPORTED otherwise; 0 is
+ * SH_ERR_INVALID_ARG); every n[i] a multiple of cols (SH_ERR_INVALID_ARG).  d_a[i]: device,
+ * cols int8 values, 16-byte aligned; d_y[i]: device, n[i] / cols int32, 4-byte aligned, read
+ * and written (zero it first for y = W a).  Rows may span chunks: each chunk adds its part
+ * of a row with one atomic add per row and half wavefront, so y[i] is exact in any order.
+ * Every check of sh_decode applies and the first error goes to *d_status; y[i] of a
+ * container that fails them is unspecified.  Asynchronous on stream.
+ */
+sh_status sh_decode_matvec_batch(const void* d_tables, const uint8_t* const* d_in,
+                                 const uint64_t* in_nbytes, const int8_t* const* d_a,
+                                 int32_t* const* d_y, const uint64_t* n, uint32_t cols,
+                                 uint32_t nseg, const sh_params* params, int32_t* d_status,
+                                 void* stream);
+
+/*
  * Streaming decode, for tensors parked compressed in host memory (the model-scale case:
  * a model's tensors streamed from host memory into HBM).  Container i (h_in[i], host,
  * in_nbytes[i] bytes, pinned for the copies to be asynchronous) is decoded with device

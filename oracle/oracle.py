@@ -54,6 +54,7 @@ def lib():
         L.orc_decode.argtypes = [u8p, C.c_uint64, i8p, C.c_uint64]
         L.orc_stats.argtypes = [u64p, C.c_int, C.c_int, u16p, u16p, C.c_uint64, C.c_uint64,
                                 C.c_uint64, C.POINTER(C.c_double)]
+        L.orc_matvec_i8.argtypes = [i8p, C.c_uint64, C.c_uint32, i8p, C.POINTER(C.c_int32)]
         _lib = L
     return _lib
 
@@ -167,6 +168,23 @@ def decode(buf: np.ndarray, n: int, raise_on_error: bool = True):
         _check(st, "decode")
         return y[:n]
     return st, y[:n]
+
+
+def matvec_i8(w: np.ndarray, cols: int, a: np.ndarray, y=None) -> np.ndarray:
+    """y + W a for the int8 matrix w (rows of cols values, row-major) and int8 vector a,
+    int32 wrapping; y defaults to zeros."""
+    w = np.ascontiguousarray(w, dtype=np.int8).reshape(-1)
+    a = np.ascontiguousarray(a, dtype=np.int8).reshape(-1)
+    rows = w.size // cols if cols else 0
+    y = np.zeros(max(rows, 1), dtype=np.int32) if y is None else np.array(y, dtype=np.int32)
+    _check(lib().orc_matvec_i8(_p(w, C.c_int8), w.size, cols, _p(a, C.c_int8),
+                               _p(y, C.c_int32)), "matvec_i8")
+    return y[:rows]
+
+
+def decode_matvec(buf: np.ndarray, n: int, cols: int, a: np.ndarray, y=None) -> np.ndarray:
+    """The fused decode's result: y + W a for the matrix W that the container holds."""
+    return matvec_i8(decode(buf, n), cols, a, y)
 
 
 def stats(h: np.ndarray, lo: np.ndarray, freq: np.ndarray, log2_L: int, payload_bits: int,

@@ -720,3 +720,18 @@ int orc_stats(const uint64_t* h256, int K, int log2_L, const uint16_t* lo,
     }
     return ORC_OK;
 }
+
+/* Decode fused into a consumer (Ecco summary page, section 3: entropy-coded data decoded
+ * inside the kernel that uses it).  The oracle's side is the definition: the decoded
+ * matrix (rows of cols values, row-major, as orc_decode writes the tensor) times the
+ * vector, each row summed exactly in 64 bits and added to y[r] modulo 2^32. */
+int orc_matvec_i8(const int8_t* w, uint64_t n, uint32_t cols, const int8_t* a, int32_t* y)
+{
+    if (cols == 0 || n % cols != 0) return ORC_ERR_INVALID;
+    for (uint64_t r = 0; r < n / cols; ++r) {
+        int64_t s = 0;
+        for (uint32_t c = 0; c < cols; ++c) s += (int64_t)w[r * cols + c] * (int64_t)a[c];
+        y[r] = (int32_t)((uint32_t)y[r] + (uint32_t)(uint64_t)s);
+    }
+    return ORC_OK;
+}

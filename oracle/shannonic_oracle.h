@@ -42,6 +42,9 @@ int orc_decode(const uint8_t* in, uint64_t nbytes, int8_t* y, uint64_t n);
 int orc_stats(const uint64_t* h256, int K, int log2_L, const uint16_t* lo,
               const uint16_t* freq, uint64_t payload_bits, uint64_t container_bytes,
               uint64_t n, double* out);
+/* The consumer of a decoded matrix in the fused decode: y[r] += sum_c w[r*cols + c] * a[c]
+ * for every row r < n / cols, wrapping like int32 addition. */
+int orc_matvec_i8(const int8_t* w, uint64_t n, uint32_t cols, const int8_t* a, int32_t* y);
 
 #ifdef __cplusplus
 }

@@ -192,6 +192,26 @@ def test_batch_argument_checks_are_synchronous():
     assert codec.sh_device_table_bytes() % 16 == 0
 
 
+def test_matvec_argument_checks_are_synchronous():
+    """Shapes the fused decode does not take are refused before any device work."""
+    lib = codec.lib()
+    pc = codec.Params(K=16, log2_L=7, chunk_symbols=4096).c()
+    fake = 1 << 20  # never dereferenced
+    ptrs = codec._ptrs([fake])
+    caps = codec._u64s([1 << 16])
+    for n, cols, status in [(1024, 0, codec.SH_ERR_INVALID_ARG),
+                            (960, 48, codec.SH_ERR_UNSUPPORTED),      # not a multiple of 32
+                            (1000, 32, codec.SH_ERR_INVALID_ARG),     # n not whole rows
+                            (65536, 32768, codec.SH_ERR_UNSUPPORTED)]:  # longer than LDS holds
+        assert lib.sh_decode_matvec_batch(fake, ptrs, caps, ptrs, ptrs, codec._u64s([n]), cols,
+                                          1, C.byref(pc), None, None) == status
+    assert lib.sh_decode_matvec_batch(fake, ptrs, caps, ptrs, ptrs, codec._u64s([1024]), 32,
+                                      0, C.byref(pc), None, None) == codec.SH_OK
+    misaligned = codec._ptrs([fake + 4])
+    assert lib.sh_decode_matvec_batch(fake, ptrs, caps, misaligned, ptrs, codec._u64s([1024]),
+                                      32, 1, C.byref(pc), None, None) == codec.SH_ERR_INVALID_ARG
+
+
 def test_tables_from_bytes_rejects_garbage():
     """Device-table images that do not form a table are reported per table, not raised."""
     words = codec.sh_device_table_bytes() // 4

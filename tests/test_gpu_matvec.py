@@ -1,0 +1,100 @@
+"""GPU parity of the fused decode (sh_decode_matvec_batch): y += W a for the int8 matrices
+that the containers hold, with W never written.  Expected values come from the oracle's
+matrix-vector product of the seeded inputs themselves (the decode is lossless); int32
+results must match exactly.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from entropy_coding_quantized_amd import codec
+from entropy_coding_quantized_amd import datagen as D
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    codec.lib()
+    return torch
+
+
+def _matvec_gpu(torch, xs, avs, cols, p, y0=None, corrupt=None):
+    """Tables and containers on the GPU, then the fused call; returns (ys, status)."""
+    dx = [torch.from_numpy(np.ascontiguousarray(x)).cuda() if x.size else
+          torch.empty(16, dtype=torch.int8, device="cuda")[:0] for x in xs]
+    tables, _ = codec.build_tables_tensors(dx, p)
+    buf, offs, caps, info, status = codec.encode_tensors(tables, dx, p)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    if corrupt is not None:  # a byte of container i's header: never a valid container
+        i, byte = corrupt
+        buf[offs[i] + byte] ^= 0x5A
+    da = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in avs]
+    rows = [x.size // cols for x in xs]
+    dy = [torch.from_numpy(np.array(y0[i] if y0 is not None else np.zeros(r), dtype=np.int32)).cuda()
+          if r else torch.zeros(4, dtype=torch.int32, device="cuda") for i, r in enumerate(rows)]
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    base = buf.data_ptr()
+    codec.sh_decode_matvec_batch(tables, [base + o for o in offs], caps,
+                                 [a.data_ptr() for a in da], [y.data_ptr() for y in dy],
+                                 [x.size for x in xs], cols, p, st)
+    torch.cuda.synchronize()
+    return [y.cpu().numpy()[:r] for y, r in zip(dy, rows)], int(st.item())
+
+
+@pytest.mark.parametrize("rows,cols,C", [
+    (4096, 1024, 4096),    # weight-shaped: four rows a chunk, rows aligned with chunks
+    (1024, 128, 8192),     # keys of one head: 64 rows a chunk
+    (64, 4096, 1024),      # a row spans four chunks
+    (700, 96, 4096),       # rows straddle chunk boundaries (4096 = 42 * 96 + 64)
+    (37, 32, 256),         # the narrowest rows, a ragged last chunk
+    (3, 16384, 4096),      # the widest rows
+    (333, 160, 2048),      # ragged last chunk, rows straddling chunks
+])
+def test_matvec_matches_oracle(torch_cuda, rows, cols, C):
+    torch = torch_cuda
+    print(f"case: matvec rows={rows} cols={cols} C={C}", flush=True)
+    rng = np.random.default_rng(rows * 7 + cols)
+    x = D.quantize(rng.laplace(0, 12, size=rows * cols))
+    a = rng.integers(-128, 128, size=cols).astype(np.int8)
+    p = codec.Params(K=16, log2_L=7, chunk_symbols=C)
+    (y,), st = _matvec_gpu(torch, [x], [a], cols, p)
+    assert st == 0
+    expect = O.matvec_i8(x, cols, a)
+    assert np.array_equal(y, expect)
+
+
+def test_matvec_batch_accumulates_per_tensor(torch_cuda):
+    """Several matrices with their own tables, vectors and starting y (y += W a), and the
+    degenerate tensors: all zero, every value once, an empty matrix."""
+    torch = torch_cuda
+    print("case: matvec batch", flush=True)
+    rng = np.random.default_rng(5)
+    cols = 256
+    xs = [D.quantize(rng.normal(0, s, size=r * cols)) for s, r in [(3.0, 40), (30.0, 129), (9.0, 7)]]
+    xs += [np.zeros(16 * cols, np.int8), D.uniform_exact(2, seed=3),
+           np.zeros(0, np.int8)]
+    avs = [rng.integers(-128, 128, size=cols).astype(np.int8) for _ in xs]
+    y0 = [rng.integers(-2**30, 2**30, size=x.size // cols) for x in xs]
+    p = codec.Params(K=16, log2_L=7, chunk_symbols=1024)
+    ys, st = _matvec_gpu(torch, xs, avs, cols, p, y0=y0)
+    assert st == 0
+    for x, a, y, y_0 in zip(xs, avs, ys, y0):
+        assert np.array_equal(y, O.matvec_i8(x, cols, a, y_0))
+
+
+def test_matvec_reports_a_corrupt_container(torch_cuda):
+    torch = torch_cuda
+    print("case: matvec corrupt", flush=True)
+    rng = np.random.default_rng(8)
+    cols = 512
+    x = D.quantize(rng.laplace(0, 10, size=64 * cols))
+    a = rng.integers(-128, 128, size=cols).astype(np.int8)
+    p = codec.Params(K=16, log2_L=7, chunk_symbols=4096)
+    _, st = _matvec_gpu(torch, [x], [a], cols, p, corrupt=(0, 0))
+    assert st == codec.SH_ERR_CORRUPT_STREAM

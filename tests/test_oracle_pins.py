@@ -481,3 +481,39 @@ def test_corrupt_streams_are_detected():
             bad[pos // 8] ^= np.uint8(1 << (pos % 8))
             caught += O.decode(bad, x.size, raise_on_error=False)[0] == -4
     assert caught >= 0.95 * 32 * 7
+
+
+def test_matvec_pins():
+    """The fused decode's oracle: row-major rows of cols values times a vector.  A one-hot
+    vector picks a column, a vector of ones gives row sums, the product is linear in the
+    vector, sums wrap like int32, and the container's matrix is the tensor itself."""
+    rng = np.random.default_rng(61)
+    rows, cols = 9, 64
+    w = rng.integers(-128, 128, size=rows * cols).astype(np.int8)
+    m = w.reshape(rows, cols).astype(np.int64)
+    for c in (0, 5, cols - 1):
+        e = np.zeros(cols, np.int8)
+        e[c] = 1
+        assert np.array_equal(O.matvec_i8(w, cols, e), m[:, c])
+        e[c] = -3
+        assert np.array_equal(O.matvec_i8(w, cols, e), -3 * m[:, c])
+    assert np.array_equal(O.matvec_i8(w, cols, np.ones(cols, np.int8)), m.sum(axis=1))
+    a = rng.integers(-60, 60, size=cols).astype(np.int8)
+    b = rng.integers(-60, 60, size=cols).astype(np.int8)
+    assert np.array_equal(O.matvec_i8(w, cols, a + b),
+                          O.matvec_i8(w, cols, a) + O.matvec_i8(w, cols, b))
+    # y accumulates and wraps modulo 2^32
+    one = np.zeros(cols, np.int8)
+    one[0] = 1
+    w1 = np.zeros(cols, np.int8)
+    w1[0] = 1
+    assert O.matvec_i8(w1, cols, one, [2**31 - 1])[0] == -2**31
+    assert O.matvec_i8(w1, cols, one, [-7])[0] == -6
+    with pytest.raises(O.OracleError):
+        O.matvec_i8(w[:100], cols, a)
+    # through a container: the matrix is the encoded tensor
+    x = D.quantize(rng.laplace(0, 9, size=40 * cols))
+    h = O.histogram(x)
+    lo, f = O.build_table(h, 16, 7)
+    buf, _ = O.encode(x, lo, f, 7, 512, 32)
+    assert np.array_equal(O.decode_matvec(buf, x.size, cols, a), O.matvec_i8(x, cols, a))
