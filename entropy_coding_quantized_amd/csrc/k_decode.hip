@@ -126,18 +126,19 @@ struct MatvecSink {
         next = wrap[0] < wrap[1] ? wrap[0] : wrap[1];
         abyte = vec_byte + col_mine + li;
     }
-    // v: the value's int8 bits in its low byte
-    __device__ __forceinline__ void put(int, uint32_t v, uint32_t) {
+    // the value: offset o plus the range's first value (e0's top byte, int8 bits); for a
+    // valid offset the sum stays in [-128, 127]
+    __device__ __forceinline__ void put(int, uint32_t o, uint32_t e0, uint32_t) {
         typedef const __attribute__((address_space(3))) int8_t lds_i8;
         acc = mad24(xp, ap, acc);
-        xp = (int32_t)(int8_t)(uint8_t)v;
+        xp = (int32_t)o + (int32_t)(int8_t)(uint8_t)(e0 >> 24);
         ap = *(lds_i8*)(uintptr_t)abyte;
     }
-    __device__ __forceinline__ void put_if(int k, uint32_t v, uint32_t t, bool act) {
+    __device__ __forceinline__ void put_if(int k, uint32_t o, uint32_t e0, uint32_t t, bool act) {
         acc = mad24(xp, ap, acc);
         xp = 0;
         ap = 0;
-        if (act) put(k, v, t);
+        if (act) put(k, o, e0, t);
     }
     // the sums of the half wavefronts whose row ended with step t go to y
     __device__ __forceinline__ void flush(bool end0, bool end1, uint32_t li, uint32_t hw) {
@@ -385,7 +386,7 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
                 __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(o + (e[k][0] >> 24)), rout,
                                                      (int)ch[k].vout, (int)(t * 32), 0);
             else
-                sink.put(k, o + (e[k][0] >> 24), t);
+                sink.put(k, o, e[k][0], t);
         }
 #pragma unroll
         for (int k = 0; k < ILP; ++k) ch[k].pos += bcast31(incl[k]) & 0xFFFFu;
@@ -433,7 +434,7 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
             const uint32_t bits = __builtin_amdgcn_alignbit(rp[1], rp[0], start);
             const uint32_t o = __builtin_amdgcn_ubfe(bits, 0, ek[1]);
             const uint32_t sb = __builtin_amdgcn_ubfe(bits, ek[1], ek[0] - ek[1]);
-            if constexpr (!Sink::kBytes) sink.put_if(k, o + (ek[0] >> 24), t, act);
+            if constexpr (!Sink::kBytes) sink.put_if(k, o, ek[0], t, act);
             if (act) {
                 c.err |= o > ((ek[0] >> 16) & 0xFF);
                 if constexpr (Sink::kBytes)
