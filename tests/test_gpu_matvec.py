@@ -98,3 +98,19 @@ def test_matvec_reports_a_corrupt_container(torch_cuda):
     p = codec.Params(K=16, log2_L=7, chunk_symbols=4096)
     _, st = _matvec_gpu(torch, [x], [a], cols, p, corrupt=(0, 0))
     assert st == codec.SH_ERR_CORRUPT_STREAM
+
+
+def test_matvec_many_tensors_span_launches(torch_cuda):
+    """More tensors than one launch carries (48): the batch is split over launches."""
+    torch = torch_cuda
+    print("case: matvec 50 tensors", flush=True)
+    rng = np.random.default_rng(12)
+    cols = 64
+    xs = [D.quantize(rng.laplace(0, rng.choice([2.0, 8.0, 20.0]), size=int(r) * cols))
+          for r in rng.integers(1, 300, size=50)]
+    avs = [rng.integers(-128, 128, size=cols).astype(np.int8) for _ in xs]
+    p = codec.Params(K=16, log2_L=7, chunk_symbols=512)
+    ys, st = _matvec_gpu(torch, xs, avs, cols, p)
+    assert st == 0
+    for x, a, y in zip(xs, avs, ys):
+        assert np.array_equal(y, O.matvec_i8(x, cols, a))
