@@ -54,17 +54,27 @@ uint64_t slots_for(uint64_t nch) { return (nch + 1) / 2 * 2; }
 
 uint64_t align256(uint64_t v) { return (v + 255) / 256 * 256; }
 
-// encode workspace for a group of segments: slots, then per-slot meta
+// encode workspace for a group of segments: slots, then per-slot meta, then per-block
+// aggregates of the chunk kernel (a block takes kChunksPerBlock chunks, so a group has at
+// most total_slots / kChunksPerBlock + kMaxInlineSegs blocks)
 struct EncLayout {
-    uint64_t meta_at, bytes;
+    uint64_t meta_at, agg_at, bytes;
     uint32_t slot_dwords;
 };
 EncLayout enc_layout(uint64_t total_slots, const sh_params* p) {
     EncLayout l;
     l.slot_dwords = encode_slot_dwords(p->chunk_symbols, p->log2_L);
     l.meta_at = align256(total_slots * l.slot_dwords * 4);
-    l.bytes = l.meta_at + align256(8 * total_slots) + 256;
+    l.agg_at = l.meta_at + align256(8 * total_slots);
+    l.bytes = l.agg_at + align256(8 * (total_slots / kChunksPerBlock + kMaxInlineSegs)) + 256;
     return l;
+}
+
+// compaction blocks of a segment: the one-kernel placement gives an empty segment a block
+// of its own (it writes the header, the index end and the totals)
+uint32_t place_blocks(uint64_t nch, bool place) {
+    const uint32_t b = blocks_for(nch, kChunksPerBlockC);
+    return place && b == 0 ? 1 : b;
 }
 
 // groups of at most kMaxInlineSegs segments: [begin, end)
@@ -309,6 +319,8 @@ sh_status sh_encode(const sh_table* table, const sh_params* params, const int8_t
     a.nseg = 0;
     a.slots = (uint32_t*)d_ws;
     a.meta = (uint32_t*)((uint8_t*)d_ws + lay.meta_at);
+    a.agg = (uint32_t*)((uint8_t*)d_ws + lay.agg_at);
+    const bool place = nch <= kPlaceMaxChunks;
     if (n > 0) {
         SlotTables slots;
         if (derive_slots(*table, &slots) != SH_OK) return SH_ERR_INVALID_ARG;
@@ -322,7 +334,7 @@ sh_status sh_encode(const sh_table* table, const sh_params* params, const int8_t
     sd.c_bytes = out_cap;
     sd.info = d_info;
     sd.n_chunks = (uint32_t)nch;
-    return launch_encode(a, blocks_for(nch, kChunksPerBlock), blocks_for(nch, kChunksPerBlockC),
+    return launch_encode(a, blocks_for(nch, kChunksPerBlock), place_blocks(nch, place), place,
                          stream);
 }
 
@@ -388,6 +400,9 @@ sh_status sh_encode_batch(const void* d_tables, const int8_t* const* d_x, const 
         a.nseg = e - b;
         uint64_t slots = 0;
         uint32_t blocks = 0, blocks_c = 0;
+        bool place = true;
+        for (uint32_t i = b; i < e; ++i)
+            place = place && n_chunks_of(n[i], params->chunk_symbols) <= kPlaceMaxChunks;
         for (uint32_t i = b; i < e; ++i) {
             SegDesc& sd = a.many[i - b];
             const uint64_t nch = n_chunks_of(n[i], params->chunk_symbols);
@@ -402,13 +417,14 @@ sh_status sh_encode_batch(const void* d_tables, const int8_t* const* d_x, const 
             sd.n_chunks = (uint32_t)nch;
             sd.slot_base = (uint32_t)slots;
             blocks += blocks_for(nch, kChunksPerBlock);
-            blocks_c += blocks_for(nch, kChunksPerBlockC);
+            blocks_c += place_blocks(nch, place);
             slots += slots_for(nch);
         }
         const EncLayout lay = enc_layout(slots, params);
         a.slots = (uint32_t*)d_ws;
         a.meta = (uint32_t*)((uint8_t*)d_ws + lay.meta_at);
-        st = launch_encode(a, blocks, blocks_c, stream);
+        a.agg = (uint32_t*)((uint8_t*)d_ws + lay.agg_at);
+        st = launch_encode(a, blocks, blocks_c, place, stream);
         if (st != SH_OK) return st;
     }
     return SH_OK;

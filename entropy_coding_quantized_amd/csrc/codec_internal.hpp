@@ -132,6 +132,7 @@ struct CodecArgs {
     int32_t* status;
     uint32_t* slots;        // encode workspace
     uint32_t* meta;         // encode workspace: per slot {start bit, field bits}
+    uint32_t* agg;          // encode workspace: per chunk-kernel block {bytes, field bits}
     union {
         struct {
             SegDesc seg;
@@ -153,6 +154,7 @@ struct KHead {
     int32_t* status;
     uint32_t* slots;
     uint32_t* meta;
+    uint32_t* agg;
 };
 template <int N>
 struct KSegs {  // N segments with device tables
@@ -204,7 +206,12 @@ sh_status launch_decode(const CodecArgs& a, uint32_t total_blocks, void* stream)
 // this many values long
 constexpr uint32_t kMaxMatvecCols = 16384;
 sh_status launch_decode_matvec(const CodecArgs& a, uint32_t total_blocks, void* stream);
+// segments of at most this many chunks are indexed and compacted by one kernel
+// (k_encode_place: each block sums the sizes of the chunks before its own, so the work
+// grows with the square of the chunk count); longer ones take the index kernel first
+constexpr uint32_t kPlaceMaxChunks = 16384;
 sh_status launch_encode(const CodecArgs& a, uint32_t total_blocks, uint32_t total_blocks_c,
+                        bool place,
                         void* stream);
 
 // encode workspace layout

@@ -17,6 +17,7 @@ namespace shn {
 // the chunk's slot 128 dwords at a time, highest first; the chunk ends up right-aligned
 // in its slot with the lanes' final states (the decoder's initial states) in front.
 constexpr int kEncBlock = 256;
+constexpr uint32_t kChunksPerBlockE = kEncBlock / 64 * 2;  // two chunks a wavefront
 constexpr uint32_t kERing = 256;
 // LDS: eight 1 KB rings (one per half wavefront, 1 KB aligned), eight 1 KB input tiles
 // (bytes of 32 steps x 32 lanes), then the value table and the encTable bytes
@@ -45,6 +46,7 @@ __device__ __forceinline__ void ring_or(uint32_t* sm, uint32_t ring_byte, uint32
 template <class A>
 __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
     __shared__ __align__(1024) uint32_t sm[kVtBase + kVtDwords];
+    __shared__ uint32_t agg_s[2];  // the block's container bytes and field bits
     const uint32_t tid = threadIdx.x, lane = tid & 63, li = lane & 31, hw = lane >> 5;
     const uint32_t block = __builtin_amdgcn_readfirstlane(blockIdx.x);
     const SegDesc* sg = codec_seg(a, block, false);
@@ -108,6 +110,7 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
     };
     v4u p0, p1;
     if (steps > 0) load_tile((steps - 1) >> 5, p0, p1);
+    if (tid < 2) agg_s[tid] = 0;
     __syncthreads();
 
     uint32_t X = L;
@@ -241,7 +244,11 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
     if (chunk < n_chunks && li == 0) {
         a.h.meta[2 * (sg->slot_base + chunk)] = Pi;
         a.h.meta[2 * (sg->slot_base + chunk) + 1] = pay;
+        atomicAdd(&agg_s[0], 4 * ((a.h.slot_dwords * 32 - Pi + 31) >> 5));
+        atomicAdd(&agg_s[1], pay);
     }
+    __syncthreads();
+    if (tid < 2) a.h.agg[2 * block + tid] = agg_s[tid];
     bad &= 0x8000u;
     report(a.h.status, bad && sg->tab && sg->tab[kDTStatus] != 0 ? SH_ERR_UNSUPPORTED
                                                               : SH_ERR_SYMBOL_NOT_IN_TABLE,
@@ -330,13 +337,97 @@ __global__ __launch_bounds__(256) void k_encode_compact(const A a) {
     }
 }
 
+// ------------------------------------------------------------------------------------
+// encode, kernels 2 and 3 in one (segments of at most kPlaceMaxChunks chunks): every block
+// finds the offset of its first chunk from the chunk kernel's per-block aggregates (the
+// container bytes of 8 chunks each) and the sizes of at most 4 chunks after the last whole
+// aggregate, writes its chunks' index entries and moves them into place; the segment's
+// first block writes the header and its last block the index end and the totals.
+// ------------------------------------------------------------------------------------
+template <class A>
+__global__ __launch_bounds__(256) void k_encode_place(const A a) {
+    __shared__ uint32_t red_b[4];
+    __shared__ unsigned long long red_f[4];
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const uint32_t block = __builtin_amdgcn_readfirstlane(blockIdx.x);
+    const SegDesc* sg = codec_seg(a, block, true);
+    const uint32_t n_chunks = sg->n_chunks;
+    const uint32_t c0 = (block - sg->first_block_c) * 4;   // this block's first chunk
+    const uint32_t index_at = header_bytes_dev(a.h.K);
+    const uint32_t payload_at = index_at + 4 * (n_chunks + 1);
+    const uint32_t* meta = a.h.meta + 2ull * sg->slot_base;
+    const uint32_t* agg = a.h.agg + 2ull * sg->first_block;  // the segment's chunk-kernel blocks
+    uint32_t* index = reinterpret_cast<uint32_t*>(sg->c + index_at);
+    const bool last = c0 + 4 >= n_chunks;
+    auto chunk_bytes = [&](uint32_t ch) {
+        return 4 * ((a.h.slot_dwords * 32 - meta[2 * ch] + 31) >> 5);
+    };
+
+    // bytes of the chunk-kernel blocks before c0 (c0 / 8 of them); in the last block also
+    // the field bits of all of them
+    const uint32_t nb_before = c0 / kChunksPerBlockE;
+    const uint32_t nb_all = (n_chunks + kChunksPerBlockE - 1) / kChunksPerBlockE;
+    uint32_t bytes = 0;
+    uint64_t fbits = 0;
+    for (uint32_t e = tid; e < (last ? nb_all : nb_before); e += 256) {
+        if (e < nb_before) bytes += agg[2 * e];
+        fbits += agg[2 * e + 1];
+    }
+    for (int sh = 32; sh >= 1; sh >>= 1) {
+        bytes += __shfl_xor(bytes, sh, 64);
+        fbits += __shfl_xor(fbits, sh, 64);
+    }
+    if (lane == 0) {
+        red_b[wv] = bytes;
+        red_f[wv] = fbits;
+    }
+    __syncthreads();
+    uint32_t off = red_b[0] + red_b[1] + red_b[2] + red_b[3];
+    // then the chunks from the last whole aggregate up to this wavefront's chunk
+    const uint32_t c = c0 + wv;
+    for (uint32_t j = nb_before * kChunksPerBlockE; j < c && j < n_chunks; ++j) off += chunk_bytes(j);
+
+    if (c0 == 0)
+        for (uint32_t i = tid; i < index_at / 4; i += 256)
+            reinterpret_cast<uint32_t*>(sg->c)[i] =
+                header_dword(sg->tab ? sg->tab + kDTHdr : inline_hdr(a), i, sg->n, n_chunks);
+    if (c < n_chunks) {
+        if (lane == 0) index[c] = off;
+        const uint32_t slot = sg->slot_base + c;
+        const uint32_t start = a.h.meta[2 * slot];
+        const uint32_t ndw = (a.h.slot_dwords * 32 - start + 31) >> 5;
+        const uint32_t* src = a.h.slots + (uint64_t)slot * a.h.slot_dwords;
+        uint32_t* d = reinterpret_cast<uint32_t*>(sg->c + payload_at + off);
+        const uint32_t s0 = start >> 5;
+        for (uint32_t j = lane; j < ndw; j += 64) {
+            const uint32_t lo = src[s0 + j];
+            const uint32_t hi = s0 + j + 1 < a.h.slot_dwords ? src[s0 + j + 1] : 0;
+            d[j] = __builtin_amdgcn_alignbit(hi, lo, start);
+        }
+    }
+    // the segment's end: the wavefront holding its last chunk (wavefront 0 of the only
+    // block of an empty segment)
+    if (last && lane == 0 && c == (n_chunks > 0 ? n_chunks - 1 : 0)) {
+        const uint32_t total = n_chunks > 0 ? off + chunk_bytes(c) : 0;
+        index[n_chunks] = total;
+        if (sg->info) {
+            sg->info->container_bytes = (uint64_t)payload_at + total;
+            sg->info->payload_bits = red_f[0] + red_f[1] + red_f[2] + red_f[3];
+        }
+    }
+}
+
 sh_status launch_encode(const CodecArgs& a, uint32_t total_blocks, uint32_t total_blocks_c,
-                        void* stream) {
+                        bool place, void* stream) {
     hipStream_t s = (hipStream_t)stream;
     with_kernel_args(a, [&](const auto& k) {
         using K = std::decay_t<decltype(k)>;
         if (total_blocks > 0)
             hipLaunchKernelGGL(k_encode_chunks<K>, dim3(total_blocks), dim3(kEncBlock), 0, s, k);
+        if (place) {
+            hipLaunchKernelGGL(k_encode_place<K>, dim3(total_blocks_c), dim3(256), 0, s, k);
+            return;
+        }
         hipLaunchKernelGGL(k_encode_index<K>, dim3(k.h.nseg), dim3(kScanBlock), 0, s, k);
         if (total_blocks_c > 0)
             hipLaunchKernelGGL(k_encode_compact<K>, dim3(total_blocks_c), dim3(256), 0, s, k);
