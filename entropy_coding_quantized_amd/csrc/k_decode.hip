@@ -11,7 +11,9 @@
 // sit back to back in the bit stream; a 32-lane DPP prefix sum of the field lengths gives
 // each lane its bit position.  Compressed words are staged through a per-chunk LDS ring
 // fed by 128-bit loads; the decode table (<= 2 KB) lives in LDS.  No MFMA: there is no
-// dense contraction.
+// dense contraction.  The same kernel either stores the decoded bytes or hands them to a
+// consumer in registers (an int8 matrix-vector product, MatvecSink), so that the decoded
+// tensor never reaches HBM.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -86,6 +88,7 @@ __device__ __forceinline__ int32_t mad24(int32_t a, int32_t b, int32_t c) {
     return d;
 }
 
+template <bool kAligned>
 struct MatvecSink {
     static constexpr bool kBytes = false;
     static constexpr uint32_t kLdsDwords = kMaxMatvecCols / 4;
@@ -98,6 +101,9 @@ struct MatvecSink {
     // per half wavefront (wave-uniform copies of both): the step that ends the current row
     // (~0 once past the chunk), the row, and the chunk's steps; next = the earlier end
     uint32_t wrap[2], row[2], steps[2], next;
+    // kAligned: rows start with every chunk (C a multiple of cols), so both halves end their
+    // rows at the same steps, every cols / 32 steps from the chunk start
+    uint32_t abase, row_mine;
     template <class A>
     __device__ __forceinline__ void init(const A& a, const SegDesc* sg, uint32_t group,
                                          uint32_t li, uint32_t hw, uint32_t n_chunks,
@@ -125,6 +131,9 @@ struct MatvecSink {
         }
         next = wrap[0] < wrap[1] ? wrap[0] : wrap[1];
         abyte = vec_byte + col_mine + li;
+        abase = vec_byte + li;
+        row_mine = hw ? row[1] : row[0];
+        if (kAligned) next = cols / 32 - 1;
     }
     // the value: offset o plus the range's first value (e0's top byte, int8 bits); for a
     // valid offset the sum stays in [-128, 127]
@@ -152,6 +161,21 @@ struct MatvecSink {
     }
     __device__ __forceinline__ void step_done(uint32_t t) {
         abyte += 32;
+        if constexpr (kAligned) {
+            // every lane's row ends here; a half whose chunk has ended holds 0 and adds
+            // nothing (its row index may be past the tensor)
+            if (__builtin_expect(t == next, 0)) {
+                acc = mad24(xp, ap, acc);
+                xp = 0;
+                const uint32_t tot = scan32((uint32_t)acc);
+                if ((__lane_id() & 31) == 31 && tot != 0) atomicAdd(y + row_mine, (int32_t)tot);
+                acc = 0;
+                ++row_mine;
+                abyte = abase;
+                next += cols / 32;
+            }
+            return;
+        }
         if (__builtin_expect(t == next, 0)) {  // one scalar compare a step; the rest once a row
             const bool end0 = t == wrap[0], end1 = t == wrap[1];
             const uint32_t lane = __lane_id(), li = lane & 31, hw = lane >> 5;
@@ -186,6 +210,7 @@ struct MatvecSink {
 // MI355X, two independent chains per lane ran slower than twice as many wavefronts.
 template <int ILP, class Sink, class A>
 __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
+    static_assert(Sink::kBytes || ILP == 1, "a consumer sink takes one chunk per half wavefront");
     constexpr uint32_t kChunksPerWave = 2 * ILP;
     constexpr uint32_t kChunksPerBlock = kDecBlock / 64 * kChunksPerWave;
     constexpr uint32_t kVecAt = kTabDwords + kChunksPerBlock * kRingStride;
@@ -480,9 +505,14 @@ sh_status launch_decode_matvec(const CodecArgs& a, uint32_t total_blocks, void* 
     if (a.nseg == 0) return SH_ERR_INVALID_ARG;  // device tables only
     with_kernel_args(a, [&](const auto& k) {
         using K = std::decay_t<decltype(k)>;
-        if constexpr (!std::is_same_v<K, KOne>)
-            hipLaunchKernelGGL((k_decode<1, MatvecSink, K>), dim3(total_blocks),
-                               dim3(kDecBlock), 0, (hipStream_t)stream, k);
+        if constexpr (!std::is_same_v<K, KOne>) {
+            if (a.C % a.cols == 0)
+                hipLaunchKernelGGL((k_decode<1, MatvecSink<true>, K>), dim3(total_blocks),
+                                   dim3(kDecBlock), 0, (hipStream_t)stream, k);
+            else
+                hipLaunchKernelGGL((k_decode<1, MatvecSink<false>, K>), dim3(total_blocks),
+                                   dim3(kDecBlock), 0, (hipStream_t)stream, k);
+        }
     });
     return hipGetLastError() == hipSuccess ? SH_OK : SH_ERR_HIP;
 }
