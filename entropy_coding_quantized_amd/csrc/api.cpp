@@ -109,7 +109,7 @@ sh_status hip_ok(hipError_t e) { return e == hipSuccess ? SH_OK : SH_ERR_HIP; }
 
 extern "C" {
 
-uint32_t sh_version(void) { return (1u << 16) | 1u; }
+uint32_t sh_version(void) { return (1u << 16) | 2u; }
 
 const char* sh_status_string(sh_status st) {
     switch (st) {

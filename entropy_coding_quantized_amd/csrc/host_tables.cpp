@@ -261,7 +261,7 @@ void write_header(const sh_table& t, uint64_t n, uint32_t C, uint32_t S, uint64_
     b[1] = 'H';
     b[2] = 'N';
     b[3] = '1';
-    b[4] = 1;
+    b[4] = 2;  // version 2: a lane's last field has no state bits
     b[5] = (uint8_t)t.log2_L;
     put(6, t.K, 2);
     put(8, n, 8);

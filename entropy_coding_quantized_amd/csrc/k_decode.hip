@@ -362,7 +362,10 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
         nc_max = nc_max > lo ? nc_max : lo;
         nc_max = nc_max > hi ? nc_max : hi;
     }
-    const uint32_t full = nc_min >> 5;
+    // steps where every lane of the wavefront's chunks decodes a value that is not its
+    // lane's last (every lane's last value lies at or after step nc / 32 - 1); the rest,
+    // where lanes may be done or at their last value, go through the general step below
+    const uint32_t full = (nc_min >> 5) > 0 ? (nc_min >> 5) - 1 : 0;
     const uint32_t steps = (nc_max + 31) >> 5;
     uint64_t bad_offsets = 0;  // lanes that decoded an offset outside its range
 
@@ -445,13 +448,16 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
         }
         ++t;
     }
-    for (; t < steps; ++t) {  // chunks shorter than the others: lanes past n_c take no bits
+    for (; t < steps; ++t) {  // lanes past n_c: no bits; lanes at their last value: no state bits
 #pragma unroll
         for (int k = 0; k < ILP; ++k) {
             DecChain& c = ch[k];
             const bool act = t * 32 + li < c.nc;
             v2u ek = e[k];
             if (!act) ek = v2u{0, 0};
+            // a lane's last field is its offset alone: the state bits are implied zero, so
+            // the field length becomes w (and the state-bit width need - w becomes 0)
+            if (act && (t + 1) * 32 + li >= c.nc) ek[0] = (ek[0] & 0xFFFF0000u) | (ek[1] & 31u);
             const uint32_t incl = scan32(ek[0]);
             const uint32_t start = c.pos - ek[0] + incl;
             const uint32_t rb = ((start >> 3) & (4 * kRing - 4)) | c.ring_byte;

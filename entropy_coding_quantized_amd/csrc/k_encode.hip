@@ -191,8 +191,11 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
         uint32_t flag = e_c.y;
         if constexpr (decltype(partial)::value) {
             const bool act = t * 32 + li < nc;
+            // a lane's last value, the first it encodes (from X = L): its k state bits
+            // are zero and are left out
+            const bool last = (t + 1) * 32 + li >= nc;
             field = act ? field : 0u;
-            len = act ? len : 0u;
+            len = act ? (last ? w : len) : 0u;
             flag = act ? flag : 0u;
         }
         bad |= flag;
@@ -207,8 +210,10 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
         e_c = e_n;
         u_n = u_nn;
     };
-    // steps where a lane of either half has no value (the tail of a short chunk) first
-    const uint32_t t_full = (nc_lo < nc_hi ? nc_lo : nc_hi) >> 5;
+    // steps where a lane of either half has no value (the tail of a short chunk) or has its
+    // last value first: every lane's last value lies at or after step nc / 32 - 1
+    uint32_t t_full = (nc_lo < nc_hi ? nc_lo : nc_hi) >> 5;
+    t_full = t_full > 0 ? t_full - 1 : 0;
     uint32_t t = steps;
     while (t > t_full) {
         step(--t, std::true_type{}, std::true_type{});

@@ -25,7 +25,7 @@
  *     *d_status beforehand and reads it back when convenient.
  *
  * Container (the bytes sh_encode writes and sh_decode reads), all integers little-endian:
- *   0   "SHN1", u8 version = 1, u8 log2_L, u16 K
+ *   0   "SHN1", u8 version = 2, u8 log2_L, u16 K
  *   8   u64 n              number of values
  *   16  u32 chunk_symbols  C
  *   20  u32 streams        S (interleaved tANS lanes per chunk)
@@ -41,7 +41,9 @@
  *   in lane order, then every value's field in (step, lane) order, then zero bits up to a
  *   whole number of 32-bit words.  A field is the offset o in its low w_s bits and, above
  *   it, the nb state bits the decoder appends to the slot's base to reach the next state.
- *   Every lane ends in slot 0.
+ *   Every lane ends in slot 0.  A lane's last field is the offset alone: the encoder starts
+ *   each lane in state L (slot 0), so the state bits of the last value are the low bits of
+ *   L, all zero, and the decoder implies them (a framing reduction; version 1 wrote them).
  */
 #ifndef SHANNONIC_H
 #define SHANNONIC_H

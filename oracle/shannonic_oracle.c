@@ -431,7 +431,9 @@ static int check_table(int K, int log2_L, const uint16_t* lo, const uint16_t* fr
  * base[s] goes out in w_s bits; then the k state bits that bring X into [f_s, 2 f_s);
  * then the state moves through encTable.  tANS encodes backwards, so each lane runs
  * from its last symbol to its first, starting in state L (slot 0); its final state is
- * the decoder's initial state.  The fields are then written in decoding order.
+ * the decoder's initial state.  The state bits of the first symbol it encodes (the lane's
+ * last) are the low bits of L, all zero, so they are left out and the decoder implies
+ * them: about H(P) bits less a lane.  The fields are then written in decoding order.
  * payload_bits receives the summed field lengths (initial states and padding excluded).
  */
 int orc_encode(const int8_t* x, uint64_t n, int K, int log2_L, const uint16_t* lo,
@@ -465,7 +467,7 @@ int orc_encode(const int8_t* x, uint64_t n, int K, int log2_L, const uint16_t* l
     out[1] = 'H';
     out[2] = 'N';
     out[3] = '1';
-    out[4] = 1;
+    out[4] = 2;
     out[5] = (uint8_t)log2_L;
     put_u16(out + 6, (uint64_t)K);
     put_u64(out + 8, n);
@@ -512,7 +514,9 @@ int orc_encode(const int8_t* x, uint64_t n, int K, int log2_L, const uint16_t* l
                 int k = 0;
                 while ((X >> k) >= 2 * (uint64_t)freq[s]) k++;
                 field[i] = o | ((X & (((uint64_t)1 << k) - 1)) << w);
-                flen[i] = w + k;
+                /* the lane's last value (encoded first, from X = L): its k state bits are
+                 * the low bits of L, all zero, and the decoder implies them */
+                flen[i] = t + 1 == T ? w : w + k;
                 X = L + enc_slot[cum[s] + ((X >> k) - freq[s])];
             }
             init[l] = X - L;
@@ -553,14 +557,15 @@ int orc_encode(const int8_t* x, uint64_t n, int K, int log2_L, const uint16_t* l
 /*
  * Decode a container into n values (paper section 4.2): from state X, decTable[X]
  * gives the range s and the state bit count; the field's low w_s bits are the offset o
- * and x = base[s] + o.  A stream is valid only if the header is consistent, every
- * offset lies inside its range, every lane ends in slot 0 (the encoder's start state)
- * and every chunk's bits end in its last 32-bit word with zero padding after them.
+ * and x = base[s] + o.  A lane's last field is the offset alone (its state bits are
+ * zero, implied).  A stream is valid only if the header is consistent, every offset lies
+ * inside its range, every lane ends in slot 0 (the encoder's start state) and every
+ * chunk's bits end in its last 32-bit word with zero padding after them.
  */
 int orc_decode(const uint8_t* in, uint64_t nbytes, int8_t* y, uint64_t n)
 {
     if (nbytes < 32) return ORC_ERR_CORRUPT;
-    if (in[0] != 'S' || in[1] != 'H' || in[2] != 'N' || in[3] != '1' || in[4] != 1)
+    if (in[0] != 'S' || in[1] != 'H' || in[2] != 'N' || in[3] != '1' || in[4] != 2)
         return ORC_ERR_CORRUPT;
     int R = in[5];
     int K = (int)get_le(in + 6, 2);
@@ -618,7 +623,8 @@ int orc_decode(const uint8_t* in, uint64_t nbytes, int8_t* y, uint64_t n)
             uint64_t slot = X[l] - L;
             int s = slot_range[slot];
             int w = ceil_log2_u64((uint64_t)(lo[s + 1] - lo[s]));
-            int need = w + slot_nb[slot];
+            /* a lane's last field holds the offset only: its state bits are zero */
+            int need = i + S >= nc ? w : w + slot_nb[slot];
             if (pos + (uint64_t)need > avail) {
                 st = ORC_ERR_CORRUPT;
                 break;
