@@ -1,6 +1,7 @@
 // Encode kernels of the Shannonic codec for gfx950 (CDNA4, wave64): the inverse of the
 // decode mapping ("Runtime encoding/decoding", paper section 4.2, Algorithm 2, of the
-// Shannonic talk notes), run backwards per lane, then a chunk index and a compaction pass.
+// Shannonic talk notes), run backwards per lane, then the chunk index and the compaction:
+// one kernel for tensors of up to kPlaceMaxChunks chunks, two for longer ones.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -261,7 +262,8 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
 }
 
 // ------------------------------------------------------------------------------------
-// encode, kernel 2: chunk index (exclusive scan of chunk sizes), header, totals
+// encode, kernel 2 of the long-tensor path: chunk index (exclusive scan of chunk sizes),
+// header, totals
 // ------------------------------------------------------------------------------------
 constexpr int kScanBlock = 1024;
 
@@ -317,7 +319,8 @@ __global__ __launch_bounds__(kScanBlock) void k_encode_index(const A a) {
 }
 
 // ------------------------------------------------------------------------------------
-// encode, kernel 3: move every chunk from its slot to its place in the payload
+// encode, kernel 3 of the long-tensor path: move every chunk from its slot to its place in
+// the payload
 // ------------------------------------------------------------------------------------
 template <class A>
 __global__ __launch_bounds__(256) void k_encode_compact(const A a) {
