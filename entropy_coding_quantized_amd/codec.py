@@ -148,7 +148,12 @@ class Params:
     streams: int = 32
 
     def c(self) -> sh_params:
-        return sh_params(self.K, self.log2_L, self.chunk_symbols, self.streams)
+        """The C struct (one per Params, built on first use: the calls only read it)."""
+        c = self.__dict__.get("_c")
+        if c is None:
+            c = sh_params(self.K, self.log2_L, self.chunk_symbols, self.streams)
+            object.__setattr__(self, "_c", c)
+        return c
 
 
 def _ptr(t) -> int:
