@@ -298,13 +298,19 @@ def sh_tables_from_device(d_tables, count: int, stream=None):
     return [out[i] for i in range(count)], [int(st[i]) for i in range(count)]
 
 
-def sh_tables_from_bytes(tables, count: int, as_array: bool = False):
+def sh_tables_from_bytes(tables, count: int, as_array: bool = False, out=None, status=None):
     """sh_tables_from_device for device-table images already in host memory.  With
-    as_array, the tables come back as one ctypes array (for sh_stats_batch)."""
-    out = (sh_table * max(count, 1))()
-    st = (C.c_int32 * max(count, 1))()
-    _check(lib().sh_tables_from_bytes(_ptr(tables), count, out, st), "sh_tables_from_bytes")
-    return (out if as_array else [out[i] for i in range(count)]), [int(st[i]) for i in range(count)]
+    as_array, the tables come back as one ctypes array (for sh_stats_batch); out and status
+    (ctypes arrays of at least count sh_table and int32) are filled instead of new ones."""
+    if out is None:
+        out = (sh_table * max(count, 1))()
+    if status is None:
+        status = (C.c_int32 * max(count, 1))()
+    if len(out) < count or len(status) < count:
+        raise ValueError("sh_tables_from_bytes: out or status holds fewer than count entries")
+    _check(lib().sh_tables_from_bytes(_ptr(tables), count, out, status), "sh_tables_from_bytes")
+    return ((out if as_array else [out[i] for i in range(count)]),
+            [int(status[i]) for i in range(count)])
 
 
 def table_from_device(d_table, stream=None) -> sh_table:
