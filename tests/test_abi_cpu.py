@@ -223,3 +223,19 @@ def test_tables_from_bytes_rejects_garbage():
     assert st == [codec.SH_ERR_CORRUPT_STREAM, codec.SH_ERR_CORRUPT_STREAM,
                   codec.SH_ERR_UNSUPPORTED]
     assert codec.raw_status("sh_tables_from_bytes", None, 1, None, None) == codec.SH_ERR_INVALID_ARG
+
+
+def test_binding_reuses_and_checks_caller_arrays():
+    """Params keeps one C struct; the table parse and the statistics refuse arrays shorter
+    than the count before calling the library."""
+    p = codec.Params(K=8, log2_L=6)
+    assert p.c() is p.c() and p.c().K == 8 and p.c().log2_L == 6
+    assert p == codec.Params(K=8, log2_L=6)
+    with pytest.raises(ValueError):
+        codec.sh_tables_from_bytes(np.zeros(4 * codec.sh_device_table_bytes(), np.uint8), 2,
+                                   out=(codec.sh_table * 1)())
+    t = codec.sh_table_from_histogram(O.histogram(D.tiny()), codec.Params())
+    with pytest.raises(ValueError):
+        codec.sh_stats_batch([t, t], out=(codec.sh_stats_t * 1)())
+    rec = codec.sh_stats_batch([t], out=(codec.sh_stats_t * 1)())
+    assert codec.stats_dicts(rec, 1)[0] == codec.sh_stats(t)
