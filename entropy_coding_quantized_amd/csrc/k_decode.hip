@@ -214,7 +214,9 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
     constexpr uint32_t kChunksPerWave = 2 * ILP;
     constexpr uint32_t kChunksPerBlock = kDecBlock / 64 * kChunksPerWave;
     constexpr uint32_t kVecAt = kTabDwords + kChunksPerBlock * kRingStride;
-    __shared__ __align__(16) uint32_t sm[kVecAt + Sink::kLdsDwords];
+    // the rings' wrapped addresses are formed with an and-or, which needs every ring on a
+    // kRingStride boundary of the LDS address space: sm is the kernel's only LDS object
+    __shared__ __align__(4 * kRingStride) uint32_t sm[kVecAt + Sink::kLdsDwords];
     const uint32_t tid = threadIdx.x, lane = tid & 63, li = lane & 31, hw = lane >> 5;
     const uint32_t block = __builtin_amdgcn_readfirstlane(blockIdx.x);
     const SegDesc* sg = codec_seg(a, block, false);
@@ -320,6 +322,9 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
             rin, (int)(index_at + 4 * n_chunks), 0, 0);
         bool bad = sg->tab && (sg->tab[kDTStatus] != 0 ||
                                (n > 0 && (sg->tab[kDTN] | sg->tab[kDTN + 1]) == 0));
+        // a device table built for other parameters than the launch's
+        report(a.h.status, SH_ERR_INVALID_ARG,
+               sg->tab && (sg->tab[kDTK] != a.h.K || sg->tab[kDTLog2L] != a.h.R));
 #pragma unroll
         for (int r = 0; r < kHdrPerLane; ++r) {
             const uint32_t i = lane + 64 * r;

@@ -82,8 +82,11 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
     const rsrc_t rslot = make_rsrc(a.h.slots + (uint64_t)slot0 * a.h.slot_dwords, 8u * a.h.slot_dwords);
     const uint32_t in_base = hw * a.h.C;          // byte offset of this chunk in rin
     const uint32_t slot_base = hw * a.h.slot_dwords * 4;
+    // a device table built for other parameters than the launch's is refused: its chunks are
+    // coded as empty (the workspace stays consistent for the placement) and the call fails
+    const bool mismatch = sg->tab && (sg->tab[kDTK] != a.h.K || sg->tab[kDTLog2L] != a.h.R);
     uint32_t nc = 0;
-    if (chunk < n_chunks) {
+    if (chunk < n_chunks && !mismatch) {
         const uint64_t first = (uint64_t)chunk * a.h.C;
         nc = (uint32_t)((n - first) < a.h.C ? (n - first) : a.h.C);
     }
@@ -256,6 +259,7 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
     __syncthreads();
     if (tid < 2) a.h.agg[2 * block + tid] = agg_s[tid];
     bad &= 0x8000u;
+    if (mismatch) report(a.h.status, SH_ERR_INVALID_ARG, true);
     report(a.h.status, bad && sg->tab && sg->tab[kDTStatus] != 0 ? SH_ERR_UNSUPPORTED
                                                               : SH_ERR_SYMBOL_NOT_IN_TABLE,
            bad != 0);

@@ -133,8 +133,10 @@ sh_status sh_histogram(const int8_t* d_x, uint64_t n, uint64_t* d_hist, void* st
 sh_status sh_table_from_histogram(const uint64_t* hist, const sh_params* params, sh_table* out);
 
 /*
- * The table of one tensor.  x is device memory when x_on_device != 0: the histogram and the
- * whole table build run on the GPU (sh_build_tables_batch with one tensor; the table is
+ * The table of one tensor: the offline step of "Preprocessing: range selection by dynamic
+ * programming" (paper section 4.1) -- the histogram h[u], the exactly-K-range DP split, the
+ * allocation of the L states, the spread and every derived entry.  x is device memory when
+ * x_on_device != 0: the histogram and the whole table build run on the GPU (sh_build_tables_batch with one tensor; the table is
  * identical to sh_table_from_histogram's), x must be 16-byte aligned, params must be ones
  * the GPU path supports, d_ws must hold sh_build_tables_workspace() bytes (256-byte
  * aligned) and the call waits for the stream.  Otherwise x is host memory, counted and
@@ -164,7 +166,10 @@ sh_status sh_encode(const sh_table* table, const sh_params* params, const int8_t
                     sh_encode_info* d_info, int32_t* d_status, void* stream);
 
 /*
- * Decode the container at d_in (device) into n int8 values (d_y, device).  in_nbytes is
+ * Decode the container at d_in (device) into n int8 values (d_y, device): the decoder of
+ * "Runtime encoding/decoding" (paper section 4.2) -- from the state X, decTable[X] gives the
+ * range s and its state-bit count, the offset o is read in w_s raw bits, the value is
+ * base[s] + o, and the state bits lead to the next state.  in_nbytes is
  * the number of readable bytes at d_in: at least the container's size (its chunk index
  * marks its end), so the output buffer of sh_encode can be passed with its capacity and
  * no host round trip.  The container must have been written with this table and these
@@ -195,6 +200,7 @@ sh_status sh_decode(const sh_table* table, const sh_params* params, const uint8_
 uint64_t sh_device_table_bytes(void);
 
 /*
+ * The tables of "Preprocessing" (paper section 4.1) moved between host and device.
  * Upload a host table for params (K and log2_L must match) to d_table.  Waits for the
  * copy.  An empty table (n = 0) is accepted: it encodes and decodes only empty tensors.
  */
@@ -236,13 +242,15 @@ sh_status sh_build_tables_batch(const int8_t* const* d_x, const uint64_t* n, uin
                                 uint64_t ws_bytes, void* stream);
 
 /*
- * sh_encode for nseg tensors with device tables: tensor i (d_x[i], n[i] values) is
+ * The encoder of "Runtime encoding/decoding" (paper section 4.2, Algorithm 2) for nseg
+ * tensors with device tables (sh_encode, batched): tensor i (d_x[i], n[i] values) is
  * encoded with table i into d_out[i] (out_cap[i] >= sh_encode_bound(n[i]) bytes, 4-byte
  * aligned), and its sh_encode_info goes to d_info[i] (d_info may be NULL).  d_ws: device
  * workspace, 256-byte aligned, of sh_encode_batch_workspace(n, nseg, params) bytes, reused
  * by every launch of the batch.  Errors of any tensor go to the one *d_status: a value
- * outside its table (SH_ERR_SYMBOL_NOT_IN_TABLE) or a table whose build failed
- * (SH_ERR_UNSUPPORTED).  Asynchronous on stream.
+ * outside its table (SH_ERR_SYMBOL_NOT_IN_TABLE), a table whose build failed
+ * (SH_ERR_UNSUPPORTED), or a device table built for another K or log2_L than params
+ * (SH_ERR_INVALID_ARG; that tensor's chunks are then coded empty).  Asynchronous on stream.
  */
 uint64_t sh_encode_batch_workspace(const uint64_t* n, uint32_t nseg, const sh_params* params);
 sh_status sh_encode_batch(const void* d_tables, const int8_t* const* d_x, const uint64_t* n,
@@ -251,9 +259,11 @@ sh_status sh_encode_batch(const void* d_tables, const int8_t* const* d_x, const 
                           sh_encode_info* d_info, int32_t* d_status, void* stream);
 
 /*
- * sh_decode for nseg containers with device tables: container i (d_in[i], in_nbytes[i]
+ * The decoder of "Runtime encoding/decoding" (paper section 4.2) for nseg containers with
+ * device tables (sh_decode, batched): container i (d_in[i], in_nbytes[i]
  * readable bytes) decodes into d_y[i] (n[i] values) with table i.  Every check of
  * sh_decode applies to every container; the first error of any goes to *d_status.
+ * A device table built for another K or log2_L than params sets SH_ERR_INVALID_ARG.
  * A table that failed to build, or was built from no values, decodes no values.
  * Asynchronous on stream.
  */
@@ -287,8 +297,10 @@ sh_status sh_decode_matvec_batch(const void* d_tables, const uint8_t* const* d_i
                                  void* stream);
 
 /*
- * Streaming decode, for tensors parked compressed in host memory (the model-scale case:
- * a model's tensors streamed from host memory into HBM).  Container i (h_in[i], host,
+ * Streaming decode (the decoder of "Runtime encoding/decoding", paper section 4.2), for
+ * tensors parked compressed in host memory: the data movement between memory tiers that
+ * "Problem: data-movement bottleneck in ML workloads" (paper sections 1 and 2) names, here
+ * a model's tensors streamed from host memory into HBM.  Container i (h_in[i], host,
  * in_nbytes[i] bytes, pinned for the copies to be asynchronous) is decoded with device
  * table i into d_y[i] (n[i] values).  Containers are copied to the device on copy_stream
  * into d_staging (256-byte aligned, staging_bytes), split into depth slots: groups of
@@ -318,7 +330,8 @@ sh_status sh_stats(const sh_table* table, uint64_t n, uint64_t payload_bits,
                    uint64_t container_bytes, sh_stats_t* out);
 
 /*
- * sh_stats for nseg tables in one call (a tensor with several tables, e.g. one per KV head).
+ * sh_stats (Theorem 1, paper section 4; %diff of paper section 5) for nseg tables in one
+ * call (a tensor with several tables, e.g. one per KV head).
  * tables: host array of nseg sh_table.  n, payload_bits, container_bytes: host arrays of
  * nseg values, or NULL for zeros.  out: host array of nseg sh_stats_t.  Returns the status
  * of the first table (in index order) that fails; every other entry is still filled.

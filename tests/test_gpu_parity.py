@@ -244,3 +244,40 @@ def test_model_tensors(torch_cuda, idx):
     _sampled_chunk_parity(torch, x, t, lo, f, cont, p, samples=32, seed=idx)
     if name == "layers.0.q_proj":
         assert bits == 0
+
+
+def _kv_head(a, h):
+    return D.kv_cache()[a, h].reshape(-1)
+
+
+@pytest.mark.parametrize("name", ["weight", "kv_k_head0", "kv_v_head5", "activations"])
+def test_stats_on_gpu_tables_and_totals_match_oracle(torch_cuda, name):
+    """a8: the library's Theorem-1 terms and measured rates, computed from the table built on
+    the GPU and the GPU encoder's totals, equal the oracle's on its own container, field by
+    field ("Theoretical basis: Theorem 1", paper section 4; %diff, paper section 5)."""
+    torch = torch_cuda
+    if name == "weight":
+        x, cfg = D.weight().reshape(-1), D.CONFIGS["weight"]
+    elif name == "activations":
+        x, cfg = D.activations().reshape(-1), D.CONFIGS["activations"]
+    else:
+        x = _kv_head(0, 0) if name == "kv_k_head0" else _kv_head(1, 5)
+        cfg = D.CONFIGS["kv_cache"]
+    print(f"case: a8 stats {name} n={x.size}", flush=True)
+    p = codec.Params(K=cfg["K"], log2_L=cfg["log2_L"], chunk_symbols=cfg["chunk"])
+    xd = torch.from_numpy(x).cuda()
+    ws = torch.empty(codec.sh_build_tables_workspace(), dtype=torch.uint8, device="cuda")
+    t = codec.sh_build_tables(xd, x.size, True, p, ws, ws.numel())
+    out, info, status = codec.encode_tensor(xd, t, p)
+    torch.cuda.synchronize()
+    cont, bits = codec.finish_encode(out, info, status)
+    got = codec.sh_stats(t, x.size, bits, cont.numel())
+
+    h = O.histogram(x)
+    lo, f = O.build_table(h, p.K, p.log2_L)
+    ref_buf, ref_bits = O.encode(x, lo, f, p.log2_L, p.chunk_symbols, 32)
+    ref = O.stats(h, lo, f, p.log2_L, ref_bits, ref_buf.size, x.size)
+    assert set(ref) <= set(got)
+    for k, v in ref.items():
+        assert abs(got[k] - v) <= 1e-12 * max(1.0, abs(v)), (k, got[k], v)
+    assert got["H"] > 0 and got["pct_payload_over_H"] < 1.0
