@@ -367,7 +367,7 @@ sh_status sh_decode(const sh_table* table, const sh_params* params, const uint8_
     sd.n = n;
     sd.c_bytes = in_nbytes;
     sd.n_chunks = (uint32_t)nch;
-    return launch_decode(a, blocks_for(nch, kChunksPerBlock), stream);
+    return launch_decode(a, blocks_for(nch, kDecodeChunksPerBlock), stream);
 }
 
 uint64_t sh_encode_batch_workspace(const uint64_t* n, uint32_t nseg, const sh_params* params) {
@@ -462,7 +462,7 @@ sh_status sh_decode_batch(const void* d_tables, const uint8_t* const* d_in,
             sd.tab = (const uint32_t*)((const uint8_t*)d_tables + (uint64_t)i * kDTBytes);
             sd.first_block = blocks;
             sd.n_chunks = (uint32_t)nch;
-            blocks += blocks_for(nch, kChunksPerBlock);
+            blocks += blocks_for(nch, kDecodeChunksPerBlock);
         }
         st = launch_decode(a, blocks, stream);
         if (st != SH_OK) return st;

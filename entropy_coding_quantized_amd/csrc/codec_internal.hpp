@@ -201,6 +201,10 @@ constexpr uint32_t kArgBytes = 257 * 256;
 
 sh_status launch_histogram(const HistArgs& h, uint32_t nseg_zero, void* stream);
 sh_status launch_build_tables(const BuildArgs& b, void* stream);
+// the decode behind sh_decode and sh_decode_batch (k_decode_rows.hip): one chunk per
+// 16-lane row, kDecodeChunksPerBlock chunks a block, decode_lds_bytes(L) of LDS a block
+constexpr uint32_t kDecodeChunksPerBlock = 16;
+uint32_t decode_lds_bytes(uint32_t L);
 sh_status launch_decode(const CodecArgs& a, uint32_t total_blocks, void* stream);
 // decode into a matrix-vector product: the vector is staged in LDS, so rows are at most
 // this many values long

@@ -1,0 +1,389 @@
+// Decode kernel of the Shannonic codec for gfx950 (CDNA4, wave64): the decoder behind
+// sh_decode and sh_decode_batch.
+//
+// Method: "Shannonic: Efficient Entropy-Optimal Compression for ML Workloads" (MLSys 2026),
+// talk notes, "Runtime encoding/decoding" (paper section 4.2): from the state X the decode
+// table gives the range s and the count of state bits; the offset o is read as w_s raw
+// bits, the value is base[s] + o, and the state bits lead to the next state.  Table
+// lookups, shifts, masks and adds only.  The container layout (chunks of C values, 32
+// interleaved tANS streams per chunk, fields in (step, stream) order) and the GPU mapping
+// below are this library's own design; the pages give no GPU design.
+//
+// Mapping: one chunk per 16-lane DPP row, so a wavefront decodes four chunks side by side.
+// Lane j of a row runs the two streams 2j and 2j+1, whose fields are adjacent in every
+// step: one 16-lane prefix sum (four DPP row shifts) of the pair's field lengths gives the
+// pair's bit position, and one two-dword LDS read brings both fields.  Compressed words
+// reach a per-chunk LDS ring through 128-bit loads; the decode table is staged in LDS as
+// 8-byte entries (measured on MI355X: a random 8-byte LDS read costs 7 clocks per
+// wavefront and CU at full occupancy, a 16-byte one 12, a 12-byte one 20).  No MFMA: there
+// is no dense contraction.
+#include "device_common.hpp"
+
+namespace shn {
+
+namespace {
+
+constexpr int kRowsBlock = 256;                    // 4 wavefronts, 16 rows = 16 chunks
+constexpr uint32_t kRowsPerBlock = kRowsBlock / 16;
+constexpr uint32_t kRRing = 256;                   // compressed dwords resident per chunk
+// a ring is followed by a copy of its dword 0 (a two-dword read never wraps) and padding
+// that keeps the next ring 16-byte aligned for the 128-bit LDS writes
+constexpr uint32_t kRRingStride = kRRing + 4;
+constexpr uint32_t kRFill = 128;                   // dwords per refill: 16 lanes x 32 bytes
+// Decoded bytes of four steps of a chunk (128 bytes, one cache line) are gathered in an LDS
+// tile and stored together: measured on MI355X, the 32-byte stores of single steps held
+// the decode near 1.7 TB/s of output however short the rest of the step was.
+constexpr uint32_t kTileSteps = 4;
+constexpr uint32_t kTileDwords = kTileSteps * 32 / 4;
+
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef const __attribute__((address_space(3))) v2u lds_v2u;
+
+// 16 bytes of the chunk starting at dword d (dwords at or past cdw read as 0); the rare
+// lanes at the chunk's end fetch their dwords one by one.
+__device__ __forceinline__ v4u load4(rsrc_t r, uint32_t chunk_byte, uint32_t d, uint32_t cdw) {
+    const bool whole = d + 4 <= cdw;
+    const v4u full = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 r, whole ? (int)(chunk_byte + 4 * d) : 0, 0, 0));
+    v4u part = {0, 0, 0, 0};
+    if (!whole && d < cdw) {
+        for (uint32_t k = 0; k < 4; ++k)
+            if (d + k < cdw)
+                part[k] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(chunk_byte + 4 * (d + k)), 0, 0);
+    }
+    return whole ? full : part;
+}
+
+// Inclusive prefix sum within each 16-lane row (DPP row shifts; lanes shifted in from
+// outside the row read 0).
+__device__ __forceinline__ uint32_t scan16(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr:8
+    return v;
+}
+
+// The ring's dword index of a bit position, (pos >> 5) mod 256, as one v_bfe_u32 (the
+// compiler would split the extract and the scaling that follows it into three operations).
+__device__ __forceinline__ uint32_t ring_dword(uint32_t pos) {
+    uint32_t d;
+    asm("v_bfe_u32 %0, %1, 5, 8" : "=v"(d) : "v"(pos));
+    return d;
+}
+
+// Value of lane 15 of this lane's row (DPP row_newbcast:15).
+__device__ __forceinline__ uint32_t row_last(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x15F, 0xF, 0xF, true);
+}
+
+// The decode entry of a state, 8 bytes in LDS:
+//   A = need | base << 16 | maxo << 24: need = w_s + nb, the field's length (used as a
+//       bit-field width as it is: only bits 0..4 count); base = the range's first value as
+//       int8 bits; maxo = |range| - 1, the largest valid offset
+//   B = w_s | next << 16: next = LDS byte address of the entry reached with zero state bits
+// A state is held as the LDS byte address of its entry.
+struct Ent {
+    uint32_t A, B;
+};
+__device__ __forceinline__ Ent read_ent(uint32_t addr) {
+    const v2u v = *(lds_v2u*)(uintptr_t)addr;
+    return Ent{v[0], v[1]};
+}
+__device__ __forceinline__ uint32_t need_of(const Ent& e) { return e.A & 0xFFu; }
+__device__ __forceinline__ uint32_t base_of(const Ent& e) { return (e.A >> 16) & 0xFFu; }
+__device__ __forceinline__ uint32_t maxo_of(const Ent& e) { return e.A >> 24; }
+__device__ __forceinline__ uint32_t next_of(const Ent& e) { return e.B >> 16; }
+
+// One chunk row's decoder state (every lane of the row holds the same values, except
+// the two states).
+struct Row {
+    uint32_t nc, cdw, cbyte, ring_byte, pos, res_hi, refill_at, vout;
+    uint32_t tile;     // LDS byte address of this lane's two bytes in step 0 of the tile
+    uint32_t sa, sb;   // states of streams 2j and 2j + 1
+    v4u pf0, pf1;      // the next refill, in flight
+};
+
+template <class A>
+__global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
+    extern __shared__ __align__(16) uint32_t dsm[];
+    const uint32_t tid = threadIdx.x, lane = tid & 63, j = lane & 15, row = lane >> 4;
+    const uint32_t block = __builtin_amdgcn_readfirstlane(blockIdx.x);
+    const SegDesc* sg = codec_seg(a, block, false);
+    const uint32_t bseg = block - sg->first_block;
+    const uint32_t wid = __builtin_amdgcn_readfirstlane(bseg * (kRowsBlock / 64) + (tid >> 6));
+    const uint32_t wv = wid & (kRowsBlock / 64 - 1);
+    const uint32_t L = a.h.L, R = a.h.R;
+    const uint32_t tab_byte = lds_offset(dsm);
+    const uint32_t rings = 2 * L;                   // dwords: the table takes L entries of 2
+    const uint32_t* dec = sg->tab ? sg->tab + kDTDec : inline_tab(a);
+    const uint32_t* hdr = sg->tab ? sg->tab + kDTHdr : inline_hdr(a);
+    const uint32_t n_chunks = sg->n_chunks;
+    const uint64_t n = sg->n;
+    const uint32_t index_at = header_bytes_dev(a.h.K);
+    const uint32_t payload_at = index_at + 4 * (n_chunks + 1);
+    const uint64_t in_nbytes = sg->c_bytes;
+    const rsrc_t rin = make_rsrc(sg->c, (uint32_t)in_nbytes);
+
+    // loads that need nothing else go out first: the row's pair of index entries and this
+    // thread's table slot
+    const uint32_t group = 4 * wid;                 // the wavefront's first chunk
+    const uint32_t chunk = group + row;
+    const v2u idx = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(
+                                                rin, (int)(index_at + 4 * (chunk < n_chunks ? chunk : 0)), 0, 0));
+    const uint32_t ts = tid < L ? tid : L - 1;      // L <= 256: one slot per thread
+    const uint32_t te0 = dec[2 * ts], te1 = dec[2 * ts + 1];
+
+    const uint64_t grp_first = (uint64_t)group * a.h.C;
+    const uint64_t grp_len = grp_first < n ? n - grp_first : 0;
+    const uint64_t grp_cap = 4ull * a.h.C;
+    const rsrc_t rout = make_rsrc(sg->x + (grp_first < n ? grp_first : 0),
+                                  (uint32_t)(grp_len < grp_cap ? grp_len : grp_cap));
+
+    Row r;
+    r.ring_byte = tab_byte + 4 * (rings + (wv * 4 + row) * kRRingStride);
+    const uint32_t tile_base =
+        tab_byte + 4 * (rings + kRowsPerBlock * kRRingStride + (wv * 4 + row) * kTileDwords);
+    r.tile = tile_base + 2 * j;
+    r.vout = row * a.h.C + 2 * j;
+    r.nc = 0;
+    r.cdw = 0;
+    r.cbyte = 0;
+    uint32_t err = 0;
+    if (chunk < n_chunks) {
+        const uint32_t o0 = idx[0], o1 = idx[1];
+        const uint64_t first = (uint64_t)chunk * a.h.C;
+        const uint32_t m = (uint32_t)((n - first) < a.h.C ? (n - first) : a.h.C);
+        const bool ok = o0 <= o1 && ((o0 | o1) & 3) == 0 &&
+                        (o1 - o0) <= 4 * chunk_bound_dwords(m, R) &&
+                        (uint64_t)payload_at + o1 <= in_nbytes;
+        if (ok) {
+            r.nc = m;
+            r.cdw = (o1 - o0) >> 2;
+            r.cbyte = payload_at + o0;
+        } else {
+            err = 1;
+        }
+    }
+    // the first two refills (ring dwords [0, 256)), and the third in flight
+    const v4u f00 = load4(rin, r.cbyte, 8 * j, r.cdw), f01 = load4(rin, r.cbyte, 8 * j + 4, r.cdw);
+    const v4u f10 = load4(rin, r.cbyte, kRFill + 8 * j, r.cdw);
+    const v4u f11 = load4(rin, r.cbyte, kRFill + 8 * j + 4, r.cdw);
+    r.res_hi = 2 * kRFill;  // dwords [res_hi - kRRing, res_hi) are in the ring
+    r.pf0 = load4(rin, r.cbyte, r.res_hi + 8 * j, r.cdw);
+    r.pf1 = load4(rin, r.cbyte, r.res_hi + 8 * j + 4, r.cdw);
+    // refills are checked every other step; one is due once the next two steps could read
+    // past res_hi (a step reads at most 32 fields of 16 bits: 16 dwords)
+    r.refill_at = r.res_hi < r.cdw ? (r.res_hi - 33) * 32 : 0xFFFFFFFFu;
+
+    if (wid == 0) {
+        // header and index ends: the container must belong to this table and fit in_nbytes;
+        // a device table that failed to build, or was built from no values, decodes nothing
+        constexpr int kHdrPerLane = (kMaxHeaderDwords + 63) / 64;
+        const uint32_t hd = index_at / 4;
+        uint32_t hv[kHdrPerLane], tv[kHdrPerLane];
+#pragma unroll
+        for (int k = 0; k < kHdrPerLane; ++k) {
+            const uint32_t i = lane + 64 * k, jj = i < hd ? i : 0;
+            hv[k] = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)(4 * jj), 0, 0);
+            tv[k] = hdr[jj];
+        }
+        const uint32_t first = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)index_at, 0, 0);
+        const uint32_t last = __builtin_amdgcn_raw_buffer_load_b32(
+            rin, (int)(index_at + 4 * n_chunks), 0, 0);
+        bool bad = sg->tab && (sg->tab[kDTStatus] != 0 ||
+                               (n > 0 && (sg->tab[kDTN] | sg->tab[kDTN + 1]) == 0));
+        // a device table built for other parameters than the launch's
+        report(a.h.status, SH_ERR_INVALID_ARG,
+               sg->tab && (sg->tab[kDTK] != a.h.K || sg->tab[kDTLog2L] != a.h.R));
+#pragma unroll
+        for (int k = 0; k < kHdrPerLane; ++k) {
+            const uint32_t i = lane + 64 * k;
+            if (i < hd) bad |= hv[k] != header_dword_of(tv[k], i, n, n_chunks);
+        }
+        bad |= first != 0 || (uint64_t)payload_at + last > in_nbytes;
+        report(a.h.status, SH_ERR_CORRUPT_STREAM, bad);
+    }
+
+    // the table's entries in the LDS form (device form: e0 = need | next slot * 8 << 16,
+    // e1 = w | base << 8 | (|range| - 1) << 16)
+    if (tid < L) {
+        dsm[2 * tid] = (te0 & 0xFFu) | ((te1 & 0xFF00u) << 8) | ((te1 & 0xFF0000u) << 8);
+        dsm[2 * tid + 1] = (te1 & 0xFFu) | ((tab_byte + (te0 >> 16)) << 16);
+    }
+    {
+        uint32_t* rg = &dsm[rings + (wv * 4 + row) * kRRingStride];
+        *reinterpret_cast<v4u*>(&rg[8 * j]) = f00;
+        *reinterpret_cast<v4u*>(&rg[8 * j + 4]) = f01;
+        *reinterpret_cast<v4u*>(&rg[kRFill + 8 * j]) = f10;
+        *reinterpret_cast<v4u*>(&rg[kRFill + 8 * j + 4]) = f11;
+        if (j == 0) rg[kRRing] = f00[0];
+    }
+    __syncthreads();
+
+    // initial slots: stream s's R bits at s * R (at most 256 bits: within the first ring
+    // words, no wrap)
+    const uint32_t lanes = r.nc < 32 ? r.nc : 32;
+    auto init_state = [&](uint32_t s) {
+        if (s >= lanes) return tab_byte;
+        const uint32_t p = s * R;
+        const lds_u32* w = (const lds_u32*)(uintptr_t)(r.ring_byte + 4 * (p >> 5));
+        const uint32_t bits = __builtin_amdgcn_alignbit(w[1], w[0], p);
+        return tab_byte + ((bits & (L - 1)) << 3);
+    };
+    r.sa = init_state(2 * j);
+    r.sb = init_state(2 * j + 1);
+    r.pos = lanes * R;
+
+    // steps where every stream of the wavefront's chunks decodes a value that is not its
+    // last (every stream's last value lies at or after step nc / 32 - 1); the rest go
+    // through the general step
+    uint32_t nc_min = 0xFFFFFFFFu, nc_max = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t v = __builtin_amdgcn_readlane(r.nc, 16 * k);
+        nc_min = nc_min < v ? nc_min : v;
+        nc_max = nc_max > v ? nc_max : v;
+    }
+    const uint32_t full = (nc_min >> 5) > 0 ? (nc_min >> 5) - 1 : 0;
+    const uint32_t steps = (nc_max + 31) >> 5;
+    uint64_t bad_offsets = 0;  // lanes that decoded an offset outside its range
+
+    auto refill = [&]() {
+        if (r.pos >= r.refill_at) {
+            const uint32_t d = (r.res_hi + 8 * j) & (kRRing - 1);
+            typedef __attribute__((address_space(3))) v4u lds_w4;
+            typedef __attribute__((address_space(3))) uint32_t lds_w1;
+            *(lds_w4*)(uintptr_t)(r.ring_byte + 4 * d) = r.pf0;
+            *(lds_w4*)(uintptr_t)(r.ring_byte + 4 * (d + 4)) = r.pf1;
+            if (d == 0) *(lds_w1*)(uintptr_t)(r.ring_byte + 4 * kRRing) = r.pf0[0];
+            r.res_hi += kRFill;
+            r.refill_at = r.res_hi < r.cdw ? (r.res_hi - 33) * 32 : 0xFFFFFFFFu;
+            r.pf0 = load4(rin, r.cbyte, r.res_hi + 8 * j, r.cdw);
+            r.pf1 = load4(rin, r.cbyte, r.res_hi + 8 * j + 4, r.cdw);
+        }
+    };
+
+    // One step: the pair's two fields are adjacent, stream 2j's first.  The entries were
+    // read at the end of the previous step, so the serial path is scan -> ring read ->
+    // bit extract -> next entry read.
+    auto full_step = [&](const Ent& ea, const Ent& eb, Ent& na, Ent& nb, uint32_t t) {
+        const uint32_t tot = need_of(ea) + need_of(eb);
+        const uint32_t posm = r.pos - tot;
+        const uint32_t incl = scan16(tot);
+        const uint32_t start = posm + incl;
+        const uint32_t rb = (ring_dword(start) << 2) + r.ring_byte;
+        const lds_u32* rp = (const lds_u32*)(uintptr_t)rb;
+        const uint32_t bits = __builtin_amdgcn_alignbit(rp[1], rp[0], start);
+        // stream 2j: bits [0, need_a); stream 2j + 1: bits [need_a, need_a + need_b)
+        const uint32_t fa = __builtin_amdgcn_ubfe(bits, 0, ea.A);
+        const uint32_t fb = __builtin_amdgcn_ubfe(bits, ea.A, eb.A);
+        const uint32_t oa = __builtin_amdgcn_ubfe(fa, 0, ea.B);
+        const uint32_t ob = __builtin_amdgcn_ubfe(fb, 0, eb.B);
+        r.sa = ((fa >> (ea.B & 31)) << 3) + next_of(ea);
+        r.sb = ((fb >> (eb.B & 31)) << 3) + next_of(eb);
+        na = read_ent(r.sa);
+        nb = read_ent(r.sb);
+        bad_offsets |= __builtin_amdgcn_ballot_w64(oa > maxo_of(ea));
+        bad_offsets |= __builtin_amdgcn_ballot_w64(ob > maxo_of(eb));
+        const uint32_t xa = oa + base_of(ea), xb = ob + base_of(eb);
+        typedef __attribute__((address_space(3))) uint16_t lds_w2;
+        *(lds_w2*)(uintptr_t)(r.tile + 32 * (t & (kTileSteps - 1))) = (uint16_t)((xa & 0xFF) | (xb << 8));
+        r.pos += row_last(incl);
+    };
+    // the tile of steps [t0, t0 + 4) to the output: lane j stores bytes [8j, 8j + 8)
+    // (LDS operations of a wavefront complete in order, so the row's writes are visible)
+    auto flush_tile = [&](uint32_t t0) {
+        const v2u w = *(lds_v2u*)(uintptr_t)(tile_base + 8 * j);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, w), rout,
+                                              (int)(row * a.h.C + 8 * j), (int)(t0 * 32), 0);
+    };
+
+    Ent ea = read_ent(r.sa), eb = read_ent(r.sb), ea2, eb2;
+    uint32_t t = 0;
+    // the waves on a SIMD take turns at the highest priority (take_turn)
+    const uint32_t slot_id = wave_slot();
+    const uint32_t full4 = full & ~(kTileSteps - 1);
+    while (t < full4) {
+        take_turn(t / kPrioSteps, slot_id);
+        const uint32_t stop = full4 - t < kPrioSteps ? full4 : t + kPrioSteps;
+        for (; t < stop; t += kTileSteps) {  // the entries alternate registers step by step
+            full_step(ea, eb, ea2, eb2, t);
+            full_step(ea2, eb2, ea, eb, t + 1);
+            refill();
+            full_step(ea, eb, ea2, eb2, t + 2);
+            full_step(ea2, eb2, ea, eb, t + 3);
+            refill();
+            flush_tile(t);
+        }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    // the general step: a stream past its chunk's end has no field, and a stream at its
+    // last value has the offset alone (its state bits are zero and implied)
+    for (; t < steps; ++t) {
+        const uint32_t s0 = t * 32 + 2 * j, s1 = s0 + 1;
+        const bool act_a = s0 < r.nc, act_b = s1 < r.nc;
+        const bool last_a = act_a && s0 + 32 >= r.nc, last_b = act_b && s1 + 32 >= r.nc;
+        const uint32_t need_a = act_a ? (last_a ? (ea.B & 31) : need_of(ea)) : 0;
+        const uint32_t need_b = act_b ? (last_b ? (eb.B & 31) : need_of(eb)) : 0;
+        const uint32_t tot = need_a + need_b;
+        const uint32_t incl = scan16(tot);
+        const uint32_t start = r.pos - tot + incl;
+        const uint32_t rb = (ring_dword(start) << 2) + r.ring_byte;
+        const lds_u32* rp = (const lds_u32*)(uintptr_t)rb;
+        const uint32_t bits = __builtin_amdgcn_alignbit(rp[1], rp[0], start);
+        const uint32_t fa = __builtin_amdgcn_ubfe(bits, 0, need_a);
+        const uint32_t fb = __builtin_amdgcn_ubfe(bits, need_a, need_b);
+        const uint32_t oa = __builtin_amdgcn_ubfe(fa, 0, act_a ? ea.B : 0u);
+        const uint32_t ob = __builtin_amdgcn_ubfe(fb, 0, act_b ? eb.B : 0u);
+        if (act_a) {
+            err |= oa > maxo_of(ea);
+            r.sa = ((fa >> (ea.B & 31)) << 3) + next_of(ea);
+        }
+        if (act_b) {
+            err |= ob > maxo_of(eb);
+            r.sb = ((fb >> (eb.B & 31)) << 3) + next_of(eb);
+        }
+        const uint32_t xa = oa + base_of(ea), xb = ob + base_of(eb);
+        if (act_b)
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)((xa & 0xFF) | (xb << 8)), rout,
+                                                  (int)r.vout, (int)(t * 32), 0);
+        else if (act_a)
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)xa, rout, (int)r.vout, (int)(t * 32), 0);
+        r.pos += row_last(incl);
+        ea = read_ent(r.sa);
+        eb = read_ent(r.sb);
+        refill();
+    }
+
+    // a valid chunk leaves every stream in slot 0 and ends in its last word, zero-padded
+    if (r.nc > 0) {
+        if (2 * j < lanes && r.sa != tab_byte) err = 1;
+        if (2 * j + 1 < lanes && r.sb != tab_byte) err = 1;
+        if (((r.pos + 31) >> 5) != r.cdw) {
+            err = 1;
+        } else if (r.pos & 31) {
+            const lds_u32* w = (const lds_u32*)(uintptr_t)(r.ring_byte + 4 * ((r.pos >> 5) & (kRRing - 1)));
+            if ((*w >> (r.pos & 31)) != 0) err = 1;
+        }
+    }
+    report(a.h.status, SH_ERR_CORRUPT_STREAM, err != 0 || bad_offsets != 0);
+}
+
+}  // namespace
+
+uint32_t decode_lds_bytes(uint32_t L) {
+    return 4 * (2 * L + kRowsPerBlock * (kRRingStride + kTileDwords));
+}
+
+sh_status launch_decode(const CodecArgs& a, uint32_t total_blocks, void* stream) {
+    if (total_blocks == 0) return SH_OK;
+    const uint32_t lds = decode_lds_bytes(a.L);
+    with_kernel_args(a, [&](const auto& k) {
+        hipLaunchKernelGGL((k_decode_rows<std::decay_t<decltype(k)>>), dim3(total_blocks),
+                           dim3(kRowsBlock), lds, (hipStream_t)stream, k);
+    });
+    return hipGetLastError() == hipSuccess ? SH_OK : SH_ERR_HIP;
+}
+
+}  // namespace shn
