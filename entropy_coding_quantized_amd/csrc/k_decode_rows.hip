@@ -25,16 +25,24 @@ namespace {
 
 constexpr int kRowsBlock = 256;                    // 4 wavefronts, 16 rows = 16 chunks
 constexpr uint32_t kRowsPerBlock = kRowsBlock / 16;
-constexpr uint32_t kRRing = 256;                   // compressed dwords resident per chunk
+constexpr uint32_t kRRingLog2 = 8;
+constexpr uint32_t kRRing = 1u << kRRingLog2;      // compressed dwords resident per chunk
 // a ring is followed by a copy of its dword 0 (a two-dword read never wraps) and padding
 // that keeps the next ring 16-byte aligned for the 128-bit LDS writes
 constexpr uint32_t kRRingStride = kRRing + 4;
-constexpr uint32_t kRFill = 128;                   // dwords per refill: 16 lanes x 32 bytes
-// Decoded bytes of four steps of a chunk (128 bytes, one cache line) are gathered in an LDS
-// tile and stored together: measured on MI355X, the 32-byte stores of single steps held
-// the decode near 1.7 TB/s of output however short the rest of the step was.
+constexpr uint32_t kRFill = kRRing / 2;            // dwords per refill
+constexpr uint32_t kFillVecs = kRFill / 64;        // 16-byte loads per lane and refill
+// Decoded bytes of kTileSteps steps of a chunk are gathered in an LDS tile and stored
+// together: measured on MI355X, the 32-byte stores of single steps held the decode near
+// 1.7 TB/s of output however short the rest of the step was.  The tiles of a block's rows
+// sit kTileStride dwords apart, 8 dwords more than a tile, so that the four rows of a
+// wavefront write different LDS banks in the same step.  (Measured side by side on one
+// GPU: 4-step tiles with 256-dword rings, 8-step tiles, 128-dword rings and a two-step
+// write through a neighbour exchange all decode the model workload within 5% of each
+// other; the simplest is kept.)
 constexpr uint32_t kTileSteps = 4;
 constexpr uint32_t kTileDwords = kTileSteps * 32 / 4;
+constexpr uint32_t kTileStride = kTileDwords + 8;
 
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef const __attribute__((address_space(3))) v2u lds_v2u;
@@ -68,7 +76,7 @@ __device__ __forceinline__ uint32_t scan16(uint32_t v) {
 // compiler would split the extract and the scaling that follows it into three operations).
 __device__ __forceinline__ uint32_t ring_dword(uint32_t pos) {
     uint32_t d;
-    asm("v_bfe_u32 %0, %1, 5, 8" : "=v"(d) : "v"(pos));
+    asm("v_bfe_u32 %0, %1, 5, %2" : "=v"(d) : "v"(pos), "i"(kRRingLog2));
     return d;
 }
 
@@ -101,7 +109,7 @@ struct Row {
     uint32_t nc, cdw, cbyte, ring_byte, pos, res_hi, refill_at, vout;
     uint32_t tile;     // LDS byte address of this lane's two bytes in step 0 of the tile
     uint32_t sa, sb;   // states of streams 2j and 2j + 1
-    v4u pf0, pf1;      // the next refill, in flight
+    v4u pf[kFillVecs]; // the next refill, in flight
 };
 
 template <class A>
@@ -143,7 +151,7 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
     Row r;
     r.ring_byte = tab_byte + 4 * (rings + (wv * 4 + row) * kRRingStride);
     const uint32_t tile_base =
-        tab_byte + 4 * (rings + kRowsPerBlock * kRRingStride + (wv * 4 + row) * kTileDwords);
+        tab_byte + 4 * (rings + kRowsPerBlock * kRRingStride + (wv * 4 + row) * kTileStride);
     r.tile = tile_base + 2 * j;
     r.vout = row * a.h.C + 2 * j;
     r.nc = 0;
@@ -166,12 +174,17 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
         }
     }
     // the first two refills (ring dwords [0, 256)), and the third in flight
-    const v4u f00 = load4(rin, r.cbyte, 8 * j, r.cdw), f01 = load4(rin, r.cbyte, 8 * j + 4, r.cdw);
-    const v4u f10 = load4(rin, r.cbyte, kRFill + 8 * j, r.cdw);
-    const v4u f11 = load4(rin, r.cbyte, kRFill + 8 * j + 4, r.cdw);
+    constexpr uint32_t kLaneFill = 4 * kFillVecs;   // dwords a lane loads per refill
+    v4u f0[kFillVecs], f1[kFillVecs];
+#pragma unroll
+    for (uint32_t v = 0; v < kFillVecs; ++v) {
+        f0[v] = load4(rin, r.cbyte, kLaneFill * j + 4 * v, r.cdw);
+        f1[v] = load4(rin, r.cbyte, kRFill + kLaneFill * j + 4 * v, r.cdw);
+    }
     r.res_hi = 2 * kRFill;  // dwords [res_hi - kRRing, res_hi) are in the ring
-    r.pf0 = load4(rin, r.cbyte, r.res_hi + 8 * j, r.cdw);
-    r.pf1 = load4(rin, r.cbyte, r.res_hi + 8 * j + 4, r.cdw);
+#pragma unroll
+    for (uint32_t v = 0; v < kFillVecs; ++v)
+        r.pf[v] = load4(rin, r.cbyte, r.res_hi + kLaneFill * j + 4 * v, r.cdw);
     // refills are checked every other step; one is due once the next two steps could read
     // past res_hi (a step reads at most 32 fields of 16 bits: 16 dwords)
     r.refill_at = r.res_hi < r.cdw ? (r.res_hi - 33) * 32 : 0xFFFFFFFFu;
@@ -213,11 +226,12 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
     }
     {
         uint32_t* rg = &dsm[rings + (wv * 4 + row) * kRRingStride];
-        *reinterpret_cast<v4u*>(&rg[8 * j]) = f00;
-        *reinterpret_cast<v4u*>(&rg[8 * j + 4]) = f01;
-        *reinterpret_cast<v4u*>(&rg[kRFill + 8 * j]) = f10;
-        *reinterpret_cast<v4u*>(&rg[kRFill + 8 * j + 4]) = f11;
-        if (j == 0) rg[kRRing] = f00[0];
+#pragma unroll
+        for (uint32_t v = 0; v < kFillVecs; ++v) {
+            *reinterpret_cast<v4u*>(&rg[kLaneFill * j + 4 * v]) = f0[v];
+            *reinterpret_cast<v4u*>(&rg[kRFill + kLaneFill * j + 4 * v]) = f1[v];
+        }
+        if (j == 0) rg[kRRing] = f0[0][0];
     }
     __syncthreads();
 
@@ -251,16 +265,18 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
 
     auto refill = [&]() {
         if (r.pos >= r.refill_at) {
-            const uint32_t d = (r.res_hi + 8 * j) & (kRRing - 1);
+            const uint32_t d = (r.res_hi + kLaneFill * j) & (kRRing - 1);
             typedef __attribute__((address_space(3))) v4u lds_w4;
             typedef __attribute__((address_space(3))) uint32_t lds_w1;
-            *(lds_w4*)(uintptr_t)(r.ring_byte + 4 * d) = r.pf0;
-            *(lds_w4*)(uintptr_t)(r.ring_byte + 4 * (d + 4)) = r.pf1;
-            if (d == 0) *(lds_w1*)(uintptr_t)(r.ring_byte + 4 * kRRing) = r.pf0[0];
+#pragma unroll
+            for (uint32_t v = 0; v < kFillVecs; ++v)
+                *(lds_w4*)(uintptr_t)(r.ring_byte + 4 * (d + 4 * v)) = r.pf[v];
+            if (d == 0) *(lds_w1*)(uintptr_t)(r.ring_byte + 4 * kRRing) = r.pf[0][0];
             r.res_hi += kRFill;
             r.refill_at = r.res_hi < r.cdw ? (r.res_hi - 33) * 32 : 0xFFFFFFFFu;
-            r.pf0 = load4(rin, r.cbyte, r.res_hi + 8 * j, r.cdw);
-            r.pf1 = load4(rin, r.cbyte, r.res_hi + 8 * j + 4, r.cdw);
+#pragma unroll
+            for (uint32_t v = 0; v < kFillVecs; ++v)
+                r.pf[v] = load4(rin, r.cbyte, r.res_hi + kLaneFill * j + 4 * v, r.cdw);
         }
     };
 
@@ -291,12 +307,19 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
         *(lds_w2*)(uintptr_t)(r.tile + 32 * (t & (kTileSteps - 1))) = (uint16_t)((xa & 0xFF) | (xb << 8));
         r.pos += row_last(incl);
     };
-    // the tile of steps [t0, t0 + 4) to the output: lane j stores bytes [8j, 8j + 8)
-    // (LDS operations of a wavefront complete in order, so the row's writes are visible)
+    // the tile of steps [t0, t0 + kTileSteps) to the output: lane j stores its share of
+    // the row's 32 * kTileSteps bytes (LDS operations of a wavefront complete in order, so
+    // the row's writes are visible)
     auto flush_tile = [&](uint32_t t0) {
-        const v2u w = *(lds_v2u*)(uintptr_t)(tile_base + 8 * j);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, w), rout,
-                                              (int)(row * a.h.C + 8 * j), (int)(t0 * 32), 0);
+        constexpr uint32_t kLaneBytes = 2 * kTileSteps;
+        const uint32_t at = row * a.h.C + kLaneBytes * j;
+        if constexpr (kLaneBytes == 16) {
+            const v4u w = *(const __attribute__((address_space(3))) v4u*)(uintptr_t)(tile_base + 16 * j);
+            __builtin_amdgcn_raw_buffer_store_b128(w, rout, (int)at, (int)(t0 * 32), 0);
+        } else {
+            const v2u w = *(lds_v2u*)(uintptr_t)(tile_base + 8 * j);
+            __builtin_amdgcn_raw_buffer_store_b64(w, rout, (int)at, (int)(t0 * 32), 0);
+        }
     };
 
     Ent ea = read_ent(r.sa), eb = read_ent(r.sb), ea2, eb2;
@@ -308,12 +331,12 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
         take_turn(t / kPrioSteps, slot_id);
         const uint32_t stop = full4 - t < kPrioSteps ? full4 : t + kPrioSteps;
         for (; t < stop; t += kTileSteps) {  // the entries alternate registers step by step
-            full_step(ea, eb, ea2, eb2, t);
-            full_step(ea2, eb2, ea, eb, t + 1);
-            refill();
-            full_step(ea, eb, ea2, eb2, t + 2);
-            full_step(ea2, eb2, ea, eb, t + 3);
-            refill();
+#pragma unroll
+            for (uint32_t k = 0; k < kTileSteps; k += 2) {
+                full_step(ea, eb, ea2, eb2, t + k);
+                full_step(ea2, eb2, ea, eb, t + k + 1);
+                refill();
+            }
             flush_tile(t);
         }
     }
@@ -373,7 +396,7 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
 }  // namespace
 
 uint32_t decode_lds_bytes(uint32_t L) {
-    return 4 * (2 * L + kRowsPerBlock * (kRRingStride + kTileDwords));
+    return 4 * (2 * L + kRowsPerBlock * (kRRingStride + kTileStride));
 }
 
 sh_status launch_decode(const CodecArgs& a, uint32_t total_blocks, void* stream) {

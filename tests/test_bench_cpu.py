@@ -34,18 +34,18 @@ def test_summarize_counters_scales_by_the_calibration_copy(tmp_path):
          "Counter_Name": "FETCH_SIZE", "Counter_Value": 131072.0},
         {"Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": 64,  # another copy: ignored
          "Counter_Name": "FETCH_SIZE", "Counter_Value": 9.0},
-        {"Kernel_Name": "void shn::k_decode<1>(x)", "Grid_Size": 1024,
+        {"Kernel_Name": "void shn::(anonymous namespace)::k_decode_rows<x>(x)", "Grid_Size": 1024,
          "Counter_Name": "FETCH_SIZE", "Counter_Value": 100.0},
-        {"Kernel_Name": "void shn::k_decode<1>(x)", "Grid_Size": 1024,
+        {"Kernel_Name": "void shn::(anonymous namespace)::k_decode_rows<x>(x)", "Grid_Size": 1024,
          "Counter_Name": "FETCH_SIZE", "Counter_Value": 300.0}])
     _write_counters(prof / f"pmc_WRITE_SIZE_{wl}", wl, [
         {"Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": copy_grid,
          "Counter_Name": "WRITE_SIZE", "Counter_Value": 262144.0},
-        {"Kernel_Name": "void shn::k_decode<1>(x)", "Grid_Size": 1024,
+        {"Kernel_Name": "void shn::(anonymous namespace)::k_decode_rows<x>(x)", "Grid_Size": 1024,
          "Counter_Name": "WRITE_SIZE", "Counter_Value": 64.0}])
     n = sum(x.size for x in bench.make_segments(wl))
     _write_counters(prof / f"pmc_SQ_{wl}", wl, [
-        {"Kernel_Name": "void shn::k_decode<1>(x)", "Grid_Size": 1024,
+        {"Kernel_Name": "void shn::(anonymous namespace)::k_decode_rows<x>(x)", "Grid_Size": 1024,
          "Counter_Name": "SQ_INSTS_VALU", "Counter_Value": float(n)},
         {"Kernel_Name": "void shn::k_encode_chunks<1>(x)", "Grid_Size": 1024,
          "Counter_Name": "SQ_INSTS_VALU", "Counter_Value": float(2 * n)}])
@@ -57,7 +57,7 @@ def test_summarize_counters_scales_by_the_calibration_copy(tmp_path):
     assert rec["WRITE_SIZE"]["scale"] == pytest.approx(1.0)
     # (mean 200 KiB x 2 + 64 KiB x 1) in bytes
     assert rec["hbm_bytes_per_launch"] == pytest.approx((200.0 * 2 + 64.0) * 1024)
-    assert rec["instructions"]["k_decode"]["valu_per_symbol"] == pytest.approx(64.0)
+    assert rec["instructions"]["k_decode_rows"]["valu_per_symbol"] == pytest.approx(64.0)
     assert rec["instructions"]["k_encode_chunks"]["valu_per_symbol"] == pytest.approx(128.0)
     assert rec["kernels_sha256_16"] == bench.kernels_hash()
 
@@ -71,7 +71,7 @@ def test_profiles_taken_from_other_sources_are_ignored(tmp_path, monkeypatch):
     assert bench.traffic_from_profile("weight") is None
     with open(tmp_path / "profiles" / "decode_traffic_weight.json", "w") as f:
         json.dump({"kernels_sha256_16": "this-source", "hbm_bytes_per_launch": 5.0,
-                   "instructions": {"k_decode": {"valu_per_symbol": 19.5}}}, f)
+                   "instructions": {"k_decode_rows": {"valu_per_symbol": 19.5}}}, f)
     assert bench.traffic_from_profile("weight") == 5.0
     assert bench.valu_per_symbol_from_profile("weight") == 19.5
 
