@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libshannonic.so")
-SOURCES = ["k_build.hip", "k_encode.hip", "k_decode.hip", "k_decode_rows.hip",
+SOURCES = ["k_build.hip", "k_encode.hip", "k_decode.hip", "k_decode_rows.hip", "noalloc.hip",
            "host_tables.cpp", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

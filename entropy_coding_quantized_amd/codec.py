@@ -78,6 +78,10 @@ _EXPORTS = {
     "sh_encode": (C.c_int32, [C.POINTER(sh_table), C.POINTER(sh_params), C.c_void_p, C.c_uint64,
                               C.c_void_p, C.c_uint64, C.c_void_p, C.c_uint64, C.c_void_p,
                               C.c_void_p, C.c_void_p]),
+    "sh_encode_noalloc_scratch_bytes": (C.c_uint64, []),
+    "sh_encode_noalloc": (C.c_int32, [C.POINTER(sh_table), C.POINTER(sh_params), C.c_void_p,
+                                      C.c_uint64, C.c_void_p, C.c_uint64, C.c_void_p, C.c_void_p,
+                                      C.c_void_p]),
     "sh_decode": (C.c_int32, [C.POINTER(sh_table), C.POINTER(sh_params), C.c_void_p, C.c_uint64,
                               C.c_void_p, C.c_uint64, C.c_void_p, C.c_void_p]),
     "sh_stats": (C.c_int32, [C.POINTER(sh_table), C.c_uint64, C.c_uint64, C.c_uint64,
@@ -226,6 +230,18 @@ def sh_encode(table: sh_table, params: Params, d_x, n: int, d_out, out_cap: int,
     st = lib().sh_encode(C.byref(table), C.byref(p), _ptr(d_x), n, _ptr(d_out), out_cap,
                          _ptr(d_ws), ws_bytes, _ptr(d_info), _ptr(d_status), _stream(stream))
     _check(st, "sh_encode")
+
+
+def sh_encode_noalloc_scratch_bytes() -> int:
+    return lib().sh_encode_noalloc_scratch_bytes()
+
+
+def sh_encode_noalloc(table: sh_table, params: Params, d_x, n: int, d_out, out_cap: int,
+                      d_info=None, d_status=None, stream=None) -> None:
+    p = params.c()
+    st = lib().sh_encode_noalloc(C.byref(table), C.byref(p), _ptr(d_x), n, _ptr(d_out), out_cap,
+                                 _ptr(d_info), _ptr(d_status), _stream(stream))
+    _check(st, "sh_encode_noalloc")
 
 
 def sh_decode(table: sh_table, params: Params, d_in, in_nbytes: int, d_y, n: int,

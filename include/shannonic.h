@@ -184,6 +184,23 @@ sh_status sh_decode(const sh_table* table, const sh_params* params, const uint8_
                     uint64_t in_nbytes, int8_t* d_y, uint64_t n, int32_t* d_status,
                     void* stream);
 
+/*
+ * sh_encode for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same arguments without the
+ * workspace.  The workspace is a file-scope device array of
+ * sh_encode_noalloc_scratch_bytes() (64 MiB) that the library holds on every GPU it runs on
+ * until the process ends; its device address is taken on the first call on each device.
+ * Tensors whose sh_encode_workspace() exceeds it are refused with SH_ERR_BUFFER_TOO_SMALL
+ * (at K = 16, log2_L = 7: about 33 M values at 4,096 values a chunk, 34 M at 16,384).  The
+ * call allocates nothing.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (other streams, other host threads) race and must be serialised by
+ * the caller.  Output, errors and asynchrony are sh_encode's.
+ */
+uint64_t sh_encode_noalloc_scratch_bytes(void);
+sh_status sh_encode_noalloc(const sh_table* table, const sh_params* params, const int8_t* d_x,
+                            uint64_t n, uint8_t* d_out, uint64_t out_cap,
+                            sh_encode_info* d_info, int32_t* d_status, void* stream);
+
 /* ---- device-resident tables and batches ---------------------------------------------
  *
  * A device table is the per-tensor state the kernels read, in device memory: the canonical
