@@ -181,6 +181,7 @@ sh_status sh_table_to_device(const sh_table* table, const sh_params* params, voi
     if (table->K != params->K || table->log2_L != params->log2_L) return SH_ERR_INVALID_ARG;
     const bool empty = table->n == 0;
     if (check_table(*table, empty) != SH_OK) return SH_ERR_INVALID_ARG;
+    if (max_field_bits(*table) > kMaxFieldBitsGpu) return SH_ERR_UNSUPPORTED;
     std::vector<uint32_t> dt(kDTDwords, 0);
     SlotTables slots;
     if (!empty && derive_slots(*table, &slots) != SH_OK) return SH_ERR_INVALID_ARG;
@@ -302,6 +303,10 @@ sh_status sh_encode(const sh_table* table, const sh_params* params, const int8_t
     if (st != SH_OK) return st;
     if (table->K != params->K || table->log2_L != params->log2_L) return SH_ERR_INVALID_ARG;
     if (check_table(*table, n == 0) != SH_OK) return SH_ERR_INVALID_ARG;
+    // the table travels in the launch's arguments: at most 256 states (larger tables go
+    // through sh_table_to_device and the batch calls)
+    if (params->log2_L > (uint32_t)kInlineMaxLog2L || max_field_bits(*table) > kMaxFieldBitsGpu)
+        return SH_ERR_UNSUPPORTED;
     if (n >= (1ull << 32)) return SH_ERR_UNSUPPORTED;
     const uint64_t bound = bound_of(n, params);
     if (bound > 0xFFFFFFFFull) return SH_ERR_UNSUPPORTED;
@@ -346,6 +351,8 @@ sh_status sh_decode(const sh_table* table, const sh_params* params, const uint8_
     if (st != SH_OK) return st;
     if (table->K != params->K || table->log2_L != params->log2_L) return SH_ERR_INVALID_ARG;
     if (check_table(*table, n == 0) != SH_OK) return SH_ERR_INVALID_ARG;
+    if (params->log2_L > (uint32_t)kInlineMaxLog2L || max_field_bits(*table) > kMaxFieldBitsGpu)
+        return SH_ERR_UNSUPPORTED;
     if (n >= (1ull << 32) || in_nbytes > 0xFFFFFFFFull) return SH_ERR_UNSUPPORTED;
     if (!aligned(d_in, 4) || !aligned(d_status, 4)) return SH_ERR_INVALID_ARG;
     const uint64_t nch = n_chunks_of(n, params->chunk_symbols);
@@ -482,6 +489,7 @@ sh_status sh_decode_matvec_batch(const void* d_tables, const uint8_t* const* d_i
     sh_status st = check_params(params);
     if (st != SH_OK) return st;
     if (cols % 32 != 0 || cols > kMaxMatvecCols) return SH_ERR_UNSUPPORTED;
+    if (params->log2_L > (uint32_t)kInlineMaxLog2L) return SH_ERR_UNSUPPORTED;  // one slot a thread
     if (!aligned(d_status, 4)) return SH_ERR_INVALID_ARG;
     for (uint32_t i = 0; i < nseg; ++i) {
         if (!d_in[i] || !aligned(d_in[i], 4) || n[i] % cols != 0) return SH_ERR_INVALID_ARG;

@@ -19,7 +19,14 @@ namespace shn {
 constexpr int kLgFrac = 24;            // fractional bits of the DP's fixed-point log2
 constexpr int kLanes = 32;             // interleaved tANS lanes per chunk (a half wavefront)
 constexpr int kMaxLog2LHost = 12;      // host table build
-constexpr int kMaxLog2LGpu = 8;        // GPU path: a field is at most 8 + 8 = 16 bits
+// GPU path: L up to 2048 states (standard tANS sizes), tables held in LDS; the decoder
+// takes two adjacent fields in one 32-bit window, so a table is usable on the GPU only when
+// its longest field, the widest range's offset bits plus log2 L state bits, is at most 16
+// bits (always at log2 L <= 8, and for K = 256, where every range is one value)
+constexpr int kMaxLog2LGpu = 11;
+constexpr uint32_t kMaxLGpu = 1u << kMaxLog2LGpu;
+constexpr int kInlineMaxLog2L = 8;     // single-tensor calls carry their tables inline
+constexpr uint32_t kMaxFieldBitsGpu = 16;
 constexpr uint32_t kMaxChunk = 65536;  // GPU path
 constexpr uint32_t kHeaderFixed = 32;  // bytes of the fixed part of the container header
 constexpr uint32_t kMaxHeaderDwords = (kHeaderFixed + 3 * 256 - 1 + 3) / 4;  // 200
@@ -69,13 +76,13 @@ void write_header(const sh_table& t, uint64_t n, uint32_t C, uint32_t S, uint64_
 constexpr uint32_t kDTK = 0, kDTLog2L = 1, kDTL = 2, kDTStatus = 3, kDTN = 4 /* u64 */;
 constexpr uint32_t kDTHdrDwords = 6;
 constexpr uint32_t kDTHdr = 8;        // 200 dwords: container header with n = n_chunks = 0
-constexpr uint32_t kDTDec = 208;      // 512 dwords: decode entries, two per slot
-constexpr uint32_t kDTVt = 720;       // 512 dwords: encode entries, two per value
-constexpr uint32_t kDTEs = 1232;      // 64 dwords: encode slot bytes
-constexpr uint32_t kDTLo = 1296;      // 129 dwords: lo[257] as u16
-constexpr uint32_t kDTFreq = 1426;    // 128 dwords: freq[256] as u16
-constexpr uint32_t kDTHist = 1554;    // 512 dwords: hist[256] as u64
-constexpr uint32_t kDTDwords = 2112;  // 8448 bytes
+constexpr uint32_t kDTLo = 208;       // 129 dwords: lo[257] as u16
+constexpr uint32_t kDTFreq = 337;     // 128 dwords: freq[256] as u16
+constexpr uint32_t kDTHist = 466;     // 512 dwords: hist[256] as u64 (8-byte aligned)
+constexpr uint32_t kDTVt = 978;       // 512 dwords: encode entries, two per value
+constexpr uint32_t kDTDec = 1490;     // 2 * kMaxLGpu dwords: decode entries, two per slot
+constexpr uint32_t kDTEs = 5586;      // kMaxLGpu / 2 dwords: encode slots as u16
+constexpr uint32_t kDTDwords = 6612;  // 26,448 bytes (16-byte multiple)
 constexpr uint32_t kDTBytes = 4 * kDTDwords;
 
 // header dwords that depend on the segment, not on the table: n (2, 3) and n_chunks (6)
@@ -92,9 +99,11 @@ SHN_HD inline uint32_t header_dword(const uint32_t* tmpl, uint32_t i, uint64_t n
 //   e1 = w_s | (int8 bits of the range base) << 8 | (|range| - 1) << 16
 // Encode entry of a value u, two dwords:
 //   v0 = bias_s (int32): the state-bit count is (X + bias_s) >> (R + 1)
-//   v1 = o | w_s << 8 | (f_s == 0) << 15 | (start_s + 512) << 16, start_s = cum_s - f_s
+//   v1 = o | w_s << 8 | (f_s == 0) << 15 | (start_s + kMaxLGpu) << 16, start_s = cum_s - f_s
 void derive_kernel_tables(const sh_table& t, const SlotTables& st, uint32_t* dec,
-                          uint32_t* vt, uint8_t* es);
+                          uint32_t* vt, uint16_t* es);
+// the longest field (offset bits of the widest range plus log2 L) of a table, in bits
+uint32_t max_field_bits(const sh_table& t);
 // st is null for a table built from no values
 void make_device_table(const sh_table& t, const SlotTables* st, uint32_t C, uint32_t S,
                        uint32_t* dt /* kDTDwords */);
@@ -138,7 +147,7 @@ struct CodecArgs {
             SegDesc seg;
             uint32_t hdr[kMaxHeaderDwords];
             uint32_t tab[2 * 256];  // decode entries (decode) or value entries (encode)
-            uint8_t es[256];        // encode slot bytes
+            uint16_t es[256];       // encode slots
         } one;
         SegDesc many[kMaxInlineSegs];  // each with a device table
     };
@@ -166,7 +175,7 @@ struct KOne {  // one segment with the tables in the arguments
     SegDesc segs[1];
     uint32_t hdr[kMaxHeaderDwords];
     uint32_t tab[2 * 256];
-    uint8_t es[256];
+    uint16_t es[256];
 };
 
 // values per histogram block: a power of two from 16 KB to 1 MB, so that a launch has about

@@ -111,13 +111,13 @@ __device__ __forceinline__ const SegDesc* codec_seg(const A& a, uint32_t block, 
 // table); which a segment uses is decided by its tab pointer
 __device__ __forceinline__ const uint32_t* inline_tab(const KOne& a) { return a.tab; }
 __device__ __forceinline__ const uint32_t* inline_hdr(const KOne& a) { return a.hdr; }
-__device__ __forceinline__ const uint8_t* inline_es(const KOne& a) { return a.es; }
+__device__ __forceinline__ const uint16_t* inline_es(const KOne& a) { return a.es; }
 template <int N>
 __device__ __forceinline__ const uint32_t* inline_tab(const KSegs<N>&) { return nullptr; }
 template <int N>
 __device__ __forceinline__ const uint32_t* inline_hdr(const KSegs<N>&) { return nullptr; }
 template <int N>
-__device__ __forceinline__ const uint8_t* inline_es(const KSegs<N>&) { return nullptr; }
+__device__ __forceinline__ const uint16_t* inline_es(const KSegs<N>&) { return nullptr; }
 
 // ---- host side: the smallest argument block for a launch ----
 inline KHead kernel_head(const CodecArgs& a) {

@@ -280,7 +280,7 @@ namespace shn {
 
 // The kernels' forms of a table (see codec_internal.hpp for the packing).
 void derive_kernel_tables(const sh_table& t, const SlotTables& st, uint32_t* dec, uint32_t* vt,
-                          uint8_t* es) {
+                          uint16_t* es) {
     const uint32_t K = t.K, R = t.log2_L, L = 1u << R;
     if (dec) {
         for (uint32_t i = 0; i < L; ++i) {
@@ -303,13 +303,22 @@ void derive_kernel_tables(const sh_table& t, const SlotTables& st, uint32_t* dec
             }
             for (uint32_t u = t.lo[s]; u < t.lo[s + 1]; ++u) {
                 vt[2 * u] = (uint32_t)bias;
-                vt[2 * u + 1] = (u - t.lo[s]) | (w << 8) | ((uint32_t)(start + 512) << 16) |
+                vt[2 * u + 1] = (u - t.lo[s]) | (w << 8) | ((uint32_t)(start + (int32_t)kMaxLGpu) << 16) |
                                 (f == 0 ? 0x8000u : 0u);
             }
         }
     }
     if (es)
-        for (uint32_t i = 0; i < L; ++i) es[i] = (uint8_t)st.enc[i];
+        for (uint32_t i = 0; i < L; ++i) es[i] = st.enc[i];
+}
+
+uint32_t max_field_bits(const sh_table& t) {
+    uint32_t w = 0;
+    for (uint32_t k = 0; k < t.K; ++k) {
+        const uint32_t wk = ceil_log2_u32(t.lo[k + 1] - t.lo[k]);
+        w = wk > w ? wk : w;
+    }
+    return w + t.log2_L;
 }
 
 void make_device_table(const sh_table& t, const SlotTables* st, uint32_t C, uint32_t S,
@@ -323,7 +332,7 @@ void make_device_table(const sh_table& t, const SlotTables* st, uint32_t C, uint
     dt[kDTHdrDwords] = header_bytes(t.K) / 4;
     write_header(t, 0, C, S, 0, dt + kDTHdr);
     if (st)
-        derive_kernel_tables(t, *st, dt + kDTDec, dt + kDTVt, reinterpret_cast<uint8_t*>(dt + kDTEs));
+        derive_kernel_tables(t, *st, dt + kDTDec, dt + kDTVt, reinterpret_cast<uint16_t*>(dt + kDTEs));
     else  // a table built from no values: every value is outside it
         for (uint32_t u = 0; u < 256; ++u) dt[kDTVt + 2 * u + 1] = 0x8000u;
     std::memcpy(dt + kDTLo, t.lo, sizeof(t.lo));

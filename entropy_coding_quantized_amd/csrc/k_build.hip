@@ -163,12 +163,17 @@ __global__ __launch_bounds__(256) void k_build_cost(const BuildArgs a) {
 // state allocation, the spread and every derived table.
 constexpr int kBuildBlock = 1024;
 
-// floor(A / f) for A < 2^20, f >= 1: a float quotient through the hardware reciprocal
-// (relative error below 2^-21, so below 1/2 in absolute terms), then corrected by one
+// floor(A / f) for A < 2^24, f >= 1: a float quotient through the hardware reciprocal (A
+// is exact in a float and the product's relative error stays below 2^-21, so the quotient
+// is at most 9 away), then a fixed number of one-step corrections with 64-bit products
 __device__ __forceinline__ uint32_t small_div(uint32_t A, uint32_t f) {
     uint32_t q = (uint32_t)((float)A * __builtin_amdgcn_rcpf((float)f));
-    if (q * f > A) --q;
-    else if ((q + 1) * f <= A) ++q;
+#pragma unroll
+    for (int i = 0; i < 12; ++i)
+        if (q > 0 && (uint64_t)q * f > A) --q;
+#pragma unroll
+    for (int i = 0; i < 12; ++i)
+        if ((uint64_t)(q + 1) * f <= A) ++q;
     return q;
 }
 
@@ -195,7 +200,7 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
     __shared__ uint64_t red_c[kBuildBlock / 64];
     __shared__ uint32_t red_j[kBuildBlock / 64];
     __shared__ uint32_t lo_s[257], freq_s[256], cum_s[257], range_of_u[256], count_s[256];
-    __shared__ uint32_t lg_s[258], gain_s[257];
+
     __shared__ uint32_t f0_s[256], add_s[256], alloc_s[2];  // state allocation: start, taken, total and check
     __shared__ uint32_t status_s;
     const uint32_t tid = threadIdx.x, lane = tid & 63, seg = blockIdx.x;
@@ -222,7 +227,6 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
             if (i < kGroups) dst[i] = v[r];
         }
     }
-    if (tid < 258) lg_s[tid] = (uint32_t)dev_fixed_log2(tid);
 
     // prefix sums of the histogram, 64-bit to check that the total fits 32 bits
     uint64_t incl = 0;
@@ -239,9 +243,7 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
         uint64_t before = 0;
         for (uint32_t w = 0; w < wave; ++w) before += red_c[w];
         prefix[tid + 1] = (uint32_t)(before + incl);
-        gain_s[tid] = tid == 0 ? 0u : lg_s[tid + 1] - lg_s[tid];
     }
-    if (tid == 256) gain_s[256] = lg_s[257] - lg_s[256];
     if (tid == 0) {
         prefix[0] = 0;
         const uint64_t total = red_c[0] + red_c[1] + red_c[2] + red_c[3];
@@ -388,11 +390,20 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
     lds_barrier();
     for (uint32_t k = tid; k < K; k += kBuildBlock) count_s[k] = prefix[lo_s[k + 1]] - prefix[lo_s[k]];
     if (wave == 0) {
-        uint32_t used = 0;
-        for (uint32_t k = lane; k < K; k += 64) used += prefix[lo_s[k + 1]] != prefix[lo_s[k]] ? 1 : 0;
+        uint32_t used = 0, wmax = 0;
+        for (uint32_t k = lane; k < K; k += 64) {
+            used += prefix[lo_s[k + 1]] != prefix[lo_s[k]] ? 1 : 0;
+            const uint32_t w = dev_ceil_log2(lo_s[k + 1] - lo_s[k]);
+            wmax = w > wmax ? w : wmax;
+        }
         used = wave_sum(used);
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t o = __shfl_xor(wmax, d, 64);
+            wmax = o > wmax ? o : wmax;
+        }
         if (lane == 0) {
-            if (used > L) status_s = (uint32_t)SH_ERR_UNSUPPORTED;
+            // more occupied ranges than states, or a field longer than the GPU path takes
+            if (used > L || wmax + R > kMaxFieldBitsGpu) status_s = (uint32_t)SH_ERR_UNSUPPORTED;
             red_j[0] = used;
             alloc_s[0] = 0;
         }
@@ -438,6 +449,12 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
     // the work per (increment, other range); others search the gain table per increment.
     uint64_t* inc = reinterpret_cast<uint64_t*>(sc);
     uint32_t* rank_of = reinterpret_cast<uint32_t*>(inc + kIncMax);
+    // gain(f) = log2(f + 1) - log2 f in the DP's fixed point, for f = 0 .. L, after them
+    uint32_t* gain_s = rank_of + kIncMax;
+    static_assert(3 * kIncMax + kMaxLGpu + 1 <= kCostEntries, "gain table inside the cost area");
+    for (uint32_t f = tid; f <= L; f += kBuildBlock)
+        gain_s[f] = f == 0 ? 0u : (uint32_t)(dev_fixed_log2(f + 1) - dev_fixed_log2(f));
+    lds_barrier();
     auto take = [&](uint32_t from) {
         const uint32_t Mp = L - from, n_inc = K * Mp;
         if (!alloc_ok || Mp == 0) return;
@@ -616,7 +633,7 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
             else k = mid + 1;
         }
         const uint32_t j = p - cum_s[k], f = freq_s[k];
-        uint32_t rank = 0;  // A = (2j + 1) f2 < 2L * L <= 2^17
+        uint32_t rank = 0;  // A = (2j + 1) f2 < 2L * L <= 2^23
         for (uint32_t k0 = 0; k0 < K; k0 += 4) {  // four ranges at a time, reads together
             uint32_t f2v[4];
 #pragma unroll
@@ -624,10 +641,11 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
 #pragma unroll
             for (uint32_t r = 0; r < 4; ++r) {
                 const uint32_t k2 = k0 + r, f2 = f2v[r];
-                const uint32_t A = (2 * j + 1) * f2;
+                if (f2 == 0) continue;  // a range without states takes no slot
+                const uint32_t A = (2 * j + 1) * f2;  // >= 1
                 const uint32_t odd_max = small_div(k2 < k ? A : A - 1, f);  // largest usable 2j'+1
                 const uint32_t c = (odd_max + 1) >> 1;
-                rank += f2 == 0 ? 0u : (c < f2 ? c : f2);
+                rank += c < f2 ? c : f2;
             }
         }
         const uint32_t x = f + j;
@@ -637,7 +655,7 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
         const uint32_t w = dev_ceil_log2(width);
         dt[kDTDec + 2 * rank] = (w + nb) | ((next * 8u) << 16);
         dt[kDTDec + 2 * rank + 1] = w | (((lo_s[k] - 128u) & 0xFFu) << 8) | ((width - 1) << 16);
-        reinterpret_cast<uint8_t*>(dt + kDTEs)[cum_s[k] + j] = (uint8_t)rank;
+        reinterpret_cast<uint16_t*>(dt + kDTEs)[cum_s[k] + j] = (uint16_t)rank;
     }
     for (uint32_t u = tid; u < 256; u += kBuildBlock) {  // the range of value u: lo_s[k] <= u < lo_s[k+1]
         uint32_t lo = 0, hi = K - 1;
@@ -661,7 +679,7 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
             start = (int32_t)cum_s[s] - (int32_t)f;
         }
         dt[kDTVt + 2 * u] = (uint32_t)bias;
-        dt[kDTVt + 2 * u + 1] = (u - lo_s[s]) | (w << 8) | ((uint32_t)(start + 512) << 16) |
+        dt[kDTVt + 2 * u + 1] = (u - lo_s[s]) | (w << 8) | ((uint32_t)(start + (int32_t)kMaxLGpu) << 16) |
                                 (f == 0 ? 0x8000u : 0u);
     }
     // canonical table, histogram and the header template (n and n_chunks left 0)

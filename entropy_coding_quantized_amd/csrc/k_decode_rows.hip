@@ -139,7 +139,7 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
     const uint32_t chunk = group + row;
     const v2u idx = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(
                                                 rin, (int)(index_at + 4 * (chunk < n_chunks ? chunk : 0)), 0, 0));
-    const uint32_t ts = tid < L ? tid : L - 1;      // L <= 256: one slot per thread
+    const uint32_t ts = tid < L ? tid : L - 1;      // slot tid (more below when L > 256)
     const uint32_t te0 = dec[2 * ts], te1 = dec[2 * ts + 1];
 
     const uint64_t grp_first = (uint64_t)group * a.h.C;
@@ -220,10 +220,13 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
 
     // the table's entries in the LDS form (device form: e0 = need | next slot * 8 << 16,
     // e1 = w | base << 8 | (|range| - 1) << 16)
-    if (tid < L) {
-        dsm[2 * tid] = (te0 & 0xFFu) | ((te1 & 0xFF00u) << 8) | ((te1 & 0xFF0000u) << 8);
-        dsm[2 * tid + 1] = (te1 & 0xFFu) | ((tab_byte + (te0 >> 16)) << 16);
-    }
+    auto stage_entry = [&](uint32_t slot, uint32_t e0, uint32_t e1) {
+        dsm[2 * slot] = (e0 & 0xFFu) | ((e1 & 0xFF00u) << 8) | ((e1 & 0xFF0000u) << 8);
+        dsm[2 * slot + 1] = (e1 & 0xFFu) | ((tab_byte + (e0 >> 16)) << 16);
+    };
+    if (tid < L) stage_entry(tid, te0, te1);
+    for (uint32_t slot = tid + kRowsBlock; slot < L; slot += kRowsBlock)
+        stage_entry(slot, dec[2 * slot], dec[2 * slot + 1]);
     {
         uint32_t* rg = &dsm[rings + (wv * 4 + row) * kRRingStride];
 #pragma unroll

@@ -20,11 +20,14 @@ namespace shn {
 constexpr int kEncBlock = 256;
 constexpr uint32_t kChunksPerBlockE = kEncBlock / 64 * 2;  // two chunks a wavefront
 constexpr uint32_t kERing = 256;
-// LDS: eight 1 KB rings (one per half wavefront, 1 KB aligned), eight 1 KB input tiles
-// (bytes of 32 steps x 32 lanes), then the value table and the encTable bytes
+// LDS (dynamic, sized by L; the kernel's only LDS, so it starts at LDS byte 0): eight 1 KB
+// rings (one per half wavefront, 1 KB aligned), eight 1 KB input tiles (bytes of 32 steps x
+// 32 lanes), the value table (512 dwords), the encTable slots (u16, L of them), then the
+// block's two totals
 constexpr uint32_t kTileBase = 8 * kERing;
 constexpr uint32_t kVtBase = kTileBase + 8 * 256;
-constexpr uint32_t kVtDwords = 512 + 64;
+constexpr uint32_t kEsBase = kVtBase + 512;
+__host__ __device__ constexpr uint32_t encode_lds_dwords(uint32_t L) { return kEsBase + (L + 1) / 2 + 2; }
 
 // OR a field (zero above its length) into a ring at bit pos; ring_byte is the ring's LDS
 // byte offset, a multiple of its 1 KB size.  The second dword is OR-ed only by the lanes
@@ -46,8 +49,7 @@ __device__ __forceinline__ void ring_or(uint32_t* sm, uint32_t ring_byte, uint32
 
 template <class A>
 __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
-    __shared__ __align__(1024) uint32_t sm[kVtBase + kVtDwords];
-    __shared__ uint32_t agg_s[2];  // the block's container bytes and field bits
+    extern __shared__ __align__(16) uint32_t sm[];
     const uint32_t tid = threadIdx.x, lane = tid & 63, li = lane & 31, hw = lane >> 5;
     const uint32_t block = __builtin_amdgcn_readfirstlane(blockIdx.x);
     const SegDesc* sg = codec_seg(a, block, false);
@@ -55,17 +57,16 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
     const uint32_t wid = __builtin_amdgcn_readfirstlane(bseg * (kEncBlock / 64) + (tid >> 6));
     const uint32_t wv = wid & (kEncBlock / 64 - 1);
     const uint32_t* vt = sg->tab ? sg->tab + kDTVt : inline_tab(a);
-    const uint8_t* es_src = sg->tab ? reinterpret_cast<const uint8_t*>(sg->tab + kDTEs)
-                                   : inline_es(a);
+    const uint16_t* es_src = sg->tab ? reinterpret_cast<const uint16_t*>(sg->tab + kDTEs)
+                                    : inline_es(a);
     const uint32_t n_chunks = sg->n_chunks;
     const uint64_t n = sg->n;
+    const uint32_t L = a.h.L, R1 = a.h.R + 1;
+    uint32_t* agg_s = &sm[kEsBase + (L + 1) / 2];  // the block's container bytes and field bits
     for (uint32_t i = tid; i < 512; i += kEncBlock) sm[kVtBase + i] = vt[i];
-    for (uint32_t i = tid; i < 64; i += kEncBlock) {
-        sm[kVtBase + 512 + i] = (uint32_t)es_src[4 * i] | ((uint32_t)es_src[4 * i + 1] << 8) |
-                                ((uint32_t)es_src[4 * i + 2] << 16) |
-                                ((uint32_t)es_src[4 * i + 3] << 24);
-    }
-    const uint8_t* es = reinterpret_cast<const uint8_t*>(&sm[kVtBase + 512]);
+    for (uint32_t i = tid; 2 * i < L; i += kEncBlock)
+        sm[kEsBase + i] = (uint32_t)es_src[2 * i] | ((uint32_t)es_src[2 * i + 1] << 16);
+    const uint16_t* es = reinterpret_cast<const uint16_t*>(&sm[kEsBase]);
     const uint32_t hi = wv * 2 + hw;       // this half wavefront's ring and tile
     const uint32_t tile = kTileBase + hi * 256;
     const uint32_t ring = hi * kERing;
@@ -82,18 +83,19 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
     const rsrc_t rslot = make_rsrc(a.h.slots + (uint64_t)slot0 * a.h.slot_dwords, 8u * a.h.slot_dwords);
     const uint32_t in_base = hw * a.h.C;          // byte offset of this chunk in rin
     const uint32_t slot_base = hw * a.h.slot_dwords * 4;
-    // a device table built for other parameters than the launch's is refused: its chunks are
-    // coded as empty (the workspace stays consistent for the placement) and the call fails
+    // a device table built for other parameters than the launch's, or one whose build
+    // failed, is refused: its chunks are coded as empty (the workspace stays consistent for
+    // the placement) and the call fails
     const bool mismatch = sg->tab && (sg->tab[kDTK] != a.h.K || sg->tab[kDTLog2L] != a.h.R);
+    const bool unusable = sg->tab && sg->tab[kDTStatus] != 0;
     uint32_t nc = 0;
-    if (chunk < n_chunks && !mismatch) {
+    if (chunk < n_chunks && !mismatch && !unusable) {
         const uint64_t first = (uint64_t)chunk * a.h.C;
         nc = (uint32_t)((n - first) < a.h.C ? (n - first) : a.h.C);
     }
     const uint32_t lanes = nc < 32 ? nc : 32;
     const uint32_t nc_lo = __builtin_amdgcn_readlane(nc, 0), nc_hi = __builtin_amdgcn_readlane(nc, 32);
     const uint32_t steps = ((nc_lo > nc_hi ? nc_lo : nc_hi) + 31) >> 5;
-    const uint32_t L = a.h.L, R1 = a.h.R + 1;
 
     // 32 bytes of input tile tl for this lane (32 steps x 32 lanes = 1 KB per tile)
     auto load_tile = [&](uint32_t tl, v4u& p0, v4u& p1) {
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
     uint32_t fmark = a.h.slot_dwords;    // dwords at or above fmark are in the slot
     uint32_t flush_at = (fmark - 128) * 32;  // once P is below this, flush a block
     // every encode entry is OR-ed in; its bit 15 marks a value in a range without states
-    uint32_t bad = sg->tab && sg->tab[kDTStatus] != 0 && nc > 0 ? 0x8000u : 0u;
+    uint32_t bad = 0;
 
     auto flush_block = [&](uint32_t blk) {  // ring dwords [blk, blk + 128) -> slot
         uint32_t* r = &sm[ring + ((blk + 4 * li) & (kERing - 1))];
@@ -188,7 +190,7 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
         else u_nn = value_at(t - 2);
         const uint2 e_n = entry(u_n);
         const uint32_t k = (uint32_t)((int)X + (int)e_c.x) >> R1;
-        const uint32_t sx = es[(e_c.y >> 16) - 512 + (X >> k)];
+        const uint32_t sx = es[(e_c.y >> 16) - kMaxLGpu + (X >> k)];
         const uint32_t w = (e_c.y >> 8) & 15;
         uint32_t field = (e_c.y & 0xFF) | (__builtin_amdgcn_ubfe(X, 0, k) << w);
         uint32_t len = w + k;
@@ -241,8 +243,15 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
     place();  // the first step's fields
     __builtin_amdgcn_s_setprio(0);
     const uint32_t pay = a.h.slot_dwords * 32 - P;  // field bits
-    // the lanes' final states, the decoder's initial states, in front of the fields
-    const uint32_t Pi = P - lanes * a.h.R;
+    // the lanes' final states, the decoder's initial states, in front of the fields.  A
+    // valid encode never exceeds the chunk's bound; the span recorded for the placement is
+    // clamped to it all the same, so that no table, however corrupt, moves the placement
+    // outside the container's bound
+    uint32_t Pi = P - lanes * a.h.R;
+    {
+        const uint32_t top = a.h.slot_dwords * 32, most = 32 * chunk_bound_dwords(nc, a.h.R);
+        if (Pi > top || top - Pi > most) Pi = top - most;
+    }
     ring_or(sm, ring_byte, Pi + li * a.h.R, li < lanes ? X - L : 0u);
     if (nc > 0) {
         while (fmark > (Pi >> 5)) {
@@ -260,9 +269,8 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
     if (tid < 2) a.h.agg[2 * block + tid] = agg_s[tid];
     bad &= 0x8000u;
     if (mismatch) report(a.h.status, SH_ERR_INVALID_ARG, true);
-    report(a.h.status, bad && sg->tab && sg->tab[kDTStatus] != 0 ? SH_ERR_UNSUPPORTED
-                                                              : SH_ERR_SYMBOL_NOT_IN_TABLE,
-           bad != 0);
+    else if (unusable) report(a.h.status, SH_ERR_UNSUPPORTED, chunk < n_chunks);
+    report(a.h.status, SH_ERR_SYMBOL_NOT_IN_TABLE, bad != 0);
 }
 
 // ------------------------------------------------------------------------------------
@@ -435,7 +443,8 @@ sh_status launch_encode(const CodecArgs& a, uint32_t total_blocks, uint32_t tota
     with_kernel_args(a, [&](const auto& k) {
         using K = std::decay_t<decltype(k)>;
         if (total_blocks > 0)
-            hipLaunchKernelGGL(k_encode_chunks<K>, dim3(total_blocks), dim3(kEncBlock), 0, s, k);
+            hipLaunchKernelGGL(k_encode_chunks<K>, dim3(total_blocks), dim3(kEncBlock),
+                               4 * encode_lds_dwords(a.L), s, k);
         if (place) {
             hipLaunchKernelGGL(k_encode_place<K>, dim3(total_blocks_c), dim3(256), 0, s, k);
             return;

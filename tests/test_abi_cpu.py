@@ -118,7 +118,7 @@ def test_argument_checks_are_synchronous():
     assert lib.sh_encode(None, C.byref(p), fake, 100, fake, 1 << 20, fake, 1 << 20, None,
                          None, None) == codec.SH_ERR_INVALID_ARG
     # unsupported parameters
-    for bad in [codec.Params(streams=16), codec.Params(log2_L=9), codec.Params(chunk_symbols=100),
+    for bad in [codec.Params(streams=16), codec.Params(log2_L=12), codec.Params(chunk_symbols=100),
                 codec.Params(chunk_symbols=1 << 17)]:
         pb = bad.c()
         assert lib.sh_encode(C.byref(t), C.byref(pb), fake, 100, fake, 1 << 20, fake, 1 << 20,
@@ -182,7 +182,7 @@ def test_batch_argument_checks_are_synchronous():
     assert need > codec.sh_build_tables_batch_workspace(1) > 0
     assert lib.sh_build_tables_batch(ptrs, n_arr, 3, C.byref(pc), fake, fake, need - 1,
                                      None) == codec.SH_ERR_BUFFER_TOO_SMALL
-    big = codec.Params(log2_L=10).c()
+    big = codec.Params(log2_L=12).c()
     assert lib.sh_build_tables_batch(ptrs, n_arr, 3, C.byref(big), fake, fake, need,
                                      None) == codec.SH_ERR_UNSUPPORTED
     # host table upload: K mismatch is found before any copy
@@ -239,3 +239,21 @@ def test_binding_reuses_and_checks_caller_arrays():
         codec.sh_stats_batch([t, t], out=(codec.sh_stats_t * 1)())
     rec = codec.sh_stats_batch([t], out=(codec.sh_stats_t * 1)())
     assert codec.stats_dicts(rec, 1)[0] == codec.sh_stats(t)
+
+
+def test_inline_tables_and_long_fields_are_refused():
+    """Single-tensor calls carry their tables in the launch (at most 256 states); larger
+    tables go through device tables.  A table whose longest field exceeds 16 bits is refused
+    by the GPU path.  All checked on the host, before any GPU work."""
+    lib = codec.lib()
+    fake = 1 << 20
+    p9 = codec.Params(log2_L=9)
+    t9 = codec.sh_table_from_histogram(O.histogram(D.tiny()), p9)
+    assert lib.sh_encode(C.byref(t9), C.byref(p9.c()), fake, 100, fake, 1 << 20, fake, 1 << 20,
+                         None, None, None) == codec.SH_ERR_UNSUPPORTED
+    assert lib.sh_decode(C.byref(t9), C.byref(p9.c()), fake, 1 << 20, fake, 100, None,
+                         None) == codec.SH_ERR_UNSUPPORTED
+    p11 = codec.Params(log2_L=11)
+    tu = codec.sh_table_from_histogram(O.histogram(D.uniform_exact(40)), p11)
+    assert lib.sh_table_to_device(C.byref(tu), C.byref(p11.c()), fake, None) == codec.SH_ERR_UNSUPPORTED
+    assert codec.sh_encode_bound(1000, p11) > 0
