@@ -31,7 +31,10 @@
  *   R5  bitstream: chunks of C symbols, S interleaved lanes (symbol i of a chunk goes
  *       to lane i mod S, step i div S), one tANS state per lane; each chunk is a
  *       little-endian LSB-first bit string of the lanes' initial states followed by
- *       the fields in (step, lane) order, padded with zeros to whole 32-bit words.
+ *       the fields in (step, lane) order, padded with zeros to a whole number of size
+ *       units (a unit is 2^u bytes, the smallest that lets every chunk's size fit 16
+ *       bits; one byte at the pages' parameters).  Chunks follow each other byte by byte;
+ *       the index holds every chunk's size in units and, every 64 chunks, a 32-bit offset.
  *       A field is the offset in its low w_s bits with the state bits above it.
  */
 #include "shannonic_oracle.h"
@@ -334,7 +337,7 @@ int orc_slot_tables(const uint16_t* freq, int K, int log2_L, uint16_t* slot_rang
 /*
  * Byte layout (all integers little-endian):
  *   0   "SHN1"          magic
- *   4   u8  version     1
+ *   4   u8  version     3
  *   5   u8  R           log2 of the number of tANS states L
  *   6   u16 K           number of ranges
  *   8   u64 n           number of symbols
@@ -345,8 +348,15 @@ int orc_slot_tables(const uint16_t* freq, int K, int log2_L, uint16_t* slot_rang
  *   32  u16 freq[K]     state counts f_k (sum L; all 0 only when n = 0)
  *   32+2K u8 lo[1..K-1] range starts (lo[0] = 0, lo[K] = 256 are implied)
  *   zero padding up to index_at = 4 * ceil((32 + 3K - 1) / 4)
- *   index_at: u32 off[n_chunks + 1], byte offsets of the chunks from the payload start
- *   payload: the chunks, each a whole number of 32-bit words
+ *   index_at: u32 goff[G + 1], G = ceil(n_chunks / 64): byte offset, from the payload
+ *             start, of chunk 64g; goff[G] = the payload's size in bytes
+ *             then u16 size[n_chunks], every chunk's size in units, then a zero u16 when
+ *             n_chunks is odd
+ *   payload: the chunks back to back (chunk c starts at goff[c / 64] plus the sizes of
+ *            the chunks before it in its group of 64), then zero bytes up to a multiple
+ *            of 4 bytes (the container's end)
+ * The unit is 2^u bytes, u the smallest with ceil(B / 2^u) <= 65535 where B is the largest
+ * chunk a valid stream can hold (chunk_bound_bytes of a whole chunk).
  */
 
 static uint64_t header_bytes(int K) { return ((uint64_t)(32 + 3 * K - 1) + 3) / 4 * 4; }
@@ -386,23 +396,40 @@ static uint64_t read_bits(const uint8_t* buf, uint64_t pos, int len)
 }
 
 /* the largest chunk a valid stream can hold: every field at its longest, 8 + R bits */
-static uint64_t chunk_bound_bytes(uint64_t nc, int log2_L, uint32_t S)
+static uint64_t chunk_bound_bits(uint64_t nc, int log2_L, uint32_t S)
 {
     uint64_t lanes = nc < S ? nc : S;
-    uint64_t bits = lanes * (uint64_t)log2_L + nc * (uint64_t)(8 + log2_L);
-    return (bits + 31) / 32 * 4;
+    return lanes * (uint64_t)log2_L + nc * (uint64_t)(8 + log2_L);
+}
+
+/* log2 of the size unit in bytes: the smallest u with ceil(B / 2^u) <= 65535, B the bound
+ * of a whole chunk in bytes */
+static int unit_log2(uint32_t C, int log2_L, uint32_t S)
+{
+    uint64_t B = (chunk_bound_bits(C, log2_L, S) + 7) / 8;
+    int u = 0;
+    while ((B + ((uint64_t)1 << u) - 1) >> u > 65535) u++;
+    return u;
+}
+
+/* bytes of the index: goff[G + 1] and size[n_chunks], padded to 4 bytes */
+static uint64_t index_bytes(uint64_t nch)
+{
+    uint64_t groups = (nch + 63) / 64;
+    return 4 * (groups + 1) + (2 * nch + 3) / 4 * 4;
 }
 
 uint64_t orc_container_bound(uint64_t n, int K, int log2_L, uint32_t C, uint32_t S)
 {
     if (C == 0 || S == 0) return 0;
     uint64_t nch = (n + C - 1) / C;
-    uint64_t total = header_bytes(K) + 4 * (nch + 1);
+    uint64_t unit = (uint64_t)1 << unit_log2(C, log2_L, S);
+    uint64_t total = 0;
     for (uint64_t c = 0; c < nch; c++) {
         uint64_t nc = (c + 1 < nch) ? C : n - c * (uint64_t)C;
-        total += chunk_bound_bytes(nc, log2_L, S);
+        total += (chunk_bound_bits(nc, log2_L, S) + 8 * unit - 1) / (8 * unit) * unit;
     }
-    return total;
+    return header_bytes(K) + index_bytes(nch) + (total + 3) / 4 * 4;
 }
 
 /* range of value u: the k with lo[k] <= u < lo[k+1] */
@@ -447,8 +474,10 @@ int orc_encode(const int8_t* x, uint64_t n, int K, int log2_L, const uint16_t* l
     const uint64_t nch = (n + C - 1) / C;
     if (nch > 0xFFFFFFFEull) return ORC_ERR_UNSUPPORTED;
     const uint64_t bound = orc_container_bound(n, K, log2_L, C, S);
-    if (bound - header_bytes(K) - 4 * (nch + 1) > 0xFFFFFFFFull) return ORC_ERR_UNSUPPORTED;
-    if (cap < header_bytes(K) + 4 * (nch + 1)) return ORC_ERR_SMALL;
+    if (bound - header_bytes(K) - index_bytes(nch) > 0xFFFFFFFFull) return ORC_ERR_UNSUPPORTED;
+    if (cap < header_bytes(K) + index_bytes(nch)) return ORC_ERR_SMALL;
+    const int ul = unit_log2(C, log2_L, S);
+    const uint64_t unit = (uint64_t)1 << ul;
 
     uint16_t slot_range[4096], slot_next[4096], enc_slot[4096];
     uint8_t slot_nb[4096];
@@ -467,7 +496,7 @@ int orc_encode(const int8_t* x, uint64_t n, int K, int log2_L, const uint16_t* l
     out[1] = 'H';
     out[2] = 'N';
     out[3] = '1';
-    out[4] = 2;
+    out[4] = 3;
     out[5] = (uint8_t)log2_L;
     put_u16(out + 6, (uint64_t)K);
     put_u64(out + 8, n);
@@ -478,10 +507,11 @@ int orc_encode(const int8_t* x, uint64_t n, int K, int log2_L, const uint16_t* l
     for (int k = 0; k < K; k++) put_u16(out + 32 + 2 * k, freq[k]);
     for (int k = 1; k < K; k++) out[32 + 2 * K + (k - 1)] = (uint8_t)lo[k];
 
-    uint8_t* index = out + hb;
-    uint64_t payload_at = hb + 4 * (nch + 1);
+    uint8_t* goff = out + hb;                      /* u32 per group of 64 chunks, + 1 */
+    uint8_t* sizes = goff + 4 * ((nch + 63) / 64 + 1);  /* u16 per chunk */
+    uint64_t payload_at = hb + index_bytes(nch);
     uint64_t off = 0, fields_total = 0;
-    put_u32(index, 0);
+    memset(goff, 0, index_bytes(nch));
 
     uint64_t* field = (uint64_t*)malloc(sizeof(uint64_t) * (size_t)(C ? C : 1));
     int* flen = (int*)malloc(sizeof(int) * (size_t)(C ? C : 1));
@@ -525,7 +555,8 @@ int orc_encode(const int8_t* x, uint64_t n, int K, int log2_L, const uint16_t* l
         /* lay the chunk out in decoding order */
         uint64_t bits = lanes * (uint64_t)log2_L;
         for (uint64_t i = 0; i < nc; i++) bits += (uint64_t)flen[i];
-        uint64_t bytes = (bits + 31) / 32 * 4;
+        uint64_t units = (bits + 8 * unit - 1) / (8 * unit);
+        uint64_t bytes = units * unit;
         if (payload_at + off + bytes > cap) {
             st = ORC_ERR_SMALL;
             break;
@@ -542,8 +573,18 @@ int orc_encode(const int8_t* x, uint64_t n, int K, int log2_L, const uint16_t* l
             pos += (uint64_t)flen[i];
             fields_total += (uint64_t)flen[i];
         }
+        if (c % 64 == 0) put_u32(goff + 4 * (c / 64), off);
+        put_u16(sizes + 2 * c, units);
         off += bytes;
-        put_u32(index + 4 * (c + 1), off);
+    }
+    if (st == ORC_OK) {
+        put_u32(goff + 4 * ((nch + 63) / 64), off);
+        uint64_t padded = (off + 3) / 4 * 4;       /* the container ends on 4 bytes */
+        if (payload_at + padded > cap) st = ORC_ERR_SMALL;
+        else {
+            memset(out + payload_at + off, 0, padded - off);
+            off = padded;
+        }
     }
     free(field);
     free(flen);
@@ -559,13 +600,15 @@ int orc_encode(const int8_t* x, uint64_t n, int K, int log2_L, const uint16_t* l
  * gives the range s and the state bit count; the field's low w_s bits are the offset o
  * and x = base[s] + o.  A lane's last field is the offset alone (its state bits are
  * zero, implied).  A stream is valid only if the header is consistent, every offset lies
- * inside its range, every lane ends in slot 0 (the encoder's start state) and every
- * chunk's bits end in its last 32-bit word with zero padding after them.
+ * inside its range, every lane ends in slot 0 (the encoder's start state), every chunk's
+ * bits end in its last size unit with zero padding after them, every group offset equals
+ * the one before it plus the sizes of the group's chunks, and the container ends right
+ * after the payload's zero padding to 4 bytes.
  */
 int orc_decode(const uint8_t* in, uint64_t nbytes, int8_t* y, uint64_t n)
 {
     if (nbytes < 32) return ORC_ERR_CORRUPT;
-    if (in[0] != 'S' || in[1] != 'H' || in[2] != 'N' || in[3] != '1' || in[4] != 2)
+    if (in[0] != 'S' || in[1] != 'H' || in[2] != 'N' || in[3] != '1' || in[4] != 3)
         return ORC_ERR_CORRUPT;
     int R = in[5];
     int K = (int)get_le(in + 6, 2);
@@ -575,7 +618,7 @@ int orc_decode(const uint8_t* in, uint64_t nbytes, int8_t* y, uint64_t n)
     if (hn != n) return ORC_ERR_INVALID;
     if (R < 1 || R > 12 || K < 1 || K > 256 || C == 0 || S == 0 || S > C) return ORC_ERR_CORRUPT;
     if (hb != header_bytes(K) || nch != (n + C - 1) / C) return ORC_ERR_CORRUPT;
-    if (nbytes < hb + 4 * (nch + 1)) return ORC_ERR_CORRUPT;
+    if (nbytes < hb + index_bytes(nch)) return ORC_ERR_CORRUPT;
     uint16_t lo[257], freq[256];
     lo[0] = 0;
     lo[K] = 256;
@@ -591,20 +634,35 @@ int orc_decode(const uint8_t* in, uint64_t nbytes, int8_t* y, uint64_t n)
     if (n > 0 && orc_slot_tables(freq, K, R, slot_range, slot_nb, slot_next, enc_slot) != ORC_OK)
         return ORC_ERR_CORRUPT;
 
-    const uint8_t* index = in + hb;
-    uint64_t payload_at = hb + 4 * (nch + 1);
-    if (get_le(index, 4) != 0) return ORC_ERR_CORRUPT;
-    if (payload_at + get_le(index + 4 * nch, 4) != nbytes) return ORC_ERR_CORRUPT;
+    const uint64_t groups = (nch + 63) / 64;
+    const uint8_t* goff = in + hb;
+    const uint8_t* sizes = goff + 4 * (groups + 1);
+    const uint64_t unit = (uint64_t)1 << unit_log2((uint32_t)C, R, (uint32_t)S);
+    uint64_t payload_at = hb + index_bytes(nch);
+    if (get_le(goff, 4) != 0) return ORC_ERR_CORRUPT;
+    for (uint64_t g = 0; g < groups; g++) {  /* every group offset follows from the sizes */
+        uint64_t sum = 0;
+        for (uint64_t c = 64 * g; c < nch && c < 64 * g + 64; c++) sum += unit * get_le(sizes + 2 * c, 2);
+        if (get_le(goff + 4 * g, 4) + sum != get_le(goff + 4 * (g + 1), 4)) return ORC_ERR_CORRUPT;
+    }
+    if (nch % 2 && get_le(sizes + 2 * nch, 2) != 0) return ORC_ERR_CORRUPT;
+    const uint64_t payload = get_le(goff + 4 * groups, 4);
+    if (payload_at + (payload + 3) / 4 * 4 != nbytes) return ORC_ERR_CORRUPT;
+    for (uint64_t b = payload_at + payload; b < nbytes; b++)
+        if (in[b]) return ORC_ERR_CORRUPT;
 
     uint64_t* X = (uint64_t*)malloc(sizeof(uint64_t) * (size_t)S);
     if (!X) return ORC_ERR_INVALID;
     int st = ORC_OK;
+    uint64_t a = 0;  /* the chunk's first byte */
     for (uint64_t c = 0; c < nch && st == ORC_OK; c++) {
-        uint64_t a = get_le(index + 4 * c, 4), b = get_le(index + 4 * (c + 1), 4);
+        if (c % 64 == 0) a = get_le(goff + 4 * (c / 64), 4);
+        const uint64_t units = get_le(sizes + 2 * c, 2);
+        uint64_t b = a + unit * units;
         uint64_t first = c * C;
         uint64_t nc = (c + 1 < nch) ? C : n - first;
         uint64_t lanes = nc < S ? nc : S;
-        if (b < a || (b - a) % 4 != 0 || b - a > chunk_bound_bytes(nc, R, (uint32_t)S)) {
+        if (units > (chunk_bound_bits(nc, R, (uint32_t)S) + 8 * unit - 1) / (8 * unit)) {
             st = ORC_ERR_CORRUPT;
             break;
         }
@@ -642,9 +700,10 @@ int orc_decode(const uint8_t* in, uint64_t nbytes, int8_t* y, uint64_t n)
         if (st != ORC_OK) break;
         for (uint64_t l = 0; l < lanes; l++)
             if (X[l] != L) st = ORC_ERR_CORRUPT;
-        if ((pos + 31) / 32 * 4 != b - a) st = ORC_ERR_CORRUPT;
+        if ((pos + 8 * unit - 1) / (8 * unit) != units) st = ORC_ERR_CORRUPT;
         for (uint64_t p = pos; p < avail && st == ORC_OK; p++)
             if (read_bits(chunk, p, 1)) st = ORC_ERR_CORRUPT;
+        a = b;
     }
     free(X);
     return st;
