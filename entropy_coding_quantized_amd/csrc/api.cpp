@@ -35,16 +35,22 @@ sh_status check_params(const sh_params* p) {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-// container bytes at most
+// the container's first payload byte: header, then the chunk index
+uint64_t payload_at_of(uint64_t nch, const sh_params* p) {
+    return header_bytes(p->K) + index_bytes_of(nch);
+}
+
+// container bytes at most: every chunk at its bound, in whole size units
 uint64_t bound_of(uint64_t n, const sh_params* p) {
     const uint64_t nch = n_chunks_of(n, p->chunk_symbols);
-    uint64_t total = header_bytes(p->K) + 4 * (nch + 1);
+    const uint32_t u = size_unit_log2(p->chunk_symbols, p->log2_L);
+    uint64_t payload = 0;
     if (nch > 0) {
-        total += 4ull * chunk_bound_dwords(p->chunk_symbols, p->log2_L) * (nch - 1);
+        payload += ((uint64_t)chunk_bound_units(p->chunk_symbols, p->log2_L, u) << u) * (nch - 1);
         const uint64_t last = n - (nch - 1) * p->chunk_symbols;
-        total += 4ull * chunk_bound_dwords((uint32_t)last, p->log2_L);
+        payload += (uint64_t)chunk_bound_units((uint32_t)last, p->log2_L, u) << u;
     }
-    return total;
+    return payload_at_of(nch, p) + (payload + 3) / 4 * 4;
 }
 
 uint32_t blocks_for(uint64_t nch, uint32_t per) { return (uint32_t)((nch + per - 1) / per); }
@@ -109,7 +115,7 @@ sh_status hip_ok(hipError_t e) { return e == hipSuccess ? SH_OK : SH_ERR_HIP; }
 
 extern "C" {
 
-uint32_t sh_version(void) { return (1u << 16) | 2u; }
+uint32_t sh_version(void) { return (1u << 16) | 3u; }
 
 const char* sh_status_string(sh_status st) {
     switch (st) {
@@ -356,8 +362,7 @@ sh_status sh_decode(const sh_table* table, const sh_params* params, const uint8_
     if (n >= (1ull << 32) || in_nbytes > 0xFFFFFFFFull) return SH_ERR_UNSUPPORTED;
     if (!aligned(d_in, 4) || !aligned(d_status, 4)) return SH_ERR_INVALID_ARG;
     const uint64_t nch = n_chunks_of(n, params->chunk_symbols);
-    const uint64_t payload_at = header_bytes(params->K) + 4 * (nch + 1);
-    if (in_nbytes < payload_at) return SH_ERR_CORRUPT_STREAM;
+    if (in_nbytes < payload_at_of(nch, params)) return SH_ERR_CORRUPT_STREAM;
     if (n == 0) return SH_OK;
 
     CodecArgs a;
@@ -451,7 +456,7 @@ sh_status sh_decode_batch(const void* d_tables, const uint8_t* const* d_in,
         if (!d_in[i] || !aligned(d_in[i], 4) || (n[i] > 0 && !d_y[i])) return SH_ERR_INVALID_ARG;
         if (n[i] >= (1ull << 32) || in_nbytes[i] > 0xFFFFFFFFull) return SH_ERR_UNSUPPORTED;
         const uint64_t nch = n_chunks_of(n[i], params->chunk_symbols);
-        if (in_nbytes[i] < header_bytes(params->K) + 4 * (nch + 1)) return SH_ERR_CORRUPT_STREAM;
+        if (in_nbytes[i] < payload_at_of(nch, params)) return SH_ERR_CORRUPT_STREAM;
     }
     for (auto [b, e] : groups_of(nseg)) {
         CodecArgs a;
@@ -497,7 +502,7 @@ sh_status sh_decode_matvec_batch(const void* d_tables, const uint8_t* const* d_i
             return SH_ERR_INVALID_ARG;
         if (n[i] >= (1ull << 32) || in_nbytes[i] > 0xFFFFFFFFull) return SH_ERR_UNSUPPORTED;
         const uint64_t nch = n_chunks_of(n[i], params->chunk_symbols);
-        if (in_nbytes[i] < header_bytes(params->K) + 4 * (nch + 1)) return SH_ERR_CORRUPT_STREAM;
+        if (in_nbytes[i] < payload_at_of(nch, params)) return SH_ERR_CORRUPT_STREAM;
     }
     for (auto [b, e] : groups_of(nseg)) {
         CodecArgs a;
@@ -549,7 +554,7 @@ sh_status sh_decode_stream(const void* d_tables, const uint8_t* const* h_in,
         if (n[i] >= (1ull << 32) || in_nbytes[i] > 0xFFFFFFFFull) return SH_ERR_UNSUPPORTED;
         if (in_nbytes[i] > slot_bytes) return SH_ERR_BUFFER_TOO_SMALL;
         const uint64_t nch = n_chunks_of(n[i], params->chunk_symbols);
-        if (in_nbytes[i] < header_bytes(params->K) + 4 * (nch + 1)) return SH_ERR_CORRUPT_STREAM;
+        if (in_nbytes[i] < payload_at_of(nch, params)) return SH_ERR_CORRUPT_STREAM;
     }
     hipStream_t cs = (hipStream_t)copy_stream, ds = (hipStream_t)stream;
     std::vector<hipEvent_t> copied(depth, nullptr), freed(depth, nullptr);

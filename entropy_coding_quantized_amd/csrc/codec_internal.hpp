@@ -58,15 +58,40 @@ inline uint32_t floor_log2_u32(uint32_t x) {
     return e;
 }
 
-// ---- container geometry ------------------------------------------------------------
+// ---- container geometry (version 3) ---------------------------------------------------
+// Chunks follow each other byte by byte, each padded to a whole number of size units of
+// 2^u bytes, u the smallest that lets the size of the largest chunk a valid stream holds
+// fit 16 bits (u = 0 for C up to 34,937 at log2 L = 7; at most 2 on the GPU path).
+// The index after the header: u32 goff[G + 1], G = ceil(n_chunks / 64) (the payload byte
+// of chunk 64g; goff[G] = the payload's size), then u16 size[n_chunks] in units, then a
+// zero u16 when n_chunks is odd.  The payload ends with zero bytes up to a multiple of 4.
+constexpr uint32_t kGroupChunks = 64;
 inline uint32_t header_bytes(uint32_t K) { return (kHeaderFixed + 3 * K - 1 + 3) / 4 * 4; }
 inline uint64_t n_chunks_of(uint64_t n, uint32_t C) { return (n + C - 1) / C; }
-// largest chunk a valid stream holds: every field at 8 + R bits, padded to 32-bit words
-SHN_HD inline uint32_t chunk_bound_dwords(uint32_t nc, uint32_t R) {
-    uint64_t lanes = nc < (uint32_t)kLanes ? nc : (uint32_t)kLanes;
-    uint64_t bits = lanes * R + (uint64_t)nc * (8 + R);
-    return (uint32_t)((bits + 31) / 32);
+// bits of the largest chunk of nc values a valid stream holds: every field at 8 + R bits
+SHN_HD inline uint64_t chunk_bound_bits(uint32_t nc, uint32_t R) {
+    const uint64_t lanes = nc < (uint32_t)kLanes ? nc : (uint32_t)kLanes;
+    return lanes * R + (uint64_t)nc * (8 + R);
 }
+// ... in 32-bit words (the encoder's per-chunk workspace slots)
+SHN_HD inline uint32_t chunk_bound_dwords(uint32_t nc, uint32_t R) {
+    return (uint32_t)((chunk_bound_bits(nc, R) + 31) / 32);
+}
+SHN_HD inline uint32_t size_unit_log2(uint32_t C, uint32_t R) {
+    const uint64_t most = (chunk_bound_bits(C, R) + 7) / 8;
+    uint32_t u = 0;
+    while (((most + (1ull << u) - 1) >> u) > 0xFFFFull) ++u;
+    return u;
+}
+SHN_HD inline uint32_t chunk_bound_units(uint32_t nc, uint32_t R, uint32_t u) {
+    return (uint32_t)((chunk_bound_bits(nc, R) + (8ull << u) - 1) >> (3 + u));
+}
+SHN_HD inline uint32_t n_groups_of(uint32_t nch) { return (nch + kGroupChunks - 1) / kGroupChunks; }
+// bytes of the index, and where its sizes start (relative to index_at)
+SHN_HD inline uint64_t index_bytes_of(uint64_t nch) {
+    return 4 * ((nch + kGroupChunks - 1) / kGroupChunks + 1) + (2 * nch + 3) / 4 * 4;
+}
+SHN_HD inline uint32_t sizes_rel_of(uint32_t nch) { return 4 * (n_groups_of(nch) + 1); }
 void write_header(const sh_table& t, uint64_t n, uint32_t C, uint32_t S, uint64_t n_chunks,
                   uint32_t* dwords /* kMaxHeaderDwords */);
 

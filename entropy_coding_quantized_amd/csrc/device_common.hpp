@@ -30,6 +30,14 @@ __device__ __forceinline__ uint32_t scan32(uint32_t v) {
     return v;
 }
 
+// Inclusive prefix sum over the whole wavefront: scan32, then lane 31 added into rows 2
+// and 3 (DPP row_bcast:31).
+__device__ __forceinline__ uint32_t scan64(uint32_t v) {
+    v = scan32(v);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false); // row_bcast:31
+    return v;
+}
+
 // Value of lane 31 of this lane's 32-lane half (ds_swizzle bit mode, or_mask = 31).
 __device__ __forceinline__ uint32_t bcast31(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x3E0);
@@ -162,6 +170,62 @@ inline HistArgsN<N> hist_args(const HistArgs& h) {
 
 __device__ __forceinline__ uint32_t header_bytes_dev(uint32_t K) {
     return (kHeaderFixed + 3 * K - 1 + 3) / 4 * 4;
+}
+
+// Where the chunks of one group of kGroupChunks (64) lie in a container (the chunk index of
+// version 3): lane i of the wavefront gets chunk 64 g + i's first byte after the group's
+// first chunk (rel) and its size in bytes (0 past the last chunk); head is the group's
+// offset from the payload start.  ok: the next group's offset (the payload's size after the
+// last group) is this one's plus the sizes of its chunks.  Every lane takes part.
+struct GroupSpans {
+    uint32_t head, rel, bytes;
+    bool ok;
+};
+__device__ __forceinline__ GroupSpans group_spans(rsrc_t rin, uint32_t index_at, uint32_t n_chunks,
+                                                  uint32_t g, uint32_t unit_log2) {
+    const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const uint32_t c = g * kGroupChunks + lane;
+    const uint32_t sizes_at = index_at + sizes_rel_of(n_chunks);
+    const uint32_t units = c < n_chunks
+        ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rin, (int)(sizes_at + 2 * c), 0, 0) : 0u;
+    const uint32_t head = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)(index_at + 4 * g), 0, 0);
+    const uint32_t next = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)(index_at + 4 * g + 4), 0, 0);
+    const uint32_t incl = scan64(units);  // at most 64 * 65535 units
+    const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
+    GroupSpans s;
+    s.head = head;
+    s.rel = (incl - units) << unit_log2;
+    s.bytes = units << unit_log2;
+    s.ok = (uint64_t)head + ((uint64_t)total << unit_log2) == next;
+    return s;
+}
+
+// The lane's value taken from lane src of the wavefront (ds_bpermute).
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, uint32_t src) {
+    return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(src << 2), (int)v);
+}
+
+// Checks of a version-3 index that no single chunk makes: the first group starts at 0, the
+// payload ends within in_nbytes and is padded with zero bytes to 4, and an odd number of
+// sizes is followed by a zero u16.  True when all hold.  Every lane takes part.
+__device__ __forceinline__ bool index_ends_ok(rsrc_t rin, uint32_t index_at, uint32_t payload_at,
+                                              uint32_t n_chunks, uint64_t in_nbytes) {
+    const uint32_t first = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)index_at, 0, 0);
+    const uint32_t pay = __builtin_amdgcn_raw_buffer_load_b32(
+        rin, (int)(index_at + 4 * n_groups_of(n_chunks)), 0, 0);
+    const uint64_t end = (uint64_t)payload_at + ((uint64_t)pay + 3) / 4 * 4;
+    bool ok = first == 0 && end <= in_nbytes;
+    if (ok && (pay & 3)) {  // the pad bytes after the payload's last byte
+        const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(
+            rin, (int)(payload_at + (pay & ~3u)), 0, 0);
+        ok = (w >> (8 * (pay & 3))) == 0;
+    }
+    if (n_chunks & 1) {
+        const uint32_t pad = __builtin_amdgcn_raw_buffer_load_b16(
+            rin, (int)(index_at + sizes_rel_of(n_chunks) + 2 * n_chunks), 0, 0);
+        ok = ok && pad == 0;
+    }
+    return ok;
 }
 
 }  // namespace shn

@@ -689,14 +689,14 @@ __global__ __launch_bounds__(kBuildBlock) void k_build_tables(const BuildArgs a)
     for (uint32_t k = tid; k < 256; k += kBuildBlock) f16[k] = k < K ? (uint16_t)freq_s[k] : 0;
     if (tid < 256) reinterpret_cast<uint64_t*>(dt + kDTHist)[tid] = h_mine;
     const uint32_t hbytes = (kHeaderFixed + 3 * K - 1 + 3) / 4 * 4;
-    // header template: the fixed 32 bytes ("SHN1", version 2, log2 L, K, n = 0, C, S,
+    // header template: the fixed 32 bytes ("SHN1", version 3, log2 L, K, n = 0, C, S,
     // n_chunks = 0, header bytes), then freq[k] as u16 and lo[1..K-1] as bytes.  Every byte
     // is computed without branches (both table reads are made, one is kept), so that the
     // lanes of a wavefront do not serialise over the cases.
     for (uint32_t d = tid; d < kMaxHeaderDwords; d += kBuildBlock) {
         uint32_t word = 0;
         if (d < kHeaderFixed / 4) {
-            word = d == 0 ? 0x314E4853u : d == 1 ? 2u | (R << 8) | ((K & 0xFFFFu) << 16)
+            word = d == 0 ? 0x314E4853u : d == 1 ? 3u | (R << 8) | ((K & 0xFFFFu) << 16)
                  : d == 4 ? a.C : d == 5 ? a.S : d == 7 ? hbytes : 0u;
         } else {
 #pragma unroll

@@ -60,6 +60,7 @@ typedef const __attribute__((address_space(3))) v2u lds_v2u;
 // Per-chunk decoder state of one half wavefront.
 struct DecChain {
     uint32_t nc, cdw, cbyte, ring, ring_byte, rot, lanes, pos, addr, res_hi, refill_at, err, vout;
+    uint32_t bit0, end;  // the chunk's first bit in its first dword; its end (ring bits)
     v4u pf;
 };
 
@@ -212,6 +213,7 @@ template <int ILP, class Sink, class A>
 __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
     static_assert(Sink::kBytes || ILP == 1, "a consumer sink takes one chunk per half wavefront");
     constexpr uint32_t kChunksPerWave = 2 * ILP;
+    static_assert(kGroupChunks % kChunksPerWave == 0, "a wavefront's chunks lie in one index group");
     constexpr uint32_t kChunksPerBlock = kDecBlock / 64 * kChunksPerWave;
     constexpr uint32_t kVecAt = kTabDwords + kChunksPerBlock * kRingStride;
     // the rings' wrapped addresses are formed with an and-or, which needs every ring on a
@@ -230,24 +232,20 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
     const uint32_t n_chunks = sg->n_chunks;
     const uint64_t n = sg->n;
     const uint32_t index_at = header_bytes_dev(a.h.K);
-    const uint32_t payload_at = index_at + 4 * (n_chunks + 1);
+    const uint32_t payload_at = index_at + (uint32_t)index_bytes_of(n_chunks);
+    const uint32_t ulog = size_unit_log2(a.h.C, a.h.R);  // chunk sizes count 2^ulog bytes
     const uint64_t in_nbytes = sg->c_bytes;
 
     // The prologue's loads go out in two waves: first everything that needs nothing else
-    // (each lane's pair of chunk-index entries and its table slot), then, once the index is
-    // in, the chunk's first payload words; LDS is written only after both waves are issued.
+    // (the table slot of each thread and the chunk sizes of the wavefront's index group),
+    // then, once the index is in, the chunk's first payload words; LDS is written only after
+    // both waves are issued.
     const rsrc_t rin = make_rsrc(sg->c, (uint32_t)in_nbytes);
     const uint32_t group = kChunksPerWave * wid;
-    v2u idx[ILP];
-#pragma unroll
-    for (int k = 0; k < ILP; ++k) {
-        const uint32_t chunk = group + 2 * k + hw;
-        idx[k] = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(
-                                             rin, (int)(index_at + 4 * (chunk < n_chunks ? chunk : 0)), 0, 0));
-    }
     // L <= 256 = kDecBlock: one slot per thread; threads past L repeat the last slot
     const uint32_t ts = tid < a.h.L ? tid : a.h.L - 1;
     const uint32_t te0 = dec[2 * ts], te1 = dec[2 * ts + 1];
+    const GroupSpans gs = group_spans(rin, index_at, n_chunks, group / kGroupChunks, ulog);
 
     // output: per-wavefront descriptor over the wavefront's chunks
     const uint64_t grp_first = (uint64_t)group * a.h.C;
@@ -278,17 +276,22 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
         c.cdw = 0;
         c.cbyte = 0;
         c.err = 0;
+        c.bit0 = 0;
+        c.end = 0;
+        const uint32_t c_rel = lane_value(gs.rel, chunk % kGroupChunks);
+        const uint32_t c_bytes = lane_value(gs.bytes, chunk % kGroupChunks);
         if (chunk < n_chunks) {
-            const uint32_t o0 = idx[k][0], o1 = idx[k][1];
             const uint64_t first = (uint64_t)chunk * a.h.C;
             const uint32_t m = (uint32_t)((n - first) < a.h.C ? (n - first) : a.h.C);
-            const bool ok = o0 <= o1 && ((o0 | o1) & 3) == 0 &&
-                            (o1 - o0) <= 4 * chunk_bound_dwords(m, a.h.R) &&
-                            (uint64_t)payload_at + o1 <= in_nbytes;
+            const uint64_t at = (uint64_t)payload_at + gs.head + c_rel;  // the chunk's first byte
+            const bool ok = gs.ok && (c_bytes >> ulog) <= chunk_bound_units(m, a.h.R, ulog) &&
+                            at + c_bytes <= in_nbytes;
             if (ok) {
                 c.nc = m;
-                c.cdw = (o1 - o0) >> 2;
-                c.cbyte = payload_at + o0;
+                c.bit0 = 8 * ((uint32_t)at & 3);
+                c.cbyte = (uint32_t)at & ~3u;
+                c.cdw = (c.bit0 + 8 * c_bytes + 31) >> 5;
+                c.end = c.bit0 + 8 * c_bytes + 32 * c.rot;
             } else {
                 c.err = 1;
             }
@@ -317,9 +320,7 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
             hv[r] = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)(4 * j), 0, 0);
             tv[r] = hdr[j];
         }
-        const uint32_t first = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)index_at, 0, 0);
-        const uint32_t last = __builtin_amdgcn_raw_buffer_load_b32(
-            rin, (int)(index_at + 4 * n_chunks), 0, 0);
+        const bool ends_ok = index_ends_ok(rin, index_at, payload_at, n_chunks, in_nbytes);
         bool bad = sg->tab && (sg->tab[kDTStatus] != 0 ||
                                (n > 0 && (sg->tab[kDTN] | sg->tab[kDTN + 1]) == 0));
         // a device table built for other parameters than the launch's
@@ -330,7 +331,7 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
             const uint32_t i = lane + 64 * r;
             if (i < hd) bad |= hv[r] != header_dword_of(tv[r], i, n, n_chunks);
         }
-        bad |= first != 0 || (uint64_t)payload_at + last > in_nbytes;
+        bad |= !ends_ok;
         report(a.h.status, SH_ERR_CORRUPT_STREAM, bad);
     }
 
@@ -355,12 +356,12 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
         // initial slots: lane l's R bits at l * R
         c.addr = tab_byte;  // LDS byte address of the current slot's decode entry
         if (li < c.lanes) {
-            const uint32_t p = li * a.h.R;  // below 32 * 8 bits: no wrap
+            const uint32_t p = c.bit0 + li * a.h.R;  // below 24 + 32 * 8 bits: no wrap
             const uint32_t bits = __builtin_amdgcn_alignbit(sm[c.ring + (p >> 5) + c.rot + 1],
                                                             sm[c.ring + (p >> 5) + c.rot], p);
             c.addr = tab_byte + ((bits & (a.h.L - 1)) << 3);
         }
-        c.pos = c.lanes * a.h.R + 32 * c.rot;  // ring bit position
+        c.pos = c.bit0 + c.lanes * a.h.R + 32 * c.rot;  // ring bit position
         const uint32_t lo = __builtin_amdgcn_readlane(c.nc, 0), hi = __builtin_amdgcn_readlane(c.nc, 32);
         nc_min = nc_min < lo ? nc_min : lo;
         nc_min = nc_min < hi ? nc_min : hi;
@@ -486,7 +487,8 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
     }
     if constexpr (!Sink::kBytes) sink.finish();
 
-    // a valid chunk leaves every lane in slot 0 and ends in its last word, zero-padded
+    // a valid chunk leaves every lane in slot 0 and ends in its last size unit, zero-padded
+    // (a unit of at most 4 bytes never straddles a dword: chunks start on unit boundaries)
     uint32_t err = 0;
 #pragma unroll
     for (int k = 0; k < ILP; ++k) {
@@ -494,9 +496,13 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
         err |= c.err;
         if (c.nc > 0) {
             if (li < c.lanes && c.addr != tab_byte) err = 1;
-            if (((c.pos - 32 * c.rot + 31) >> 5) != c.cdw) err = 1;
-            else if ((c.pos & 31) && (sm[c.ring + ((c.pos >> 5) & (kRing - 1))] >> (c.pos & 31)) != 0)
+            if (c.pos > c.end || c.end - c.pos >= (8u << ulog)) {
                 err = 1;
+            } else if (c.pos < c.end) {
+                const uint32_t gap = c.end - c.pos;
+                const uint32_t pad = sm[c.ring + ((c.pos >> 5) & (kRing - 1))] >> (c.pos & 31);
+                if ((gap < 32 ? pad & ((1u << gap) - 1) : pad) != 0) err = 1;
+            }
         }
     }
     report(a.h.status, SH_ERR_CORRUPT_STREAM, err != 0 || bad_offsets != 0);

@@ -107,6 +107,8 @@ __device__ __forceinline__ uint32_t next_of(const Ent& e) { return e.B >> 16; }
 // the two states).
 struct Row {
     uint32_t nc, cdw, cbyte, ring_byte, pos, res_hi, refill_at, vout;
+    uint32_t end;      // bit position of the chunk's end (its first bit is at bit 0..24 of
+                       // the chunk's first dword, the dword holding its first byte)
     uint32_t tile;     // LDS byte address of this lane's two bytes in step 0 of the tile
     uint32_t sa, sb;   // states of streams 2j and 2j + 1
     v4u pf[kFillVecs]; // the next refill, in flight
@@ -129,18 +131,20 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
     const uint32_t n_chunks = sg->n_chunks;
     const uint64_t n = sg->n;
     const uint32_t index_at = header_bytes_dev(a.h.K);
-    const uint32_t payload_at = index_at + 4 * (n_chunks + 1);
+    const uint32_t payload_at = index_at + (uint32_t)index_bytes_of(n_chunks);
+    const uint32_t ulog = size_unit_log2(a.h.C, R);  // chunk sizes count units of 2^ulog bytes
     const uint64_t in_nbytes = sg->c_bytes;
     const rsrc_t rin = make_rsrc(sg->c, (uint32_t)in_nbytes);
 
-    // loads that need nothing else go out first: the row's pair of index entries and this
-    // thread's table slot
+    // loads that need nothing else go out first: this thread's table slot and the sizes of
+    // the chunks of the wavefront's group of 64 (its four chunks lie in one group)
     const uint32_t group = 4 * wid;                 // the wavefront's first chunk
     const uint32_t chunk = group + row;
-    const v2u idx = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(
-                                                rin, (int)(index_at + 4 * (chunk < n_chunks ? chunk : 0)), 0, 0));
     const uint32_t ts = tid < L ? tid : L - 1;      // slot tid (more below when L > 256)
     const uint32_t te0 = dec[2 * ts], te1 = dec[2 * ts + 1];
+    const GroupSpans gs = group_spans(rin, index_at, n_chunks, group / kGroupChunks, ulog);
+    const uint32_t c_rel = lane_value(gs.rel, chunk % kGroupChunks);
+    const uint32_t c_bytes = lane_value(gs.bytes, chunk % kGroupChunks);
 
     const uint64_t grp_first = (uint64_t)group * a.h.C;
     const uint64_t grp_len = grp_first < n ? n - grp_first : 0;
@@ -157,18 +161,21 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
     r.nc = 0;
     r.cdw = 0;
     r.cbyte = 0;
+    r.end = 0;
+    uint32_t bit0 = 0;  // the chunk's first bit within its first dword
     uint32_t err = 0;
     if (chunk < n_chunks) {
-        const uint32_t o0 = idx[0], o1 = idx[1];
         const uint64_t first = (uint64_t)chunk * a.h.C;
         const uint32_t m = (uint32_t)((n - first) < a.h.C ? (n - first) : a.h.C);
-        const bool ok = o0 <= o1 && ((o0 | o1) & 3) == 0 &&
-                        (o1 - o0) <= 4 * chunk_bound_dwords(m, R) &&
-                        (uint64_t)payload_at + o1 <= in_nbytes;
+        const uint64_t at = (uint64_t)payload_at + gs.head + c_rel;  // the chunk's first byte
+        const bool ok = gs.ok && (c_bytes >> ulog) <= chunk_bound_units(m, R, ulog) &&
+                        at + c_bytes <= in_nbytes;
         if (ok) {
             r.nc = m;
-            r.cdw = (o1 - o0) >> 2;
-            r.cbyte = payload_at + o0;
+            bit0 = 8 * ((uint32_t)at & 3);
+            r.cbyte = (uint32_t)at & ~3u;
+            r.end = bit0 + 8 * c_bytes;
+            r.cdw = (r.end + 31) >> 5;
         } else {
             err = 1;
         }
@@ -201,9 +208,7 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
             hv[k] = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)(4 * jj), 0, 0);
             tv[k] = hdr[jj];
         }
-        const uint32_t first = __builtin_amdgcn_raw_buffer_load_b32(rin, (int)index_at, 0, 0);
-        const uint32_t last = __builtin_amdgcn_raw_buffer_load_b32(
-            rin, (int)(index_at + 4 * n_chunks), 0, 0);
+        const bool ends_ok = index_ends_ok(rin, index_at, payload_at, n_chunks, in_nbytes);
         bool bad = sg->tab && (sg->tab[kDTStatus] != 0 ||
                                (n > 0 && (sg->tab[kDTN] | sg->tab[kDTN + 1]) == 0));
         // a device table built for other parameters than the launch's
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
             const uint32_t i = lane + 64 * k;
             if (i < hd) bad |= hv[k] != header_dword_of(tv[k], i, n, n_chunks);
         }
-        bad |= first != 0 || (uint64_t)payload_at + last > in_nbytes;
+        bad |= !ends_ok;
         report(a.h.status, SH_ERR_CORRUPT_STREAM, bad);
     }
 
@@ -238,19 +243,19 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
     }
     __syncthreads();
 
-    // initial slots: stream s's R bits at s * R (at most 256 bits: within the first ring
-    // words, no wrap)
+    // initial slots: stream s's R bits at bit0 + s * R (at most 376 bits: within the first
+    // ring words, no wrap)
     const uint32_t lanes = r.nc < 32 ? r.nc : 32;
     auto init_state = [&](uint32_t s) {
         if (s >= lanes) return tab_byte;
-        const uint32_t p = s * R;
+        const uint32_t p = bit0 + s * R;
         const lds_u32* w = (const lds_u32*)(uintptr_t)(r.ring_byte + 4 * (p >> 5));
         const uint32_t bits = __builtin_amdgcn_alignbit(w[1], w[0], p);
         return tab_byte + ((bits & (L - 1)) << 3);
     };
     r.sa = init_state(2 * j);
     r.sb = init_state(2 * j + 1);
-    r.pos = lanes * R;
+    r.pos = bit0 + lanes * R;
 
     // steps where every stream of the wavefront's chunks decodes a value that is not its
     // last (every stream's last value lies at or after step nc / 32 - 1); the rest go
@@ -382,15 +387,18 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
         refill();
     }
 
-    // a valid chunk leaves every stream in slot 0 and ends in its last word, zero-padded
+    // a valid chunk leaves every stream in slot 0 and ends in its last size unit, zero-padded
+    // (a unit of at most 4 bytes never straddles a dword: chunks start on unit boundaries)
     if (r.nc > 0) {
         if (2 * j < lanes && r.sa != tab_byte) err = 1;
         if (2 * j + 1 < lanes && r.sb != tab_byte) err = 1;
-        if (((r.pos + 31) >> 5) != r.cdw) {
+        if (r.pos > r.end || r.end - r.pos >= (8u << ulog)) {
             err = 1;
-        } else if (r.pos & 31) {
+        } else if (r.pos < r.end) {
             const lds_u32* w = (const lds_u32*)(uintptr_t)(r.ring_byte + 4 * ((r.pos >> 5) & (kRRing - 1)));
-            if ((*w >> (r.pos & 31)) != 0) err = 1;
+            const uint32_t gap = r.end - r.pos;
+            const uint32_t pad = *w >> (r.pos & 31);
+            if ((gap < 32 ? pad & ((1u << gap) - 1) : pad) != 0) err = 1;
         }
     }
     report(a.h.status, SH_ERR_CORRUPT_STREAM, err != 0 || bad_offsets != 0);

@@ -47,6 +47,11 @@ __device__ __forceinline__ void ring_or(uint32_t* sm, uint32_t ring_byte, uint32
                               __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
+// container bytes of a chunk of the given bits: whole size units of 2^ulog bytes
+__device__ __forceinline__ uint32_t chunk_bytes_of(uint32_t bits, uint32_t ulog) {
+    return ((bits + (8u << ulog) - 1) >> (3 + ulog)) << ulog;
+}
+
 template <class A>
 __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
     extern __shared__ __align__(16) uint32_t sm[];
@@ -249,7 +254,7 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
     // outside the container's bound
     uint32_t Pi = P - lanes * a.h.R;
     {
-        const uint32_t top = a.h.slot_dwords * 32, most = 32 * chunk_bound_dwords(nc, a.h.R);
+        const uint32_t top = a.h.slot_dwords * 32, most = (uint32_t)chunk_bound_bits(nc, a.h.R);
         if (Pi > top || top - Pi > most) Pi = top - most;
     }
     ring_or(sm, ring_byte, Pi + li * a.h.R, li < lanes ? X - L : 0u);
@@ -262,7 +267,7 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
     if (chunk < n_chunks && li == 0) {
         a.h.meta[2 * (sg->slot_base + chunk)] = Pi;
         a.h.meta[2 * (sg->slot_base + chunk) + 1] = pay;
-        atomicAdd(&agg_s[0], 4 * ((a.h.slot_dwords * 32 - Pi + 31) >> 5));
+        atomicAdd(&agg_s[0], chunk_bytes_of(a.h.slot_dwords * 32 - Pi, size_unit_log2(a.h.C, a.h.R)));
         atomicAdd(&agg_s[1], pay);
     }
     __syncthreads();
@@ -271,6 +276,36 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
     if (mismatch) report(a.h.status, SH_ERR_INVALID_ARG, true);
     else if (unusable) report(a.h.status, SH_ERR_UNSUPPORTED, chunk < n_chunks);
     report(a.h.status, SH_ERR_SYMBOL_NOT_IN_TABLE, bad != 0);
+}
+
+// ------------------------------------------------------------------------------------
+// a chunk from its workspace slot to the container: bytes [d0, d1) of the container take the
+// slot's bits from start on, byte d0 + i bits [start + 8i, start + 8i + 8) (bits past the
+// slot's end read 0).  Whole container dwords are stored as dwords, the partial ones at
+// either end byte by byte: the neighbouring chunks own their other bytes.  The 64 lanes of a
+// wavefront share the work.
+// ------------------------------------------------------------------------------------
+__device__ __forceinline__ void move_chunk(const uint32_t* src, uint32_t slot_dwords,
+                                           uint32_t start, uint8_t* c, uint32_t d0, uint32_t d1,
+                                           uint32_t lane) {
+    auto bits32 = [&](uint32_t bit) {  // 32 slot bits from bit on
+        const uint32_t w = bit >> 5;
+        const uint32_t lo = w < slot_dwords ? src[w] : 0u;
+        const uint32_t hi = w + 1 < slot_dwords ? src[w + 1] : 0u;
+        return __builtin_amdgcn_alignbit(hi, lo, bit);
+    };
+    const uint32_t q0 = (d0 + 3) >> 2, q1 = d1 >> 2;       // whole dwords [q0, q1)
+    const uint32_t head_end = 4 * q0 < d1 ? 4 * q0 : d1;    // bytes [d0, head_end)
+    const uint32_t tail_at = 4 * q1 > head_end ? 4 * q1 : head_end;  // bytes [tail_at, d1)
+    uint32_t* cw = reinterpret_cast<uint32_t*>(c);
+    for (uint32_t q = q0 + lane; q < q1; q += 64) cw[q] = bits32(start + 8 * (4 * q - d0));
+    if (lane < 3) {
+        const uint32_t b = d0 + lane;
+        if (b < head_end) c[b] = (uint8_t)bits32(start + 8 * (b - d0));
+    } else if (lane < 6) {
+        const uint32_t b = tail_at + lane - 3;
+        if (b < d1) c[b] = (uint8_t)bits32(start + 8 * (b - d0));
+    }
 }
 
 // ------------------------------------------------------------------------------------
@@ -287,9 +322,12 @@ __global__ __launch_bounds__(kScanBlock) void k_encode_index(const A a) {
     const SegDesc* sg = &a.segs[blockIdx.x];
     const uint32_t n_chunks = sg->n_chunks;
     const uint32_t index_at = header_bytes_dev(a.h.K);
+    const uint32_t payload_at = index_at + (uint32_t)index_bytes_of(n_chunks);
+    const uint32_t ulog = size_unit_log2(a.h.C, a.h.R);
     const uint32_t* tmpl = sg->tab ? sg->tab + kDTHdr : inline_hdr(a);
-    const uint32_t* meta = a.h.meta + 2ull * sg->slot_base;
-    uint32_t* index = reinterpret_cast<uint32_t*>(sg->c + index_at);
+    uint32_t* meta = a.h.meta + 2ull * sg->slot_base;
+    uint32_t* goff = reinterpret_cast<uint32_t*>(sg->c + index_at);
+    uint16_t* sizes = reinterpret_cast<uint16_t*>(sg->c + index_at + sizes_rel_of(n_chunks));
     uint32_t* hdr = reinterpret_cast<uint32_t*>(sg->c);
     for (uint32_t i = tid; i < index_at / 4; i += kScanBlock) hdr[i] = header_dword(tmpl, i, sg->n, n_chunks);
     if (tid == 0) bits_sum = 0;
@@ -300,16 +338,11 @@ __global__ __launch_bounds__(kScanBlock) void k_encode_index(const A a) {
         const uint32_t c = base + tid;
         uint32_t bytes = 0;
         if (c < n_chunks) {
-            const uint32_t start = meta[2 * c];
-            bytes = 4 * ((a.h.slot_dwords * 32 - start + 31) >> 5);
+            bytes = chunk_bytes_of(a.h.slot_dwords * 32 - meta[2 * c], ulog);
             my_bits += meta[2 * c + 1];
         }
         // wavefront inclusive scan, then across the 16 wavefronts
-        uint32_t v = bytes;
-        for (int sh = 1; sh < 64; sh <<= 1) {
-            const uint32_t o = __shfl_up(v, sh, 64);
-            if (lane >= (uint32_t)sh) v += o;
-        }
+        const uint32_t v = scan64(bytes);
         if (lane == 63) wsum[wv] = v;
         __syncthreads();
         uint32_t before = 0, all = 0;
@@ -317,15 +350,23 @@ __global__ __launch_bounds__(kScanBlock) void k_encode_index(const A a) {
             before += w < wv ? wsum[w] : 0;
             all += wsum[w];
         }
-        if (c < n_chunks) index[c] = carry + before + v - bytes;
+        if (c < n_chunks) {
+            const uint32_t off = carry + before + v - bytes;
+            meta[2 * c + 1] = off;  // the chunk's payload offset, for the compaction
+            sizes[c] = (uint16_t)(bytes >> ulog);
+            if (c % kGroupChunks == 0) goff[c / kGroupChunks] = off;
+        }
         carry += all;
         __syncthreads();
     }
-    if (tid == 0) index[n_chunks] = carry;
+    if (tid == 0) {
+        goff[n_groups_of(n_chunks)] = carry;
+        if (n_chunks & 1) sizes[n_chunks] = 0;
+    }
     atomicAdd(&bits_sum, (unsigned long long)my_bits);
     __syncthreads();
     if (tid == 0 && sg->info) {
-        sg->info->container_bytes = (uint64_t)index_at + 4ull * (n_chunks + 1) + carry;
+        sg->info->container_bytes = (uint64_t)payload_at + (carry + 3) / 4 * 4;
         sg->info->payload_bits = bits_sum;
     }
 }
@@ -341,20 +382,15 @@ __global__ __launch_bounds__(256) void k_encode_compact(const A a) {
     const SegDesc* sg = codec_seg(a, block, true);
     const uint32_t c = (block - sg->first_block_c) * 4 + (threadIdx.x >> 6);
     if (c >= sg->n_chunks) return;
-    const uint32_t index_at = header_bytes_dev(a.h.K);
-    const uint32_t payload_at = index_at + 4 * (sg->n_chunks + 1);
+    const uint32_t payload_at = header_bytes_dev(a.h.K) + (uint32_t)index_bytes_of(sg->n_chunks);
     const uint32_t slot = sg->slot_base + c;
     const uint32_t start = a.h.meta[2 * slot];
-    const uint32_t ndw = (a.h.slot_dwords * 32 - start + 31) >> 5;
-    const uint32_t off = reinterpret_cast<const uint32_t*>(sg->c + index_at)[c];
-    const uint32_t* s = a.h.slots + (uint64_t)slot * a.h.slot_dwords;
-    uint32_t* d = reinterpret_cast<uint32_t*>(sg->c + payload_at + off);
-    const uint32_t s0 = start >> 5;
-    for (uint32_t j = lane; j < ndw; j += 64) {
-        const uint32_t lo = s[s0 + j];
-        const uint32_t hi = s0 + j + 1 < a.h.slot_dwords ? s[s0 + j + 1] : 0;
-        d[j] = __builtin_amdgcn_alignbit(hi, lo, start);
-    }
+    const uint32_t off = a.h.meta[2 * slot + 1];  // written by the index kernel
+    const uint32_t bytes = chunk_bytes_of(a.h.slot_dwords * 32 - start, size_unit_log2(a.h.C, a.h.R));
+    // the last chunk also writes the zero bytes that end the payload on 4 bytes
+    const uint32_t end = c + 1 == sg->n_chunks ? (off + bytes + 3) / 4 * 4 : off + bytes;
+    move_chunk(a.h.slots + (uint64_t)slot * a.h.slot_dwords, a.h.slot_dwords, start, sg->c,
+               payload_at + off, payload_at + end, lane);
 }
 
 // ------------------------------------------------------------------------------------
@@ -374,13 +410,15 @@ __global__ __launch_bounds__(256) void k_encode_place(const A a) {
     const uint32_t n_chunks = sg->n_chunks;
     const uint32_t c0 = (block - sg->first_block_c) * 4;   // this block's first chunk
     const uint32_t index_at = header_bytes_dev(a.h.K);
-    const uint32_t payload_at = index_at + 4 * (n_chunks + 1);
+    const uint32_t payload_at = index_at + (uint32_t)index_bytes_of(n_chunks);
+    const uint32_t ulog = size_unit_log2(a.h.C, a.h.R);
     const uint32_t* meta = a.h.meta + 2ull * sg->slot_base;
     const uint32_t* agg = a.h.agg + 2ull * sg->first_block;  // the segment's chunk-kernel blocks
-    uint32_t* index = reinterpret_cast<uint32_t*>(sg->c + index_at);
+    uint32_t* goff = reinterpret_cast<uint32_t*>(sg->c + index_at);
+    uint16_t* sizes = reinterpret_cast<uint16_t*>(sg->c + index_at + sizes_rel_of(n_chunks));
     const bool last = c0 + 4 >= n_chunks;
     auto chunk_bytes = [&](uint32_t ch) {
-        return 4 * ((a.h.slot_dwords * 32 - meta[2 * ch] + 31) >> 5);
+        return chunk_bytes_of(a.h.slot_dwords * 32 - meta[2 * ch], ulog);
     };
 
     // bytes of the chunk-kernel blocks before c0 (c0 / 8 of them); in the last block also
@@ -412,26 +450,26 @@ __global__ __launch_bounds__(256) void k_encode_place(const A a) {
             reinterpret_cast<uint32_t*>(sg->c)[i] =
                 header_dword(sg->tab ? sg->tab + kDTHdr : inline_hdr(a), i, sg->n, n_chunks);
     if (c < n_chunks) {
-        if (lane == 0) index[c] = off;
         const uint32_t slot = sg->slot_base + c;
         const uint32_t start = a.h.meta[2 * slot];
-        const uint32_t ndw = (a.h.slot_dwords * 32 - start + 31) >> 5;
-        const uint32_t* src = a.h.slots + (uint64_t)slot * a.h.slot_dwords;
-        uint32_t* d = reinterpret_cast<uint32_t*>(sg->c + payload_at + off);
-        const uint32_t s0 = start >> 5;
-        for (uint32_t j = lane; j < ndw; j += 64) {
-            const uint32_t lo = src[s0 + j];
-            const uint32_t hi = s0 + j + 1 < a.h.slot_dwords ? src[s0 + j + 1] : 0;
-            d[j] = __builtin_amdgcn_alignbit(hi, lo, start);
+        const uint32_t bytes = chunk_bytes(c);
+        if (lane == 0) {
+            sizes[c] = (uint16_t)(bytes >> ulog);
+            if (c % kGroupChunks == 0) goff[c / kGroupChunks] = off;
         }
+        // the last chunk also writes the zero bytes that end the payload on 4 bytes
+        const uint32_t end = c + 1 == n_chunks ? (off + bytes + 3) / 4 * 4 : off + bytes;
+        move_chunk(a.h.slots + (uint64_t)slot * a.h.slot_dwords, a.h.slot_dwords, start, sg->c,
+                   payload_at + off, payload_at + end, lane);
     }
     // the segment's end: the wavefront holding its last chunk (wavefront 0 of the only
     // block of an empty segment)
     if (last && lane == 0 && c == (n_chunks > 0 ? n_chunks - 1 : 0)) {
         const uint32_t total = n_chunks > 0 ? off + chunk_bytes(c) : 0;
-        index[n_chunks] = total;
+        goff[n_groups_of(n_chunks)] = total;
+        if (n_chunks & 1) sizes[n_chunks] = 0;
         if (sg->info) {
-            sg->info->container_bytes = (uint64_t)payload_at + total;
+            sg->info->container_bytes = (uint64_t)payload_at + (total + 3) / 4 * 4;
             sg->info->payload_bits = red_f[0] + red_f[1] + red_f[2] + red_f[3];
         }
     }

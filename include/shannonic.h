@@ -25,7 +25,7 @@
  *     *d_status beforehand and reads it back when convenient.
  *
  * Container (the bytes sh_encode writes and sh_decode reads), all integers little-endian:
- *   0   "SHN1", u8 version = 2, u8 log2_L, u16 K
+ *   0   "SHN1", u8 version = 3, u8 log2_L, u16 K
  *   8   u64 n              number of values
  *   16  u32 chunk_symbols  C
  *   20  u32 streams        S (interleaved tANS lanes per chunk)
@@ -34,16 +34,26 @@
  *   32  u16 freq[K]        tANS state count of every range (sum L)
  *   32+2K u8 lo[1..K-1]    first value u of ranges 1..K-1 (range 0 starts at 0, the
  *                          last ends at 256); zero padding up to index_at
- *   index_at: u32 off[n_chunks + 1], byte offset of every chunk from the payload start
- *   payload: chunk c holds values [c*C, c*C + n_c).  Value i of a chunk belongs to lane
- *   i mod S at step i div S.  The chunk is an LSB-first bit string (bit b is bit b mod 8
- *   of byte b / 8): the initial tANS slot of each of its min(S, n_c) lanes in log2_L bits,
- *   in lane order, then every value's field in (step, lane) order, then zero bits up to a
- *   whole number of 32-bit words.  A field is the offset o in its low w_s bits and, above
- *   it, the nb state bits the decoder appends to the slot's base to reach the next state.
- *   Every lane ends in slot 0.  A lane's last field is the offset alone: the encoder starts
- *   each lane in state L (slot 0), so the state bits of the last value are the low bits of
- *   L, all zero, and the decoder implies them (a framing reduction; version 1 wrote them).
+ *   index_at: u32 goff[G + 1], G = ceil(n_chunks / 64): the payload byte where chunk 64g
+ *             starts; goff[G] = the payload's size in bytes.  Then u16 size[n_chunks],
+ *             every chunk's size in units of 2^u bytes, u the smallest with
+ *             ceil(B / 2^u) <= 65535 for B = ceil((min(S, C) log2_L + C (8 + log2_L)) / 8),
+ *             the largest chunk a valid stream holds (u = 0 at the pages' parameters).
+ *             Then a zero u16 when n_chunks is odd.  Chunk c starts at goff[c / 64] plus
+ *             the sizes of the chunks before it in its group of 64.
+ *   payload: the chunks back to back, then zero bytes up to a multiple of 4 (the
+ *   container's end).  Chunk c holds values [c*C, c*C + n_c).  Value i of a chunk belongs
+ *   to lane i mod S at step i div S.  The chunk is an LSB-first bit string (bit b is bit
+ *   b mod 8 of byte b / 8): the initial tANS slot of each of its min(S, n_c) lanes in
+ *   log2_L bits, in lane order, then every value's field in (step, lane) order, then zero
+ *   bits up to a whole number of size units.  A field is the offset o in its low w_s bits
+ *   and, above it, the nb state bits the decoder appends to the slot's base to reach the
+ *   next state.  Every lane ends in slot 0.  A lane's last field is the offset alone: the
+ *   encoder starts each lane in state L (slot 0), so the state bits of the last value are
+ *   the low bits of L, all zero, and the decoder implies them.
+ *   (Version 2 padded every chunk to 32-bit words with a u32 offset per chunk; version 1
+ *   also wrote the last fields' state bits.  Both are framing choices: the pages fix what
+ *   a chunk codes, not how chunks are laid out.)
  */
 #ifndef SHANNONIC_H
 #define SHANNONIC_H
@@ -63,7 +73,9 @@ typedef int32_t sh_status;
 #define SH_ERR_BUFFER_TOO_SMALL (-5)     /* output or workspace capacity below the bound    */
 #define SH_ERR_HIP (-6)                  /* a HIP runtime call failed                       */
 
-/* Codec parameters.  The GPU path supports 1 <= K <= 256, 1 <= log2_L <= 8,
+/* Codec parameters.  The GPU path supports 1 <= K <= 256, 1 <= log2_L <= 11 (tables with
+ * fields of at most 16 bits, the widest range's offset bits plus log2_L; sh_encode and
+ * sh_decode, which carry the table in their launch arguments, take log2_L <= 8),
  * streams == 32 and chunk_symbols a multiple of 32 in [32, 65536].
  * The pages' configuration is K = 16, log2_L = 7 (530 B of codec state,
  * "Codec state footprint", paper section 4.1 and Appendix A). */
@@ -171,7 +183,7 @@ sh_status sh_encode(const sh_table* table, const sh_params* params, const int8_t
  * range s and its state-bit count, the offset o is read in w_s raw bits, the value is
  * base[s] + o, and the state bits lead to the next state.  in_nbytes is
  * the number of readable bytes at d_in: at least the container's size (its chunk index
- * marks its end), so the output buffer of sh_encode can be passed with its capacity and
+ * gives the payload's size), so the output buffer of sh_encode can be passed with its capacity and
  * no host round trip.  The container must have been written with this table and these
  * params; its header is checked on the GPU.  Any inconsistency -- header, chunk index, an offset outside its
  * range, a lane not ending in slot 0, bits past a chunk's end or non-zero padding, a

@@ -52,3 +52,10 @@ def chunk_spans(buf: np.ndarray, n: int, K: int, C: int, log2_L: int, S: int = 3
         spans.append((at, at + size))
         at += size
     return spans, hb + index_bytes(nch)
+
+
+def chunk_bytes(buf, n: int, K: int, C: int, log2_L: int, c: int, S: int = 32):
+    """The bytes of chunk c (its size units, padding included)."""
+    spans, pay0 = chunk_spans(buf, n, K, C, log2_L, S)
+    a, b = spans[c]
+    return np.asarray(buf[pay0 + a: pay0 + b])

@@ -11,6 +11,7 @@ import pytest
 
 from entropy_coding_quantized_amd import codec
 from entropy_coding_quantized_amd import datagen as D
+import container_layout as CL
 from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -104,14 +105,14 @@ def _check_containers(buf, offs, info, xs, tabs, p, whole=None):
         else:
             C_ = p.chunk_symbols
             nch = (x.size + C_ - 1) // C_
-            hb = (32 + 3 * p.K - 1 + 3) // 4 * 4
-            idx = np.frombuffer(got[hb: hb + 4 * (nch + 1)].tobytes(), dtype="<u4")
-            pay0 = hb + 4 * (nch + 1)
-            assert pay0 + int(idx[-1]) == nbytes
+            spans, pay0 = CL.chunk_spans(got, x.size, p.K, C_, p.log2_L)
+            assert pay0 + (spans[-1][1] + 3) // 4 * 4 == nbytes
             for c in {0, nch // 2, nch - 1}:
-                one, _ = O.encode(x[c * C_: (c + 1) * C_], lo, f, p.log2_L, C_, 32)
-                assert np.array_equal(got[pay0 + int(idx[c]): pay0 + int(idx[c + 1])],
-                                      one[hb + 8:]), f"container {i} chunk {c}"
+                part = x[c * C_: (c + 1) * C_]
+                one, _ = O.encode(part, lo, f, p.log2_L, C_, 32)
+                assert np.array_equal(CL.chunk_bytes(got, x.size, p.K, C_, p.log2_L, c),
+                                      CL.chunk_bytes(one, part.size, p.K, C_, p.log2_L, 0)), \
+                    f"container {i} chunk {c}"
 
 
 def _roundtrip_batch(torch, xs, p, whole=None):
@@ -179,9 +180,7 @@ def test_batch_errors(torch_cuda):
     b2 = buf.clone()
     i = 1
     nbytes = int(info[i, 0].item())
-    hb = (32 + 3 * p.K - 1 + 3) // 4 * 4
-    nch = (ns[i] + p.chunk_symbols - 1) // p.chunk_symbols
-    pos = offs[i] + hb + 4 * (nch + 1)     # first payload byte: initial states of lane 0..
+    pos = offs[i] + CL.payload_at(ns[i], p.K, p.chunk_symbols)  # initial states of lane 0..
     b2[pos] ^= 0x01
     bad = b2[offs[i]: offs[i] + nbytes].cpu().numpy()
     st_o, _ = O.decode(bad, ns[i], raise_on_error=False)

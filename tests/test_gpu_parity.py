@@ -12,6 +12,7 @@ import pytest
 
 from entropy_coding_quantized_amd import codec
 from entropy_coding_quantized_amd import datagen as D
+import container_layout as CL
 from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -144,7 +145,7 @@ def test_symbol_outside_table(torch_cuda):
 def test_corruption_matches_oracle(torch_cuda):
     """Damaged containers: the GPU reports exactly what the oracle reports."""
     torch = torch_cuda
-    x = D.tiny(n=40000)
+    x = D.tiny(n=36000)  # 9 chunks: an odd count, so the index ends with a pad
     p = codec.Params()
     t, lo, f = _table(x, 16, 7)
     ref, _ = O.encode(x, lo, f, 7, 4096, 32)
@@ -155,15 +156,28 @@ def test_corruption_matches_oracle(torch_cuda):
         pos = int(rng.integers(0, bad.size * 8))
         bad[pos // 8] ^= np.uint8(1 << (pos % 8))
         cases.append(bad)
-    hb = (32 + 3 * 16 - 1 + 3) // 4 * 4
-    bad = ref.copy()
-    bad[hb + 8: hb + 12] = np.frombuffer(np.uint32(7).tobytes(), np.uint8)  # misaligned offset
-    cases.append(bad)
+    # index damage: a group offset, a chunk size one unit longer or shorter, the odd-count pad,
+    # a tail pad byte
+    hb = CL.header_bytes(16)
+    nch = (x.size + 4095) // 4096
+    sizes_at = hb + 4 * ((nch + 63) // 64 + 1)
+    for at, val in [(hb, 1), (hb + 4, 3), (sizes_at, None), (sizes_at + 2 * (nch - 1), None),
+                    (sizes_at + 2 * nch, 1), (ref.size - 1, 1)]:
+        bad = ref.copy()
+        if val is None:
+            v = int(bad[at]) | (int(bad[at + 1]) << 8)
+            for d in (1, -1):
+                b2 = bad.copy()
+                b2[at: at + 2] = np.frombuffer(np.uint16(v + d).tobytes(), np.uint8)
+                cases.append(b2)
+            continue
+        bad[at] ^= np.uint8(val)
+        cases.append(bad)
     agree = 0
     for c in cases:
         st_o, y_o = O.decode(c, x.size, raise_on_error=False)
         cd = torch.from_numpy(np.ascontiguousarray(c)).cuda()
-        if c.size < hb + 4 * 11:
+        if c.size < CL.payload_at(x.size, 16, 4096):
             continue
         y, st = _gpu_decode(torch, cd, x.size, t, p)
         assert st in (0, codec.SH_ERR_CORRUPT_STREAM)
@@ -180,18 +194,16 @@ def _sampled_chunk_parity(torch, x, t, lo, f, cont, p, samples=64, seed=0):
     n = x.size
     nch = (n + C_ - 1) // C_
     K = p.K
-    hb = (32 + 3 * K - 1 + 3) // 4 * 4
-    head = cont[: hb + 4 * (nch + 1)].cpu().numpy()
-    idx = np.frombuffer(head[hb:].tobytes(), dtype="<u4")
-    pay0 = hb + 4 * (nch + 1)
+    head = cont[: CL.payload_at(n, K, C_)].cpu().numpy()
+    spans, pay0 = CL.chunk_spans(head, n, K, C_, p.log2_L)
     rng = np.random.default_rng(seed)
     pick = set(rng.choice(nch, size=min(samples, nch), replace=False).tolist()) | {0, nch - 1}
     for c in sorted(pick):
         part = x[c * C_: min(n, (c + 1) * C_)]
         one, _ = O.encode(part, lo, f, p.log2_L, C_, 32)
-        one_pay = one[hb + 8:]
-        got = cont[pay0 + int(idx[c]): pay0 + int(idx[c + 1])].cpu().numpy()
-        assert np.array_equal(got, one_pay), f"chunk {c}"
+        a, b = spans[c]
+        got = cont[pay0 + a: pay0 + b].cpu().numpy()
+        assert np.array_equal(got, CL.chunk_bytes(one, part.size, K, C_, p.log2_L, 0)), f"chunk {c}"
 
 
 def test_kv_cache_workload(torch_cuda):

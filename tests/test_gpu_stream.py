@@ -7,6 +7,7 @@ import pytest
 
 from entropy_coding_quantized_amd import codec
 from entropy_coding_quantized_amd import datagen as D
+import container_layout as CL
 
 pytestmark = pytest.mark.gpu
 
@@ -114,19 +115,17 @@ def test_model_layers_streamed(torch_cuda):
     assert tst == [0] * len(idx)
     rng = np.random.default_rng(31)
     C_ = p.chunk_symbols
-    hb = (32 + 3 * p.K - 1 + 3) // 4 * 4
     for k, x in enumerate(dx):
         xh = x.cpu().numpy()
         lo, f = O.build_table(O.histogram(xh), p.K, p.log2_L)
         assert (tabs[k].lo_array == lo).all() and (tabs[k].freq_array == f).all(), idx[k]
         nch = (xh.size + C_ - 1) // C_
         cont = buf[offs[k]: offs[k] + sizes[k]].cpu().numpy()
-        index = np.frombuffer(cont[hb: hb + 4 * (nch + 1)].tobytes(), dtype="<u4")
-        pay0 = hb + 4 * (nch + 1)
         for c in set(rng.choice(nch, size=min(6, nch), replace=False).tolist()) | {nch - 1}:
-            one, _ = O.encode(xh[c * C_: (c + 1) * C_], lo, f, p.log2_L, C_, 32)
-            assert np.array_equal(cont[pay0 + int(index[c]): pay0 + int(index[c + 1])],
-                                  one[hb + 8:]), (idx[k], c)
+            part = xh[c * C_: (c + 1) * C_]
+            one, _ = O.encode(part, lo, f, p.log2_L, C_, 32)
+            assert np.array_equal(CL.chunk_bytes(cont, xh.size, p.K, C_, p.log2_L, c),
+                                  CL.chunk_bytes(one, part.size, p.K, C_, p.log2_L, 0)), (idx[k], c)
     # park and stream back
     starts, at = [], 0
     for s in sizes:
