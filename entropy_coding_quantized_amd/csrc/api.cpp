@@ -17,7 +17,7 @@ using namespace shn;
 
 namespace {
 
-constexpr uint32_t kChunksPerBlock = 8;   // decode and encode chunk kernels
+constexpr uint32_t kChunksPerBlock = 8;   // matrix-vector decode kernel
 constexpr uint32_t kChunksPerBlockC = 4;  // compaction kernel
 
 bool gpu_params_ok(const sh_params* p) {
@@ -55,14 +55,14 @@ uint64_t bound_of(uint64_t n, const sh_params* p) {
 
 uint32_t blocks_for(uint64_t nch, uint32_t per) { return (uint32_t)((nch + per - 1) / per); }
 
-// slots a segment takes in the encode workspace: its chunks rounded up to pairs
-uint64_t slots_for(uint64_t nch) { return (nch + 1) / 2 * 2; }
+// slots a segment takes in the encode workspace: its chunks rounded up to a wavefront's four
+uint64_t slots_for(uint64_t nch) { return (nch + 3) / 4 * 4; }
 
 uint64_t align256(uint64_t v) { return (v + 255) / 256 * 256; }
 
 // encode workspace for a group of segments: slots, then per-slot meta, then per-block
-// aggregates of the chunk kernel (a block takes kChunksPerBlock chunks, so a group has at
-// most total_slots / kChunksPerBlock + kMaxInlineSegs blocks)
+// aggregates of the chunk kernel (a block takes kEncodeChunksPerBlock chunks, so a group has
+// at most total_slots / kEncodeChunksPerBlock + kMaxInlineSegs blocks)
 struct EncLayout {
     uint64_t meta_at, agg_at, bytes;
     uint32_t slot_dwords;
@@ -72,7 +72,7 @@ EncLayout enc_layout(uint64_t total_slots, const sh_params* p) {
     l.slot_dwords = encode_slot_dwords(p->chunk_symbols, p->log2_L);
     l.meta_at = align256(total_slots * l.slot_dwords * 4);
     l.agg_at = l.meta_at + align256(8 * total_slots);
-    l.bytes = l.agg_at + align256(8 * (total_slots / kChunksPerBlock + kMaxInlineSegs)) + 256;
+    l.bytes = l.agg_at + align256(8 * (total_slots / kEncodeChunksPerBlock + kMaxInlineSegs)) + 256;
     return l;
 }
 
@@ -345,7 +345,7 @@ sh_status sh_encode(const sh_table* table, const sh_params* params, const int8_t
     sd.c_bytes = out_cap;
     sd.info = d_info;
     sd.n_chunks = (uint32_t)nch;
-    return launch_encode(a, blocks_for(nch, kChunksPerBlock), place_blocks(nch, place), place,
+    return launch_encode(a, blocks_for(nch, kEncodeChunksPerBlock), place_blocks(nch, place), place,
                          stream);
 }
 
@@ -428,7 +428,7 @@ sh_status sh_encode_batch(const void* d_tables, const int8_t* const* d_x, const 
             sd.first_block_c = blocks_c;
             sd.n_chunks = (uint32_t)nch;
             sd.slot_base = (uint32_t)slots;
-            blocks += blocks_for(nch, kChunksPerBlock);
+            blocks += blocks_for(nch, kEncodeChunksPerBlock);
             blocks_c += place_blocks(nch, place);
             slots += slots_for(nch);
         }

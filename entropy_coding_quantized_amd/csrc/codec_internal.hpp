@@ -244,6 +244,8 @@ sh_status launch_decode(const CodecArgs& a, uint32_t total_blocks, void* stream)
 // this many values long
 constexpr uint32_t kMaxMatvecCols = 16384;
 sh_status launch_decode_matvec(const CodecArgs& a, uint32_t total_blocks, void* stream);
+// the encoder's chunk kernel: one chunk per 16-lane row, 16 chunks a block
+constexpr uint32_t kEncodeChunksPerBlock = 16;
 // segments of at most this many chunks are indexed and compacted by one kernel
 // (k_encode_place: each block sums the sizes of the chunks before its own, so the work
 // grows with the square of the chunk count); longer ones take the index kernel first

@@ -11,83 +11,136 @@ namespace shn {
 // ------------------------------------------------------------------------------------
 // encode, kernel 1: every chunk into a worst-case slot of the workspace
 // ------------------------------------------------------------------------------------
-// tANS encodes backwards.  Each lane walks its values from the last step to the first;
-// at every step the 32 fields of a chunk are placed right to left: the step's fields end
-// where the later steps' fields begin, so a 32-lane prefix sum of the lengths gives every
-// field's bit position.  Fields are OR-ed into a 256-dword LDS ring that is flushed to
-// the chunk's slot 128 dwords at a time, highest first; the chunk ends up right-aligned
-// in its slot with the lanes' final states (the decoder's initial states) in front.
-constexpr int kEncBlock = 256;
-constexpr uint32_t kChunksPerBlockE = kEncBlock / 64 * 2;  // two chunks a wavefront
-constexpr uint32_t kERing = 256;
-// LDS (dynamic, sized by L; the kernel's only LDS, so it starts at LDS byte 0): eight 1 KB
-// rings (one per half wavefront, 1 KB aligned), eight 1 KB input tiles (bytes of 32 steps x
-// 32 lanes), the value table (512 dwords), the encTable slots (u16, L of them), then the
+// The decoder's mapping run backwards: one chunk per 16-lane DPP row, lane j of a row runs
+// the streams 2j and 2j + 1, whose fields are adjacent in every step.  tANS encodes
+// backwards, so each stream walks its values from the last step to the first and every
+// step's fields are placed right to left: the step's pairs of fields end where the later
+// steps' fields begin, and a 16-lane prefix sum of the pairs' lengths gives every pair's bit
+// position.  Pairs are OR-ed into a 128-dword LDS ring per chunk that is flushed to the
+// chunk's slot 64 dwords at a time, highest first; the chunk ends up right-aligned in its
+// slot with the streams' final states (the decoder's initial states) in front.
+constexpr int kEncRowsBlock = 256;                 // 4 wavefronts, 16 rows = 16 chunks
+static_assert(kEncodeChunksPerBlock == kEncRowsBlock / 16, "one chunk per 16-lane row");
+constexpr uint32_t kERing = 128;                   // ring dwords per chunk
+constexpr uint32_t kEFlush = 64;                   // dwords per flush
+constexpr uint32_t kETileSteps = 16;               // input steps staged at a time
+constexpr uint32_t kETileBytes = kETileSteps * 32;
+// LDS (dynamic; the kernel's only LDS, so it starts at LDS byte 0): the value entries (two
+// dwords per value, at a 2 KB boundary so that an entry's address is one AND-OR), the
+// rings (512 B each, 512 B aligned), the encTable (a dword per slot, holding the next
+// state L + slot), the input tiles (u = x + 128 of kETileSteps steps of a chunk), then the
 // block's two totals
-constexpr uint32_t kTileBase = 8 * kERing;
-constexpr uint32_t kVtBase = kTileBase + 8 * 256;
-constexpr uint32_t kEsBase = kVtBase + 512;
-__host__ __device__ constexpr uint32_t encode_lds_dwords(uint32_t L) { return kEsBase + (L + 1) / 2 + 2; }
-
-// OR a field (zero above its length) into a ring at bit pos; ring_byte is the ring's LDS
-// byte offset, a multiple of its 1 KB size.  The second dword is OR-ed only by the lanes
-// whose field reaches into it: the 32 fields of a step share a few dwords, and same-address
-// LDS atomics serialise.
-__device__ __forceinline__ void ring_or(uint32_t* sm, uint32_t ring_byte, uint32_t pos,
-                                        uint32_t field) {
-    typedef __attribute__((address_space(3))) uint32_t lds_word;
-    const uint64_t wide = (uint64_t)field << (pos & 31);
-    const uint32_t b = pos >> 3;
-    const uint32_t a0 = (b & 0x3FC) | ring_byte, a1 = ((b + 4) & 0x3FC) | ring_byte;
-    (void)sm;  // the rings sit at LDS byte 0 of the block's only __shared__ array
-    __hip_atomic_fetch_or((lds_word*)(uintptr_t)a0, (uint32_t)wide, __ATOMIC_RELAXED,
-                          __HIP_MEMORY_SCOPE_WORKGROUP);
-    if ((uint32_t)(wide >> 32))
-        __hip_atomic_fetch_or((lds_word*)(uintptr_t)a1, (uint32_t)(wide >> 32), __ATOMIC_RELAXED,
-                              __HIP_MEMORY_SCOPE_WORKGROUP);
+constexpr uint32_t kEVtByte = 0;
+constexpr uint32_t kERingsByte = kEVtByte + 256 * 8;                                 // 2 KB
+constexpr uint32_t kEEsByte = kERingsByte + kEncodeChunksPerBlock * kERing * 4;      // 10 KB
+__host__ __device__ constexpr uint32_t encode_tiles_byte(uint32_t L) {
+    return (kEEsByte + 4 * L + 15) / 16 * 16;
 }
+__host__ __device__ constexpr uint32_t encode_lds_bytes(uint32_t L) {
+    return encode_tiles_byte(L) + kEncodeChunksPerBlock * kETileBytes + 16;
+}
+static_assert(kEEsByte >= 4 * kMaxLGpu && kEEsByte + 4 * kMaxLGpu < 32768,
+              "encTable addresses stay positive and below bit 15 of an entry");
 
 // container bytes of a chunk of the given bits: whole size units of 2^ulog bytes
 __device__ __forceinline__ uint32_t chunk_bytes_of(uint32_t bits, uint32_t ulog) {
     return ((bits + (8u << ulog) - 1) >> (3 + ulog)) << ulog;
 }
 
+typedef __attribute__((address_space(3))) uint32_t lds_w32;
+typedef const __attribute__((address_space(3))) uint16_t lds_r16;
+typedef const __attribute__((address_space(3))) uint32_t lds_r32;
+typedef unsigned int v2u_e __attribute__((ext_vector_type(2)));
+
+// OR a pair of fields (at most 32 bits) into a ring at bit pos; ring_byte is the ring's LDS
+// byte address, a multiple of its 512 B.  The second dword is OR-ed only by the lanes whose
+// pair reaches into it: the pairs of a step share a few dwords, and same-address LDS
+// atomics serialise.
+__device__ __forceinline__ void ring_or2(uint32_t ring_byte, uint32_t pos, uint32_t field) {
+    const uint64_t wide = (uint64_t)field << (pos & 31);
+    const uint32_t b = pos >> 3;
+    const uint32_t a0 = (b & (4 * kERing - 4)) | ring_byte;
+    const uint32_t a1 = ((b + 4) & (4 * kERing - 4)) | ring_byte;
+    __hip_atomic_fetch_or((lds_w32*)(uintptr_t)a0, (uint32_t)wide, __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_WORKGROUP);
+    if ((uint32_t)(wide >> 32))
+        __hip_atomic_fetch_or((lds_w32*)(uintptr_t)a1, (uint32_t)(wide >> 32), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Inclusive prefix sum within each 16-lane row (DPP row shifts).
+__device__ __forceinline__ uint32_t escan16(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr:8
+    return v;
+}
+// Value of lane 15 of this lane's row (DPP row_newbcast:15).  The empty asm keeps the
+// broadcast a v_mov_b32_dpp of its own: folded into the subtraction that uses it (as
+// v_subrev_u32_dpp) the broadcast was measured on MI355X not to take effect, every lane
+// subtracting its own value.
+__device__ __forceinline__ uint32_t erow_last(uint32_t v) {
+    uint32_t b = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x15F, 0xF, 0xF, true);
+    asm volatile("" : "+v"(b));
+    return b;
+}
+
+// An encode entry in LDS, two dwords:
+//   B = bias_s & 0xFFFFFF | w_s << 24: the state-bit count is bits R+1.. of X + B (the
+//       bias's sign bits above bit 23 do not reach them)
+//   A = o | (encTable byte address of range s's first slot, minus 4 f_s) << 16 |
+//       (f_s == 0) << 31
+struct EEnt {
+    uint32_t B, A;
+};
+
 template <class A>
-__global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
-    extern __shared__ __align__(16) uint32_t sm[];
-    const uint32_t tid = threadIdx.x, lane = tid & 63, li = lane & 31, hw = lane >> 5;
+__global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
+    extern __shared__ __align__(16) uint32_t esm[];
+    const uint32_t tid = threadIdx.x, lane = tid & 63, j = lane & 15, row = lane >> 4;
     const uint32_t block = __builtin_amdgcn_readfirstlane(blockIdx.x);
     const SegDesc* sg = codec_seg(a, block, false);
     const uint32_t bseg = block - sg->first_block;
-    const uint32_t wid = __builtin_amdgcn_readfirstlane(bseg * (kEncBlock / 64) + (tid >> 6));
-    const uint32_t wv = wid & (kEncBlock / 64 - 1);
+    const uint32_t wid = __builtin_amdgcn_readfirstlane(bseg * (kEncRowsBlock / 64) + (tid >> 6));
+    const uint32_t rowi = (wid & (kEncRowsBlock / 64 - 1)) * 4 + row;  // row in the block
+    const uint32_t n_chunks = sg->n_chunks;
+    const uint64_t n = sg->n;
+    const uint32_t L = a.h.L, R = a.h.R, R1 = a.h.R + 1;
+    const uint32_t base = lds_offset(esm);  // 0: the only LDS of the kernel
+    const uint32_t ring_byte = base + kERingsByte + 4 * kERing * rowi;
+    const uint32_t tile_byte = base + encode_tiles_byte(L) + kETileBytes * rowi;
+    const uint32_t vt_byte = base + kEVtByte, es_byte = base + kEEsByte;
+    uint32_t* agg_s = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(esm) + encode_tiles_byte(L) +
+                                                  kEncodeChunksPerBlock * kETileBytes);
+
+    // the tables in their LDS form (device form: v0 = bias, v1 = o | w << 8 | (f == 0) << 15 |
+    // (start + kMaxLGpu) << 16, start = cum - f; encTable entries are slots)
     const uint32_t* vt = sg->tab ? sg->tab + kDTVt : inline_tab(a);
     const uint16_t* es_src = sg->tab ? reinterpret_cast<const uint16_t*>(sg->tab + kDTEs)
                                     : inline_es(a);
-    const uint32_t n_chunks = sg->n_chunks;
-    const uint64_t n = sg->n;
-    const uint32_t L = a.h.L, R1 = a.h.R + 1;
-    uint32_t* agg_s = &sm[kEsBase + (L + 1) / 2];  // the block's container bytes and field bits
-    for (uint32_t i = tid; i < 512; i += kEncBlock) sm[kVtBase + i] = vt[i];
-    for (uint32_t i = tid; 2 * i < L; i += kEncBlock)
-        sm[kEsBase + i] = (uint32_t)es_src[2 * i] | ((uint32_t)es_src[2 * i + 1] << 16);
-    const uint16_t* es = reinterpret_cast<const uint16_t*>(&sm[kEsBase]);
-    const uint32_t hi = wv * 2 + hw;       // this half wavefront's ring and tile
-    const uint32_t tile = kTileBase + hi * 256;
-    const uint32_t ring = hi * kERing;
-    const uint32_t ring_byte = lds_offset(sm) + 4 * ring;  // 1 KB aligned
-    for (uint32_t i = li; i < kERing; i += 32) sm[ring + i] = 0;
+    {
+        const uint32_t v0 = vt[2 * tid], v1 = vt[2 * tid + 1];  // value tid (256 threads)
+        const uint32_t start4 = es_byte + 4 * ((v1 >> 16) - kMaxLGpu);
+        esm[kEVtByte / 4 + 2 * tid] = (v0 & 0xFFFFFFu) | (((v1 >> 8) & 15u) << 24);
+        esm[kEVtByte / 4 + 2 * tid + 1] = (v1 & 0xFFu) | (start4 << 16) | ((v1 & 0x8000u) << 16);
+    }
+    for (uint32_t i = tid; i < L; i += kEncRowsBlock) esm[kEEsByte / 4 + i] = L + es_src[i];
+    for (uint32_t i = j; i < kERing; i += 16) esm[kERingsByte / 4 + kERing * rowi + i] = 0;
+    if (tid < 2) agg_s[tid] = 0;
 
-    const uint32_t pair = 2 * wid;
-    const uint32_t chunk = pair + hw;
-    const uint64_t pair_first = (uint64_t)pair * a.h.C;
-    const uint64_t pair_len = pair_first < n ? n - pair_first : 0;
-    const rsrc_t rin = make_rsrc(sg->x + (pair_first < n ? pair_first : 0),
-                                 (uint32_t)(pair_len < 2ull * a.h.C ? pair_len : 2ull * a.h.C));
-    const uint32_t slot0 = sg->slot_base + (pair < n_chunks ? pair : 0);
-    const rsrc_t rslot = make_rsrc(a.h.slots + (uint64_t)slot0 * a.h.slot_dwords, 8u * a.h.slot_dwords);
-    const uint32_t in_base = hw * a.h.C;          // byte offset of this chunk in rin
-    const uint32_t slot_base = hw * a.h.slot_dwords * 4;
+    // the wavefront's four chunks, one per row
+    const uint32_t group = 4 * wid;
+    const uint32_t chunk = group + row;
+    const uint64_t grp_first = (uint64_t)group * a.h.C;
+    const uint64_t grp_len = grp_first < n ? n - grp_first : 0;
+    const rsrc_t rin = make_rsrc(sg->x + (grp_first < n ? grp_first : 0),
+                                 (uint32_t)(grp_len < 4ull * a.h.C ? grp_len : 4ull * a.h.C));
+    const uint32_t slot0 = sg->slot_base + (group < n_chunks ? group : 0);
+    const rsrc_t rslot = make_rsrc(a.h.slots + (uint64_t)slot0 * a.h.slot_dwords,
+                                   16u * a.h.slot_dwords);
+    const uint32_t in_row = row * a.h.C;                   // byte of this row's chunk in rin
+    const uint32_t slot_row = row * a.h.slot_dwords * 4;   // byte of its slot in rslot
     // a device table built for other parameters than the launch's, or one whose build
     // failed, is refused: its chunks are coded as empty (the workspace stays consistent for
     // the placement) and the call fails
@@ -99,131 +152,146 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
         nc = (uint32_t)((n - first) < a.h.C ? (n - first) : a.h.C);
     }
     const uint32_t lanes = nc < 32 ? nc : 32;
-    const uint32_t nc_lo = __builtin_amdgcn_readlane(nc, 0), nc_hi = __builtin_amdgcn_readlane(nc, 32);
-    const uint32_t steps = ((nc_lo > nc_hi ? nc_lo : nc_hi) + 31) >> 5;
+    uint32_t nc_min = 0xFFFFFFFFu, nc_max = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t v = __builtin_amdgcn_readlane(nc, 16 * k);
+        nc_min = nc_min < v ? nc_min : v;
+        nc_max = nc_max > v ? nc_max : v;
+    }
+    const uint32_t steps = (nc_max + 31) >> 5;
 
-    // 32 bytes of input tile tl for this lane (32 steps x 32 lanes = 1 KB per tile)
-    auto load_tile = [&](uint32_t tl, v4u& p0, v4u& p1) {
-        const uint32_t b = tl * 1024 + 32 * li;   // chunk-relative byte
-        if (b + 32 <= nc) {
-            p0 = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rin, (int)(in_base + b), 0, 0));
-            p1 = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rin, (int)(in_base + b + 16), 0, 0));
+    // Lane j stages step 16 T + j of tile T: 32 bytes.  Past a short chunk's end lies the
+    // end of the wavefront's range (a 16-byte load reaching past it reads 0 as a whole, so
+    // the lanes at the end read byte by byte) or the next chunk, whose values go unused.
+    const uint32_t in_len = (uint32_t)(grp_len < 4ull * a.h.C ? grp_len : 4ull * a.h.C);
+    auto load_tile = [&](uint32_t T, v4u& p0, v4u& p1) {
+        const uint32_t b = in_row + (kETileSteps * T + j) * 32;
+        if (b + 32 <= in_len) {
+            p0 = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rin, (int)b, 0, 0));
+            p1 = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rin, (int)(b + 16), 0, 0));
         } else {
             p0 = v4u{0, 0, 0, 0};
             p1 = v4u{0, 0, 0, 0};
             for (uint32_t k = 0; k < 32; ++k)
-                if (b + k < nc) {
-                    const uint32_t byte = __builtin_amdgcn_raw_buffer_load_b8(rin, (int)(in_base + b + k), 0, 0);
+                if (b + k < in_len) {
+                    const uint32_t byte = __builtin_amdgcn_raw_buffer_load_b8(rin, (int)(b + k), 0, 0);
                     if (k < 16) p0[k >> 2] |= byte << (8 * (k & 3));
                     else p1[(k - 16) >> 2] |= byte << (8 * (k & 3));
                 }
         }
     };
-    v4u p0, p1;
-    if (steps > 0) load_tile((steps - 1) >> 5, p0, p1);
-    if (tid < 2) agg_s[tid] = 0;
+    v4u p0 = {0, 0, 0, 0}, p1 = {0, 0, 0, 0};
+    if (steps > 0) load_tile((steps - 1) / kETileSteps, p0, p1);
     __syncthreads();
 
-    uint32_t X = L;
     uint32_t P = a.h.slot_dwords * 32;   // fields go below P, right to left
     uint32_t fmark = a.h.slot_dwords;    // dwords at or above fmark are in the slot
-    uint32_t flush_at = (fmark - 128) * 32;  // once P is below this, flush a block
-    // every encode entry is OR-ed in; its bit 15 marks a value in a range without states
-    uint32_t bad = 0;
+    uint32_t flush_at = (fmark - kEFlush) * 32;  // once P is below this, flush a block
+    uint32_t bad = 0;                    // entries OR-ed in: bit 31 marks a range without states
 
-    auto flush_block = [&](uint32_t blk) {  // ring dwords [blk, blk + 128) -> slot
-        uint32_t* r = &sm[ring + ((blk + 4 * li) & (kERing - 1))];
-        const v4u v = *reinterpret_cast<v4u*>(r);
-        *reinterpret_cast<v4u*>(r) = v4u{0, 0, 0, 0};
-        __builtin_amdgcn_raw_buffer_store_b128(v, rslot, (int)(slot_base + 4 * (blk + 4 * li)), 0, 0);
+    auto flush_block = [&](uint32_t blk) {  // ring dwords [blk, blk + 64) -> slot
+        typedef __attribute__((address_space(3))) v4u lds_v4;
+        lds_v4* r = (lds_v4*)(uintptr_t)(ring_byte + 4 * ((blk + 4 * j) & (kERing - 1)));
+        const v4u v = *r;
+        *r = v4u{0, 0, 0, 0};
+        __builtin_amdgcn_raw_buffer_store_b128(v, rslot, (int)(slot_row + 4 * (blk + 4 * j)), 0, 0);
     };
-
-    // Values are read two steps ahead and table entries one step ahead, so the only LDS
-    // read on the chain from one step to the next is the state-dependent encTable read,
-    // and no read waits for the previous step's ring writes.
     auto stage = [&]() {  // the tile in p0/p1 into LDS, as u = x + 128
+        typedef __attribute__((address_space(3))) v4u lds_v4;
         const v4u flip = {0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};
-        *reinterpret_cast<v4u*>(&sm[tile + 8 * li]) = p0 ^ flip;
-        *reinterpret_cast<v4u*>(&sm[tile + 8 * li + 4]) = p1 ^ flip;
+        *(lds_v4*)(uintptr_t)(tile_byte + 32 * j) = p0 ^ flip;
+        *(lds_v4*)(uintptr_t)(tile_byte + 32 * j + 16) = p1 ^ flip;
     };
-    auto value_at = [&](uint32_t t) {  // u of step t, from the staged tile t >> 5
-        return (uint32_t)reinterpret_cast<const uint8_t*>(&sm[tile])[(t & 31) * 32 + li];
+    auto pair_at = [&](uint32_t t) {  // u of streams 2j and 2j + 1 at step t (staged)
+        return (uint32_t) * (lds_r16*)(uintptr_t)(tile_byte + 32 * (t & (kETileSteps - 1)) + 2 * j);
     };
-    auto entry = [&](uint32_t u) {  // encode entry of value u
-        return *reinterpret_cast<const uint2*>(&sm[kVtBase + 2 * u]);
+    // entries of the pair's two values (the table sits on a 2 KB boundary)
+    auto entry_at = [&](uint32_t addr) {
+        const v2u_e v = *(const __attribute__((address_space(3))) v2u_e*)(uintptr_t)addr;
+        return EEnt{v[0], v[1]};
     };
-    // step t2's value, staging its tile first when t2 is the first step of a tile; the tile it
-    // replaces is no longer read (the values of later steps are in registers)
+    auto entry_lo = [&](uint32_t pair) { return entry_at(((pair << 3) & 0x7F8u) | vt_byte); };
+    auto entry_hi = [&](uint32_t pair) { return entry_at(((pair >> 5) & 0x7F8u) | vt_byte); };
+    // step t2's pair of values, staging its tile first when t2 is the tile's first step in
+    // this (backward) order; the tile it replaces is no longer read
     auto fetch = [&](uint32_t t2) {
-        if ((t2 & 31) == 31) {
+        if ((t2 & (kETileSteps - 1)) == kETileSteps - 1) {
             stage();
-            if (t2 >= 32) load_tile((t2 >> 5) - 1, p0, p1);
+            if (t2 >= kETileSteps) load_tile(t2 / kETileSteps - 1, p0, p1);
         }
-        return value_at(t2);
+        return pair_at(t2);
     };
-    uint2 e_c = {0, 0};
+
+    // Values are read two steps ahead and entries one step ahead, so the only LDS read on
+    // the chain from one step to the next is the state-dependent encTable read.
+    EEnt ea = {0, 0}, eb = {0, 0};
     uint32_t u_n = 0;
+    uint32_t Xa = L, Xb = L;
     if (steps > 0) {
         stage();
-        if (steps - 1 >= 32) load_tile(((steps - 1) >> 5) - 1, p0, p1);
-        const uint32_t u_c = value_at(steps - 1);
+        if (steps - 1 >= kETileSteps) load_tile((steps - 1) / kETileSteps - 1, p0, p1);
+        const uint32_t u_c = pair_at(steps - 1);
         if (steps >= 2) u_n = fetch(steps - 2);
-        e_c = entry(u_c);
+        ea = entry_lo(u_c);
+        eb = entry_hi(u_c);
     }
-    // A step's fields are placed one step late, so that the state update of step t, whose
-    // encTable read is in flight, overlaps the placement of step t + 1's fields.
-    uint32_t len_p = 0, field_p = 0;  // nothing to place before the first step
-    auto place = [&]() {  // the carried fields, right to left below P
-        const uint32_t incl = scan32(len_p);
-        P -= bcast31_valu(incl);
-        ring_or(sm, ring_byte, P + incl - len_p, field_p);
-    };
-    // Checked every other step: P then falls at most 48 dwords past flush_at before the
-    // flush (two steps and the final placement), and the ring keeps 256.
     auto flush_due = [&]() {
-        if (P < flush_at) {  // dwords from P's word + 129 up are final
-            fmark -= 128;
-            flush_at -= 128 * 32;
+        if (P < flush_at) {  // dwords from P's dword + 1 up are final
+            fmark -= kEFlush;
+            flush_at -= kEFlush * 32;
             flush_block(fmark);
         }
     };
+    // one stream's step: the next state's encTable read goes out first
+    auto code = [&](const EEnt& e, uint32_t X, uint32_t& Xn, uint32_t& field, uint32_t& len) {
+        const uint32_t k = __builtin_amdgcn_ubfe(X + e.B, R1, 5);
+        const uint32_t addr = ((X >> k) << 2) + __builtin_amdgcn_ubfe(e.A, 16, 15);
+        Xn = *(lds_r32*)(uintptr_t)addr;
+        const uint32_t w = e.B >> 24;
+        field = (__builtin_amdgcn_ubfe(X, 0, k) << w) | (e.A & 0xFFu);
+        len = w + k;
+    };
     // may_stage: false for a step whose t is known even (t - 2 is then never a tile's first
-    // step, and for t = 0 the value read is a harmless, unused byte of the tile)
+    // step in backward order, and for t = 0 the value read is a harmless, unused one)
     auto step = [&](uint32_t t, auto partial, auto may_stage) {
         uint32_t u_nn;
         if constexpr (decltype(may_stage)::value) u_nn = t >= 2 ? fetch(t - 2) : 0u;
-        else u_nn = value_at(t - 2);
-        const uint2 e_n = entry(u_n);
-        const uint32_t k = (uint32_t)((int)X + (int)e_c.x) >> R1;
-        const uint32_t sx = es[(e_c.y >> 16) - kMaxLGpu + (X >> k)];
-        const uint32_t w = (e_c.y >> 8) & 15;
-        uint32_t field = (e_c.y & 0xFF) | (__builtin_amdgcn_ubfe(X, 0, k) << w);
-        uint32_t len = w + k;
-        uint32_t flag = e_c.y;
+        else u_nn = pair_at(t - 2);
+        const EEnt na = entry_lo(u_n), nb = entry_hi(u_n);
+        uint32_t Xan, Xbn, fa, fb, la, lb;
+        code(ea, Xa, Xan, fa, la);
+        code(eb, Xb, Xbn, fb, lb);
+        uint32_t flag = ea.A | eb.A;
         if constexpr (decltype(partial)::value) {
-            const bool act = t * 32 + li < nc;
-            // a lane's last value, the first it encodes (from X = L): its k state bits
-            // are zero and are left out
-            const bool last = (t + 1) * 32 + li >= nc;
-            field = act ? field : 0u;
-            len = act ? (last ? w : len) : 0u;
-            flag = act ? flag : 0u;
+            const uint32_t s0 = t * 32 + 2 * j, s1 = s0 + 1;
+            const bool act_a = s0 < nc, act_b = s1 < nc;
+            // a stream's last value, the first it encodes (from X = L): its state bits are
+            // zero and are left out
+            la = act_a ? (s0 + 32 >= nc ? ea.B >> 24 : la) : 0u;
+            lb = act_b ? (s1 + 32 >= nc ? eb.B >> 24 : lb) : 0u;
+            fa = act_a ? fa : 0u;
+            fb = act_b ? fb : 0u;
+            flag = (act_a ? ea.A : 0u) | (act_b ? eb.A : 0u);
+            Xa = act_a ? Xan : Xa;
+            Xb = act_b ? Xbn : Xb;
+        } else {
+            Xa = Xan;
+            Xb = Xbn;
         }
         bad |= flag;
-        place();
-        if constexpr (decltype(partial)::value) {
-            X = t * 32 + li < nc ? L + sx : X;
-        } else {
-            X = L + sx;
-        }
-        len_p = len;
-        field_p = field;
-        e_c = e_n;
+        const uint32_t lp = la + lb;
+        const uint32_t fp = fa | (fb << la);
+        const uint32_t incl = escan16(lp);
+        P -= erow_last(incl);
+        ring_or2(ring_byte, P + incl - lp, fp);
+        ea = na;
+        eb = nb;
         u_n = u_nn;
     };
-    // steps where a lane of either half has no value (the tail of a short chunk) or has its
-    // last value first: every lane's last value lies at or after step nc / 32 - 1
-    uint32_t t_full = (nc_lo < nc_hi ? nc_lo : nc_hi) >> 5;
+    // steps where a stream of some row has no value (the tail of a short chunk) or has its
+    // last value: every stream's last value lies at or after step nc / 32 - 1
+    uint32_t t_full = nc_min >> 5;
     t_full = t_full > 0 ? t_full - 1 : 0;
     uint32_t t = steps;
     while (t > t_full) {
@@ -239,40 +307,42 @@ __global__ __launch_bounds__(kEncBlock) void k_encode_chunks(const A a) {
     while (t > 0) {
         take_turn(t / kPrioSteps, slot_id);
         const uint32_t stop = t > kPrioSteps ? t - kPrioSteps : 0;  // t and kPrioSteps even
-        while (t > stop) {  // two steps per iteration: the carried values need no copies
+        while (t > stop) {  // two steps per check: a step places at most 16 dwords
             step(--t, std::false_type{}, std::true_type{});   // odd t
             step(--t, std::false_type{}, std::false_type{});  // even t
             flush_due();
         }
     }
-    place();  // the first step's fields
     __builtin_amdgcn_s_setprio(0);
-    const uint32_t pay = a.h.slot_dwords * 32 - P;  // field bits
-    // the lanes' final states, the decoder's initial states, in front of the fields.  A
+    const uint32_t top = a.h.slot_dwords * 32;
+    const uint32_t pay = top - P;  // field bits
+    // the streams' final states, the decoder's initial states, in front of the fields.  A
     // valid encode never exceeds the chunk's bound; the span recorded for the placement is
     // clamped to it all the same, so that no table, however corrupt, moves the placement
     // outside the container's bound
-    uint32_t Pi = P - lanes * a.h.R;
+    uint32_t Pi = P - lanes * R;
     {
-        const uint32_t top = a.h.slot_dwords * 32, most = (uint32_t)chunk_bound_bits(nc, a.h.R);
+        const uint32_t most = (uint32_t)chunk_bound_bits(nc, R);
         if (Pi > top || top - Pi > most) Pi = top - most;
     }
-    ring_or(sm, ring_byte, Pi + li * a.h.R, li < lanes ? X - L : 0u);
-    if (nc > 0) {
-        while (fmark > (Pi >> 5)) {
-            fmark -= 128;
-            flush_block(fmark);
-        }
+    {
+        const uint32_t sa = 2 * j < lanes ? Xa - L : 0u, sb = 2 * j + 1 < lanes ? Xb - L : 0u;
+        ring_or2(ring_byte, Pi + 2 * j * R, sa | (sb << R));
     }
-    if (chunk < n_chunks && li == 0) {
+    while (fmark > (Pi >> 5)) {
+        fmark -= kEFlush;
+        flush_block(fmark);
+    }
+    const uint32_t ulog = size_unit_log2(a.h.C, R);
+    if (chunk < n_chunks && j == 0) {
         a.h.meta[2 * (sg->slot_base + chunk)] = Pi;
         a.h.meta[2 * (sg->slot_base + chunk) + 1] = pay;
-        atomicAdd(&agg_s[0], chunk_bytes_of(a.h.slot_dwords * 32 - Pi, size_unit_log2(a.h.C, a.h.R)));
+        atomicAdd(&agg_s[0], chunk_bytes_of(top - Pi, ulog));
         atomicAdd(&agg_s[1], pay);
     }
     __syncthreads();
     if (tid < 2) a.h.agg[2 * block + tid] = agg_s[tid];
-    bad &= 0x8000u;
+    bad &= 0x80000000u;
     if (mismatch) report(a.h.status, SH_ERR_INVALID_ARG, true);
     else if (unusable) report(a.h.status, SH_ERR_UNSUPPORTED, chunk < n_chunks);
     report(a.h.status, SH_ERR_SYMBOL_NOT_IN_TABLE, bad != 0);
@@ -396,7 +466,7 @@ __global__ __launch_bounds__(256) void k_encode_compact(const A a) {
 // ------------------------------------------------------------------------------------
 // encode, kernels 2 and 3 in one (segments of at most kPlaceMaxChunks chunks): every block
 // finds the offset of its first chunk from the chunk kernel's per-block aggregates (the
-// container bytes of 8 chunks each) and the sizes of at most 4 chunks after the last whole
+// container bytes of 16 chunks each) and the sizes of at most 15 chunks after the last whole
 // aggregate, writes its chunks' index entries and moves them into place; the segment's
 // first block writes the header and its last block the index end and the totals.
 // ------------------------------------------------------------------------------------
@@ -423,8 +493,8 @@ __global__ __launch_bounds__(256) void k_encode_place(const A a) {
 
     // bytes of the chunk-kernel blocks before c0 (c0 / 8 of them); in the last block also
     // the field bits of all of them
-    const uint32_t nb_before = c0 / kChunksPerBlockE;
-    const uint32_t nb_all = (n_chunks + kChunksPerBlockE - 1) / kChunksPerBlockE;
+    const uint32_t nb_before = c0 / kEncodeChunksPerBlock;
+    const uint32_t nb_all = (n_chunks + kEncodeChunksPerBlock - 1) / kEncodeChunksPerBlock;
     uint32_t bytes = 0;
     uint64_t fbits = 0;
     for (uint32_t e = tid; e < (last ? nb_all : nb_before); e += 256) {
@@ -443,7 +513,7 @@ __global__ __launch_bounds__(256) void k_encode_place(const A a) {
     uint32_t off = red_b[0] + red_b[1] + red_b[2] + red_b[3];
     // then the chunks from the last whole aggregate up to this wavefront's chunk
     const uint32_t c = c0 + wv;
-    for (uint32_t j = nb_before * kChunksPerBlockE; j < c && j < n_chunks; ++j) off += chunk_bytes(j);
+    for (uint32_t j = nb_before * kEncodeChunksPerBlock; j < c && j < n_chunks; ++j) off += chunk_bytes(j);
 
     if (c0 == 0)
         for (uint32_t i = tid; i < index_at / 4; i += 256)
@@ -481,8 +551,8 @@ sh_status launch_encode(const CodecArgs& a, uint32_t total_blocks, uint32_t tota
     with_kernel_args(a, [&](const auto& k) {
         using K = std::decay_t<decltype(k)>;
         if (total_blocks > 0)
-            hipLaunchKernelGGL(k_encode_chunks<K>, dim3(total_blocks), dim3(kEncBlock),
-                               4 * encode_lds_dwords(a.L), s, k);
+            hipLaunchKernelGGL(k_encode_chunks<K>, dim3(total_blocks), dim3(kEncRowsBlock),
+                               encode_lds_bytes(a.L), s, k);
         if (place) {
             hipLaunchKernelGGL(k_encode_place<K>, dim3(total_blocks_c), dim3(256), 0, s, k);
             return;
