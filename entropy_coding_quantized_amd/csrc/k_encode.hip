@@ -358,6 +358,7 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
 __device__ __forceinline__ void move_chunk(const uint32_t* src, uint32_t slot_dwords,
                                            uint32_t start, uint8_t* c, uint32_t d0, uint32_t d1,
                                            uint32_t lane) {
+    typedef uint32_t v4u_d __attribute__((ext_vector_type(4), aligned(4)));  // dword aligned
     auto bits32 = [&](uint32_t bit) {  // 32 slot bits from bit on
         const uint32_t w = bit >> 5;
         const uint32_t lo = w < slot_dwords ? src[w] : 0u;
@@ -368,7 +369,26 @@ __device__ __forceinline__ void move_chunk(const uint32_t* src, uint32_t slot_dw
     const uint32_t head_end = 4 * q0 < d1 ? 4 * q0 : d1;    // bytes [d0, head_end)
     const uint32_t tail_at = 4 * q1 > head_end ? 4 * q1 : head_end;  // bytes [tail_at, d1)
     uint32_t* cw = reinterpret_cast<uint32_t*>(c);
-    for (uint32_t q = q0 + lane; q < q1; q += 64) cw[q] = bits32(start + 8 * (4 * q - d0));
+    // whole dwords four at a time: dword q0 + i takes the slot bits from sb0 + 32 i on, so
+    // every lane's four come from five consecutive slot dwords and one shift
+    const uint32_t sb0 = start + 8 * (4 * q0 - d0);
+    const uint32_t w0 = sb0 >> 5, sh = sb0 & 31;
+    for (uint32_t i = 4 * lane; q0 + i < q1; i += 256) {
+        const uint32_t w = w0 + i;
+        if (q0 + i + 4 <= q1 && w + 5 <= slot_dwords) {
+            const v4u_d a = *reinterpret_cast<const v4u_d*>(src + w);
+            const uint32_t e = src[w + 4];
+            v4u_d o;
+            o[0] = __builtin_amdgcn_alignbit(a[1], a[0], sh);
+            o[1] = __builtin_amdgcn_alignbit(a[2], a[1], sh);
+            o[2] = __builtin_amdgcn_alignbit(a[3], a[2], sh);
+            o[3] = __builtin_amdgcn_alignbit(e, a[3], sh);
+            *reinterpret_cast<v4u_d*>(cw + q0 + i) = o;
+        } else {
+            for (uint32_t k = 0; k < 4 && q0 + i + k < q1; ++k)
+                cw[q0 + i + k] = bits32(sb0 + 32 * (i + k));
+        }
+    }
     if (lane < 3) {
         const uint32_t b = d0 + lane;
         if (b < head_end) c[b] = (uint8_t)bits32(start + 8 * (b - d0));
@@ -491,7 +511,7 @@ __global__ __launch_bounds__(256) void k_encode_place(const A a) {
         return chunk_bytes_of(a.h.slot_dwords * 32 - meta[2 * ch], ulog);
     };
 
-    // bytes of the chunk-kernel blocks before c0 (c0 / 8 of them); in the last block also
+    // bytes of the chunk-kernel blocks before c0 (c0 / 16 of them); in the last block also
     // the field bits of all of them
     const uint32_t nb_before = c0 / kEncodeChunksPerBlock;
     const uint32_t nb_all = (n_chunks + kEncodeChunksPerBlock - 1) / kEncodeChunksPerBlock;
@@ -511,9 +531,15 @@ __global__ __launch_bounds__(256) void k_encode_place(const A a) {
     }
     __syncthreads();
     uint32_t off = red_b[0] + red_b[1] + red_b[2] + red_b[3];
-    // then the chunks from the last whole aggregate up to this wavefront's chunk
+    // then the chunks from the last whole aggregate up to this wavefront's chunk (at most 15),
+    // one per lane
     const uint32_t c = c0 + wv;
-    for (uint32_t j = nb_before * kEncodeChunksPerBlock; j < c && j < n_chunks; ++j) off += chunk_bytes(j);
+    {
+        const uint32_t j = nb_before * kEncodeChunksPerBlock + lane;
+        uint32_t part = j < c && j < n_chunks ? chunk_bytes(j) : 0u;
+        for (int sh = 8; sh >= 1; sh >>= 1) part += __shfl_xor(part, sh, 64);
+        off += __builtin_amdgcn_readfirstlane(part);
+    }
 
     if (c0 == 0)
         for (uint32_t i = tid; i < index_at / 4; i += 256)
