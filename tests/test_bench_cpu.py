@@ -18,7 +18,8 @@ pytestmark = pytest.mark.filterwarnings("ignore")
 def _write_counters(path, workload, rows):
     os.makedirs(path, exist_ok=True)
     with open(os.path.join(path, f"{workload}_counter_collection.csv"), "w", newline="") as f:
-        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"])
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name",
+                                          "Counter_Value"])
         w.writeheader()
         for r in rows:
             w.writerow(r)
@@ -28,26 +29,31 @@ def test_summarize_counters_scales_by_the_calibration_copy(tmp_path):
     wl = "tiny"
     prof = tmp_path / "prof"
     copy_grid = (256 << 20) // 2048
-    # FETCH_SIZE reads half of the copy's 256 MiB, WRITE_SIZE all of it
+    # FETCH_SIZE reads half of the copy's 256 MiB, WRITE_SIZE all of it.  The calibration
+    # copies come after the last decode; a copy with the same grid before it is another copy
     _write_counters(prof / f"pmc_FETCH_SIZE_{wl}", wl, [
-        {"Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": copy_grid,
-         "Counter_Name": "FETCH_SIZE", "Counter_Value": 131072.0},
-        {"Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": 64,  # another copy: ignored
+        {"Dispatch_Id": 1, "Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": copy_grid,
+         "Counter_Name": "FETCH_SIZE", "Counter_Value": 2907.0},
+        {"Dispatch_Id": 2, "Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": 64,
          "Counter_Name": "FETCH_SIZE", "Counter_Value": 9.0},
-        {"Kernel_Name": "void shn::(anonymous namespace)::k_decode_rows<x>(x)", "Grid_Size": 1024,
-         "Counter_Name": "FETCH_SIZE", "Counter_Value": 100.0},
-        {"Kernel_Name": "void shn::(anonymous namespace)::k_decode_rows<x>(x)", "Grid_Size": 1024,
-         "Counter_Name": "FETCH_SIZE", "Counter_Value": 300.0}])
+        {"Dispatch_Id": 3, "Kernel_Name": "void shn::(anonymous namespace)::k_decode_rows<x>(x)",
+         "Grid_Size": 1024, "Counter_Name": "FETCH_SIZE", "Counter_Value": 100.0},
+        {"Dispatch_Id": 4, "Kernel_Name": "void shn::(anonymous namespace)::k_decode_rows<x>(x)",
+         "Grid_Size": 1024, "Counter_Name": "FETCH_SIZE", "Counter_Value": 300.0},
+        {"Dispatch_Id": 5, "Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": copy_grid,
+         "Counter_Name": "FETCH_SIZE", "Counter_Value": 131072.0}])
     _write_counters(prof / f"pmc_WRITE_SIZE_{wl}", wl, [
-        {"Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": copy_grid,
-         "Counter_Name": "WRITE_SIZE", "Counter_Value": 262144.0},
-        {"Kernel_Name": "void shn::(anonymous namespace)::k_decode_rows<x>(x)", "Grid_Size": 1024,
-         "Counter_Name": "WRITE_SIZE", "Counter_Value": 64.0}])
+        {"Dispatch_Id": 1, "Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": copy_grid,
+         "Counter_Name": "WRITE_SIZE", "Counter_Value": 5789.0},
+        {"Dispatch_Id": 3, "Kernel_Name": "void shn::(anonymous namespace)::k_decode_rows<x>(x)",
+         "Grid_Size": 1024, "Counter_Name": "WRITE_SIZE", "Counter_Value": 64.0},
+        {"Dispatch_Id": 5, "Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": copy_grid,
+         "Counter_Name": "WRITE_SIZE", "Counter_Value": 262144.0}])
     n = sum(x.size for x in bench.make_segments(wl))
     _write_counters(prof / f"pmc_SQ_{wl}", wl, [
-        {"Kernel_Name": "void shn::(anonymous namespace)::k_decode_rows<x>(x)", "Grid_Size": 1024,
-         "Counter_Name": "SQ_INSTS_VALU", "Counter_Value": float(n)},
-        {"Kernel_Name": "void shn::k_encode_chunks<1>(x)", "Grid_Size": 1024,
+        {"Dispatch_Id": 1, "Kernel_Name": "void shn::(anonymous namespace)::k_decode_rows<x>(x)",
+         "Grid_Size": 1024, "Counter_Name": "SQ_INSTS_VALU", "Counter_Value": float(n)},
+        {"Dispatch_Id": 2, "Kernel_Name": "void shn::k_encode_chunks<1>(x)", "Grid_Size": 1024,
          "Counter_Name": "SQ_INSTS_VALU", "Counter_Value": float(2 * n)}])
     out = tmp_path / "out"
     os.makedirs(out)
