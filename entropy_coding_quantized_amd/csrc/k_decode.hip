@@ -508,6 +508,19 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
     report(a.h.status, SH_ERR_CORRUPT_STREAM, err != 0 || bad_offsets != 0);
 }
 
+// The decode of launches with few chunks (sh_decode, sh_decode_batch): one chunk per
+// 32-lane half wavefront twice the wavefronts of the row decoder for the same chunks,
+// which is what a launch that cannot fill the GPU needs.  Tables of at most 256 states.
+sh_status launch_decode_halves(const CodecArgs& a, uint32_t total_blocks, void* stream) {
+    if (total_blocks == 0) return SH_OK;
+    if (a.L > (uint32_t)kDecBlock) return SH_ERR_UNSUPPORTED;
+    with_kernel_args(a, [&](const auto& k) {
+        hipLaunchKernelGGL((k_decode<1, Bytes, std::decay_t<decltype(k)>>), dim3(total_blocks),
+                           dim3(kDecBlock), 0, (hipStream_t)stream, k);
+    });
+    return hipGetLastError() == hipSuccess ? SH_OK : SH_ERR_HIP;
+}
+
 sh_status launch_decode_matvec(const CodecArgs& a, uint32_t total_blocks, void* stream) {
     if (total_blocks == 0) return SH_OK;
     if (a.nseg == 0) return SH_ERR_INVALID_ARG;  // device tables only

@@ -85,10 +85,13 @@ def test_ragged_sizes(torch_cuda, n):
     _case(torch_cuda, x)
 
 
-@pytest.mark.parametrize("n,C_", [(16384 * 64, 64), (16384 * 64 + 64, 64), (20000 * 32 + 5, 32)])
+@pytest.mark.parametrize("n,C_", [(16383 * 64, 64), (16384 * 64, 64), (16384 * 64 + 64, 64),
+                                  (20000 * 32 + 5, 32)])
 def test_chunk_counts_around_the_one_kernel_placement(torch_cuda, n, C_):
     """Up to 16384 chunks a tensor the encoder indexes and compacts in one kernel, beyond it
-    the index comes first from its own kernel: both give the oracle's container."""
+    the index comes first from its own kernel: both give the oracle's container.  The decode
+    switches kernels at the same count (half-wavefront chunks below 16384, 16-lane rows from
+    there on): both decode the oracle's container."""
     print(f"case: chunks n={n} C={C_} ({(n + C_ - 1) // C_} chunks)", flush=True)
     x = D.quantize(np.random.default_rng(n).laplace(0, 10, size=n))
     _case(torch_cuda, x, C_=C_)

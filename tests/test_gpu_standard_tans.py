@@ -65,6 +65,16 @@ def test_standard_tans_at_512_to_2048_states(torch_cuda, log2_L, host_tables):
     _roundtrip_device_tables(torch_cuda, xs, p, host_tables)
 
 
+@pytest.mark.parametrize("K,log2_L,C", [(16, 7, 34944), (256, 11, 65536)])
+def test_chunk_sizes_in_two_and_four_byte_units(torch_cuda, K, log2_L, C):
+    """Chunks whose largest valid size passes 65,535 bytes count their sizes in 2- and
+    4-byte units: encoder placement and decoder chunk search against the oracle."""
+    print(f"case: K={K} L={1 << log2_L} C={C}", flush=True)
+    p = codec.Params(K=K, log2_L=log2_L, chunk_symbols=C, streams=32)
+    xs = [D.weight().reshape(-1)[:3 * C + 4097], D.tiny(seed=11, n=C - 32)]
+    _roundtrip_device_tables(torch_cuda, xs, p, host_tables=False)
+
+
 def test_shannonic_ranges_with_more_states(torch_cuda):
     """K = 16 at L = 512: allowed while the widest range keeps every field within 16 bits."""
     print("case: K=16 L=512", flush=True)

@@ -537,3 +537,27 @@ def test_matvec_pins():
     lo, f = O.build_table(h, 16, 7)
     buf, _ = O.encode(x, lo, f, 7, 512, 32)
     assert np.array_equal(O.decode_matvec(buf, x.size, cols, a), O.matvec_i8(x, cols, a))
+
+
+@pytest.mark.parametrize("C,R,unit", [(34912, 7, 1), (34944, 7, 2), (65536, 11, 4)])
+def test_size_units_follow_the_largest_chunk(C, R, unit):
+    """Chunk sizes count units of 2^u bytes, u the smallest that lets the largest valid
+    chunk's size fit 16 bits (at log2 L = 7 a chunk of 34,912 values is at most 65,488 bytes,
+    one of 34,944 at most 65,548).  Every chunk is the fewest units that hold its bits: the
+    lanes' initial states plus its field bits, the latter from encoding the chunk alone."""
+    K = 256 if R == 11 else 16
+    x = D.tiny(seed=21, n=2 * C + 1234)
+    lo, f = O.build_table(O.histogram(x), K, R)
+    if K == 256:
+        assert max(int(b) - int(a) for a, b in zip(lo[:-1], lo[1:])) == 1
+    buf, _ = O.encode(x, lo, f, R, C, 32)
+    assert (O.decode(buf, x.size) == x).all()
+    assert CL.unit_bytes(C, R, 32) == unit
+    spans, pay0 = CL.chunk_spans(buf, x.size, K, C, R)
+    for c, (a, b) in enumerate(spans):
+        assert a % unit == 0 and (b - a) % unit == 0
+        part = x[c * C: (c + 1) * C]
+        _, field_bits = O.encode(part, lo, f, R, C, 32)
+        need = (32 * R + field_bits + 7) // 8
+        assert b - a - unit < need <= b - a, (c, b - a, need)
+    assert (buf.size - pay0) % 4 == 0 and buf.size - pay0 - spans[-1][1] < 4
