@@ -290,8 +290,9 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
 
     // One step: the pair's two fields are adjacent, stream 2j's first.  The entries were
     // read at the end of the previous step, so the serial path is scan -> ring read ->
-    // bit extract -> next entry read.
-    auto full_step = [&](const Ent& ea, const Ent& eb, Ent& na, Ent& nb, uint32_t t) {
+    // bit extract -> next entry read.  k is the step's place in the tile (a constant in the
+    // unrolled loop, so the tile writes take their offset from the instruction).
+    auto full_step = [&](const Ent& ea, const Ent& eb, Ent& na, Ent& nb, uint32_t k) {
         const uint32_t tot = need_of(ea) + need_of(eb);
         const uint32_t posm = r.pos - tot;
         const uint32_t incl = scan16(tot);
@@ -311,8 +312,11 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
         bad_offsets |= __builtin_amdgcn_ballot_w64(oa > maxo_of(ea));
         bad_offsets |= __builtin_amdgcn_ballot_w64(ob > maxo_of(eb));
         const uint32_t xa = oa + base_of(ea), xb = ob + base_of(eb);
-        typedef __attribute__((address_space(3))) uint16_t lds_w2;
-        *(lds_w2*)(uintptr_t)(r.tile + 32 * (t & (kTileSteps - 1))) = (uint16_t)((xa & 0xFF) | (xb << 8));
+        // two byte writes (volatile, so that they stay two): one VALU op fewer than packing
+        // the pair into a 16-bit write
+        typedef volatile __attribute__((address_space(3))) uint8_t lds_w1b;
+        *(lds_w1b*)(uintptr_t)(r.tile + 32 * k) = (uint8_t)xa;
+        *(lds_w1b*)(uintptr_t)(r.tile + 32 * k + 1) = (uint8_t)xb;
         r.pos += row_last(incl);
     };
     // the tile of steps [t0, t0 + kTileSteps) to the output: lane j stores its share of
@@ -341,8 +345,8 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
         for (; t < stop; t += kTileSteps) {  // the entries alternate registers step by step
 #pragma unroll
             for (uint32_t k = 0; k < kTileSteps; k += 2) {
-                full_step(ea, eb, ea2, eb2, t + k);
-                full_step(ea2, eb2, ea, eb, t + k + 1);
+                full_step(ea, eb, ea2, eb2, k);
+                full_step(ea2, eb2, ea, eb, k + 1);
                 refill();
             }
             flush_tile(t);

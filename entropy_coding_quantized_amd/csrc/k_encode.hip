@@ -25,6 +25,12 @@ constexpr uint32_t kERing = 128;                   // ring dwords per chunk
 constexpr uint32_t kEFlush = 64;                   // dwords per flush
 constexpr uint32_t kETileSteps = 16;               // input steps staged at a time
 constexpr uint32_t kETileBytes = kETileSteps * 32;
+// The four rows of a wavefront write their rings and read their tiles at similar offsets in
+// the same steps: their tiles sit 32 bytes apart beyond their size and their ring origins 8
+// dwords apart (ring dword (d + 8 row) mod 128 holds slot dword d), so that the rows use
+// different LDS banks.
+constexpr uint32_t kETileStride = kETileBytes + 32;
+constexpr uint32_t kERowTurn = 8;                  // ring dwords per row of the wavefront
 // LDS (dynamic; the kernel's only LDS, so it starts at LDS byte 0): the value entries (two
 // dwords per value, at a 2 KB boundary so that an entry's address is one AND-OR), the
 // rings (512 B each, 512 B aligned), the encTable (a dword per slot, holding the next
@@ -37,7 +43,7 @@ __host__ __device__ constexpr uint32_t encode_tiles_byte(uint32_t L) {
     return (kEEsByte + 4 * L + 15) / 16 * 16;
 }
 __host__ __device__ constexpr uint32_t encode_lds_bytes(uint32_t L) {
-    return encode_tiles_byte(L) + kEncodeChunksPerBlock * kETileBytes + 16;
+    return encode_tiles_byte(L) + kEncodeChunksPerBlock * kETileStride + 16;
 }
 static_assert(kEEsByte >= 4 * kMaxLGpu && kEEsByte + 4 * kMaxLGpu < 32768,
               "encTable addresses stay positive and below bit 15 of an entry");
@@ -109,10 +115,10 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
     const uint32_t L = a.h.L, R = a.h.R, R1 = a.h.R + 1;
     const uint32_t base = lds_offset(esm);  // 0: the only LDS of the kernel
     const uint32_t ring_byte = base + kERingsByte + 4 * kERing * rowi;
-    const uint32_t tile_byte = base + encode_tiles_byte(L) + kETileBytes * rowi;
+    const uint32_t tile_byte = base + encode_tiles_byte(L) + kETileStride * rowi;
     const uint32_t vt_byte = base + kEVtByte, es_byte = base + kEEsByte;
     uint32_t* agg_s = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(esm) + encode_tiles_byte(L) +
-                                                  kEncodeChunksPerBlock * kETileBytes);
+                                                  kEncodeChunksPerBlock * kETileStride);
 
     // the tables in their LDS form (device form: v0 = bias, v1 = o | w << 8 | (f == 0) << 15 |
     // (start + kMaxLGpu) << 16, start = cum - f; encTable entries are slots)
@@ -185,14 +191,17 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
     if (steps > 0) load_tile((steps - 1) / kETileSteps, p0, p1);
     __syncthreads();
 
-    uint32_t P = a.h.slot_dwords * 32;   // fields go below P, right to left
+    // bit positions are kept turned by the row's ring origin: position p stands for slot bit
+    // p - turn
+    const uint32_t turn = 32 * kERowTurn * row;
+    uint32_t P = a.h.slot_dwords * 32 + turn;   // fields go below P, right to left
     uint32_t fmark = a.h.slot_dwords;    // dwords at or above fmark are in the slot
-    uint32_t flush_at = (fmark - kEFlush) * 32;  // once P is below this, flush a block
+    uint32_t flush_at = (fmark - kEFlush) * 32 + turn;  // once P is below this, flush a block
     uint32_t bad = 0;                    // entries OR-ed in: bit 31 marks a range without states
 
     auto flush_block = [&](uint32_t blk) {  // ring dwords [blk, blk + 64) -> slot
         typedef __attribute__((address_space(3))) v4u lds_v4;
-        lds_v4* r = (lds_v4*)(uintptr_t)(ring_byte + 4 * ((blk + 4 * j) & (kERing - 1)));
+        lds_v4* r = (lds_v4*)(uintptr_t)(ring_byte + 4 * ((blk + kERowTurn * row + 4 * j) & (kERing - 1)));
         const v4u v = *r;
         *r = v4u{0, 0, 0, 0};
         __builtin_amdgcn_raw_buffer_store_b128(v, rslot, (int)(slot_row + 4 * (blk + 4 * j)), 0, 0);
@@ -315,19 +324,19 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
     }
     __builtin_amdgcn_s_setprio(0);
     const uint32_t top = a.h.slot_dwords * 32;
-    const uint32_t pay = top - P;  // field bits
+    const uint32_t pay = top + turn - P;  // field bits
     // the streams' final states, the decoder's initial states, in front of the fields.  A
     // valid encode never exceeds the chunk's bound; the span recorded for the placement is
     // clamped to it all the same, so that no table, however corrupt, moves the placement
     // outside the container's bound
-    uint32_t Pi = P - lanes * R;
+    uint32_t Pi = P - turn - lanes * R;
     {
         const uint32_t most = (uint32_t)chunk_bound_bits(nc, R);
         if (Pi > top || top - Pi > most) Pi = top - most;
     }
     {
         const uint32_t sa = 2 * j < lanes ? Xa - L : 0u, sb = 2 * j + 1 < lanes ? Xb - L : 0u;
-        ring_or2(ring_byte, Pi + 2 * j * R, sa | (sb << R));
+        ring_or2(ring_byte, Pi + turn + 2 * j * R, sa | (sb << R));
     }
     while (fmark > (Pi >> 5)) {
         fmark -= kEFlush;
