@@ -35,16 +35,19 @@ struct DecodePath {
     sh_status (*launch)(const CodecArgs&, uint32_t, void*);
 };
 DecodePath decode_path(uint64_t total_chunks, const sh_params* p) {
-    if (total_chunks < kHalfDecodeMaxChunks && p->log2_L <= (uint32_t)kInlineMaxLog2L)
-        return {kChunksPerBlock, launch_decode_halves};
+    if (total_chunks < kHalfDecodeMaxChunks) {
+        if (p->streams == kStreamsWide) return {kWideHalvesChunksPerBlock, launch_decode_wide_halves};
+        if (p->log2_L <= (uint32_t)kInlineMaxLog2L) return {kChunksPerBlock, launch_decode_halves};
+    }
     return {kDecodeChunksPerBlock, launch_decode};
 }
 constexpr uint32_t kChunksPerBlockC = 4;  // compaction kernel
 
 bool gpu_params_ok(const sh_params* p) {
     return p && p->K >= 1 && p->K <= 256 && p->log2_L >= 1 && p->log2_L <= (uint32_t)kMaxLog2LGpu &&
-           p->streams == (uint32_t)kLanes && p->chunk_symbols >= 32 &&
-           p->chunk_symbols <= kMaxChunk && p->chunk_symbols % 32 == 0;
+           (p->streams == kStreamsNarrow || p->streams == kStreamsWide) &&
+           p->chunk_symbols >= p->streams && p->chunk_symbols <= kMaxChunk &&
+           p->chunk_symbols % p->streams == 0;
 }
 
 // INVALID_ARG for nonsense, UNSUPPORTED for valid parameters the GPU path does not take
@@ -64,12 +67,13 @@ uint64_t payload_at_of(uint64_t nch, const sh_params* p) {
 // container bytes at most: every chunk at its bound, in whole size units
 uint64_t bound_of(uint64_t n, const sh_params* p) {
     const uint64_t nch = n_chunks_of(n, p->chunk_symbols);
-    const uint32_t u = size_unit_log2(p->chunk_symbols, p->log2_L);
+    const uint32_t u = size_unit_log2(p->chunk_symbols, p->log2_L, p->streams);
     uint64_t payload = 0;
     if (nch > 0) {
-        payload += ((uint64_t)chunk_bound_units(p->chunk_symbols, p->log2_L, u) << u) * (nch - 1);
+        payload += ((uint64_t)chunk_bound_units(p->chunk_symbols, p->log2_L, u, p->streams) << u) *
+                   (nch - 1);
         const uint64_t last = n - (nch - 1) * p->chunk_symbols;
-        payload += (uint64_t)chunk_bound_units((uint32_t)last, p->log2_L, u) << u;
+        payload += (uint64_t)chunk_bound_units((uint32_t)last, p->log2_L, u, p->streams) << u;
     }
     return payload_at_of(nch, p) + (payload + 3) / 4 * 4;
 }
@@ -90,7 +94,7 @@ struct EncLayout {
 };
 EncLayout enc_layout(uint64_t total_slots, const sh_params* p) {
     EncLayout l;
-    l.slot_dwords = encode_slot_dwords(p->chunk_symbols, p->log2_L);
+    l.slot_dwords = encode_slot_dwords(p->chunk_symbols, p->log2_L, p->streams);
     l.meta_at = align256(total_slots * l.slot_dwords * 4);
     l.agg_at = l.meta_at + align256(8 * total_slots);
     l.bytes = l.agg_at + align256(8 * (total_slots / kEncodeChunksPerBlock + kMaxInlineSegs)) + 256;
@@ -126,7 +130,8 @@ void fill_codec_common(CodecArgs& a, const sh_params* p, int32_t* d_status) {
     a.R = p->log2_L;
     a.L = 1u << p->log2_L;
     a.K = p->K;
-    a.slot_dwords = encode_slot_dwords(p->chunk_symbols, p->log2_L);
+    a.S = p->streams;
+    a.slot_dwords = encode_slot_dwords(p->chunk_symbols, p->log2_L, p->streams);
     a.status = d_status;
 }
 
@@ -358,7 +363,7 @@ sh_status sh_encode(const sh_table* table, const sh_params* params, const int8_t
         if (derive_slots(*table, &slots) != SH_OK) return SH_ERR_INVALID_ARG;
         derive_kernel_tables(*table, slots, nullptr, a.one.tab, a.one.es);
     }
-    write_header(*table, n, params->chunk_symbols, (uint32_t)kLanes, nch, a.one.hdr);
+    write_header(*table, n, params->chunk_symbols, params->streams, nch, a.one.hdr);
     SegDesc& sd = a.one.seg;
     sd.x = (uint8_t*)d_x;
     sd.c = d_out;
@@ -393,7 +398,7 @@ sh_status sh_decode(const sh_table* table, const sh_params* params, const uint8_
     SlotTables slots;
     if (derive_slots(*table, &slots) != SH_OK) return SH_ERR_INVALID_ARG;
     derive_kernel_tables(*table, slots, a.one.tab, nullptr, nullptr);
-    write_header(*table, n, params->chunk_symbols, (uint32_t)kLanes, nch, a.one.hdr);
+    write_header(*table, n, params->chunk_symbols, params->streams, nch, a.one.hdr);
     SegDesc& sd = a.one.seg;
     sd.x = (uint8_t*)d_y;
     sd.c = (uint8_t*)d_in;
@@ -519,6 +524,7 @@ sh_status sh_decode_matvec_batch(const void* d_tables, const uint8_t* const* d_i
     sh_status st = check_params(params);
     if (st != SH_OK) return st;
     if (cols % 32 != 0 || cols > kMaxMatvecCols) return SH_ERR_UNSUPPORTED;
+    if (params->streams != kStreamsNarrow) return SH_ERR_UNSUPPORTED;  // half-wavefront kernel
     if (params->log2_L > (uint32_t)kInlineMaxLog2L) return SH_ERR_UNSUPPORTED;  // one slot a thread
     if (!aligned(d_status, 4)) return SH_ERR_INVALID_ARG;
     for (uint32_t i = 0; i < nseg; ++i) {

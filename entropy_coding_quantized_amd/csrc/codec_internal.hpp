@@ -17,7 +17,9 @@
 namespace shn {
 
 constexpr int kLgFrac = 24;            // fractional bits of the DP's fixed-point log2
-constexpr int kLanes = 32;             // interleaved tANS lanes per chunk (a half wavefront)
+// interleaved tANS streams per chunk on the GPU path: 32 (two a lane of a 16-lane row, or
+// one a lane of a half wavefront) or 64 (four a lane of a 16-lane row)
+constexpr uint32_t kStreamsNarrow = 32, kStreamsWide = 64;
 constexpr int kMaxLog2LHost = 12;      // host table build
 // GPU path: L up to 2048 states (standard tANS sizes), tables held in LDS; the decoder
 // takes two adjacent fields in one 32-bit window, so a table is usable on the GPU only when
@@ -68,23 +70,24 @@ inline uint32_t floor_log2_u32(uint32_t x) {
 constexpr uint32_t kGroupChunks = 64;
 inline uint32_t header_bytes(uint32_t K) { return (kHeaderFixed + 3 * K - 1 + 3) / 4 * 4; }
 inline uint64_t n_chunks_of(uint64_t n, uint32_t C) { return (n + C - 1) / C; }
-// bits of the largest chunk of nc values a valid stream holds: every field at 8 + R bits
-SHN_HD inline uint64_t chunk_bound_bits(uint32_t nc, uint32_t R) {
-    const uint64_t lanes = nc < (uint32_t)kLanes ? nc : (uint32_t)kLanes;
+// bits of the largest chunk of nc values a valid stream of S streams holds: the initial
+// states and every field at 8 + R bits
+SHN_HD inline uint64_t chunk_bound_bits(uint32_t nc, uint32_t R, uint32_t S) {
+    const uint64_t lanes = nc < S ? nc : S;
     return lanes * R + (uint64_t)nc * (8 + R);
 }
 // ... in 32-bit words (the encoder's per-chunk workspace slots)
-SHN_HD inline uint32_t chunk_bound_dwords(uint32_t nc, uint32_t R) {
-    return (uint32_t)((chunk_bound_bits(nc, R) + 31) / 32);
+SHN_HD inline uint32_t chunk_bound_dwords(uint32_t nc, uint32_t R, uint32_t S) {
+    return (uint32_t)((chunk_bound_bits(nc, R, S) + 31) / 32);
 }
-SHN_HD inline uint32_t size_unit_log2(uint32_t C, uint32_t R) {
-    const uint64_t most = (chunk_bound_bits(C, R) + 7) / 8;
+SHN_HD inline uint32_t size_unit_log2(uint32_t C, uint32_t R, uint32_t S) {
+    const uint64_t most = (chunk_bound_bits(C, R, S) + 7) / 8;
     uint32_t u = 0;
     while (((most + (1ull << u) - 1) >> u) > 0xFFFFull) ++u;
     return u;
 }
-SHN_HD inline uint32_t chunk_bound_units(uint32_t nc, uint32_t R, uint32_t u) {
-    return (uint32_t)((chunk_bound_bits(nc, R) + (8ull << u) - 1) >> (3 + u));
+SHN_HD inline uint32_t chunk_bound_units(uint32_t nc, uint32_t R, uint32_t u, uint32_t S) {
+    return (uint32_t)((chunk_bound_bits(nc, R, S) + (8ull << u) - 1) >> (3 + u));
 }
 SHN_HD inline uint32_t n_groups_of(uint32_t nch) { return (nch + kGroupChunks - 1) / kGroupChunks; }
 // bytes of the index, and where its sizes start (relative to index_at)
@@ -158,7 +161,7 @@ constexpr uint32_t kMaxInlineSegs = 48;  // descriptors carried in one launch's 
 // launch on the host grows with the size of its arguments.
 struct CodecArgs {
     uint32_t nseg;          // 0: a single segment with host-built tables (one), else many
-    uint32_t C, R, L, K;
+    uint32_t C, R, L, K, S;
     union {
         uint32_t slot_dwords;   // encode: dwords per slot, a multiple of 128
         uint32_t cols;          // decode into a matrix-vector product: values per row
@@ -180,7 +183,7 @@ struct CodecArgs {
 
 // ---- kernel argument blocks ----
 struct KHead {
-    uint32_t nseg, C, R, L, K;
+    uint32_t nseg, C, R, L, K, S;
     union {
         uint32_t slot_dwords;
         uint32_t cols;
@@ -236,15 +239,19 @@ constexpr uint32_t kArgBytes = 257 * 256;
 sh_status launch_histogram(const HistArgs& h, uint32_t nseg_zero, void* stream);
 sh_status launch_build_tables(const BuildArgs& b, void* stream);
 // the decode behind sh_decode and sh_decode_batch (k_decode_rows.hip): one chunk per
-// 16-lane row, kDecodeChunksPerBlock chunks a block, decode_lds_bytes(L) of LDS a block
+// 16-lane row (two or four streams a lane), kDecodeChunksPerBlock chunks a block; and, for
+// launches of few chunks of 64 streams, one chunk per half wavefront (two streams a lane),
+// kWideHalvesChunksPerBlock chunks a block
 constexpr uint32_t kDecodeChunksPerBlock = 16;
-uint32_t decode_lds_bytes(uint32_t L);
 sh_status launch_decode(const CodecArgs& a, uint32_t total_blocks, void* stream);
+constexpr uint32_t kWideHalvesChunksPerBlock = 8;
+sh_status launch_decode_wide_halves(const CodecArgs& a, uint32_t total_blocks, void* stream);
 // decode into a matrix-vector product: the vector is staged in LDS, so rows are at most
 // this many values long
 constexpr uint32_t kMaxMatvecCols = 16384;
 sh_status launch_decode_matvec(const CodecArgs& a, uint32_t total_blocks, void* stream);
-// the encoder's chunk kernel: one chunk per 16-lane row, 16 chunks a block
+// the encoder's chunk kernel: one chunk per 16-lane row (two or four streams a lane), 16
+// chunks a block
 constexpr uint32_t kEncodeChunksPerBlock = 16;
 // segments of at most this many chunks are indexed and compacted by one kernel
 // (k_encode_place: each block sums the sizes of the chunks before its own, so the work
@@ -255,8 +262,8 @@ sh_status launch_encode(const CodecArgs& a, uint32_t total_blocks, uint32_t tota
                         void* stream);
 
 // encode workspace layout
-inline uint32_t encode_slot_dwords(uint32_t C, uint32_t R) {
-    uint32_t d = chunk_bound_dwords(C, R) + 1;
+inline uint32_t encode_slot_dwords(uint32_t C, uint32_t R, uint32_t S) {
+    uint32_t d = chunk_bound_dwords(C, R, S) + 1;
     return (d + 127) / 128 * 128;
 }
 

@@ -129,8 +129,8 @@ __device__ __forceinline__ const uint16_t* inline_es(const KSegs<N>&) { return n
 
 // ---- host side: the smallest argument block for a launch ----
 inline KHead kernel_head(const CodecArgs& a) {
-    return KHead{a.nseg ? a.nseg : 1, a.C, a.R, a.L, a.K, {a.slot_dwords}, a.status, a.slots, a.meta,
-                 a.agg};
+    return KHead{a.nseg ? a.nseg : 1, a.C, a.R, a.L, a.K, a.S, {a.slot_dwords}, a.status, a.slots,
+                 a.meta, a.agg};
 }
 inline KOne kernel_one(const CodecArgs& a) {
     KOne k;

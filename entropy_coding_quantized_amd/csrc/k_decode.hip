@@ -233,7 +233,7 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
     const uint64_t n = sg->n;
     const uint32_t index_at = header_bytes_dev(a.h.K);
     const uint32_t payload_at = index_at + (uint32_t)index_bytes_of(n_chunks);
-    const uint32_t ulog = size_unit_log2(a.h.C, a.h.R);  // chunk sizes count 2^ulog bytes
+    const uint32_t ulog = size_unit_log2(a.h.C, a.h.R, kStreamsNarrow);  // units of 2^ulog bytes
     const uint64_t in_nbytes = sg->c_bytes;
 
     // The prologue's loads go out in two waves: first everything that needs nothing else
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
             const uint64_t first = (uint64_t)chunk * a.h.C;
             const uint32_t m = (uint32_t)((n - first) < a.h.C ? (n - first) : a.h.C);
             const uint64_t at = (uint64_t)payload_at + gs.head + c_rel;  // the chunk's first byte
-            const bool ok = gs.ok && (c_bytes >> ulog) <= chunk_bound_units(m, a.h.R, ulog) &&
+            const bool ok = gs.ok && (c_bytes >> ulog) <= chunk_bound_units(m, a.h.R, ulog, kStreamsNarrow) &&
                             at + c_bytes <= in_nbytes;
             if (ok) {
                 c.nc = m;
@@ -513,7 +513,7 @@ __global__ __launch_bounds__(kDecBlock) void k_decode(const A a) {
 // which is what a launch that cannot fill the GPU needs.  Tables of at most 256 states.
 sh_status launch_decode_halves(const CodecArgs& a, uint32_t total_blocks, void* stream) {
     if (total_blocks == 0) return SH_OK;
-    if (a.L > (uint32_t)kDecBlock) return SH_ERR_UNSUPPORTED;
+    if (a.L > (uint32_t)kDecBlock || a.S != kStreamsNarrow) return SH_ERR_UNSUPPORTED;
     with_kernel_args(a, [&](const auto& k) {
         hipLaunchKernelGGL((k_decode<1, Bytes, std::decay_t<decltype(k)>>), dim3(total_blocks),
                            dim3(kDecBlock), 0, (hipStream_t)stream, k);
@@ -524,6 +524,7 @@ sh_status launch_decode_halves(const CodecArgs& a, uint32_t total_blocks, void* 
 sh_status launch_decode_matvec(const CodecArgs& a, uint32_t total_blocks, void* stream) {
     if (total_blocks == 0) return SH_OK;
     if (a.nseg == 0) return SH_ERR_INVALID_ARG;  // device tables only
+    if (a.S != kStreamsNarrow) return SH_ERR_UNSUPPORTED;
     with_kernel_args(a, [&](const auto& k) {
         using K = std::decay_t<decltype(k)>;
         if constexpr (!std::is_same_v<K, KOne>) {

@@ -5,44 +5,64 @@
 // talk notes, "Runtime encoding/decoding" (paper section 4.2): from the state X the decode
 // table gives the range s and the count of state bits; the offset o is read as w_s raw
 // bits, the value is base[s] + o, and the state bits lead to the next state.  Table
-// lookups, shifts, masks and adds only.  The container layout (chunks of C values, 32
+// lookups, shifts, masks and adds only.  The container layout (chunks of C values, 32 or 64
 // interleaved tANS streams per chunk, fields in (step, stream) order) and the GPU mapping
 // below are this library's own design; the pages give no GPU design.
 //
-// Mapping: one chunk per 16-lane DPP row, so a wavefront decodes four chunks side by side.
-// Lane j of a row runs the two streams 2j and 2j+1, whose fields are adjacent in every
-// step: one 16-lane prefix sum (four DPP row shifts) of the pair's field lengths gives the
-// pair's bit position, and one two-dword LDS read brings both fields.  Compressed words
-// reach a per-chunk LDS ring through 128-bit loads; the decode table is staged in LDS as
-// 8-byte entries (measured on MI355X: a random 8-byte LDS read costs 7 clocks per
-// wavefront and CU at full occupancy, a 16-byte one 12, a 12-byte one 20).  No MFMA: there
-// is no dense contraction.
+// Mapping: one chunk per row of W lanes, a 16-lane DPP row (W = 16) or a half wavefront
+// (W = 32), so a wavefront decodes 64 / W chunks side by side.  Lane j of a row runs P
+// adjacent streams, P j to P j + P - 1 (W P streams a chunk: 16 x 2 for chunks of 32
+// streams, 16 x 4 or 32 x 2 for chunks of 64), whose fields are adjacent in every step: one
+// W-lane prefix sum (DPP) of the lanes' field lengths gives every lane's bit position, and
+// one LDS read of two (P = 2) or three (P = 4) ring dwords brings all its fields.  Rows of 32
+// lanes give a launch with few chunks twice the wavefronts of rows of 16.
+// Compressed words reach a per-chunk LDS ring through 128-bit loads; the decode table is
+// staged in LDS as 8-byte entries (measured on MI355X: a random 8-byte LDS read costs 7
+// clocks per wavefront and CU at full occupancy, a 16-byte one 12, a 12-byte one 20).  No
+// MFMA: there is no dense contraction.
 #include "device_common.hpp"
 
 namespace shn {
 
 namespace {
 
-constexpr int kRowsBlock = 256;                    // 4 wavefronts, 16 rows = 16 chunks
-constexpr uint32_t kRowsPerBlock = kRowsBlock / 16;
+constexpr int kRowsBlock = 256;                    // 4 wavefronts, 256 / W rows = chunks
 constexpr uint32_t kRRingLog2 = 8;
 constexpr uint32_t kRRing = 1u << kRRingLog2;      // compressed dwords resident per chunk
-// a ring is followed by a copy of its dword 0 (a two-dword read never wraps) and padding
-// that keeps the next ring 16-byte aligned for the 128-bit LDS writes
+// a ring is followed by copies of its first dwords (a lane's read of two or three dwords
+// never wraps) and padding that keeps the next ring 16-byte aligned for the 128-bit writes
 constexpr uint32_t kRRingStride = kRRing + 4;
 constexpr uint32_t kRFill = kRRing / 2;            // dwords per refill
-constexpr uint32_t kFillVecs = kRFill / 64;        // 16-byte loads per lane and refill
 // Decoded bytes of kTileSteps steps of a chunk are gathered in an LDS tile and stored
 // together: measured on MI355X, the 32-byte stores of single steps held the decode near
 // 1.7 TB/s of output however short the rest of the step was.  The tiles of a block's rows
-// sit kTileStride dwords apart, 8 dwords more than a tile, so that the four rows of a
-// wavefront write different LDS banks in the same step.  (Measured side by side on one
-// GPU: 4-step tiles with 256-dword rings, 8-step tiles, 128-dword rings and a two-step
-// write through a neighbour exchange all decode the model workload within 5% of each
-// other; the simplest is kept.)
+// sit 8 dwords more than a tile apart, so that the four rows of a wavefront write
+// different LDS banks in the same step.  (Measured side by side on one GPU: 4-step tiles
+// with 256-dword rings, 8-step tiles, 128-dword rings and a two-step write through a
+// neighbour exchange all decode the model workload within 5% of each other; the simplest
+// is kept.)
 constexpr uint32_t kTileSteps = 4;
-constexpr uint32_t kTileDwords = kTileSteps * 32 / 4;
-constexpr uint32_t kTileStride = kTileDwords + 8;
+
+// Geometry of a row of W lanes that run P streams each.
+template <int W, int P>
+struct RowGeom {
+    static_assert((W == 16 && (P == 2 || P == 4)) || (W == 32 && P == 2), "16 x 2, 16 x 4, 32 x 2");
+    static constexpr uint32_t kS = W * P;                      // streams of a chunk
+    static constexpr uint32_t kRowsPerWave = 64 / W;
+    static constexpr uint32_t kRowsPerBlock = kRowsBlock / W;
+    static constexpr uint32_t kFillVecs = kRFill / (4 * W);    // 16-byte loads a lane, a refill
+    static constexpr uint32_t kTileDwords = kTileSteps * kS / 4;
+    static constexpr uint32_t kTileStride = kTileDwords + 8;
+    static constexpr uint32_t kWin = P == 2 ? 2 : 3;           // ring dwords a lane reads a step
+    // Refills are checked every other step.  A step's fields take at most kS * 16 bits, kS / 2
+    // dwords, and a lane reads up to kWin - 1 dwords past its first bit's dword; so once the
+    // position is below (res_hi - kMargin) * 32 the next two steps read only dwords below
+    // res_hi, and from there on a refill is due: the dwords it overwrites, those below
+    // res_hi - kRFill, are all read, and the kS dwords two steps advance at most leave the
+    // next refill for a later check.
+    static constexpr uint32_t kMargin = kS + kWin - 1;
+    static_assert(kMargin <= kRFill && kS < kRFill, "one refill a check, over read dwords only");
+};
 
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef const __attribute__((address_space(3))) v2u lds_v2u;
@@ -71,6 +91,12 @@ __device__ __forceinline__ uint32_t scan16(uint32_t v) {
     v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr:8
     return v;
 }
+// ... within each row of W lanes
+template <int W>
+__device__ __forceinline__ uint32_t scan_row(uint32_t v) {
+    if constexpr (W == 16) return scan16(v);
+    else return scan32(v);
+}
 
 // The ring's dword index of a bit position, (pos >> 5) mod 256, as one v_bfe_u32 (the
 // compiler would split the extract and the scaling that follows it into three operations).
@@ -80,15 +106,18 @@ __device__ __forceinline__ uint32_t ring_dword(uint32_t pos) {
     return d;
 }
 
-// Value of lane 15 of this lane's row (DPP row_newbcast:15).
+// Value of the last lane of this lane's row of W lanes: lane 15 of a 16-lane row (DPP
+// row_newbcast:15), lane 31 of a half wavefront (ds_swizzle).
+template <int W>
 __device__ __forceinline__ uint32_t row_last(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x15F, 0xF, 0xF, true);
+    if constexpr (W == 16) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x15F, 0xF, 0xF, true);
+    else return bcast31(v);
 }
 
 // The decode entry of a state, 8 bytes in LDS:
 //   A = need | base << 16 | maxo << 24: need = w_s + nb, the field's length (used as a
-//       bit-field width as it is: only bits 0..4 count); base = the range's first value as
-//       int8 bits; maxo = |range| - 1, the largest valid offset
+//       bit-field width or shift as it is: only bits 0..4 count); base = the range's first
+//       value as int8 bits; maxo = |range| - 1, the largest valid offset
 //   B = w_s | next << 16: next = LDS byte address of the entry reached with zero state bits
 // A state is held as the LDS byte address of its entry.
 struct Ent {
@@ -103,21 +132,47 @@ __device__ __forceinline__ uint32_t base_of(const Ent& e) { return (e.A >> 16) &
 __device__ __forceinline__ uint32_t maxo_of(const Ent& e) { return e.A >> 24; }
 __device__ __forceinline__ uint32_t next_of(const Ent& e) { return e.B >> 16; }
 
-// One chunk row's decoder state (every lane of the row holds the same values, except
-// the two states).
+// The fields of a lane's P streams from the bits at its first field's position: w[0..kWin)
+// are the ring dwords from that position's dword on, and n[i] holds field i's length in its
+// bits 0..4 (fields are at most 16 bits, a lane's P fields at most 16 P bits).
+template <int P>
+__device__ __forceinline__ void split_fields(const uint32_t* w, uint32_t start, const uint32_t* n,
+                                             uint32_t* f) {
+    const uint32_t lo = __builtin_amdgcn_alignbit(w[1], w[0], start);
+    f[0] = __builtin_amdgcn_ubfe(lo, 0, n[0]);
+    if constexpr (P == 2) {
+        f[1] = __builtin_amdgcn_ubfe(lo, n[0], n[1]);
+    } else {
+        // 64 bits from the position (hi:lo); t1 = its 32 bits from field 1 on, t2 from field
+        // 2 on (the high word shifted along, so that fields 2 and 3 are whole in t2)
+        const uint32_t hi = __builtin_amdgcn_alignbit(w[2], w[1], start);
+        const uint32_t t1 = __builtin_amdgcn_alignbit(hi, lo, n[0]);
+        const uint32_t h1 = hi >> (n[0] & 31);
+        const uint32_t t2 = __builtin_amdgcn_alignbit(h1, t1, n[1]);
+        f[1] = __builtin_amdgcn_ubfe(t1, 0, n[1]);
+        f[2] = __builtin_amdgcn_ubfe(t2, 0, n[2]);
+        f[3] = __builtin_amdgcn_ubfe(t2, n[2], n[3]);
+    }
+}
+
+// One chunk row's decoder state (every lane of the row holds the same values, except the
+// states).
+template <int W, int P>
 struct Row {
     uint32_t nc, cdw, cbyte, ring_byte, pos, res_hi, refill_at, vout;
     uint32_t end;      // bit position of the chunk's end (its first bit is at bit 0..24 of
                        // the chunk's first dword, the dword holding its first byte)
-    uint32_t tile;     // LDS byte address of this lane's two bytes in step 0 of the tile
-    uint32_t sa, sb;   // states of streams 2j and 2j + 1
-    v4u pf[kFillVecs]; // the next refill, in flight
+    uint32_t tile;     // LDS byte address of this lane's bytes in step 0 of the tile
+    uint32_t s[P];     // states of streams P j .. P j + P - 1
+    v4u pf[RowGeom<W, P>::kFillVecs]; // the next refill, in flight
 };
 
-template <class A>
+template <class A, int W, int P>
 __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
+    using G = RowGeom<W, P>;
+    constexpr uint32_t kS = G::kS, kRowsPerWave = G::kRowsPerWave, kFillVecs = G::kFillVecs;
     extern __shared__ __align__(16) uint32_t dsm[];
-    const uint32_t tid = threadIdx.x, lane = tid & 63, j = lane & 15, row = lane >> 4;
+    const uint32_t tid = threadIdx.x, lane = tid & 63, j = lane % W, row = lane / W;
     const uint32_t block = __builtin_amdgcn_readfirstlane(blockIdx.x);
     const SegDesc* sg = codec_seg(a, block, false);
     const uint32_t bseg = block - sg->first_block;
@@ -132,13 +187,14 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
     const uint64_t n = sg->n;
     const uint32_t index_at = header_bytes_dev(a.h.K);
     const uint32_t payload_at = index_at + (uint32_t)index_bytes_of(n_chunks);
-    const uint32_t ulog = size_unit_log2(a.h.C, R);  // chunk sizes count units of 2^ulog bytes
+    const uint32_t ulog = size_unit_log2(a.h.C, R, kS);  // chunk sizes count units of 2^ulog bytes
     const uint64_t in_nbytes = sg->c_bytes;
     const rsrc_t rin = make_rsrc(sg->c, (uint32_t)in_nbytes);
 
     // loads that need nothing else go out first: this thread's table slot and the sizes of
-    // the chunks of the wavefront's group of 64 (its four chunks lie in one group)
-    const uint32_t group = 4 * wid;                 // the wavefront's first chunk
+    // the chunks of the wavefront's group of 64 (its chunks lie in one group)
+    static_assert(kGroupChunks % kRowsPerWave == 0, "a wavefront's chunks lie in one group");
+    const uint32_t group = kRowsPerWave * wid;      // the wavefront's first chunk
     const uint32_t chunk = group + row;
     const uint32_t ts = tid < L ? tid : L - 1;      // slot tid (more below when L > 256)
     const uint32_t te0 = dec[2 * ts], te1 = dec[2 * ts + 1];
@@ -148,16 +204,17 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
 
     const uint64_t grp_first = (uint64_t)group * a.h.C;
     const uint64_t grp_len = grp_first < n ? n - grp_first : 0;
-    const uint64_t grp_cap = 4ull * a.h.C;
+    const uint64_t grp_cap = (uint64_t)kRowsPerWave * a.h.C;
     const rsrc_t rout = make_rsrc(sg->x + (grp_first < n ? grp_first : 0),
                                   (uint32_t)(grp_len < grp_cap ? grp_len : grp_cap));
 
-    Row r;
-    r.ring_byte = tab_byte + 4 * (rings + (wv * 4 + row) * kRRingStride);
+    Row<W, P> r;
+    const uint32_t rowi = wv * kRowsPerWave + row;  // the row in the block
+    r.ring_byte = tab_byte + 4 * (rings + rowi * kRRingStride);
     const uint32_t tile_base =
-        tab_byte + 4 * (rings + kRowsPerBlock * kRRingStride + (wv * 4 + row) * kTileStride);
-    r.tile = tile_base + 2 * j;
-    r.vout = row * a.h.C + 2 * j;
+        tab_byte + 4 * (rings + G::kRowsPerBlock * kRRingStride + rowi * G::kTileStride);
+    r.tile = tile_base + P * j;
+    r.vout = row * a.h.C + P * j;
     r.nc = 0;
     r.cdw = 0;
     r.cbyte = 0;
@@ -168,7 +225,7 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
         const uint64_t first = (uint64_t)chunk * a.h.C;
         const uint32_t m = (uint32_t)((n - first) < a.h.C ? (n - first) : a.h.C);
         const uint64_t at = (uint64_t)payload_at + gs.head + c_rel;  // the chunk's first byte
-        const bool ok = gs.ok && (c_bytes >> ulog) <= chunk_bound_units(m, R, ulog) &&
+        const bool ok = gs.ok && (c_bytes >> ulog) <= chunk_bound_units(m, R, ulog, kS) &&
                         at + c_bytes <= in_nbytes;
         if (ok) {
             r.nc = m;
@@ -192,9 +249,7 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
 #pragma unroll
     for (uint32_t v = 0; v < kFillVecs; ++v)
         r.pf[v] = load4(rin, r.cbyte, r.res_hi + kLaneFill * j + 4 * v, r.cdw);
-    // refills are checked every other step; one is due once the next two steps could read
-    // past res_hi (a step reads at most 32 fields of 16 bits: 16 dwords)
-    r.refill_at = r.res_hi < r.cdw ? (r.res_hi - 33) * 32 : 0xFFFFFFFFu;
+    r.refill_at = r.res_hi < r.cdw ? (r.res_hi - G::kMargin) * 32 : 0xFFFFFFFFu;
 
     if (wid == 0) {
         // header and index ends: the container must belong to this table and fit in_nbytes;
@@ -233,19 +288,22 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
     for (uint32_t slot = tid + kRowsBlock; slot < L; slot += kRowsBlock)
         stage_entry(slot, dec[2 * slot], dec[2 * slot + 1]);
     {
-        uint32_t* rg = &dsm[rings + (wv * 4 + row) * kRRingStride];
+        uint32_t* rg = &dsm[rings + rowi * kRRingStride];
 #pragma unroll
         for (uint32_t v = 0; v < kFillVecs; ++v) {
             *reinterpret_cast<v4u*>(&rg[kLaneFill * j + 4 * v]) = f0[v];
             *reinterpret_cast<v4u*>(&rg[kRFill + kLaneFill * j + 4 * v]) = f1[v];
         }
-        if (j == 0) rg[kRRing] = f0[0][0];
+        if (j == 0) {
+            rg[kRRing] = f0[0][0];
+            rg[kRRing + 1] = f0[0][1];
+        }
     }
     __syncthreads();
 
-    // initial slots: stream s's R bits at bit0 + s * R (at most 376 bits: within the first
-    // ring words, no wrap)
-    const uint32_t lanes = r.nc < 32 ? r.nc : 32;
+    // initial slots: stream s's R bits at bit0 + s * R (at most 24 + 63 * 11 + 11 bits: within
+    // the first ring words, no wrap)
+    const uint32_t lanes = r.nc < kS ? r.nc : kS;
     auto init_state = [&](uint32_t s) {
         if (s >= lanes) return tab_byte;
         const uint32_t p = bit0 + s * R;
@@ -253,88 +311,90 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
         const uint32_t bits = __builtin_amdgcn_alignbit(w[1], w[0], p);
         return tab_byte + ((bits & (L - 1)) << 3);
     };
-    r.sa = init_state(2 * j);
-    r.sb = init_state(2 * j + 1);
+#pragma unroll
+    for (int i = 0; i < P; ++i) r.s[i] = init_state(P * j + i);
     r.pos = bit0 + lanes * R;
 
     // steps where every stream of the wavefront's chunks decodes a value that is not its
-    // last (every stream's last value lies at or after step nc / 32 - 1); the rest go
+    // last (every stream's last value lies at or after step nc / kS - 1); the rest go
     // through the general step
     uint32_t nc_min = 0xFFFFFFFFu, nc_max = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint32_t v = __builtin_amdgcn_readlane(r.nc, 16 * k);
+    for (uint32_t k = 0; k < kRowsPerWave; ++k) {
+        const uint32_t v = __builtin_amdgcn_readlane(r.nc, W * k);
         nc_min = nc_min < v ? nc_min : v;
         nc_max = nc_max > v ? nc_max : v;
     }
-    const uint32_t full = (nc_min >> 5) > 0 ? (nc_min >> 5) - 1 : 0;
-    const uint32_t steps = (nc_max + 31) >> 5;
+    const uint32_t full = nc_min / kS > 0 ? nc_min / kS - 1 : 0;
+    const uint32_t steps = (nc_max + kS - 1) / kS;
     uint64_t bad_offsets = 0;  // lanes that decoded an offset outside its range
 
     auto refill = [&]() {
         if (r.pos >= r.refill_at) {
             const uint32_t d = (r.res_hi + kLaneFill * j) & (kRRing - 1);
             typedef __attribute__((address_space(3))) v4u lds_w4;
-            typedef __attribute__((address_space(3))) uint32_t lds_w1;
+            typedef __attribute__((address_space(3))) v2u lds_w2;
 #pragma unroll
             for (uint32_t v = 0; v < kFillVecs; ++v)
                 *(lds_w4*)(uintptr_t)(r.ring_byte + 4 * (d + 4 * v)) = r.pf[v];
-            if (d == 0) *(lds_w1*)(uintptr_t)(r.ring_byte + 4 * kRRing) = r.pf[0][0];
+            if (d == 0) *(lds_w2*)(uintptr_t)(r.ring_byte + 4 * kRRing) = v2u{r.pf[0][0], r.pf[0][1]};
             r.res_hi += kRFill;
-            r.refill_at = r.res_hi < r.cdw ? (r.res_hi - 33) * 32 : 0xFFFFFFFFu;
+            r.refill_at = r.res_hi < r.cdw ? (r.res_hi - G::kMargin) * 32 : 0xFFFFFFFFu;
 #pragma unroll
             for (uint32_t v = 0; v < kFillVecs; ++v)
                 r.pf[v] = load4(rin, r.cbyte, r.res_hi + kLaneFill * j + 4 * v, r.cdw);
         }
     };
 
-    // One step: the pair's two fields are adjacent, stream 2j's first.  The entries were
-    // read at the end of the previous step, so the serial path is scan -> ring read ->
-    // bit extract -> next entry read.  k is the step's place in the tile (a constant in the
+    // One step: the lane's P fields are adjacent, stream P j's first.  The entries were read
+    // at the end of the previous step, so the serial path is scan -> ring read -> bit
+    // extract -> next entry read.  k is the step's place in the tile (a constant in the
     // unrolled loop, so the tile writes take their offset from the instruction).
-    auto full_step = [&](const Ent& ea, const Ent& eb, Ent& na, Ent& nb, uint32_t k) {
-        const uint32_t tot = need_of(ea) + need_of(eb);
+    auto full_step = [&](const Ent* e, Ent* ne, uint32_t k) {
+        uint32_t tot = 0, nd[P], w[G::kWin], f[P];
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            tot += need_of(e[i]);
+            nd[i] = e[i].A;  // bits 0..4: the need
+        }
         const uint32_t posm = r.pos - tot;
-        const uint32_t incl = scan16(tot);
+        const uint32_t incl = scan_row<W>(tot);
         const uint32_t start = posm + incl;
-        const uint32_t rb = (ring_dword(start) << 2) + r.ring_byte;
-        const lds_u32* rp = (const lds_u32*)(uintptr_t)rb;
-        const uint32_t bits = __builtin_amdgcn_alignbit(rp[1], rp[0], start);
-        // stream 2j: bits [0, need_a); stream 2j + 1: bits [need_a, need_a + need_b)
-        const uint32_t fa = __builtin_amdgcn_ubfe(bits, 0, ea.A);
-        const uint32_t fb = __builtin_amdgcn_ubfe(bits, ea.A, eb.A);
-        const uint32_t oa = __builtin_amdgcn_ubfe(fa, 0, ea.B);
-        const uint32_t ob = __builtin_amdgcn_ubfe(fb, 0, eb.B);
-        r.sa = ((fa >> (ea.B & 31)) << 3) + next_of(ea);
-        r.sb = ((fb >> (eb.B & 31)) << 3) + next_of(eb);
-        na = read_ent(r.sa);
-        nb = read_ent(r.sb);
-        bad_offsets |= __builtin_amdgcn_ballot_w64(oa > maxo_of(ea));
-        bad_offsets |= __builtin_amdgcn_ballot_w64(ob > maxo_of(eb));
-        const uint32_t xa = oa + base_of(ea), xb = ob + base_of(eb);
-        // two byte writes (volatile, so that they stay two): one VALU op fewer than packing
-        // the pair into a 16-bit write
+        const lds_u32* rp = (const lds_u32*)(uintptr_t)((ring_dword(start) << 2) + r.ring_byte);
+#pragma unroll
+        for (uint32_t i = 0; i < G::kWin; ++i) w[i] = rp[i];
+        split_fields<P>(w, start, nd, f);
         typedef volatile __attribute__((address_space(3))) uint8_t lds_w1b;
-        *(lds_w1b*)(uintptr_t)(r.tile + 32 * k) = (uint8_t)xa;
-        *(lds_w1b*)(uintptr_t)(r.tile + 32 * k + 1) = (uint8_t)xb;
-        r.pos += row_last(incl);
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const uint32_t o = __builtin_amdgcn_ubfe(f[i], 0, e[i].B);
+            r.s[i] = ((f[i] >> (e[i].B & 31)) << 3) + next_of(e[i]);
+            ne[i] = read_ent(r.s[i]);
+            bad_offsets |= __builtin_amdgcn_ballot_w64(o > maxo_of(e[i]));
+            // byte writes (volatile, so that they stay single bytes): fewer VALU operations
+            // than packing the lane's bytes into one write
+            *(lds_w1b*)(uintptr_t)(r.tile + kS * k + i) = (uint8_t)(o + base_of(e[i]));
+        }
+        r.pos += row_last<W>(incl);
     };
     // the tile of steps [t0, t0 + kTileSteps) to the output: lane j stores its share of
-    // the row's 32 * kTileSteps bytes (LDS operations of a wavefront complete in order, so
+    // the row's kS * kTileSteps bytes (LDS operations of a wavefront complete in order, so
     // the row's writes are visible)
     auto flush_tile = [&](uint32_t t0) {
-        constexpr uint32_t kLaneBytes = 2 * kTileSteps;
+        constexpr uint32_t kLaneBytes = P * kTileSteps;
         const uint32_t at = row * a.h.C + kLaneBytes * j;
         if constexpr (kLaneBytes == 16) {
             const v4u w = *(const __attribute__((address_space(3))) v4u*)(uintptr_t)(tile_base + 16 * j);
-            __builtin_amdgcn_raw_buffer_store_b128(w, rout, (int)at, (int)(t0 * 32), 0);
+            __builtin_amdgcn_raw_buffer_store_b128(w, rout, (int)at, (int)(t0 * kS), 0);
         } else {
             const v2u w = *(lds_v2u*)(uintptr_t)(tile_base + 8 * j);
-            __builtin_amdgcn_raw_buffer_store_b64(w, rout, (int)at, (int)(t0 * 32), 0);
+            __builtin_amdgcn_raw_buffer_store_b64(w, rout, (int)at, (int)(t0 * kS), 0);
         }
     };
 
-    Ent ea = read_ent(r.sa), eb = read_ent(r.sb), ea2, eb2;
+    Ent ea[P], eb[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) ea[i] = read_ent(r.s[i]);
     uint32_t t = 0;
     // the waves on a SIMD take turns at the highest priority (take_turn)
     const uint32_t slot_id = wave_slot();
@@ -345,8 +405,8 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
         for (; t < stop; t += kTileSteps) {  // the entries alternate registers step by step
 #pragma unroll
             for (uint32_t k = 0; k < kTileSteps; k += 2) {
-                full_step(ea, eb, ea2, eb2, k);
-                full_step(ea2, eb2, ea, eb, k + 1);
+                full_step(ea, eb, k);
+                full_step(eb, ea, k + 1);
                 refill();
             }
             flush_tile(t);
@@ -356,46 +416,44 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
     // the general step: a stream past its chunk's end has no field, and a stream at its
     // last value has the offset alone (its state bits are zero and implied)
     for (; t < steps; ++t) {
-        const uint32_t s0 = t * 32 + 2 * j, s1 = s0 + 1;
-        const bool act_a = s0 < r.nc, act_b = s1 < r.nc;
-        const bool last_a = act_a && s0 + 32 >= r.nc, last_b = act_b && s1 + 32 >= r.nc;
-        const uint32_t need_a = act_a ? (last_a ? (ea.B & 31) : need_of(ea)) : 0;
-        const uint32_t need_b = act_b ? (last_b ? (eb.B & 31) : need_of(eb)) : 0;
-        const uint32_t tot = need_a + need_b;
-        const uint32_t incl = scan16(tot);
+        uint32_t nd[P], w[G::kWin], f[P], tot = 0;
+        bool act[P];
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const uint32_t s = t * kS + P * j + i;
+            act[i] = s < r.nc;
+            const bool last = act[i] && s + kS >= r.nc;
+            nd[i] = act[i] ? (last ? (ea[i].B & 31) : need_of(ea[i])) : 0;
+            tot += nd[i];
+        }
+        const uint32_t incl = scan_row<W>(tot);
         const uint32_t start = r.pos - tot + incl;
-        const uint32_t rb = (ring_dword(start) << 2) + r.ring_byte;
-        const lds_u32* rp = (const lds_u32*)(uintptr_t)rb;
-        const uint32_t bits = __builtin_amdgcn_alignbit(rp[1], rp[0], start);
-        const uint32_t fa = __builtin_amdgcn_ubfe(bits, 0, need_a);
-        const uint32_t fb = __builtin_amdgcn_ubfe(bits, need_a, need_b);
-        const uint32_t oa = __builtin_amdgcn_ubfe(fa, 0, act_a ? ea.B : 0u);
-        const uint32_t ob = __builtin_amdgcn_ubfe(fb, 0, act_b ? eb.B : 0u);
-        if (act_a) {
-            err |= oa > maxo_of(ea);
-            r.sa = ((fa >> (ea.B & 31)) << 3) + next_of(ea);
+        const lds_u32* rp = (const lds_u32*)(uintptr_t)((ring_dword(start) << 2) + r.ring_byte);
+#pragma unroll
+        for (uint32_t i = 0; i < G::kWin; ++i) w[i] = rp[i];
+        split_fields<P>(w, start, nd, f);
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const uint32_t o = __builtin_amdgcn_ubfe(f[i], 0, act[i] ? ea[i].B : 0u);
+            if (act[i]) {
+                err |= o > maxo_of(ea[i]);
+                r.s[i] = ((f[i] >> (ea[i].B & 31)) << 3) + next_of(ea[i]);
+                __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(o + base_of(ea[i])), rout,
+                                                     (int)(r.vout + i), (int)(t * kS), 0);
+            }
         }
-        if (act_b) {
-            err |= ob > maxo_of(eb);
-            r.sb = ((fb >> (eb.B & 31)) << 3) + next_of(eb);
-        }
-        const uint32_t xa = oa + base_of(ea), xb = ob + base_of(eb);
-        if (act_b)
-            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)((xa & 0xFF) | (xb << 8)), rout,
-                                                  (int)r.vout, (int)(t * 32), 0);
-        else if (act_a)
-            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)xa, rout, (int)r.vout, (int)(t * 32), 0);
-        r.pos += row_last(incl);
-        ea = read_ent(r.sa);
-        eb = read_ent(r.sb);
+        r.pos += row_last<W>(incl);
+#pragma unroll
+        for (int i = 0; i < P; ++i) ea[i] = read_ent(r.s[i]);
         refill();
     }
 
     // a valid chunk leaves every stream in slot 0 and ends in its last size unit, zero-padded
     // (a unit of at most 4 bytes never straddles a dword: chunks start on unit boundaries)
     if (r.nc > 0) {
-        if (2 * j < lanes && r.sa != tab_byte) err = 1;
-        if (2 * j + 1 < lanes && r.sb != tab_byte) err = 1;
+#pragma unroll
+        for (int i = 0; i < P; ++i)
+            if (P * j + i < lanes && r.s[i] != tab_byte) err = 1;
         if (r.pos > r.end || r.end - r.pos >= (8u << ulog)) {
             err = 1;
         } else if (r.pos < r.end) {
@@ -408,20 +466,34 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
     report(a.h.status, SH_ERR_CORRUPT_STREAM, err != 0 || bad_offsets != 0);
 }
 
-}  // namespace
-
-uint32_t decode_lds_bytes(uint32_t L) {
-    return 4 * (2 * L + kRowsPerBlock * (kRRingStride + kTileStride));
+template <int W, int P>
+uint32_t rows_lds_bytes(uint32_t L) {
+    using G = RowGeom<W, P>;
+    return 4 * (2 * L + G::kRowsPerBlock * (kRRingStride + G::kTileStride));
 }
 
-sh_status launch_decode(const CodecArgs& a, uint32_t total_blocks, void* stream) {
+template <int W, int P>
+sh_status launch_rows(const CodecArgs& a, uint32_t total_blocks, void* stream) {
     if (total_blocks == 0) return SH_OK;
-    const uint32_t lds = decode_lds_bytes(a.L);
+    const uint32_t lds = rows_lds_bytes<W, P>(a.L);
     with_kernel_args(a, [&](const auto& k) {
-        hipLaunchKernelGGL((k_decode_rows<std::decay_t<decltype(k)>>), dim3(total_blocks),
+        hipLaunchKernelGGL((k_decode_rows<std::decay_t<decltype(k)>, W, P>), dim3(total_blocks),
                            dim3(kRowsBlock), lds, (hipStream_t)stream, k);
     });
     return hipGetLastError() == hipSuccess ? SH_OK : SH_ERR_HIP;
+}
+
+}  // namespace
+
+sh_status launch_decode(const CodecArgs& a, uint32_t total_blocks, void* stream) {
+    if (a.S == kStreamsNarrow) return launch_rows<16, 2>(a, total_blocks, stream);
+    if (a.S == kStreamsWide) return launch_rows<16, 4>(a, total_blocks, stream);
+    return SH_ERR_UNSUPPORTED;
+}
+
+sh_status launch_decode_wide_halves(const CodecArgs& a, uint32_t total_blocks, void* stream) {
+    if (a.S != kStreamsWide) return SH_ERR_UNSUPPORTED;
+    return launch_rows<32, 2>(a, total_blocks, stream);
 }
 
 }  // namespace shn

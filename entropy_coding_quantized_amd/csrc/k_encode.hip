@@ -11,26 +11,39 @@ namespace shn {
 // ------------------------------------------------------------------------------------
 // encode, kernel 1: every chunk into a worst-case slot of the workspace
 // ------------------------------------------------------------------------------------
-// The decoder's mapping run backwards: one chunk per 16-lane DPP row, lane j of a row runs
-// the streams 2j and 2j + 1, whose fields are adjacent in every step.  tANS encodes
-// backwards, so each stream walks its values from the last step to the first and every
-// step's fields are placed right to left: the step's pairs of fields end where the later
-// steps' fields begin, and a 16-lane prefix sum of the pairs' lengths gives every pair's bit
-// position.  Pairs are OR-ed into a 128-dword LDS ring per chunk that is flushed to the
-// chunk's slot 64 dwords at a time, highest first; the chunk ends up right-aligned in its
-// slot with the streams' final states (the decoder's initial states) in front.
+// The decoder's mapping run backwards: one chunk per 16-lane DPP row, lane j of a row runs P
+// adjacent streams, P j to P j + P - 1 (P = 2 for chunks of 32 streams, 4 for chunks of 64),
+// whose fields are adjacent in every step.  tANS encodes backwards, so each stream walks its
+// values from the last step to the first and every step's fields are placed right to left:
+// the step's fields end where the later steps' fields begin, and a 16-lane prefix sum of the
+// lanes' field lengths gives every lane's bit position.  A lane's fields are OR-ed, a pair
+// at a time, into a 128-dword LDS ring per chunk that is flushed to the chunk's slot 64
+// dwords at a time, highest first; the chunk ends up right-aligned in its slot with the
+// streams' final states (the decoder's initial states) in front.
 constexpr int kEncRowsBlock = 256;                 // 4 wavefronts, 16 rows = 16 chunks
 static_assert(kEncodeChunksPerBlock == kEncRowsBlock / 16, "one chunk per 16-lane row");
 constexpr uint32_t kERing = 128;                   // ring dwords per chunk
 constexpr uint32_t kEFlush = 64;                   // dwords per flush
 constexpr uint32_t kETileSteps = 16;               // input steps staged at a time
-constexpr uint32_t kETileBytes = kETileSteps * 32;
 // The four rows of a wavefront write their rings and read their tiles at similar offsets in
 // the same steps: their tiles sit 32 bytes apart beyond their size and their ring origins 8
 // dwords apart (ring dword (d + 8 row) mod 128 holds slot dword d), so that the rows use
 // different LDS banks.
-constexpr uint32_t kETileStride = kETileBytes + 32;
 constexpr uint32_t kERowTurn = 8;                  // ring dwords per row of the wavefront
+template <int P>
+struct EncGeom {
+    static_assert(P == 2 || P == 4, "two or four streams a lane");
+    static constexpr uint32_t kS = 16 * P;                  // streams of a chunk
+    static constexpr uint32_t kTileBytes = kETileSteps * kS;
+    static constexpr uint32_t kTileStride = kTileBytes + 32;
+    static constexpr uint32_t kTileVecs = kS / 16;          // 16-byte loads a lane stages
+    // The ring holds every dword not yet flushed.  After a flush check the fields reach no
+    // lower than 64 dwords below the flush mark; checks come at least every other step, and
+    // a step places at most kS fields of 16 bits, kS / 2 dwords; so the unflushed dwords span
+    // at most 64 + kS dwords (128 at P = 4: the ring exactly; the mark's own dword, the
+    // lowest one's twin in the ring, is flushed and zero).
+    static_assert(kEFlush + kS <= kERing, "two steps fit in the ring");
+};
 // LDS (dynamic; the kernel's only LDS, so it starts at LDS byte 0): the value entries (two
 // dwords per value, at a 2 KB boundary so that an entry's address is one AND-OR), the
 // rings (512 B each, 512 B aligned), the encTable (a dword per slot, holding the next
@@ -42,8 +55,9 @@ constexpr uint32_t kEEsByte = kERingsByte + kEncodeChunksPerBlock * kERing * 4; 
 __host__ __device__ constexpr uint32_t encode_tiles_byte(uint32_t L) {
     return (kEEsByte + 4 * L + 15) / 16 * 16;
 }
+template <int P>
 __host__ __device__ constexpr uint32_t encode_lds_bytes(uint32_t L) {
-    return encode_tiles_byte(L) + kEncodeChunksPerBlock * kETileStride + 16;
+    return encode_tiles_byte(L) + kEncodeChunksPerBlock * EncGeom<P>::kTileStride + 16;
 }
 static_assert(kEEsByte >= 4 * kMaxLGpu && kEEsByte + 4 * kMaxLGpu < 32768,
               "encTable addresses stay positive and below bit 15 of an entry");
@@ -101,8 +115,10 @@ struct EEnt {
     uint32_t B, A;
 };
 
-template <class A>
+template <class A, int P>
 __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
+    using G = EncGeom<P>;
+    constexpr uint32_t kS = G::kS;
     extern __shared__ __align__(16) uint32_t esm[];
     const uint32_t tid = threadIdx.x, lane = tid & 63, j = lane & 15, row = lane >> 4;
     const uint32_t block = __builtin_amdgcn_readfirstlane(blockIdx.x);
@@ -115,10 +131,10 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
     const uint32_t L = a.h.L, R = a.h.R, R1 = a.h.R + 1;
     const uint32_t base = lds_offset(esm);  // 0: the only LDS of the kernel
     const uint32_t ring_byte = base + kERingsByte + 4 * kERing * rowi;
-    const uint32_t tile_byte = base + encode_tiles_byte(L) + kETileStride * rowi;
+    const uint32_t tile_byte = base + encode_tiles_byte(L) + G::kTileStride * rowi;
     const uint32_t vt_byte = base + kEVtByte, es_byte = base + kEEsByte;
     uint32_t* agg_s = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(esm) + encode_tiles_byte(L) +
-                                                  kEncodeChunksPerBlock * kETileStride);
+                                                  kEncodeChunksPerBlock * G::kTileStride);
 
     // the tables in their LDS form (device form: v0 = bias, v1 = o | w << 8 | (f == 0) << 15 |
     // (start + kMaxLGpu) << 16, start = cum - f; encTable entries are slots)
@@ -157,7 +173,7 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
         const uint64_t first = (uint64_t)chunk * a.h.C;
         nc = (uint32_t)((n - first) < a.h.C ? (n - first) : a.h.C);
     }
-    const uint32_t lanes = nc < 32 ? nc : 32;
+    const uint32_t lanes = nc < kS ? nc : kS;
     uint32_t nc_min = 0xFFFFFFFFu, nc_max = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -165,38 +181,40 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
         nc_min = nc_min < v ? nc_min : v;
         nc_max = nc_max > v ? nc_max : v;
     }
-    const uint32_t steps = (nc_max + 31) >> 5;
+    const uint32_t steps = (nc_max + kS - 1) / kS;
 
-    // Lane j stages step 16 T + j of tile T: 32 bytes.  Past a short chunk's end lies the
+    // Lane j stages step 16 T + j of tile T: kS bytes.  Past a short chunk's end lies the
     // end of the wavefront's range (a 16-byte load reaching past it reads 0 as a whole, so
     // the lanes at the end read byte by byte) or the next chunk, whose values go unused.
     const uint32_t in_len = (uint32_t)(grp_len < 4ull * a.h.C ? grp_len : 4ull * a.h.C);
-    auto load_tile = [&](uint32_t T, v4u& p0, v4u& p1) {
-        const uint32_t b = in_row + (kETileSteps * T + j) * 32;
-        if (b + 32 <= in_len) {
-            p0 = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rin, (int)b, 0, 0));
-            p1 = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rin, (int)(b + 16), 0, 0));
+    auto load_tile = [&](uint32_t T, v4u* pv) {
+        const uint32_t b = in_row + (kETileSteps * T + j) * kS;
+        if (b + kS <= in_len) {
+#pragma unroll
+            for (uint32_t v = 0; v < G::kTileVecs; ++v)
+                pv[v] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rin, (int)(b + 16 * v), 0, 0));
         } else {
-            p0 = v4u{0, 0, 0, 0};
-            p1 = v4u{0, 0, 0, 0};
-            for (uint32_t k = 0; k < 32; ++k)
+#pragma unroll
+            for (uint32_t v = 0; v < G::kTileVecs; ++v) pv[v] = v4u{0, 0, 0, 0};
+            for (uint32_t k = 0; k < kS; ++k)
                 if (b + k < in_len) {
                     const uint32_t byte = __builtin_amdgcn_raw_buffer_load_b8(rin, (int)(b + k), 0, 0);
-                    if (k < 16) p0[k >> 2] |= byte << (8 * (k & 3));
-                    else p1[(k - 16) >> 2] |= byte << (8 * (k & 3));
+                    pv[k >> 4][(k >> 2) & 3] |= byte << (8 * (k & 3));
                 }
         }
     };
-    v4u p0 = {0, 0, 0, 0}, p1 = {0, 0, 0, 0};
-    if (steps > 0) load_tile((steps - 1) / kETileSteps, p0, p1);
+    v4u pv[G::kTileVecs];
+#pragma unroll
+    for (uint32_t v = 0; v < G::kTileVecs; ++v) pv[v] = v4u{0, 0, 0, 0};
+    if (steps > 0) load_tile((steps - 1) / kETileSteps, pv);
     __syncthreads();
 
     // bit positions are kept turned by the row's ring origin: position p stands for slot bit
     // p - turn
     const uint32_t turn = 32 * kERowTurn * row;
-    uint32_t P = a.h.slot_dwords * 32 + turn;   // fields go below P, right to left
+    uint32_t fpos = a.h.slot_dwords * 32 + turn;  // fields go below fpos, right to left
     uint32_t fmark = a.h.slot_dwords;    // dwords at or above fmark are in the slot
-    uint32_t flush_at = (fmark - kEFlush) * 32 + turn;  // once P is below this, flush a block
+    uint32_t flush_at = (fmark - kEFlush) * 32 + turn;  // once fpos is below this, flush a block
     uint32_t bad = 0;                    // entries OR-ed in: bit 31 marks a range without states
 
     auto flush_block = [&](uint32_t blk) {  // ring dwords [blk, blk + 64) -> slot
@@ -206,59 +224,66 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
         *r = v4u{0, 0, 0, 0};
         __builtin_amdgcn_raw_buffer_store_b128(v, rslot, (int)(slot_row + 4 * (blk + 4 * j)), 0, 0);
     };
-    auto stage = [&]() {  // the tile in p0/p1 into LDS, as u = x + 128
+    auto stage = [&]() {  // the tile in pv into LDS, as u = x + 128
         typedef __attribute__((address_space(3))) v4u lds_v4;
         const v4u flip = {0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};
-        *(lds_v4*)(uintptr_t)(tile_byte + 32 * j) = p0 ^ flip;
-        *(lds_v4*)(uintptr_t)(tile_byte + 32 * j + 16) = p1 ^ flip;
+#pragma unroll
+        for (uint32_t v = 0; v < G::kTileVecs; ++v)
+            *(lds_v4*)(uintptr_t)(tile_byte + kS * j + 16 * v) = pv[v] ^ flip;
     };
-    auto pair_at = [&](uint32_t t) {  // u of streams 2j and 2j + 1 at step t (staged)
-        return (uint32_t) * (lds_r16*)(uintptr_t)(tile_byte + 32 * (t & (kETileSteps - 1)) + 2 * j);
+    auto vals_at = [&](uint32_t t) {  // u of the lane's P streams at step t (staged), a byte each
+        const uint32_t at = tile_byte + kS * (t & (kETileSteps - 1)) + P * j;
+        if constexpr (P == 2) return (uint32_t) * (lds_r16*)(uintptr_t)at;
+        else return *(lds_r32*)(uintptr_t)at;
     };
-    // entries of the pair's two values (the table sits on a 2 KB boundary)
-    auto entry_at = [&](uint32_t addr) {
-        const v2u_e v = *(const __attribute__((address_space(3))) v2u_e*)(uintptr_t)addr;
+    // the entry of byte i of vals (the table sits on a 2 KB boundary)
+    auto entry_of = [&](uint32_t vals, int i) {
+        const uint32_t off = i == 0 ? (vals << 3) & 0x7F8u : (vals >> (8 * i - 3)) & 0x7F8u;
+        const v2u_e v = *(const __attribute__((address_space(3))) v2u_e*)(uintptr_t)(off | vt_byte);
         return EEnt{v[0], v[1]};
     };
-    auto entry_lo = [&](uint32_t pair) { return entry_at(((pair << 3) & 0x7F8u) | vt_byte); };
-    auto entry_hi = [&](uint32_t pair) { return entry_at(((pair >> 5) & 0x7F8u) | vt_byte); };
-    // step t2's pair of values, staging its tile first when t2 is the tile's first step in
-    // this (backward) order; the tile it replaces is no longer read
+    // step t2's values, staging its tile first when t2 is the tile's first step in this
+    // (backward) order; the tile it replaces is no longer read
     auto fetch = [&](uint32_t t2) {
         if ((t2 & (kETileSteps - 1)) == kETileSteps - 1) {
             stage();
-            if (t2 >= kETileSteps) load_tile(t2 / kETileSteps - 1, p0, p1);
+            if (t2 >= kETileSteps) load_tile(t2 / kETileSteps - 1, pv);
         }
-        return pair_at(t2);
+        return vals_at(t2);
     };
 
     // Values are read two steps ahead and entries one step ahead, so the only LDS read on
     // the chain from one step to the next is the state-dependent encTable read.
-    EEnt ea = {0, 0}, eb = {0, 0};
+    EEnt e[P];
+    uint32_t X[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        e[i] = EEnt{0, 0};
+        X[i] = L;
+    }
     uint32_t u_n = 0;
-    uint32_t Xa = L, Xb = L;
     if (steps > 0) {
         stage();
-        if (steps - 1 >= kETileSteps) load_tile((steps - 1) / kETileSteps - 1, p0, p1);
-        const uint32_t u_c = pair_at(steps - 1);
+        if (steps - 1 >= kETileSteps) load_tile((steps - 1) / kETileSteps - 1, pv);
+        const uint32_t u_c = vals_at(steps - 1);
         if (steps >= 2) u_n = fetch(steps - 2);
-        ea = entry_lo(u_c);
-        eb = entry_hi(u_c);
+#pragma unroll
+        for (int i = 0; i < P; ++i) e[i] = entry_of(u_c, i);
     }
     auto flush_due = [&]() {
-        if (P < flush_at) {  // dwords from P's dword + 1 up are final
+        if (fpos < flush_at) {  // dwords from fpos's dword + 1 up are final
             fmark -= kEFlush;
             flush_at -= kEFlush * 32;
             flush_block(fmark);
         }
     };
     // one stream's step: the next state's encTable read goes out first
-    auto code = [&](const EEnt& e, uint32_t X, uint32_t& Xn, uint32_t& field, uint32_t& len) {
-        const uint32_t k = __builtin_amdgcn_ubfe(X + e.B, R1, 5);
-        const uint32_t addr = ((X >> k) << 2) + __builtin_amdgcn_ubfe(e.A, 16, 15);
-        Xn = *(lds_r32*)(uintptr_t)addr;
-        const uint32_t w = e.B >> 24;
-        field = (__builtin_amdgcn_ubfe(X, 0, k) << w) | (e.A & 0xFFu);
+    auto code = [&](const EEnt& en, uint32_t x, uint32_t& xn, uint32_t& field, uint32_t& len) {
+        const uint32_t k = __builtin_amdgcn_ubfe(x + en.B, R1, 5);
+        const uint32_t addr = ((x >> k) << 2) + __builtin_amdgcn_ubfe(en.A, 16, 15);
+        xn = *(lds_r32*)(uintptr_t)addr;
+        const uint32_t w = en.B >> 24;
+        field = (__builtin_amdgcn_ubfe(x, 0, k) << w) | (en.A & 0xFFu);
         len = w + k;
     };
     // may_stage: false for a step whose t is known even (t - 2 is then never a tile's first
@@ -266,41 +291,54 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
     auto step = [&](uint32_t t, auto partial, auto may_stage) {
         uint32_t u_nn;
         if constexpr (decltype(may_stage)::value) u_nn = t >= 2 ? fetch(t - 2) : 0u;
-        else u_nn = pair_at(t - 2);
-        const EEnt na = entry_lo(u_n), nb = entry_hi(u_n);
-        uint32_t Xan, Xbn, fa, fb, la, lb;
-        code(ea, Xa, Xan, fa, la);
-        code(eb, Xb, Xbn, fb, lb);
-        uint32_t flag = ea.A | eb.A;
+        else u_nn = vals_at(t - 2);
+        EEnt ne[P];
+#pragma unroll
+        for (int i = 0; i < P; ++i) ne[i] = entry_of(u_n, i);
+        uint32_t Xn[P], f[P], l[P];
+#pragma unroll
+        for (int i = 0; i < P; ++i) code(e[i], X[i], Xn[i], f[i], l[i]);
+        uint32_t flag = 0;
         if constexpr (decltype(partial)::value) {
-            const uint32_t s0 = t * 32 + 2 * j, s1 = s0 + 1;
-            const bool act_a = s0 < nc, act_b = s1 < nc;
-            // a stream's last value, the first it encodes (from X = L): its state bits are
-            // zero and are left out
-            la = act_a ? (s0 + 32 >= nc ? ea.B >> 24 : la) : 0u;
-            lb = act_b ? (s1 + 32 >= nc ? eb.B >> 24 : lb) : 0u;
-            fa = act_a ? fa : 0u;
-            fb = act_b ? fb : 0u;
-            flag = (act_a ? ea.A : 0u) | (act_b ? eb.A : 0u);
-            Xa = act_a ? Xan : Xa;
-            Xb = act_b ? Xbn : Xb;
+#pragma unroll
+            for (int i = 0; i < P; ++i) {
+                const uint32_t si = t * kS + P * j + i;
+                const bool act = si < nc;
+                // a stream's last value, the first it encodes (from X = L): its state bits
+                // are zero and are left out
+                l[i] = act ? (si + kS >= nc ? e[i].B >> 24 : l[i]) : 0u;
+                f[i] = act ? f[i] : 0u;
+                flag |= act ? e[i].A : 0u;
+                X[i] = act ? Xn[i] : X[i];
+            }
         } else {
-            Xa = Xan;
-            Xb = Xbn;
+#pragma unroll
+            for (int i = 0; i < P; ++i) {
+                flag |= e[i].A;
+                X[i] = Xn[i];
+            }
         }
         bad |= flag;
-        const uint32_t lp = la + lb;
-        const uint32_t fp = fa | (fb << la);
+        // the lane's fields, stream P j's lowest: pairs of at most 32 bits
+        const uint32_t l01 = l[0] + l[1];
+        const uint32_t f01 = f[0] | (f[1] << l[0]);
+        uint32_t lp = l01, f23 = 0;
+        if constexpr (P == 4) {
+            lp += l[2] + l[3];
+            f23 = f[2] | (f[3] << l[2]);
+        }
         const uint32_t incl = escan16(lp);
-        P -= erow_last(incl);
-        ring_or2(ring_byte, P + incl - lp, fp);
-        ea = na;
-        eb = nb;
+        fpos -= erow_last(incl);
+        const uint32_t at = fpos + incl - lp;
+        ring_or2(ring_byte, at, f01);
+        if constexpr (P == 4) ring_or2(ring_byte, at + l01, f23);
+#pragma unroll
+        for (int i = 0; i < P; ++i) e[i] = ne[i];
         u_n = u_nn;
     };
     // steps where a stream of some row has no value (the tail of a short chunk) or has its
-    // last value: every stream's last value lies at or after step nc / 32 - 1
-    uint32_t t_full = nc_min >> 5;
+    // last value: every stream's last value lies at or after step nc / kS - 1
+    uint32_t t_full = nc_min / kS;
     t_full = t_full > 0 ? t_full - 1 : 0;
     uint32_t t = steps;
     while (t > t_full) {
@@ -316,7 +354,7 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
     while (t > 0) {
         take_turn(t / kPrioSteps, slot_id);
         const uint32_t stop = t > kPrioSteps ? t - kPrioSteps : 0;  // t and kPrioSteps even
-        while (t > stop) {  // two steps per check: a step places at most 16 dwords
+        while (t > stop) {  // two steps per check: a step places at most kS / 2 dwords
             step(--t, std::false_type{}, std::true_type{});   // odd t
             step(--t, std::false_type{}, std::false_type{});  // even t
             flush_due();
@@ -324,25 +362,27 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
     }
     __builtin_amdgcn_s_setprio(0);
     const uint32_t top = a.h.slot_dwords * 32;
-    const uint32_t pay = top + turn - P;  // field bits
+    const uint32_t pay = top + turn - fpos;  // field bits
     // the streams' final states, the decoder's initial states, in front of the fields.  A
     // valid encode never exceeds the chunk's bound; the span recorded for the placement is
     // clamped to it all the same, so that no table, however corrupt, moves the placement
     // outside the container's bound
-    uint32_t Pi = P - turn - lanes * R;
+    uint32_t Pi = fpos - turn - lanes * R;
     {
-        const uint32_t most = (uint32_t)chunk_bound_bits(nc, R);
+        const uint32_t most = (uint32_t)chunk_bound_bits(nc, R, kS);
         if (Pi > top || top - Pi > most) Pi = top - most;
     }
-    {
-        const uint32_t sa = 2 * j < lanes ? Xa - L : 0u, sb = 2 * j + 1 < lanes ? Xb - L : 0u;
-        ring_or2(ring_byte, Pi + turn + 2 * j * R, sa | (sb << R));
+#pragma unroll
+    for (int i = 0; i < P; i += 2) {  // two states (at most 22 bits) at a time
+        const uint32_t s0 = P * j + i < lanes ? X[i] - L : 0u;
+        const uint32_t s1 = P * j + i + 1 < lanes ? X[i + 1] - L : 0u;
+        ring_or2(ring_byte, Pi + turn + (P * j + i) * R, s0 | (s1 << R));
     }
     while (fmark > (Pi >> 5)) {
         fmark -= kEFlush;
         flush_block(fmark);
     }
-    const uint32_t ulog = size_unit_log2(a.h.C, R);
+    const uint32_t ulog = size_unit_log2(a.h.C, R, kS);
     if (chunk < n_chunks && j == 0) {
         a.h.meta[2 * (sg->slot_base + chunk)] = Pi;
         a.h.meta[2 * (sg->slot_base + chunk) + 1] = pay;
@@ -422,7 +462,7 @@ __global__ __launch_bounds__(kScanBlock) void k_encode_index(const A a) {
     const uint32_t n_chunks = sg->n_chunks;
     const uint32_t index_at = header_bytes_dev(a.h.K);
     const uint32_t payload_at = index_at + (uint32_t)index_bytes_of(n_chunks);
-    const uint32_t ulog = size_unit_log2(a.h.C, a.h.R);
+    const uint32_t ulog = size_unit_log2(a.h.C, a.h.R, a.h.S);
     const uint32_t* tmpl = sg->tab ? sg->tab + kDTHdr : inline_hdr(a);
     uint32_t* meta = a.h.meta + 2ull * sg->slot_base;
     uint32_t* goff = reinterpret_cast<uint32_t*>(sg->c + index_at);
@@ -485,7 +525,7 @@ __global__ __launch_bounds__(256) void k_encode_compact(const A a) {
     const uint32_t slot = sg->slot_base + c;
     const uint32_t start = a.h.meta[2 * slot];
     const uint32_t off = a.h.meta[2 * slot + 1];  // written by the index kernel
-    const uint32_t bytes = chunk_bytes_of(a.h.slot_dwords * 32 - start, size_unit_log2(a.h.C, a.h.R));
+    const uint32_t bytes = chunk_bytes_of(a.h.slot_dwords * 32 - start, size_unit_log2(a.h.C, a.h.R, a.h.S));
     // the last chunk also writes the zero bytes that end the payload on 4 bytes
     const uint32_t end = c + 1 == sg->n_chunks ? (off + bytes + 3) / 4 * 4 : off + bytes;
     move_chunk(a.h.slots + (uint64_t)slot * a.h.slot_dwords, a.h.slot_dwords, start, sg->c,
@@ -510,7 +550,7 @@ __global__ __launch_bounds__(256) void k_encode_place(const A a) {
     const uint32_t c0 = (block - sg->first_block_c) * 4;   // this block's first chunk
     const uint32_t index_at = header_bytes_dev(a.h.K);
     const uint32_t payload_at = index_at + (uint32_t)index_bytes_of(n_chunks);
-    const uint32_t ulog = size_unit_log2(a.h.C, a.h.R);
+    const uint32_t ulog = size_unit_log2(a.h.C, a.h.R, a.h.S);
     const uint32_t* meta = a.h.meta + 2ull * sg->slot_base;
     const uint32_t* agg = a.h.agg + 2ull * sg->first_block;  // the segment's chunk-kernel blocks
     uint32_t* goff = reinterpret_cast<uint32_t*>(sg->c + index_at);
@@ -582,12 +622,18 @@ __global__ __launch_bounds__(256) void k_encode_place(const A a) {
 
 sh_status launch_encode(const CodecArgs& a, uint32_t total_blocks, uint32_t total_blocks_c,
                         bool place, void* stream) {
+    if (a.S != kStreamsNarrow && a.S != kStreamsWide) return SH_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     with_kernel_args(a, [&](const auto& k) {
         using K = std::decay_t<decltype(k)>;
-        if (total_blocks > 0)
-            hipLaunchKernelGGL(k_encode_chunks<K>, dim3(total_blocks), dim3(kEncRowsBlock),
-                               encode_lds_bytes(a.L), s, k);
+        if (total_blocks > 0) {
+            if (a.S == kStreamsWide)
+                hipLaunchKernelGGL((k_encode_chunks<K, 4>), dim3(total_blocks), dim3(kEncRowsBlock),
+                                   encode_lds_bytes<4>(a.L), s, k);
+            else
+                hipLaunchKernelGGL((k_encode_chunks<K, 2>), dim3(total_blocks), dim3(kEncRowsBlock),
+                                   encode_lds_bytes<2>(a.L), s, k);
+        }
         if (place) {
             hipLaunchKernelGGL(k_encode_place<K>, dim3(total_blocks_c), dim3(256), 0, s, k);
             return;

@@ -124,10 +124,14 @@ CONFIGS = {
     "tiny": dict(K=16, log2_L=7, chunk=4096, streams=32),
     "weight": dict(K=16, log2_L=7, chunk=4096, streams=32),
     "kv_cache": dict(K=16, log2_L=7, chunk=8192, streams=32),
-    "activations": dict(K=16, log2_L=7, chunk=16384, streams=32),
-    # the model-scale workload fixes no chunk size: 16,384 values (as for the activations)
-    # keep the per-chunk framing (lane initial states, index entry, padding) near 0.3% of H
-    # on these weights, where 4,096 cost about 1.2%
+    # the activation workload fixes no stream count: 64 streams a chunk give its 8,192 chunks
+    # twice the independent streams of 32, at about 0.13% of H more framing (measured on
+    # MI355X: decode 98.8 -> 81.6 us with four streams a lane, encode 168 -> 152 us)
+    "activations": dict(K=16, log2_L=7, chunk=16384, streams=64),
+    # the model-scale workload fixes neither: 16,384 values (as for the activations) keep the
+    # per-chunk framing (lane initial states, index entry, padding) near 0.3% of H on these
+    # weights, where 4,096 cost about 1.2%; its launches fill the GPU, and 64 streams
+    # decoded them only 0.8% faster than 32 for 0.12% of H more framing
     "model": dict(K=16, log2_L=7, chunk=16384, streams=32),
 }
 

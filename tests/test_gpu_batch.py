@@ -99,19 +99,20 @@ def _check_containers(buf, offs, info, xs, tabs, p, whole=None):
         nbytes, bits = int(info[i, 0]), int(info[i, 1])
         got = b[offs[i]: offs[i] + nbytes]
         if whole is None or i in whole:
-            ref, ref_bits = O.encode(x, lo, f, p.log2_L, p.chunk_symbols, 32)
+            ref, ref_bits = O.encode(x, lo, f, p.log2_L, p.chunk_symbols, p.streams)
             assert got.size == ref.size and np.array_equal(got, ref), f"container {i}"
             assert bits == ref_bits, f"container {i}"
         else:
             C_ = p.chunk_symbols
             nch = (x.size + C_ - 1) // C_
-            spans, pay0 = CL.chunk_spans(got, x.size, p.K, C_, p.log2_L)
+            spans, pay0 = CL.chunk_spans(got, x.size, p.K, C_, p.log2_L, p.streams)
             assert pay0 + (spans[-1][1] + 3) // 4 * 4 == nbytes
             for c in {0, nch // 2, nch - 1}:
                 part = x[c * C_: (c + 1) * C_]
-                one, _ = O.encode(part, lo, f, p.log2_L, C_, 32)
-                assert np.array_equal(CL.chunk_bytes(got, x.size, p.K, C_, p.log2_L, c),
-                                      CL.chunk_bytes(one, part.size, p.K, C_, p.log2_L, 0)), \
+                one, _ = O.encode(part, lo, f, p.log2_L, C_, p.streams)
+                assert np.array_equal(CL.chunk_bytes(got, x.size, p.K, C_, p.log2_L, c, p.streams),
+                                      CL.chunk_bytes(one, part.size, p.K, C_, p.log2_L, 0,
+                                                     p.streams)), \
                     f"container {i} chunk {c}"
 
 
@@ -133,20 +134,27 @@ def _roundtrip_batch(torch, xs, p, whole=None):
     return tables, buf, offs, caps, info
 
 
-@pytest.mark.parametrize("C_", [4096, 32, 96, 16384])
-def test_batch_mixed_tensors(torch_cuda, C_):
-    """More tensors than one launch carries (48), ragged sizes and degenerate tensors."""
-    print(f"case: batch of 61 mixed tensors C={C_}", flush=True)
-    n_max = 120000 if C_ >= 4096 else 9000
+@pytest.mark.parametrize("C_,S,n_max", [(4096, 32, 0), (32, 32, 0), (96, 32, 0), (16384, 32, 0),
+                                        (4096, 64, 0), (64, 64, 0), (192, 64, 0), (16384, 64, 0),
+                                        (64, 64, 50000)])
+def test_batch_mixed_tensors(torch_cuda, C_, S, n_max):
+    """More tensors than one launch carries (48), ragged sizes and degenerate tensors.  With
+    n_max = 50000 at C = 64 the first launch holds more than 16,384 chunks and the second
+    fewer, so chunks of 64 streams go through both decode mappings (16-lane rows with four
+    streams a lane, half wavefronts with two)."""
+    print(f"case: batch of 61 mixed tensors C={C_} S={S} n_max={n_max}", flush=True)
+    if n_max == 0:
+        n_max = 120000 if C_ >= 4096 else 9000
     xs = _mixed_tensors(C_, 61, n_max)
-    _roundtrip_batch(torch_cuda, xs, codec.Params(chunk_symbols=C_))
+    _roundtrip_batch(torch_cuda, xs, codec.Params(chunk_symbols=C_, streams=S))
 
 
 def test_batch_kv_cache(torch_cuda):
     """The KV-cache layer: one table per (K/V, head), all 16 slabs in one launch each."""
     torch = torch_cuda
     cfg = D.CONFIGS["kv_cache"]
-    p = codec.Params(K=cfg["K"], log2_L=cfg["log2_L"], chunk_symbols=cfg["chunk"])
+    p = codec.Params(K=cfg["K"], log2_L=cfg["log2_L"], chunk_symbols=cfg["chunk"],
+                     streams=cfg["streams"])
     print("case: kv_cache batch of 16 slabs", flush=True)
     kv = D.kv_cache()
     xs = [kv[a, h].reshape(-1) for a in range(2) for h in range(8)]
@@ -158,7 +166,8 @@ def test_batch_model_tensors(torch_cuda):
     layer 1's k and v projections, full size, in one batch."""
     torch = torch_cuda
     cfg = D.CONFIGS["model"]
-    p = codec.Params(K=cfg["K"], log2_L=cfg["log2_L"], chunk_symbols=cfg["chunk"])
+    p = codec.Params(K=cfg["K"], log2_L=cfg["log2_L"], chunk_symbols=cfg["chunk"],
+                     streams=cfg["streams"])
     print("case: model tensors 0..6, 8, 9 batch", flush=True)
     xs = [D.model_tensor(i).reshape(-1) for i in list(range(7)) + [8, 9]]
     _, _, _, _, info = _roundtrip_batch(torch, xs, p, whole={0, 1, 3})

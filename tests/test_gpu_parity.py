@@ -48,11 +48,11 @@ def _gpu_decode(torch, cont, n, t, p):
     return y, int(status.item())
 
 
-def _case(torch, x, K=16, log2_L=7, C_=4096):
+def _case(torch, x, K=16, log2_L=7, C_=4096, S=32):
     x = np.ascontiguousarray(x, dtype=np.int8).reshape(-1)
-    p = codec.Params(K=K, log2_L=log2_L, chunk_symbols=C_)
+    p = codec.Params(K=K, log2_L=log2_L, chunk_symbols=C_, streams=S)
     t, lo, f = _table(x, K, log2_L)
-    ref, ref_bits = O.encode(x, lo, f, log2_L, C_, 32)
+    ref, ref_bits = O.encode(x, lo, f, log2_L, C_, S)
     # GPU decode of the oracle's stream
     y, st = _gpu_decode(torch, torch.from_numpy(ref).cuda(), x.size, t, p)
     assert st == 0
@@ -78,30 +78,42 @@ def test_weight_workload(torch_cuda):
     _case(torch_cuda, D.weight())
 
 
-@pytest.mark.parametrize("n", [1, 2, 31, 32, 33, 63, 64, 65, 4095, 4096, 4097, 8191, 12345])
-def test_ragged_sizes(torch_cuda, n):
-    print(f"case: ragged n={n}", flush=True)
+@pytest.mark.parametrize("S", [32, 64])
+@pytest.mark.parametrize("n", [1, 2, 31, 32, 33, 63, 64, 65, 127, 129, 4095, 4096, 4097, 8191,
+                               12345])
+def test_ragged_sizes(torch_cuda, n, S):
+    print(f"case: ragged n={n} S={S}", flush=True)
     x = D.quantize(np.random.default_rng(n).normal(0, 15, size=n))
-    _case(torch_cuda, x)
+    _case(torch_cuda, x, S=S)
 
 
-@pytest.mark.parametrize("n,C_", [(16383 * 64, 64), (16384 * 64, 64), (16384 * 64 + 64, 64),
-                                  (20000 * 32 + 5, 32)])
-def test_chunk_counts_around_the_one_kernel_placement(torch_cuda, n, C_):
+@pytest.mark.parametrize("n,C_,S", [(16383 * 64, 64, 32), (16384 * 64, 64, 32),
+                                    (16384 * 64 + 64, 64, 32), (20000 * 32 + 5, 32, 32),
+                                    (16384 * 64, 64, 64), (16384 * 64 + 64, 64, 64),
+                                    (20000 * 64 + 5, 64, 64)])
+def test_chunk_counts_around_the_one_kernel_placement(torch_cuda, n, C_, S):
     """Up to 16384 chunks a tensor the encoder indexes and compacts in one kernel, beyond it
     the index comes first from its own kernel: both give the oracle's container.  The decode
-    switches kernels at the same count (half-wavefront chunks below 16384, 16-lane rows from
-    there on): both decode the oracle's container."""
-    print(f"case: chunks n={n} C={C_} ({(n + C_ - 1) // C_} chunks)", flush=True)
+    of 32-stream chunks switches kernels at the same count (half-wavefront chunks below
+    16384, 16-lane rows from there on): both decode the oracle's container.  Chunks of C = S
+    values hold one value a stream."""
+    print(f"case: chunks n={n} C={C_} S={S} ({(n + C_ - 1) // C_} chunks)", flush=True)
     x = D.quantize(np.random.default_rng(n).laplace(0, 10, size=n))
-    _case(torch_cuda, x, C_=C_)
+    _case(torch_cuda, x, C_=C_, S=S)
 
 
-@pytest.mark.parametrize("K,log2_L,C_", [(1, 7, 4096), (2, 1, 32), (3, 2, 64), (16, 8, 4096),
-                                         (64, 8, 1024), (256, 8, 4096), (16, 5, 8192),
-                                         (16, 7, 65536), (8, 4, 96), (16, 7, 16384)])
-def test_parameter_grid(torch_cuda, K, log2_L, C_):
-    print(f"case: grid K={K} R={log2_L} C={C_}", flush=True)
+@pytest.mark.parametrize("K,log2_L,C_,S", [(1, 7, 4096, 32), (2, 1, 32, 32), (3, 2, 64, 32),
+                                           (16, 8, 4096, 32), (64, 8, 1024, 32),
+                                           (256, 8, 4096, 32), (16, 5, 8192, 32),
+                                           (16, 7, 65536, 32), (8, 4, 96, 32),
+                                           (16, 7, 16384, 32),
+                                           (1, 7, 4096, 64), (2, 1, 64, 64), (3, 2, 128, 64),
+                                           (16, 8, 4096, 64), (64, 8, 1024, 64),
+                                           (256, 8, 4096, 64), (16, 5, 8192, 64),
+                                           (16, 7, 65536, 64), (8, 4, 192, 64),
+                                           (16, 7, 16384, 64)])
+def test_parameter_grid(torch_cuda, K, log2_L, C_, S):
+    print(f"case: grid K={K} R={log2_L} C={C_} S={S}", flush=True)
     rng = np.random.default_rng(K * 1000 + log2_L * 10 + C_)
     n = int(rng.integers(3 * C_ // 2, 3 * C_ + 1000)) if C_ <= 16384 else 2 * C_ + 77
     sigma = 60.0 if K >= 64 else 12.0
@@ -109,14 +121,15 @@ def test_parameter_grid(torch_cuda, K, log2_L, C_):
     h = O.histogram(x)
     if (h > 0).sum() > (1 << log2_L) and K >= (1 << log2_L):
         x = np.clip(x, -(1 << (log2_L - 1)), (1 << (log2_L - 1)) - 1).astype(np.int8)
-    _case(torch_cuda, x, K, log2_L, C_)
+    _case(torch_cuda, x, K, log2_L, C_, S)
 
 
-def test_all_zero_and_uniform(torch_cuda):
-    print("case: all-zero and exactly uniform", flush=True)
-    ref = _case(torch_cuda, np.zeros(70001, dtype=np.int8))
+@pytest.mark.parametrize("S", [32, 64])
+def test_all_zero_and_uniform(torch_cuda, S):
+    print(f"case: all-zero and exactly uniform S={S}", flush=True)
+    ref = _case(torch_cuda, np.zeros(70001, dtype=np.int8), S=S)
     assert ref.size > 0
-    _case(torch_cuda, D.uniform_exact(300))
+    _case(torch_cuda, D.uniform_exact(300), S=S)
 
 
 def test_histogram_and_device_table_build(torch_cuda):
@@ -145,13 +158,15 @@ def test_symbol_outside_table(torch_cuda):
     assert int(status.item()) == codec.SH_ERR_SYMBOL_NOT_IN_TABLE
 
 
-def test_corruption_matches_oracle(torch_cuda):
+@pytest.mark.parametrize("S", [32, 64])
+def test_corruption_matches_oracle(torch_cuda, S):
     """Damaged containers: the GPU reports exactly what the oracle reports."""
     torch = torch_cuda
+    print(f"case: corruption S={S}", flush=True)
     x = D.tiny(n=36000)  # 9 chunks: an odd count, so the index ends with a pad
-    p = codec.Params()
+    p = codec.Params(streams=S)
     t, lo, f = _table(x, 16, 7)
-    ref, _ = O.encode(x, lo, f, 7, 4096, 32)
+    ref, _ = O.encode(x, lo, f, 7, 4096, S)
     rng = np.random.default_rng(3)
     cases = [ref[:-4], ref[:-1]]
     for _ in range(40):
@@ -198,21 +213,23 @@ def _sampled_chunk_parity(torch, x, t, lo, f, cont, p, samples=64, seed=0):
     nch = (n + C_ - 1) // C_
     K = p.K
     head = cont[: CL.payload_at(n, K, C_)].cpu().numpy()
-    spans, pay0 = CL.chunk_spans(head, n, K, C_, p.log2_L)
+    spans, pay0 = CL.chunk_spans(head, n, K, C_, p.log2_L, p.streams)
     rng = np.random.default_rng(seed)
     pick = set(rng.choice(nch, size=min(samples, nch), replace=False).tolist()) | {0, nch - 1}
     for c in sorted(pick):
         part = x[c * C_: min(n, (c + 1) * C_)]
-        one, _ = O.encode(part, lo, f, p.log2_L, C_, 32)
+        one, _ = O.encode(part, lo, f, p.log2_L, C_, p.streams)
         a, b = spans[c]
         got = cont[pay0 + a: pay0 + b].cpu().numpy()
-        assert np.array_equal(got, CL.chunk_bytes(one, part.size, K, C_, p.log2_L, 0)), f"chunk {c}"
+        assert np.array_equal(got, CL.chunk_bytes(one, part.size, K, C_, p.log2_L, 0, p.streams)), \
+            f"chunk {c}"
 
 
 def test_kv_cache_workload(torch_cuda):
     torch = torch_cuda
     cfg = D.CONFIGS["kv_cache"]
-    p = codec.Params(K=cfg["K"], log2_L=cfg["log2_L"], chunk_symbols=cfg["chunk"])
+    p = codec.Params(K=cfg["K"], log2_L=cfg["log2_L"], chunk_symbols=cfg["chunk"],
+                     streams=cfg["streams"])
     kv = D.kv_cache()
     for a in range(2):
         for h in range(8):
@@ -223,7 +240,7 @@ def test_kv_cache_workload(torch_cuda):
             y, st = _gpu_decode(torch, cont, x.size, t, p)
             assert st == 0 and torch.equal(y, xd)
             if h in (0, 5):   # one K head and one V head compared whole with the oracle
-                ref, ref_bits = O.encode(x, lo, f, p.log2_L, p.chunk_symbols, 32)
+                ref, ref_bits = O.encode(x, lo, f, p.log2_L, p.chunk_symbols, p.streams)
                 assert np.array_equal(cont.cpu().numpy(), ref) and bits == ref_bits
             else:
                 _sampled_chunk_parity(torch, x, t, lo, f, cont, p, samples=16, seed=h)
@@ -232,7 +249,8 @@ def test_kv_cache_workload(torch_cuda):
 def test_activation_workload(torch_cuda):
     torch = torch_cuda
     cfg = D.CONFIGS["activations"]
-    p = codec.Params(K=cfg["K"], log2_L=cfg["log2_L"], chunk_symbols=cfg["chunk"])
+    p = codec.Params(K=cfg["K"], log2_L=cfg["log2_L"], chunk_symbols=cfg["chunk"],
+                     streams=cfg["streams"])
     print("case: activations [16,2048,4096] C=16384", flush=True)
     x = D.activations().reshape(-1)
     t, lo, f = _table(x, p.K, p.log2_L)
@@ -248,7 +266,8 @@ def test_activation_workload(torch_cuda):
 def test_model_tensors(torch_cuda, idx):
     torch = torch_cuda
     cfg = D.CONFIGS["model"]
-    p = codec.Params(K=cfg["K"], log2_L=cfg["log2_L"], chunk_symbols=cfg["chunk"])
+    p = codec.Params(K=cfg["K"], log2_L=cfg["log2_L"], chunk_symbols=cfg["chunk"],
+                     streams=cfg["streams"])
     name, shape = D.model_layout()[idx]
     print(f"case: model tensor {idx} {name} {shape}", flush=True)
     x = D.model_tensor(idx).reshape(-1)
@@ -279,7 +298,8 @@ def test_stats_on_gpu_tables_and_totals_match_oracle(torch_cuda, name):
         x = _kv_head(0, 0) if name == "kv_k_head0" else _kv_head(1, 5)
         cfg = D.CONFIGS["kv_cache"]
     print(f"case: a8 stats {name} n={x.size}", flush=True)
-    p = codec.Params(K=cfg["K"], log2_L=cfg["log2_L"], chunk_symbols=cfg["chunk"])
+    p = codec.Params(K=cfg["K"], log2_L=cfg["log2_L"], chunk_symbols=cfg["chunk"],
+                     streams=cfg["streams"])
     xd = torch.from_numpy(x).cuda()
     ws = torch.empty(codec.sh_build_tables_workspace(), dtype=torch.uint8, device="cuda")
     t = codec.sh_build_tables(xd, x.size, True, p, ws, ws.numel())
@@ -290,7 +310,7 @@ def test_stats_on_gpu_tables_and_totals_match_oracle(torch_cuda, name):
 
     h = O.histogram(x)
     lo, f = O.build_table(h, p.K, p.log2_L)
-    ref_buf, ref_bits = O.encode(x, lo, f, p.log2_L, p.chunk_symbols, 32)
+    ref_buf, ref_bits = O.encode(x, lo, f, p.log2_L, p.chunk_symbols, p.streams)
     ref = O.stats(h, lo, f, p.log2_L, ref_bits, ref_buf.size, x.size)
     assert set(ref) <= set(got)
     for k, v in ref.items():

@@ -47,7 +47,7 @@ def _roundtrip_device_tables(torch, xs, p, host_tables):
         x = np.ascontiguousarray(x).reshape(-1)
         lo, f = O.build_table(O.histogram(x), p.K, p.log2_L)
         assert (got_tabs[i].lo_array == lo).all() and (got_tabs[i].freq_array == f).all()
-        ref, ref_bits = O.encode(x, lo, f, p.log2_L, p.chunk_symbols, 32)
+        ref, ref_bits = O.encode(x, lo, f, p.log2_L, p.chunk_symbols, p.streams)
         n_bytes = int(inf[i, 0])
         got = buf[offs[i]:offs[i] + n_bytes].cpu().numpy()
         assert got.size == ref.size and np.array_equal(got, ref), f"tensor {i}: container differs"
@@ -55,24 +55,33 @@ def _roundtrip_device_tables(torch, xs, p, host_tables):
         assert np.array_equal(y[starts[i]:starts[i] + x.size].cpu().numpy(), x)
 
 
-@pytest.mark.parametrize("log2_L", [9, 10, 11])
+@pytest.mark.parametrize("log2_L,S", [(9, 32), (10, 32), (11, 32), (11, 64)])
 @pytest.mark.parametrize("host_tables", [False, True])
-def test_standard_tans_at_512_to_2048_states(torch_cuda, log2_L, host_tables):
-    print(f"case: K=256 L={1 << log2_L} host_tables={host_tables}", flush=True)
-    p = codec.Params(K=256, log2_L=log2_L, chunk_symbols=4096, streams=32)
+def test_standard_tans_at_512_to_2048_states(torch_cuda, log2_L, S, host_tables):
+    print(f"case: K=256 L={1 << log2_L} S={S} host_tables={host_tables}", flush=True)
+    p = codec.Params(K=256, log2_L=log2_L, chunk_symbols=4096, streams=S)
     xs = [D.weight().reshape(-1)[:1_000_003], D.tiny(seed=9, n=70_001),
           D.uniform_exact(50), np.zeros(5000, dtype=np.int8)]
     _roundtrip_device_tables(torch_cuda, xs, p, host_tables)
 
 
-@pytest.mark.parametrize("K,log2_L,C", [(16, 7, 34944), (256, 11, 65536)])
-def test_chunk_sizes_in_two_and_four_byte_units(torch_cuda, K, log2_L, C):
+@pytest.mark.parametrize("K,log2_L,C,S", [(16, 7, 34944, 32), (256, 11, 65536, 32),
+                                          (16, 7, 34944, 64), (256, 11, 65536, 64)])
+def test_chunk_sizes_in_two_and_four_byte_units(torch_cuda, K, log2_L, C, S):
     """Chunks whose largest valid size passes 65,535 bytes count their sizes in 2- and
     4-byte units: encoder placement and decoder chunk search against the oracle."""
-    print(f"case: K={K} L={1 << log2_L} C={C}", flush=True)
-    p = codec.Params(K=K, log2_L=log2_L, chunk_symbols=C, streams=32)
+    print(f"case: K={K} L={1 << log2_L} C={C} S={S}", flush=True)
+    p = codec.Params(K=K, log2_L=log2_L, chunk_symbols=C, streams=S)
     xs = [D.weight().reshape(-1)[:3 * C + 4097], D.tiny(seed=11, n=C - 32)]
     _roundtrip_device_tables(torch_cuda, xs, p, host_tables=False)
+
+
+def test_standard_tans_in_many_chunks_of_64_streams(torch_cuda):
+    """K = 256 at L = 2048 in 64-value chunks of 64 streams: more than 16,384 chunks in one
+    launch, so the decode runs 16-lane rows of four streams a lane with the largest table."""
+    print("case: K=256 L=2048 C=64 S=64, 17,188 chunks", flush=True)
+    p = codec.Params(K=256, log2_L=11, chunk_symbols=64, streams=64)
+    _roundtrip_device_tables(torch_cuda, [D.weight().reshape(-1)[:1_100_003]], p, host_tables=False)
 
 
 def test_shannonic_ranges_with_more_states(torch_cuda):

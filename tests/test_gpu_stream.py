@@ -102,7 +102,8 @@ def test_model_layers_streamed(torch_cuda):
     from oracle import oracle as O
     torch = torch_cuda
     cfg = D.CONFIGS["model"]
-    p = codec.Params(K=cfg["K"], log2_L=cfg["log2_L"], chunk_symbols=cfg["chunk"])
+    p = codec.Params(K=cfg["K"], log2_L=cfg["log2_L"], chunk_symbols=cfg["chunk"],
+                     streams=cfg["streams"])
     idx = list(range(7)) + list(range(7 * 31, 7 * 32))
     print(f"case: model tensors {idx} via the GPU generator, streamed", flush=True)
     dx = [D.model_tensor_torch(i, "cuda").view(-1) for i in idx]
@@ -123,9 +124,10 @@ def test_model_layers_streamed(torch_cuda):
         cont = buf[offs[k]: offs[k] + sizes[k]].cpu().numpy()
         for c in set(rng.choice(nch, size=min(6, nch), replace=False).tolist()) | {nch - 1}:
             part = xh[c * C_: (c + 1) * C_]
-            one, _ = O.encode(part, lo, f, p.log2_L, C_, 32)
-            assert np.array_equal(CL.chunk_bytes(cont, xh.size, p.K, C_, p.log2_L, c),
-                                  CL.chunk_bytes(one, part.size, p.K, C_, p.log2_L, 0)), (idx[k], c)
+            one, _ = O.encode(part, lo, f, p.log2_L, C_, p.streams)
+            assert np.array_equal(CL.chunk_bytes(cont, xh.size, p.K, C_, p.log2_L, c, p.streams),
+                                  CL.chunk_bytes(one, part.size, p.K, C_, p.log2_L, 0, p.streams)), \
+                (idx[k], c)
     # park and stream back
     starts, at = [], 0
     for s in sizes:
