@@ -76,7 +76,9 @@ typedef int32_t sh_status;
 /* Codec parameters.  The GPU path supports 1 <= K <= 256, 1 <= log2_L <= 11 (tables with
  * fields of at most 16 bits, the widest range's offset bits plus log2_L; sh_encode and
  * sh_decode, which carry the table in their launch arguments, take log2_L <= 8),
- * streams == 32 and chunk_symbols a multiple of 32 in [32, 65536].
+ * streams 32 or 64, and chunk_symbols a multiple of streams in [streams, 65536].  More
+ * streams give a launch with few chunks more independent state machines at a framing cost
+ * of about log2_L bits a stream and chunk; the fused matrix-vector decode takes 32.
  * The pages' configuration is K = 16, log2_L = 7 (530 B of codec state,
  * "Codec state footprint", paper section 4.1 and Appendix A). */
 typedef struct {
@@ -311,6 +313,7 @@ sh_status sh_decode_batch(const void* d_tables, const uint8_t* const* d_in,
  * decompression inside the kernels that consume the data, applied to this container with
  * a matrix-vector product as the consumer (an int8 weight matrix times an int8 activation
  * vector, or int8 keys times a query).
+ * params->streams must be 32 (SH_ERR_UNSUPPORTED otherwise).
  * cols: a multiple of 32, at most 16384 (SH_ERR_UNSUPPORTED otherwise; 0 is
  * SH_ERR_INVALID_ARG); every n[i] a multiple of cols (SH_ERR_INVALID_ARG).  d_a[i]: device,
  * cols int8 values, 16-byte aligned; d_y[i]: device, n[i] / cols int32, 4-byte aligned, read
