@@ -129,10 +129,11 @@ CONFIGS = {
     # MI355X: decode 98.8 -> 81.6 us with four streams a lane, encode 168 -> 152 us)
     "activations": dict(K=16, log2_L=7, chunk=16384, streams=64),
     # the model-scale workload fixes neither: 16,384 values (as for the activations) keep the
-    # per-chunk framing (lane initial states, index entry, padding) near 0.3% of H on these
-    # weights, where 4,096 cost about 1.2%; its launches fill the GPU, and 64 streams
-    # decoded them only 0.8% faster than 32 for 0.12% of H more framing
-    "model": dict(K=16, log2_L=7, chunk=16384, streams=32),
+    # per-chunk framing (lane initial states, index entry, padding) near 0.4% of H on these
+    # weights, where 4,096 cost about 1.2%; 64 streams (four a lane, one LDS write of the
+    # lane's four bytes a step) decoded a 48-tensor launch in 625 us against 676 us for 32,
+    # for 0.12% of H more framing
+    "model": dict(K=16, log2_L=7, chunk=16384, streams=64),
 }
 
 
