@@ -25,17 +25,18 @@ static_assert(kEncodeChunksPerBlock == kEncRowsBlock / 16, "one chunk per 16-lan
 constexpr uint32_t kERing = 128;                   // ring dwords per chunk
 constexpr uint32_t kEFlush = 64;                   // dwords per flush
 constexpr uint32_t kETileSteps = 16;               // input steps staged at a time
-// The four rows of a wavefront write their rings and read their tiles at similar offsets in
-// the same steps: their tiles sit 32 bytes apart beyond their size and their ring origins 8
-// dwords apart (ring dword (d + 8 row) mod 128 holds slot dword d), so that the rows use
-// different LDS banks.
-constexpr uint32_t kERowTurn = 8;                  // ring dwords per row of the wavefront
 template <int P>
 struct EncGeom {
     static_assert(P == 2 || P == 4, "two or four streams a lane");
     static constexpr uint32_t kS = 16 * P;                  // streams of a chunk
     static constexpr uint32_t kTileBytes = kETileSteps * kS;
-    static constexpr uint32_t kTileStride = kTileBytes + 32;
+    // The four rows of a wavefront write their rings and read their tiles at similar offsets
+    // in the same steps.  A row reads P bytes a lane of a tile step (16 P bytes, 4 P banks)
+    // and ORs about 16 P x 6.5 bits of fields a step into its ring (some 3 P dwords), so the
+    // tiles sit 16 P bytes apart beyond their size and the ring origins 4 P dwords apart (ring
+    // dword (d + 4 P row) mod 128 holds slot dword d): the rows use different LDS banks.
+    static constexpr uint32_t kTileStride = kTileBytes + 16 * P;
+    static constexpr uint32_t kRowTurn = 4 * P;             // ring dwords per row of the wavefront
     static constexpr uint32_t kTileVecs = kS / 16;          // 16-byte loads a lane stages
     // The ring holds every dword not yet flushed.  After a flush check the fields reach no
     // lower than 64 dwords below the flush mark; checks come at least every other step, and
@@ -119,7 +120,9 @@ template <class A, int P>
 __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
     using G = EncGeom<P>;
     constexpr uint32_t kS = G::kS;
-    extern __shared__ __align__(16) uint32_t esm[];
+    // the entry and ring addresses below are formed with AND-OR, so the LDS block must
+    // start on a 2 KB boundary (it is the kernel's only LDS, at byte 0)
+    extern __shared__ __align__(2048) uint32_t esm[];
     const uint32_t tid = threadIdx.x, lane = tid & 63, j = lane & 15, row = lane >> 4;
     const uint32_t block = __builtin_amdgcn_readfirstlane(blockIdx.x);
     const SegDesc* sg = codec_seg(a, block, false);
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
 
     // bit positions are kept turned by the row's ring origin: position p stands for slot bit
     // p - turn
-    const uint32_t turn = 32 * kERowTurn * row;
+    const uint32_t turn = 32 * G::kRowTurn * row;
     uint32_t fpos = a.h.slot_dwords * 32 + turn;  // fields go below fpos, right to left
     uint32_t fmark = a.h.slot_dwords;    // dwords at or above fmark are in the slot
     uint32_t flush_at = (fmark - kEFlush) * 32 + turn;  // once fpos is below this, flush a block
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
 
     auto flush_block = [&](uint32_t blk) {  // ring dwords [blk, blk + 64) -> slot
         typedef __attribute__((address_space(3))) v4u lds_v4;
-        lds_v4* r = (lds_v4*)(uintptr_t)(ring_byte + 4 * ((blk + kERowTurn * row + 4 * j) & (kERing - 1)));
+        lds_v4* r = (lds_v4*)(uintptr_t)(ring_byte + 4 * ((blk + G::kRowTurn * row + 4 * j) & (kERing - 1)));
         const v4u v = *r;
         *r = v4u{0, 0, 0, 0};
         __builtin_amdgcn_raw_buffer_store_b128(v, rslot, (int)(slot_row + 4 * (blk + 4 * j)), 0, 0);
