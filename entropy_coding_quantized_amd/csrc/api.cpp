@@ -35,6 +35,7 @@ struct DecodePath {
     sh_status (*launch)(const CodecArgs&, uint32_t, void*);
 };
 DecodePath decode_path(uint64_t total_chunks, const sh_params* p) {
+    if (p->streams == kStreamsWidest) return {kWideHalvesChunksPerBlock, launch_decode_wide_halves};
     if (total_chunks < kHalfDecodeMaxChunks) {
         if (p->streams == kStreamsWide) return {kWideHalvesChunksPerBlock, launch_decode_wide_halves};
         if (p->log2_L <= (uint32_t)kInlineMaxLog2L) return {kChunksPerBlock, launch_decode_halves};
@@ -45,7 +46,8 @@ constexpr uint32_t kChunksPerBlockC = 4;  // compaction kernel
 
 bool gpu_params_ok(const sh_params* p) {
     return p && p->K >= 1 && p->K <= 256 && p->log2_L >= 1 && p->log2_L <= (uint32_t)kMaxLog2LGpu &&
-           (p->streams == kStreamsNarrow || p->streams == kStreamsWide) &&
+           (p->streams == kStreamsNarrow || p->streams == kStreamsWide ||
+            p->streams == kStreamsWidest) &&
            p->chunk_symbols >= p->streams && p->chunk_symbols <= kMaxChunk &&
            p->chunk_symbols % p->streams == 0;
 }

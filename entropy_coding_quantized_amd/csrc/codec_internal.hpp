@@ -18,8 +18,10 @@ namespace shn {
 
 constexpr int kLgFrac = 24;            // fractional bits of the DP's fixed-point log2
 // interleaved tANS streams per chunk on the GPU path: 32 (two a lane of a 16-lane row, or
-// one a lane of a half wavefront) or 64 (four a lane of a 16-lane row)
-constexpr uint32_t kStreamsNarrow = 32, kStreamsWide = 64;
+// one a lane of a half wavefront), 64 (four a lane of a 16-lane row, or two a lane of a half
+// wavefront) or 128 (four a lane of a half wavefront to decode, eight a lane of a 16-lane
+// row to encode)
+constexpr uint32_t kStreamsNarrow = 32, kStreamsWide = 64, kStreamsWidest = 128;
 constexpr int kMaxLog2LHost = 12;      // host table build
 // GPU path: L up to 2048 states (standard tANS sizes), tables held in LDS; the decoder
 // takes two adjacent fields in one 32-bit window, so a table is usable on the GPU only when
@@ -240,8 +242,8 @@ sh_status launch_histogram(const HistArgs& h, uint32_t nseg_zero, void* stream);
 sh_status launch_build_tables(const BuildArgs& b, void* stream);
 // the decode behind sh_decode and sh_decode_batch (k_decode_rows.hip): one chunk per
 // 16-lane row (two or four streams a lane), kDecodeChunksPerBlock chunks a block; and, for
-// launches of few chunks of 64 streams, one chunk per half wavefront (two streams a lane),
-// kWideHalvesChunksPerBlock chunks a block
+// launches of few chunks of 64 streams and every launch of chunks of 128, one chunk per half
+// wavefront (two or four streams a lane), kWideHalvesChunksPerBlock chunks a block
 constexpr uint32_t kDecodeChunksPerBlock = 16;
 sh_status launch_decode(const CodecArgs& a, uint32_t total_blocks, void* stream);
 constexpr uint32_t kWideHalvesChunksPerBlock = 8;
@@ -250,8 +252,8 @@ sh_status launch_decode_wide_halves(const CodecArgs& a, uint32_t total_blocks, v
 // this many values long
 constexpr uint32_t kMaxMatvecCols = 16384;
 sh_status launch_decode_matvec(const CodecArgs& a, uint32_t total_blocks, void* stream);
-// the encoder's chunk kernel: one chunk per 16-lane row (two or four streams a lane), 16
-// chunks a block
+// the encoder's chunk kernel: one chunk per 16-lane row (two, four or eight streams a
+// lane), 16 chunks a block
 constexpr uint32_t kEncodeChunksPerBlock = 16;
 // segments of at most this many chunks are indexed and compacted by one kernel
 // (k_encode_place: each block sums the sizes of the chunks before its own, so the work

@@ -5,17 +5,17 @@
 // talk notes, "Runtime encoding/decoding" (paper section 4.2): from the state X the decode
 // table gives the range s and the count of state bits; the offset o is read as w_s raw
 // bits, the value is base[s] + o, and the state bits lead to the next state.  Table
-// lookups, shifts, masks and adds only.  The container layout (chunks of C values, 32 or 64
-// interleaved tANS streams per chunk, fields in (step, stream) order) and the GPU mapping
+// lookups, shifts, masks and adds only.  The container layout (chunks of C values, 32, 64 or
+// 128 interleaved tANS streams per chunk, fields in (step, stream) order) and the GPU mapping
 // below are this library's own design; the pages give no GPU design.
 //
 // Mapping: one chunk per row of W lanes, a 16-lane DPP row (W = 16) or a half wavefront
 // (W = 32), so a wavefront decodes 64 / W chunks side by side.  Lane j of a row runs P
 // adjacent streams, P j to P j + P - 1 (W P streams a chunk: 16 x 2 for chunks of 32
-// streams, 16 x 4 or 32 x 2 for chunks of 64), whose fields are adjacent in every step: one
-// W-lane prefix sum (DPP) of the lanes' field lengths gives every lane's bit position, and
-// one LDS read of two (P = 2) or three (P = 4) ring dwords brings all its fields.  Rows of 32
-// lanes give a launch with few chunks twice the wavefronts of rows of 16.
+// streams, 16 x 4 or 32 x 2 for chunks of 64, 32 x 4 for 128), whose fields are adjacent in
+// every step: one W-lane prefix sum (DPP) of the lanes' field lengths gives every lane's bit
+// position, and one LDS read of two (P = 2) or three (P = 4) ring dwords brings all its
+// fields.  Rows of 32 lanes give a launch with few chunks twice the wavefronts of rows of 16.
 // Compressed words reach a per-chunk LDS ring through 128-bit loads; the decode table is
 // staged in LDS as 8-byte entries (measured on MI355X: a random 8-byte LDS read costs 7
 // clocks per wavefront and CU at full occupancy, a 16-byte one 12, a 12-byte one 20).  No
@@ -27,12 +27,6 @@ namespace shn {
 namespace {
 
 constexpr int kRowsBlock = 256;                    // 4 wavefronts, 256 / W rows = chunks
-constexpr uint32_t kRRingLog2 = 8;
-constexpr uint32_t kRRing = 1u << kRRingLog2;      // compressed dwords resident per chunk
-// a ring is followed by copies of its first dwords (a lane's read of two or three dwords
-// never wraps) and padding that keeps the next ring 16-byte aligned for the 128-bit writes
-constexpr uint32_t kRRingStride = kRRing + 4;
-constexpr uint32_t kRFill = kRRing / 2;            // dwords per refill
 // Decoded bytes of kTileSteps steps of a chunk are gathered in an LDS tile and stored
 // together: measured on MI355X, the 32-byte stores of single steps held the decode near
 // 1.7 TB/s of output however short the rest of the step was.  The tiles of a block's rows
@@ -46,10 +40,19 @@ constexpr uint32_t kTileSteps = 4;
 // Geometry of a row of W lanes that run P streams each.
 template <int W, int P>
 struct RowGeom {
-    static_assert((W == 16 && (P == 2 || P == 4)) || (W == 32 && P == 2), "16 x 2, 16 x 4, 32 x 2");
+    static_assert((W == 16 && (P == 2 || P == 4)) || (W == 32 && (P == 2 || P == 4)),
+                  "16 x 2, 16 x 4, 32 x 2, 32 x 4");
     static constexpr uint32_t kS = W * P;                      // streams of a chunk
     static constexpr uint32_t kRowsPerWave = 64 / W;
     static constexpr uint32_t kRowsPerBlock = kRowsBlock / W;
+    // compressed dwords resident per chunk: 256, 512 for chunks of 128 streams (whose steps
+    // take up to 64 dwords)
+    static constexpr uint32_t kRingLog2 = kS == 128 ? 9 : 8;
+    static constexpr uint32_t kRing = 1u << kRingLog2;
+    // a ring is followed by copies of its first dwords (a lane's read of two or three dwords
+    // never wraps) and padding that keeps the next ring 16-byte aligned for the 128-bit writes
+    static constexpr uint32_t kRingStride = kRing + 4;
+    static constexpr uint32_t kRFill = kRing / 2;              // dwords per refill
     static constexpr uint32_t kFillVecs = kRFill / (4 * W);    // 16-byte loads a lane, a refill
     static constexpr uint32_t kTileDwords = kTileSteps * kS / 4;
     static constexpr uint32_t kTileStride = kTileDwords + 8;
@@ -98,11 +101,12 @@ __device__ __forceinline__ uint32_t scan_row(uint32_t v) {
     else return scan32(v);
 }
 
-// The ring's dword index of a bit position, (pos >> 5) mod 256, as one v_bfe_u32 (the
+// The ring's dword index of a bit position, (pos >> 5) mod 2^kLog2, as one v_bfe_u32 (the
 // compiler would split the extract and the scaling that follows it into three operations).
+template <uint32_t kLog2>
 __device__ __forceinline__ uint32_t ring_dword(uint32_t pos) {
     uint32_t d;
-    asm("v_bfe_u32 %0, %1, 5, %2" : "=v"(d) : "v"(pos), "i"(kRRingLog2));
+    asm("v_bfe_u32 %0, %1, 5, %2" : "=v"(d) : "v"(pos), "i"(kLog2));
     return d;
 }
 
@@ -171,6 +175,7 @@ template <class A, int W, int P>
 __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
     using G = RowGeom<W, P>;
     constexpr uint32_t kS = G::kS, kRowsPerWave = G::kRowsPerWave, kFillVecs = G::kFillVecs;
+    constexpr uint32_t kRRing = G::kRing, kRRingStride = G::kRingStride, kRFill = G::kRFill;
     extern __shared__ __align__(16) uint32_t dsm[];
     const uint32_t tid = threadIdx.x, lane = tid & 63, j = lane % W, row = lane / W;
     const uint32_t block = __builtin_amdgcn_readfirstlane(blockIdx.x);
@@ -237,7 +242,7 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
             err = 1;
         }
     }
-    // the first two refills (ring dwords [0, 256)), and the third in flight
+    // the first two refills (the whole ring), and the third in flight
     constexpr uint32_t kLaneFill = 4 * kFillVecs;   // dwords a lane loads per refill
     v4u f0[kFillVecs], f1[kFillVecs];
 #pragma unroll
@@ -301,7 +306,7 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
     }
     __syncthreads();
 
-    // initial slots: stream s's R bits at bit0 + s * R (at most 24 + 63 * 11 + 11 bits: within
+    // initial slots: stream s's R bits at bit0 + s * R (at most 24 + 127 * 11 + 11 bits: within
     // the first ring words, no wrap)
     const uint32_t lanes = r.nc < kS ? r.nc : kS;
     auto init_state = [&](uint32_t s) {
@@ -360,7 +365,7 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
         const uint32_t posm = r.pos - tot;
         const uint32_t incl = scan_row<W>(tot);
         const uint32_t start = posm + incl;
-        const lds_u32* rp = (const lds_u32*)(uintptr_t)((ring_dword(start) << 2) + r.ring_byte);
+        const lds_u32* rp = (const lds_u32*)(uintptr_t)((ring_dword<G::kRingLog2>(start) << 2) + r.ring_byte);
 #pragma unroll
         for (uint32_t i = 0; i < G::kWin; ++i) w[i] = rp[i];
         split_fields<P>(w, start, nd, f);
@@ -438,7 +443,7 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
         }
         const uint32_t incl = scan_row<W>(tot);
         const uint32_t start = r.pos - tot + incl;
-        const lds_u32* rp = (const lds_u32*)(uintptr_t)((ring_dword(start) << 2) + r.ring_byte);
+        const lds_u32* rp = (const lds_u32*)(uintptr_t)((ring_dword<G::kRingLog2>(start) << 2) + r.ring_byte);
 #pragma unroll
         for (uint32_t i = 0; i < G::kWin; ++i) w[i] = rp[i];
         split_fields<P>(w, start, nd, f);
@@ -479,7 +484,7 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
 template <int W, int P>
 uint32_t rows_lds_bytes(uint32_t L) {
     using G = RowGeom<W, P>;
-    return 4 * (2 * L + G::kRowsPerBlock * (kRRingStride + G::kTileStride));
+    return 4 * (2 * L + G::kRowsPerBlock * (G::kRingStride + G::kTileStride));
 }
 
 template <int W, int P>
@@ -502,8 +507,9 @@ sh_status launch_decode(const CodecArgs& a, uint32_t total_blocks, void* stream)
 }
 
 sh_status launch_decode_wide_halves(const CodecArgs& a, uint32_t total_blocks, void* stream) {
-    if (a.S != kStreamsWide) return SH_ERR_UNSUPPORTED;
-    return launch_rows<32, 2>(a, total_blocks, stream);
+    if (a.S == kStreamsWide) return launch_rows<32, 2>(a, total_blocks, stream);
+    if (a.S == kStreamsWidest) return launch_rows<32, 4>(a, total_blocks, stream);
+    return SH_ERR_UNSUPPORTED;
 }
 
 }  // namespace shn

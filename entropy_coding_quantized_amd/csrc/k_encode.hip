@@ -22,46 +22,46 @@ namespace shn {
 // streams' final states (the decoder's initial states) in front.
 constexpr int kEncRowsBlock = 256;                 // 4 wavefronts, 16 rows = 16 chunks
 static_assert(kEncodeChunksPerBlock == kEncRowsBlock / 16, "one chunk per 16-lane row");
-constexpr uint32_t kERing = 128;                   // ring dwords per chunk
 constexpr uint32_t kEFlush = 64;                   // dwords per flush
-constexpr uint32_t kETileSteps = 16;               // input steps staged at a time
+// LDS (dynamic; the kernel's only LDS, so it starts at LDS byte 0): the value entries (two
+// dwords per value, at a 2 KB boundary so that an entry's address is one AND-OR), the
+// rings (one per chunk, aligned to their size), the encTable (a dword per slot, holding the
+// next state L + slot), the input tiles (u = x + 128 of kTileSteps steps of a chunk), then
+// the block's two totals
+constexpr uint32_t kEVtByte = 0;
+constexpr uint32_t kERingsByte = kEVtByte + 256 * 8;                                 // 2 KB
 template <int P>
 struct EncGeom {
-    static_assert(P == 2 || P == 4, "two or four streams a lane");
+    static_assert(P == 2 || P == 4 || P == 8, "two, four or eight streams a lane");
     static constexpr uint32_t kS = 16 * P;                  // streams of a chunk
-    static constexpr uint32_t kTileBytes = kETileSteps * kS;
+    // The ring holds every dword not yet flushed.  After a flush check the fields reach no
+    // lower than 64 dwords below the flush mark; checks come at least every other step, and
+    // a step places at most kS fields of 16 bits, kS / 2 dwords; so the unflushed dwords span
+    // at most 64 + kS dwords: 128 dwords (the ring exactly at P = 4; the mark's own dword,
+    // the lowest one's twin in the ring, is flushed and zero), 256 at P = 8.
+    static constexpr uint32_t kRing = P == 8 ? 256 : 128;
+    static_assert(kEFlush + kS <= kRing, "two steps fit in the ring");
+    static constexpr uint32_t kTileSteps = P == 8 ? 8 : 16;  // input steps staged at a time
+    static constexpr uint32_t kTileBytes = kTileSteps * kS;
+    static constexpr uint32_t kLaneStage = kTileBytes / 16;  // bytes a lane stages
+    static constexpr uint32_t kTileVecs = kLaneStage / 16;   // 16-byte loads a lane stages
     // The four rows of a wavefront write their rings and read their tiles at similar offsets
     // in the same steps.  A row reads P bytes a lane of a tile step (16 P bytes, 4 P banks)
     // and ORs about 16 P x 6.5 bits of fields a step into its ring (some 3 P dwords), so the
     // tiles sit 16 P bytes apart beyond their size and the ring origins 4 P dwords apart (ring
-    // dword (d + 4 P row) mod 128 holds slot dword d): the rows use different LDS banks.
+    // dword (d + 4 P row) mod kRing holds slot dword d): the rows use different LDS banks.
     static constexpr uint32_t kTileStride = kTileBytes + 16 * P;
     static constexpr uint32_t kRowTurn = 4 * P;             // ring dwords per row of the wavefront
-    static constexpr uint32_t kTileVecs = kS / 16;          // 16-byte loads a lane stages
-    // The ring holds every dword not yet flushed.  After a flush check the fields reach no
-    // lower than 64 dwords below the flush mark; checks come at least every other step, and
-    // a step places at most kS fields of 16 bits, kS / 2 dwords; so the unflushed dwords span
-    // at most 64 + kS dwords (128 at P = 4: the ring exactly; the mark's own dword, the
-    // lowest one's twin in the ring, is flushed and zero).
-    static_assert(kEFlush + kS <= kERing, "two steps fit in the ring");
+    static constexpr uint32_t kEsByte = kERingsByte + kEncodeChunksPerBlock * kRing * 4;
+    static_assert(kEsByte >= 4 * kMaxLGpu && kEsByte + 4 * kMaxLGpu < 32768,
+                  "encTable addresses stay positive and below bit 15 of an entry");
+    __host__ __device__ static constexpr uint32_t tiles_byte(uint32_t L) {
+        return (kEsByte + 4 * L + 15) / 16 * 16;
+    }
+    __host__ __device__ static constexpr uint32_t lds_bytes(uint32_t L) {
+        return tiles_byte(L) + kEncodeChunksPerBlock * kTileStride + 16;
+    }
 };
-// LDS (dynamic; the kernel's only LDS, so it starts at LDS byte 0): the value entries (two
-// dwords per value, at a 2 KB boundary so that an entry's address is one AND-OR), the
-// rings (512 B each, 512 B aligned), the encTable (a dword per slot, holding the next
-// state L + slot), the input tiles (u = x + 128 of kETileSteps steps of a chunk), then the
-// block's two totals
-constexpr uint32_t kEVtByte = 0;
-constexpr uint32_t kERingsByte = kEVtByte + 256 * 8;                                 // 2 KB
-constexpr uint32_t kEEsByte = kERingsByte + kEncodeChunksPerBlock * kERing * 4;      // 10 KB
-__host__ __device__ constexpr uint32_t encode_tiles_byte(uint32_t L) {
-    return (kEEsByte + 4 * L + 15) / 16 * 16;
-}
-template <int P>
-__host__ __device__ constexpr uint32_t encode_lds_bytes(uint32_t L) {
-    return encode_tiles_byte(L) + kEncodeChunksPerBlock * EncGeom<P>::kTileStride + 16;
-}
-static_assert(kEEsByte >= 4 * kMaxLGpu && kEEsByte + 4 * kMaxLGpu < 32768,
-              "encTable addresses stay positive and below bit 15 of an entry");
 
 // container bytes of a chunk of the given bits: whole size units of 2^ulog bytes
 __device__ __forceinline__ uint32_t chunk_bytes_of(uint32_t bits, uint32_t ulog) {
@@ -73,15 +73,16 @@ typedef const __attribute__((address_space(3))) uint16_t lds_r16;
 typedef const __attribute__((address_space(3))) uint32_t lds_r32;
 typedef unsigned int v2u_e __attribute__((ext_vector_type(2)));
 
-// OR a pair of fields (at most 32 bits) into a ring at bit pos; ring_byte is the ring's LDS
-// byte address, a multiple of its 512 B.  The second dword is OR-ed only by the lanes whose
-// pair reaches into it: the pairs of a step share a few dwords, and same-address LDS
-// atomics serialise.
+// OR a pair of fields (at most 32 bits) into a ring of kRing dwords at bit pos; ring_byte is
+// the ring's LDS byte address, a multiple of its size.  The second dword is OR-ed only by
+// the lanes whose pair reaches into it: the pairs of a step share a few dwords, and
+// same-address LDS atomics serialise.
+template <uint32_t kRing>
 __device__ __forceinline__ void ring_or2(uint32_t ring_byte, uint32_t pos, uint32_t field) {
     const uint64_t wide = (uint64_t)field << (pos & 31);
     const uint32_t b = pos >> 3;
-    const uint32_t a0 = (b & (4 * kERing - 4)) | ring_byte;
-    const uint32_t a1 = ((b + 4) & (4 * kERing - 4)) | ring_byte;
+    const uint32_t a0 = (b & (4 * kRing - 4)) | ring_byte;
+    const uint32_t a1 = ((b + 4) & (4 * kRing - 4)) | ring_byte;
     __hip_atomic_fetch_or((lds_w32*)(uintptr_t)a0, (uint32_t)wide, __ATOMIC_RELAXED,
                           __HIP_MEMORY_SCOPE_WORKGROUP);
     if ((uint32_t)(wide >> 32))
@@ -119,7 +120,9 @@ struct EEnt {
 template <class A, int P>
 __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
     using G = EncGeom<P>;
-    constexpr uint32_t kS = G::kS;
+    constexpr uint32_t kS = G::kS, kERing = G::kRing, kETileSteps = G::kTileSteps;
+    constexpr uint32_t kEEsByte = G::kEsByte;
+    using VT = std::conditional_t<P == 8, uint64_t, uint32_t>;  // a lane's P values, a byte each
     // the entry and ring addresses below are formed with AND-OR, so the LDS block must
     // start on a 2 KB boundary (it is the kernel's only LDS, at byte 0)
     extern __shared__ __align__(2048) uint32_t esm[];
@@ -134,9 +137,9 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
     const uint32_t L = a.h.L, R = a.h.R, R1 = a.h.R + 1;
     const uint32_t base = lds_offset(esm);  // 0: the only LDS of the kernel
     const uint32_t ring_byte = base + kERingsByte + 4 * kERing * rowi;
-    const uint32_t tile_byte = base + encode_tiles_byte(L) + G::kTileStride * rowi;
+    const uint32_t tile_byte = base + G::tiles_byte(L) + G::kTileStride * rowi;
     const uint32_t vt_byte = base + kEVtByte, es_byte = base + kEEsByte;
-    uint32_t* agg_s = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(esm) + encode_tiles_byte(L) +
+    uint32_t* agg_s = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(esm) + G::tiles_byte(L) +
                                                   kEncodeChunksPerBlock * G::kTileStride);
 
     // the tables in their LDS form (device form: v0 = bias, v1 = o | w << 8 | (f == 0) << 15 |
@@ -186,20 +189,22 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
     }
     const uint32_t steps = (nc_max + kS - 1) / kS;
 
-    // Lane j stages step 16 T + j of tile T: kS bytes.  Past a short chunk's end lies the
-    // end of the wavefront's range (a 16-byte load reaching past it reads 0 as a whole, so
-    // the lanes at the end read byte by byte) or the next chunk, whose values go unused.
+    // Lane j stages bytes [kLaneStage j, kLaneStage (j + 1)) of tile T (step 16 T + j when a
+    // tile is 16 steps).  Past a short chunk's end lies the end of the wavefront's range (a
+    // 16-byte load reaching past it reads 0 as a whole, so the lanes at the end read byte by
+    // byte) or the next chunk, whose values go unused.
+    constexpr uint32_t kLaneStage = G::kLaneStage;
     const uint32_t in_len = (uint32_t)(grp_len < 4ull * a.h.C ? grp_len : 4ull * a.h.C);
     auto load_tile = [&](uint32_t T, v4u* pv) {
-        const uint32_t b = in_row + (kETileSteps * T + j) * kS;
-        if (b + kS <= in_len) {
+        const uint32_t b = in_row + G::kTileBytes * T + kLaneStage * j;
+        if (b + kLaneStage <= in_len) {
 #pragma unroll
             for (uint32_t v = 0; v < G::kTileVecs; ++v)
                 pv[v] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rin, (int)(b + 16 * v), 0, 0));
         } else {
 #pragma unroll
             for (uint32_t v = 0; v < G::kTileVecs; ++v) pv[v] = v4u{0, 0, 0, 0};
-            for (uint32_t k = 0; k < kS; ++k)
+            for (uint32_t k = 0; k < kLaneStage; ++k)
                 if (b + k < in_len) {
                     const uint32_t byte = __builtin_amdgcn_raw_buffer_load_b8(rin, (int)(b + k), 0, 0);
                     pv[k >> 4][(k >> 2) & 3] |= byte << (8 * (k & 3));
@@ -232,16 +237,18 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
         const v4u flip = {0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};
 #pragma unroll
         for (uint32_t v = 0; v < G::kTileVecs; ++v)
-            *(lds_v4*)(uintptr_t)(tile_byte + kS * j + 16 * v) = pv[v] ^ flip;
+            *(lds_v4*)(uintptr_t)(tile_byte + kLaneStage * j + 16 * v) = pv[v] ^ flip;
     };
-    auto vals_at = [&](uint32_t t) {  // u of the lane's P streams at step t (staged), a byte each
+    auto vals_at = [&](uint32_t t) -> VT {  // u of the lane's P streams at step t (staged)
         const uint32_t at = tile_byte + kS * (t & (kETileSteps - 1)) + P * j;
         if constexpr (P == 2) return (uint32_t) * (lds_r16*)(uintptr_t)at;
-        else return *(lds_r32*)(uintptr_t)at;
+        else if constexpr (P == 4) return *(lds_r32*)(uintptr_t)at;
+        else return *(const __attribute__((address_space(3))) uint64_t*)(uintptr_t)at;
     };
     // the entry of byte i of vals (the table sits on a 2 KB boundary)
-    auto entry_of = [&](uint32_t vals, int i) {
-        const uint32_t off = i == 0 ? (vals << 3) & 0x7F8u : (vals >> (8 * i - 3)) & 0x7F8u;
+    auto entry_of = [&](VT vals, int i) {
+        const uint32_t off = i == 0 ? ((uint32_t)vals << 3) & 0x7F8u
+                                    : (uint32_t)(vals >> (8 * i - 3)) & 0x7F8u;
         const v2u_e v = *(const __attribute__((address_space(3))) v2u_e*)(uintptr_t)(off | vt_byte);
         return EEnt{v[0], v[1]};
     };
@@ -264,11 +271,11 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
         e[i] = EEnt{0, 0};
         X[i] = L;
     }
-    uint32_t u_n = 0;
+    VT u_n = 0;
     if (steps > 0) {
         stage();
         if (steps - 1 >= kETileSteps) load_tile((steps - 1) / kETileSteps - 1, pv);
-        const uint32_t u_c = vals_at(steps - 1);
+        const VT u_c = vals_at(steps - 1);
         if (steps >= 2) u_n = fetch(steps - 2);
 #pragma unroll
         for (int i = 0; i < P; ++i) e[i] = entry_of(u_c, i);
@@ -292,8 +299,8 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
     // may_stage: false for a step whose t is known even (t - 2 is then never a tile's first
     // step in backward order, and for t = 0 the value read is a harmless, unused one)
     auto step = [&](uint32_t t, auto partial, auto may_stage) {
-        uint32_t u_nn;
-        if constexpr (decltype(may_stage)::value) u_nn = t >= 2 ? fetch(t - 2) : 0u;
+        VT u_nn;
+        if constexpr (decltype(may_stage)::value) u_nn = t >= 2 ? fetch(t - 2) : VT(0);
         else u_nn = vals_at(t - 2);
         EEnt ne[P];
 #pragma unroll
@@ -323,18 +330,21 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
         }
         bad |= flag;
         // the lane's fields, stream P j's lowest: pairs of at most 32 bits
-        const uint32_t l01 = l[0] + l[1];
-        const uint32_t f01 = f[0] | (f[1] << l[0]);
-        uint32_t lp = l01, f23 = 0;
-        if constexpr (P == 4) {
-            lp += l[2] + l[3];
-            f23 = f[2] | (f[3] << l[2]);
+        uint32_t fp[P / 2], lq[P / 2], lp = 0;
+#pragma unroll
+        for (int k = 0; k < P / 2; ++k) {
+            fp[k] = f[2 * k] | (f[2 * k + 1] << l[2 * k]);
+            lq[k] = l[2 * k] + l[2 * k + 1];
+            lp += lq[k];
         }
         const uint32_t incl = escan16(lp);
         fpos -= erow_last(incl);
-        const uint32_t at = fpos + incl - lp;
-        ring_or2(ring_byte, at, f01);
-        if constexpr (P == 4) ring_or2(ring_byte, at + l01, f23);
+        uint32_t at = fpos + incl - lp;
+#pragma unroll
+        for (int k = 0; k < P / 2; ++k) {
+            ring_or2<kERing>(ring_byte, at, fp[k]);
+            at += lq[k];
+        }
 #pragma unroll
         for (int i = 0; i < P; ++i) e[i] = ne[i];
         u_n = u_nn;
@@ -379,7 +389,7 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
     for (int i = 0; i < P; i += 2) {  // two states (at most 22 bits) at a time
         const uint32_t s0 = P * j + i < lanes ? X[i] - L : 0u;
         const uint32_t s1 = P * j + i + 1 < lanes ? X[i + 1] - L : 0u;
-        ring_or2(ring_byte, Pi + turn + (P * j + i) * R, s0 | (s1 << R));
+        ring_or2<kERing>(ring_byte, Pi + turn + (P * j + i) * R, s0 | (s1 << R));
     }
     while (fmark > (Pi >> 5)) {
         fmark -= kEFlush;
@@ -625,17 +635,21 @@ __global__ __launch_bounds__(256) void k_encode_place(const A a) {
 
 sh_status launch_encode(const CodecArgs& a, uint32_t total_blocks, uint32_t total_blocks_c,
                         bool place, void* stream) {
-    if (a.S != kStreamsNarrow && a.S != kStreamsWide) return SH_ERR_UNSUPPORTED;
+    if (a.S != kStreamsNarrow && a.S != kStreamsWide && a.S != kStreamsWidest)
+        return SH_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     with_kernel_args(a, [&](const auto& k) {
         using K = std::decay_t<decltype(k)>;
         if (total_blocks > 0) {
-            if (a.S == kStreamsWide)
+            if (a.S == kStreamsWidest)
+                hipLaunchKernelGGL((k_encode_chunks<K, 8>), dim3(total_blocks), dim3(kEncRowsBlock),
+                                   EncGeom<8>::lds_bytes(a.L), s, k);
+            else if (a.S == kStreamsWide)
                 hipLaunchKernelGGL((k_encode_chunks<K, 4>), dim3(total_blocks), dim3(kEncRowsBlock),
-                                   encode_lds_bytes<4>(a.L), s, k);
+                                   EncGeom<4>::lds_bytes(a.L), s, k);
             else
                 hipLaunchKernelGGL((k_encode_chunks<K, 2>), dim3(total_blocks), dim3(kEncRowsBlock),
-                                   encode_lds_bytes<2>(a.L), s, k);
+                                   EncGeom<2>::lds_bytes(a.L), s, k);
         }
         if (place) {
             hipLaunchKernelGGL(k_encode_place<K>, dim3(total_blocks_c), dim3(256), 0, s, k);

@@ -103,7 +103,8 @@ def test_stats_batch_matches_single_calls():
 
 @pytest.mark.parametrize("n", [0, 1, 31, 32, 63, 64, 4095, 4096, 4097, 123457, 4194304])
 @pytest.mark.parametrize("C_,R,S", [(4096, 7, 32), (32, 1, 32), (8192, 8, 32), (16384, 7, 32),
-                                    (4096, 7, 64), (64, 1, 64), (16384, 7, 64), (65536, 11, 64)])
+                                    (4096, 7, 64), (64, 1, 64), (16384, 7, 64), (65536, 11, 64),
+                                    (128, 7, 128), (16384, 7, 128), (65536, 11, 128)])
 def test_encode_bound_matches_oracle(n, C_, R, S):
     p = codec.Params(K=16, log2_L=R, chunk_symbols=C_, streams=S)
     assert codec.sh_encode_bound(n, p) == O.container_bound(n, 16, R, C_, S)
@@ -119,9 +120,10 @@ def test_argument_checks_are_synchronous():
     assert lib.sh_encode(None, C.byref(p), fake, 100, fake, 1 << 20, fake, 1 << 20, None,
                          None, None) == codec.SH_ERR_INVALID_ARG
     # unsupported parameters
-    for bad in [codec.Params(streams=16), codec.Params(streams=128), codec.Params(log2_L=12),
+    for bad in [codec.Params(streams=16), codec.Params(streams=96), codec.Params(log2_L=12),
                 codec.Params(chunk_symbols=100), codec.Params(chunk_symbols=1 << 17),
-                codec.Params(chunk_symbols=96, streams=64), codec.Params(chunk_symbols=32, streams=64)]:
+                codec.Params(chunk_symbols=96, streams=64), codec.Params(chunk_symbols=32, streams=64),
+                codec.Params(chunk_symbols=192, streams=128), codec.Params(streams=256)]:
         pb = bad.c()
         assert lib.sh_encode(C.byref(t), C.byref(pb), fake, 100, fake, 1 << 20, fake, 1 << 20,
                              None, None, None) in (codec.SH_ERR_UNSUPPORTED, codec.SH_ERR_INVALID_ARG)

@@ -136,7 +136,7 @@ def _roundtrip_batch(torch, xs, p, whole=None):
 
 @pytest.mark.parametrize("C_,S,n_max", [(4096, 32, 0), (32, 32, 0), (96, 32, 0), (16384, 32, 0),
                                         (4096, 64, 0), (64, 64, 0), (192, 64, 0), (16384, 64, 0),
-                                        (64, 64, 50000)])
+                                        (64, 64, 50000), (4096, 128, 0), (128, 128, 0)])
 def test_batch_mixed_tensors(torch_cuda, C_, S, n_max):
     """More tensors than one launch carries (48), ragged sizes and degenerate tensors.  With
     n_max = 50000 at C = 64 the first launch holds more than 16,384 chunks and the second

@@ -78,7 +78,7 @@ def test_weight_workload(torch_cuda):
     _case(torch_cuda, D.weight())
 
 
-@pytest.mark.parametrize("S", [32, 64])
+@pytest.mark.parametrize("S", [32, 64, 128])
 @pytest.mark.parametrize("n", [1, 2, 31, 32, 33, 63, 64, 65, 127, 129, 4095, 4096, 4097, 8191,
                                12345])
 def test_ragged_sizes(torch_cuda, n, S):
@@ -90,7 +90,8 @@ def test_ragged_sizes(torch_cuda, n, S):
 @pytest.mark.parametrize("n,C_,S", [(16383 * 64, 64, 32), (16384 * 64, 64, 32),
                                     (16384 * 64 + 64, 64, 32), (20000 * 32 + 5, 32, 32),
                                     (16384 * 64, 64, 64), (16384 * 64 + 64, 64, 64),
-                                    (20000 * 64 + 5, 64, 64)])
+                                    (20000 * 64 + 5, 64, 64), (16384 * 128 + 128, 128, 128),
+                                    (1000 * 128 + 77, 128, 128)])
 def test_chunk_counts_around_the_one_kernel_placement(torch_cuda, n, C_, S):
     """Up to 16384 chunks a tensor the encoder indexes and compacts in one kernel, beyond it
     the index comes first from its own kernel: both give the oracle's container.  The decode
@@ -111,7 +112,11 @@ def test_chunk_counts_around_the_one_kernel_placement(torch_cuda, n, C_, S):
                                            (16, 8, 4096, 64), (64, 8, 1024, 64),
                                            (256, 8, 4096, 64), (16, 5, 8192, 64),
                                            (16, 7, 65536, 64), (8, 4, 192, 64),
-                                           (16, 7, 16384, 64)])
+                                           (16, 7, 16384, 64),
+                                           (1, 7, 4096, 128), (2, 1, 128, 128),
+                                           (3, 2, 256, 128), (16, 8, 4096, 128),
+                                           (256, 8, 4096, 128), (16, 7, 65536, 128),
+                                           (8, 4, 384, 128), (16, 7, 16384, 128)])
 def test_parameter_grid(torch_cuda, K, log2_L, C_, S):
     print(f"case: grid K={K} R={log2_L} C={C_} S={S}", flush=True)
     rng = np.random.default_rng(K * 1000 + log2_L * 10 + C_)
@@ -124,7 +129,7 @@ def test_parameter_grid(torch_cuda, K, log2_L, C_, S):
     _case(torch_cuda, x, K, log2_L, C_, S)
 
 
-@pytest.mark.parametrize("S", [32, 64])
+@pytest.mark.parametrize("S", [32, 64, 128])
 def test_all_zero_and_uniform(torch_cuda, S):
     print(f"case: all-zero and exactly uniform S={S}", flush=True)
     ref = _case(torch_cuda, np.zeros(70001, dtype=np.int8), S=S)
@@ -158,7 +163,7 @@ def test_symbol_outside_table(torch_cuda):
     assert int(status.item()) == codec.SH_ERR_SYMBOL_NOT_IN_TABLE
 
 
-@pytest.mark.parametrize("S", [32, 64])
+@pytest.mark.parametrize("S", [32, 64, 128])
 def test_corruption_matches_oracle(torch_cuda, S):
     """Damaged containers: the GPU reports exactly what the oracle reports."""
     torch = torch_cuda

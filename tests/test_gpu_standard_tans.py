@@ -55,7 +55,7 @@ def _roundtrip_device_tables(torch, xs, p, host_tables):
         assert np.array_equal(y[starts[i]:starts[i] + x.size].cpu().numpy(), x)
 
 
-@pytest.mark.parametrize("log2_L,S", [(9, 32), (10, 32), (11, 32), (11, 64)])
+@pytest.mark.parametrize("log2_L,S", [(9, 32), (10, 32), (11, 32), (11, 64), (11, 128)])
 @pytest.mark.parametrize("host_tables", [False, True])
 def test_standard_tans_at_512_to_2048_states(torch_cuda, log2_L, S, host_tables):
     print(f"case: K=256 L={1 << log2_L} S={S} host_tables={host_tables}", flush=True)
@@ -66,7 +66,8 @@ def test_standard_tans_at_512_to_2048_states(torch_cuda, log2_L, S, host_tables)
 
 
 @pytest.mark.parametrize("K,log2_L,C,S", [(16, 7, 34944, 32), (256, 11, 65536, 32),
-                                          (16, 7, 34944, 64), (256, 11, 65536, 64)])
+                                          (16, 7, 34944, 64), (256, 11, 65536, 64),
+                                          (256, 11, 65536, 128)])
 def test_chunk_sizes_in_two_and_four_byte_units(torch_cuda, K, log2_L, C, S):
     """Chunks whose largest valid size passes 65,535 bytes count their sizes in 2- and
     4-byte units: encoder placement and decoder chunk search against the oracle."""
