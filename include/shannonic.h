@@ -76,7 +76,7 @@ typedef int32_t sh_status;
 /* Codec parameters.  The GPU path supports 1 <= K <= 256, 1 <= log2_L <= 11 (tables with
  * fields of at most 16 bits, the widest range's offset bits plus log2_L; sh_encode and
  * sh_decode, which carry the table in their launch arguments, take log2_L <= 8),
- * streams 32 or 64, and chunk_symbols a multiple of streams in [streams, 65536].  More
+ * streams 32, 64 or 128, and chunk_symbols a multiple of streams in [streams, 65536].  More
  * streams give a launch with few chunks more independent state machines at a framing cost
  * of about log2_L bits a stream and chunk; the fused matrix-vector decode takes 32.
  * The pages' configuration is K = 16, log2_L = 7 (530 B of codec state,
