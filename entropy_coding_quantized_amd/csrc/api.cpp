@@ -23,10 +23,12 @@ namespace {
 constexpr uint32_t kChunksPerBlock = 8;   // the half-wavefront decode kernels
 // A decode launch of fewer chunks than this cannot fill the GPU with the row decoder's 4
 // chunks a wavefront (the chunks' steps are serial, so the launch takes the steps of one
-// chunk times the step's latency); below it the half-wavefront decoder, with twice the
-// wavefronts, is used (measured on MI355X: 1,024 chunks 20.4 against 26.2 us, 8,192 chunks
-// 93.8 against 95.5 us; a 48-tensor model launch of 91,000 chunks 0.37 against 0.50 of
-// 8 TB/s the other way)
+// chunk times the step's latency); below it chunks go one per half wavefront, twice the
+// wavefronts: for chunks of 32 streams the half-wavefront decoder (measured on MI355X: 1,024
+// chunks 20.4 against 26.2 us, 8,192 chunks 93.8 against 95.5 us; a 48-tensor model launch
+// of 91,000 chunks 0.37 against 0.50 of 8 TB/s the other way), for chunks of 64 the row
+// decoder's 32-lane rows (8,192 chunks: 76 against 81.6 us).  Chunks of 128 streams always
+// take 32-lane rows (four streams a lane).
 constexpr uint64_t kHalfDecodeMaxChunks = 16384;
 
 // the decode of a launch group of total_chunks chunks: blocks per chunk count and launcher
