@@ -53,9 +53,10 @@ def _both(torch, x, p):
     return a
 
 
-def test_noalloc_matches_sh_encode_twice_the_second_smaller(torch_cuda):
-    p = codec.Params(K=16, log2_L=7, chunk_symbols=4096, streams=32)
-    print("case: no-alloc encode, weight 4096x1024 then tiny 65536", flush=True)
+@pytest.mark.parametrize("S", [32, 64, 128])
+def test_noalloc_matches_sh_encode_twice_the_second_smaller(torch_cuda, S):
+    p = codec.Params(K=16, log2_L=7, chunk_symbols=4096, streams=S)
+    print(f"case: no-alloc encode S={S}, weight 4096x1024 then tiny 65536", flush=True)
     big = _both(torch_cuda, D.weight(), p)
     small = _both(torch_cuda, D.tiny(), p)
     assert small.size < big.size
