@@ -137,26 +137,47 @@ __device__ __forceinline__ uint32_t maxo_of(const Ent& e) { return e.A >> 24; }
 __device__ __forceinline__ uint32_t next_of(const Ent& e) { return e.B >> 16; }
 
 // The fields of a lane's P streams from the bits at its first field's position: w[0..kWin)
-// are the ring dwords from that position's dword on, and n[i] holds field i's length in its
-// bits 0..4 (fields are at most 16 bits, a lane's P fields at most 16 P bits).
+// are the ring dwords from that position's dword on, n[i] holds field i's length in its bits
+// 0..4 and n01 is the first two lengths' sum (fields are at most 16 bits, so two fit the low
+// word whole, and a lane's P fields take at most 16 P bits).
 template <int P>
 __device__ __forceinline__ void split_fields(const uint32_t* w, uint32_t start, const uint32_t* n,
-                                             uint32_t* f) {
+                                             uint32_t* f, uint32_t n01) {
     const uint32_t lo = __builtin_amdgcn_alignbit(w[1], w[0], start);
     f[0] = __builtin_amdgcn_ubfe(lo, 0, n[0]);
-    if constexpr (P == 2) {
-        f[1] = __builtin_amdgcn_ubfe(lo, n[0], n[1]);
-    } else {
-        // 64 bits from the position (hi:lo); t1 = its 32 bits from field 1 on, t2 from field
-        // 2 on (the high word shifted along, so that fields 2 and 3 are whole in t2)
+    f[1] = __builtin_amdgcn_ubfe(lo, n[0], n[1]);
+    if constexpr (P == 4) {
+        // fields 2 and 3 from the 64 bits at the position (hi:lo) shifted past the first two
+        // (one 64-bit shift: n01 may be 32)
         const uint32_t hi = __builtin_amdgcn_alignbit(w[2], w[1], start);
-        const uint32_t t1 = __builtin_amdgcn_alignbit(hi, lo, n[0]);
-        const uint32_t h1 = hi >> (n[0] & 31);
-        const uint32_t t2 = __builtin_amdgcn_alignbit(h1, t1, n[1]);
-        f[1] = __builtin_amdgcn_ubfe(t1, 0, n[1]);
+        const uint32_t t2 = (uint32_t)((((uint64_t)hi << 32) | lo) >> n01);
         f[2] = __builtin_amdgcn_ubfe(t2, 0, n[2]);
         f[3] = __builtin_amdgcn_ubfe(t2, n[2], n[3]);
     }
+}
+
+// A decoded value's byte, the low byte of o + (A >> 16) (the range's first value in bits
+// 16..23 of the entry word A), added straight into byte B of a packed dword: one VOP2 add
+// with a byte destination.  byte0 zeroes the other bytes, put_byte keeps them.
+__device__ __forceinline__ uint32_t byte0(uint32_t o, uint32_t A) {
+    uint32_t x;
+    asm("v_add_u32_sdwa %0, %1, %2 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_1"
+        : "=v"(x) : "v"(o), "v"(A));
+    return x;
+}
+template <int B>
+__device__ __forceinline__ uint32_t put_byte(uint32_t x, uint32_t o, uint32_t A) {
+    static_assert(B >= 1 && B <= 3, "bytes 1..3");
+    if constexpr (B == 1)
+        asm("v_add_u32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:WORD_1"
+            : "+v"(x) : "v"(o), "v"(A));
+    else if constexpr (B == 2)
+        asm("v_add_u32_sdwa %0, %1, %2 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:WORD_1"
+            : "+v"(x) : "v"(o), "v"(A));
+    else
+        asm("v_add_u32_sdwa %0, %1, %2 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:WORD_1"
+            : "+v"(x) : "v"(o), "v"(A));
+    return x;
 }
 
 // One chunk row's decoder state (every lane of the row holds the same values, except the
@@ -356,19 +377,19 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
     // extract -> next entry read.  k is the step's place in the tile (a constant in the
     // unrolled loop, so the tile writes take their offset from the instruction).
     auto full_step = [&](const Ent* e, Ent* ne, uint32_t k) {
-        uint32_t tot = 0, nd[P], w[G::kWin], f[P], x[P];
+        uint32_t tot, nd[P], w[G::kWin], f[P], x[P], packed = 0;
+        const uint32_t n01 = need_of(e[0]) + need_of(e[1]);
+        if constexpr (P == 2) tot = n01;
+        else tot = n01 + ((e[2].A + e[3].A) & 0xFFu);  // two needs of at most 16: no carry out
 #pragma unroll
-        for (int i = 0; i < P; ++i) {
-            tot += need_of(e[i]);
-            nd[i] = e[i].A;  // bits 0..4: the need
-        }
+        for (int i = 0; i < P; ++i) nd[i] = e[i].A;  // bits 0..4: the need
         const uint32_t posm = r.pos - tot;
         const uint32_t incl = scan_row<W>(tot);
         const uint32_t start = posm + incl;
         const lds_u32* rp = (const lds_u32*)(uintptr_t)((ring_dword<G::kRingLog2>(start) << 2) + r.ring_byte);
 #pragma unroll
         for (uint32_t i = 0; i < G::kWin; ++i) w[i] = rp[i];
-        split_fields<P>(w, start, nd, f);
+        split_fields<P>(w, start, nd, f, n01);
         typedef volatile __attribute__((address_space(3))) uint8_t lds_w1b;
 #pragma unroll
         for (int i = 0; i < P; ++i) {
@@ -376,19 +397,27 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
             r.s[i] = ((f[i] >> (e[i].B & 31)) << 3) + next_of(e[i]);
             ne[i] = read_ent(r.s[i]);
             bad_offsets |= __builtin_amdgcn_ballot_w64(o > maxo_of(e[i]));
-            x[i] = o + base_of(e[i]);  // the value's int8 bits in bits 0..7
+            if constexpr (P == 2) {
+                x[i] = o + base_of(e[i]);  // the value's int8 bits in bits 0..7
+            } else if (i == 0) {
+                packed = byte0(o, e[i].A);
+            } else if (i == 1) {
+                packed = put_byte<1>(packed, o, e[i].A);
+            } else if (i == 2) {
+                packed = put_byte<2>(packed, o, e[i].A);
+            } else {
+                packed = put_byte<3>(packed, o, e[i].A);
+            }
         }
         // the lane's bytes into the tile.  Two: two byte writes (volatile, so that they stay
-        // single bytes); four: packed into one dword (two bytes packed into one 16-bit write
-        // were measured slower than two byte writes, four bytes in one dword faster than four)
+        // single bytes); four: one dword (two bytes packed into one 16-bit write were
+        // measured slower than two byte writes, four bytes in one dword faster than four)
         if constexpr (P == 2) {
             *(lds_w1b*)(uintptr_t)(r.tile + kS * k) = (uint8_t)x[0];
             *(lds_w1b*)(uintptr_t)(r.tile + kS * k + 1) = (uint8_t)x[1];
         } else {
             typedef __attribute__((address_space(3))) uint32_t lds_w4b;
-            const uint32_t x01 = __builtin_amdgcn_perm(x[1], x[0], 0x0c0c0400u);  // x0, x1, 0, 0
-            const uint32_t x23 = __builtin_amdgcn_perm(x[3], x[2], 0x0c0c0400u);  // x2, x3, 0, 0
-            *(lds_w4b*)(uintptr_t)(r.tile + kS * k) = __builtin_amdgcn_perm(x23, x01, 0x05040100u);
+            *(lds_w4b*)(uintptr_t)(r.tile + kS * k) = packed;
         }
         r.pos += row_last<W>(incl);
     };
@@ -446,7 +475,7 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
         const lds_u32* rp = (const lds_u32*)(uintptr_t)((ring_dword<G::kRingLog2>(start) << 2) + r.ring_byte);
 #pragma unroll
         for (uint32_t i = 0; i < G::kWin; ++i) w[i] = rp[i];
-        split_fields<P>(w, start, nd, f);
+        split_fields<P>(w, start, nd, f, nd[0] + nd[1]);
 #pragma unroll
         for (int i = 0; i < P; ++i) {
             const uint32_t o = __builtin_amdgcn_ubfe(f[i], 0, act[i] ? ea[i].B : 0u);
