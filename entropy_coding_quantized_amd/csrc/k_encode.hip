@@ -108,6 +108,23 @@ __device__ __forceinline__ uint32_t erow_last(uint32_t v) {
     return b;
 }
 
+// Byte B of v times 8 (the LDS byte offset of value entry number byte B of v): one VOP2
+// shift reading a byte of its operand, where the compiler would extract and scale in two.
+template <int B>
+__device__ __forceinline__ uint32_t byte_x8(uint32_t v) {
+    static_assert(B >= 0 && B <= 3, "bytes 0..3");
+    uint32_t r;
+    if constexpr (B == 0)
+        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(v));
+    else if constexpr (B == 1)
+        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(v));
+    else if constexpr (B == 2)
+        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(v));
+    else
+        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(v));
+    return r;
+}
+
 // An encode entry in LDS, two dwords:
 //   B = bias_s & 0xFFFFFF | w_s << 24: the state-bit count is bits R+1.. of X + B (the
 //       bias's sign bits above bit 23 do not reach them)
@@ -247,8 +264,9 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
     };
     // the entry of byte i of vals (the table sits on a 2 KB boundary)
     auto entry_of = [&](VT vals, int i) {
-        const uint32_t off = i == 0 ? ((uint32_t)vals << 3) & 0x7F8u
-                                    : (uint32_t)(vals >> (8 * i - 3)) & 0x7F8u;
+        const uint32_t word = i < 4 ? (uint32_t)vals : (uint32_t)((uint64_t)vals >> 32);
+        const uint32_t off = (i & 3) == 0 ? byte_x8<0>(word) : (i & 3) == 1 ? byte_x8<1>(word)
+                           : (i & 3) == 2 ? byte_x8<2>(word) : byte_x8<3>(word);
         const v2u_e v = *(const __attribute__((address_space(3))) v2u_e*)(uintptr_t)(off | vt_byte);
         return EEnt{v[0], v[1]};
     };
