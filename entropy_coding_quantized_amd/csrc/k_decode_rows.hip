@@ -423,9 +423,9 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
     };
     // the tile of steps [t0, t0 + kTileSteps) to the output: lane j stores its share of
     // the row's kS * kTileSteps bytes (LDS operations of a wavefront complete in order, so
-    // the row's writes are visible)
+    // the row's writes are visible); a lane's share lies within one step
+    constexpr uint32_t kLaneBytes = P * kTileSteps;
     auto flush_tile = [&](uint32_t t0) {
-        constexpr uint32_t kLaneBytes = P * kTileSteps;
         const uint32_t at = row * a.h.C + kLaneBytes * j;
         if constexpr (kLaneBytes == 16) {
             const v4u w = *(const __attribute__((address_space(3))) v4u*)(uintptr_t)(tile_base + 16 * j);
@@ -435,6 +435,7 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
             __builtin_amdgcn_raw_buffer_store_b64(w, rout, (int)at, (int)(t0 * kS), 0);
         }
     };
+    static_assert(kS % kLaneBytes == 0, "a lane's share of a tile lies within one step");
 
     Ent ea[P], eb[P];
 #pragma unroll
@@ -457,6 +458,38 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
         }
     }
     __builtin_amdgcn_s_setprio(0);
+    // the full steps after the last whole tile (fewer than kTileSteps, the same for the
+    // wavefront's rows), then their part of a tile: only the steps that hold a stream's last
+    // value go through the general step
+    static_assert(kTileSteps == 4, "up to three full steps after the last whole tile");
+    if (t < full) {
+        const uint32_t left = full - t;
+        full_step(ea, eb, 0);
+        if (left > 1) {
+            full_step(eb, ea, 1);
+            refill();
+            if (left > 2) {
+                full_step(ea, eb, 2);
+#pragma unroll
+                for (int i = 0; i < P; ++i) ea[i] = eb[i];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < P; ++i) ea[i] = eb[i];
+        }
+        refill();
+        if (kLaneBytes * j < left * kS) {
+            const uint32_t at = row * a.h.C + kLaneBytes * j;
+            if constexpr (kLaneBytes == 16) {
+                const v4u w = *(const __attribute__((address_space(3))) v4u*)(uintptr_t)(tile_base + 16 * j);
+                __builtin_amdgcn_raw_buffer_store_b128(w, rout, (int)at, (int)(t * kS), 0);
+            } else {
+                const v2u w = *(lds_v2u*)(uintptr_t)(tile_base + 8 * j);
+                __builtin_amdgcn_raw_buffer_store_b64(w, rout, (int)at, (int)(t * kS), 0);
+            }
+        }
+        t = full;
+    }
     // the general step: a stream past its chunk's end has no field, and a stream at its
     // last value has the offset alone (its state bits are zero and implied)
     for (; t < steps; ++t) {
