@@ -377,29 +377,32 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
     // extract -> next entry read.  k is the step's place in the tile (a constant in the
     // unrolled loop, so the tile writes take their offset from the instruction).
     auto full_step = [&](const Ent* e, Ent* ne, uint32_t k) {
-        uint32_t tot, nd[P], w[G::kWin], f[P], x[P], packed = 0;
+        uint32_t tot, nd[P], w[G::kWin], f[P], packed = 0;
         const uint32_t n01 = need_of(e[0]) + need_of(e[1]);
         if constexpr (P == 2) tot = n01;
         else tot = n01 + ((e[2].A + e[3].A) & 0xFFu);  // two needs of at most 16: no carry out
 #pragma unroll
         for (int i = 0; i < P; ++i) nd[i] = e[i].A;  // bits 0..4: the need
-        const uint32_t posm = r.pos - tot;
         const uint32_t incl = scan_row<W>(tot);
-        const uint32_t start = posm + incl;
+        // the lane's first bit: in a 16-lane row the previous lane's inclusive sum (a DPP
+        // row shift, zero for lane 0) added to the row's position in one operation; a
+        // 32-lane row's shift would not cross from lane 15 to lane 16
+        uint32_t start;
+        if constexpr (W == 16)
+            start = r.pos + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x111, 0xF, 0xF, true);
+        else
+            start = r.pos - tot + incl;
         const lds_u32* rp = (const lds_u32*)(uintptr_t)((ring_dword<G::kRingLog2>(start) << 2) + r.ring_byte);
 #pragma unroll
         for (uint32_t i = 0; i < G::kWin; ++i) w[i] = rp[i];
         split_fields<P>(w, start, nd, f, n01);
-        typedef volatile __attribute__((address_space(3))) uint8_t lds_w1b;
 #pragma unroll
         for (int i = 0; i < P; ++i) {
             const uint32_t o = __builtin_amdgcn_ubfe(f[i], 0, e[i].B);
             r.s[i] = ((f[i] >> (e[i].B & 31)) << 3) + next_of(e[i]);
             ne[i] = read_ent(r.s[i]);
             bad_offsets |= __builtin_amdgcn_ballot_w64(o > maxo_of(e[i]));
-            if constexpr (P == 2) {
-                x[i] = o + base_of(e[i]);  // the value's int8 bits in bits 0..7
-            } else if (i == 0) {
+            if (i == 0) {
                 packed = byte0(o, e[i].A);
             } else if (i == 1) {
                 packed = put_byte<1>(packed, o, e[i].A);
@@ -409,12 +412,11 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
                 packed = put_byte<3>(packed, o, e[i].A);
             }
         }
-        // the lane's bytes into the tile.  Two: two byte writes (volatile, so that they stay
-        // single bytes); four: one dword (two bytes packed into one 16-bit write were
-        // measured slower than two byte writes, four bytes in one dword faster than four)
+        // the lane's bytes into the tile, packed by the byte-destination adds above: one
+        // 16-bit write for two, one dword for four
         if constexpr (P == 2) {
-            *(lds_w1b*)(uintptr_t)(r.tile + kS * k) = (uint8_t)x[0];
-            *(lds_w1b*)(uintptr_t)(r.tile + kS * k + 1) = (uint8_t)x[1];
+            typedef __attribute__((address_space(3))) uint16_t lds_w2b;
+            *(lds_w2b*)(uintptr_t)(r.tile + kS * k) = (uint16_t)packed;
         } else {
             typedef __attribute__((address_space(3))) uint32_t lds_w4b;
             *(lds_w4b*)(uintptr_t)(r.tile + kS * k) = packed;
