@@ -383,15 +383,20 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
         else tot = n01 + ((e[2].A + e[3].A) & 0xFFu);  // two needs of at most 16: no carry out
 #pragma unroll
         for (int i = 0; i < P; ++i) nd[i] = e[i].A;  // bits 0..4: the need
-        const uint32_t incl = scan_row<W>(tot);
-        // the lane's first bit: in a 16-lane row the previous lane's inclusive sum (a DPP
-        // row shift, zero for lane 0) added to the row's position in one operation; a
-        // 32-lane row's shift would not cross from lane 15 to lane 16
-        uint32_t start;
+        // the lane's first bit: the row's position plus the previous lane's inclusive sum
+        // within its 16 lanes (one DPP add with a row shift, which reads zero for lane 0);
+        // in a 32-lane row the upper 16 lanes then add lane 15's sum (row_bcast:15, rows 1
+        // and 3 only).  The two adds are written out because the compiler makes four
+        // operations of the masked broadcast; the s_nop gives the DPP source, written by
+        // the scan just before, its two wait states.
+        const uint32_t incl = scan16(tot);
+        uint32_t start = r.pos;
         if constexpr (W == 16)
-            start = r.pos + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x111, 0xF, 0xF, true);
+            start += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x111, 0xF, 0xF, true);
         else
-            start = r.pos - tot + incl;
+            asm("s_nop 1\n\tv_add_u32_dpp %0, %1, %0 row_shr:1 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+                "v_add_u32_dpp %0, %1, %0 row_bcast:15 row_mask:0xa bank_mask:0xf"
+                : "+v"(start) : "v"(incl));
         const lds_u32* rp = (const lds_u32*)(uintptr_t)((ring_dword<G::kRingLog2>(start) << 2) + r.ring_byte);
 #pragma unroll
         for (uint32_t i = 0; i < G::kWin; ++i) w[i] = rp[i];
@@ -421,7 +426,9 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
             typedef __attribute__((address_space(3))) uint32_t lds_w4b;
             *(lds_w4b*)(uintptr_t)(r.tile + kS * k) = packed;
         }
-        r.pos += row_last<W>(incl);
+        // the next step's position: the end of the row's last lane
+        if constexpr (W == 16) r.pos += row_last<W>(incl);
+        else r.pos = bcast31(start + tot);
     };
     // the tile of steps [t0, t0 + kTileSteps) to the output: lane j stores its share of
     // the row's kS * kTileSteps bytes (LDS operations of a wavefront complete in order, so
