@@ -25,7 +25,7 @@ static_assert(kEncodeChunksPerBlock == kEncRowsBlock / 16, "one chunk per 16-lan
 constexpr uint32_t kEFlush = 64;                   // dwords per flush
 // LDS (dynamic; the kernel's only LDS, so it starts at LDS byte 0): the value entries (two
 // dwords per value, at a 2 KB boundary so that an entry's address is one AND-OR), the
-// rings (one per chunk, aligned to their size), the encTable (a dword per slot, holding the
+// rings (one per chunk, each followed by its spill dword), the encTable (a dword per slot, holding the
 // next state L + slot), the input tiles (u = x + 128 of kTileSteps steps of a chunk), then
 // the block's two totals
 constexpr uint32_t kEVtByte = 0;
@@ -39,8 +39,11 @@ struct EncGeom {
     // a step places at most kS fields of 16 bits, kS / 2 dwords; so the unflushed dwords span
     // at most 64 + kS dwords: 128 dwords (the ring exactly at P = 4; the mark's own dword,
     // the lowest one's twin in the ring, is flushed and zero), 256 at P = 8.
-    static constexpr uint32_t kRing = P == 8 ? 256 : 128;
+    static constexpr uint32_t kRingLog2 = P == 8 ? 8 : 7;
+    static constexpr uint32_t kRing = 1u << kRingLog2;
     static_assert(kEFlush + kS <= kRing, "two steps fit in the ring");
+    // a ring's LDS: its kRing dwords, the spill dword (ring_or2), padding to 16 bytes
+    static constexpr uint32_t kRingStride = kRing + 4;
     static constexpr uint32_t kTileSteps = P == 8 ? 8 : 16;  // input steps staged at a time
     static constexpr uint32_t kTileBytes = kTileSteps * kS;
     static constexpr uint32_t kLaneStage = kTileBytes / 16;  // bytes a lane stages
@@ -52,7 +55,7 @@ struct EncGeom {
     // dword (d + 4 P row) mod kRing holds slot dword d): the rows use different LDS banks.
     static constexpr uint32_t kTileStride = kTileBytes + 16 * P;
     static constexpr uint32_t kRowTurn = 4 * P;             // ring dwords per row of the wavefront
-    static constexpr uint32_t kEsByte = kERingsByte + kEncodeChunksPerBlock * kRing * 4;
+    static constexpr uint32_t kEsByte = kERingsByte + kEncodeChunksPerBlock * kRingStride * 4;
     static_assert(kEsByte >= 4 * kMaxLGpu && kEsByte + 4 * kMaxLGpu < 32768,
                   "encTable addresses stay positive and below bit 15 of an entry");
     __host__ __device__ static constexpr uint32_t tiles_byte(uint32_t L) {
@@ -73,20 +76,24 @@ typedef const __attribute__((address_space(3))) uint16_t lds_r16;
 typedef const __attribute__((address_space(3))) uint32_t lds_r32;
 typedef unsigned int v2u_e __attribute__((ext_vector_type(2)));
 
-// OR a pair of fields (at most 32 bits) into a ring of kRing dwords at bit pos; ring_byte is
-// the ring's LDS byte address, a multiple of its size.  The second dword is OR-ed only by
-// the lanes whose pair reaches into it: the pairs of a step share a few dwords, and
-// same-address LDS atomics serialise.
-template <uint32_t kRing>
+// OR a pair of fields (at most 32 bits) into a ring of 2^kRingLog2 dwords at bit pos;
+// ring_byte is the ring's LDS byte address.  A pair that reaches past the ring's last dword
+// goes on into the spill dword after it, which holds bits of ring dword 0 until that dword is
+// flushed (flush_block folds it in), so the second dword is always the first one's address
+// plus 4, an instruction offset.  The second dword is OR-ed only by the lanes whose pair
+// reaches into it: the pairs of a step share a few dwords, and same-address LDS atomics
+// serialise.  The address is one v_bfe_u32 and one v_lshl_add_u32 (the compiler would
+// split the extract, the scaling and the add into more operations).
+template <uint32_t kRingLog2>
 __device__ __forceinline__ void ring_or2(uint32_t ring_byte, uint32_t pos, uint32_t field) {
     const uint64_t wide = (uint64_t)field << (pos & 31);
-    const uint32_t b = pos >> 3;
-    const uint32_t a0 = (b & (4 * kRing - 4)) | ring_byte;
-    const uint32_t a1 = ((b + 4) & (4 * kRing - 4)) | ring_byte;
-    __hip_atomic_fetch_or((lds_w32*)(uintptr_t)a0, (uint32_t)wide, __ATOMIC_RELAXED,
-                          __HIP_MEMORY_SCOPE_WORKGROUP);
+    uint32_t a;
+    asm("v_bfe_u32 %0, %1, 5, %2\n\tv_lshl_add_u32 %0, %0, 2, %3"
+        : "=&v"(a) : "v"(pos), "i"(kRingLog2), "v"(ring_byte));
+    lds_w32* a0 = (lds_w32*)(uintptr_t)a;
+    __hip_atomic_fetch_or(a0, (uint32_t)wide, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     if ((uint32_t)(wide >> 32))
-        __hip_atomic_fetch_or((lds_w32*)(uintptr_t)a1, (uint32_t)(wide >> 32), __ATOMIC_RELAXED,
+        __hip_atomic_fetch_or(a0 + 1, (uint32_t)(wide >> 32), __ATOMIC_RELAXED,
                               __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
@@ -140,8 +147,8 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
     constexpr uint32_t kS = G::kS, kERing = G::kRing, kETileSteps = G::kTileSteps;
     constexpr uint32_t kEEsByte = G::kEsByte;
     using VT = std::conditional_t<P == 8, uint64_t, uint32_t>;  // a lane's P values, a byte each
-    // the entry and ring addresses below are formed with AND-OR, so the LDS block must
-    // start on a 2 KB boundary (it is the kernel's only LDS, at byte 0)
+    // the entry addresses below are formed with AND-OR, so the LDS block must start on a
+    // 2 KB boundary (it is the kernel's only LDS, at byte 0)
     extern __shared__ __align__(2048) uint32_t esm[];
     const uint32_t tid = threadIdx.x, lane = tid & 63, j = lane & 15, row = lane >> 4;
     const uint32_t block = __builtin_amdgcn_readfirstlane(blockIdx.x);
@@ -153,7 +160,7 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
     const uint64_t n = sg->n;
     const uint32_t L = a.h.L, R = a.h.R, R1 = a.h.R + 1;
     const uint32_t base = lds_offset(esm);  // 0: the only LDS of the kernel
-    const uint32_t ring_byte = base + kERingsByte + 4 * kERing * rowi;
+    const uint32_t ring_byte = base + kERingsByte + 4 * G::kRingStride * rowi;
     const uint32_t tile_byte = base + G::tiles_byte(L) + G::kTileStride * rowi;
     const uint32_t vt_byte = base + kEVtByte, es_byte = base + kEEsByte;
     uint32_t* agg_s = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(esm) + G::tiles_byte(L) +
@@ -171,7 +178,7 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
         esm[kEVtByte / 4 + 2 * tid + 1] = (v1 & 0xFFu) | (start4 << 16) | ((v1 & 0x8000u) << 16);
     }
     for (uint32_t i = tid; i < L; i += kEncRowsBlock) esm[kEEsByte / 4 + i] = L + es_src[i];
-    for (uint32_t i = j; i < kERing; i += 16) esm[kERingsByte / 4 + kERing * rowi + i] = 0;
+    for (uint32_t i = j; i < G::kRingStride; i += 16) esm[kERingsByte / 4 + G::kRingStride * rowi + i] = 0;
     if (tid < 2) agg_s[tid] = 0;
 
     // the wavefront's four chunks, one per row
@@ -244,9 +251,15 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
 
     auto flush_block = [&](uint32_t blk) {  // ring dwords [blk, blk + 64) -> slot
         typedef __attribute__((address_space(3))) v4u lds_v4;
-        lds_v4* r = (lds_v4*)(uintptr_t)(ring_byte + 4 * ((blk + G::kRowTurn * row + 4 * j) & (kERing - 1)));
-        const v4u v = *r;
+        const uint32_t idx = (blk + G::kRowTurn * row + 4 * j) & (kERing - 1);
+        lds_v4* r = (lds_v4*)(uintptr_t)(ring_byte + 4 * idx);
+        v4u v = *r;
         *r = v4u{0, 0, 0, 0};
+        if (idx == 0) {  // ring dword 0 with the bits carried into the spill dword
+            lds_w32* spill = (lds_w32*)(uintptr_t)(ring_byte + 4 * kERing);
+            v[0] |= *spill;
+            *spill = 0;
+        }
         __builtin_amdgcn_raw_buffer_store_b128(v, rslot, (int)(slot_row + 4 * (blk + 4 * j)), 0, 0);
     };
     auto stage = [&]() {  // the tile in pv into LDS, as u = x + 128
@@ -360,7 +373,7 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
         uint32_t at = fpos + incl - lp;
 #pragma unroll
         for (int k = 0; k < P / 2; ++k) {
-            ring_or2<kERing>(ring_byte, at, fp[k]);
+            ring_or2<G::kRingLog2>(ring_byte, at, fp[k]);
             at += lq[k];
         }
 #pragma unroll
@@ -407,7 +420,7 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
     for (int i = 0; i < P; i += 2) {  // two states (at most 22 bits) at a time
         const uint32_t s0 = P * j + i < lanes ? X[i] - L : 0u;
         const uint32_t s1 = P * j + i + 1 < lanes ? X[i + 1] - L : 0u;
-        ring_or2<kERing>(ring_byte, Pi + turn + (P * j + i) * R, s0 | (s1 << R));
+        ring_or2<G::kRingLog2>(ring_byte, Pi + turn + (P * j + i) * R, s0 | (s1 << R));
     }
     while (fmark > (Pi >> 5)) {
         fmark -= kEFlush;
