@@ -36,6 +36,7 @@ constexpr int kRowsBlock = 256;                    // 4 wavefronts, 256 / W rows
 // neighbour exchange all decode the model workload within 5% of each other; the simplest
 // is kept.)
 constexpr uint32_t kTileSteps = 4;
+static_assert(kPrioSteps % kTileSteps == 0, "a turn covers whole tiles");
 
 // Geometry of a row of W lanes that run P streams each.
 template <int W, int P>
