@@ -141,6 +141,18 @@ struct EEnt {
     uint32_t B, A;
 };
 
+// A value's field, o | s << w (s: the state bits, o: the offset), in two VOP2 operations
+// that read w from byte 3 of B and o from byte 0 of A (the compiler would extract both
+// first).
+__device__ __forceinline__ uint32_t field_of(uint32_t s, const EEnt& en) {
+    uint32_t t, f;
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3 src1_sel:DWORD"
+        : "=v"(t) : "v"(en.B), "v"(s));
+    asm("v_or_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0"
+        : "=v"(f) : "v"(t), "v"(en.A));
+    return f;
+}
+
 template <class A, int P>
 __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
     using G = EncGeom<P>;
@@ -323,9 +335,8 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
         const uint32_t k = __builtin_amdgcn_ubfe(x + en.B, R1, 5);
         const uint32_t addr = ((x >> k) << 2) + __builtin_amdgcn_ubfe(en.A, 16, 15);
         xn = *(lds_r32*)(uintptr_t)addr;
-        const uint32_t w = en.B >> 24;
-        field = (__builtin_amdgcn_ubfe(x, 0, k) << w) | (en.A & 0xFFu);
-        len = w + k;
+        field = field_of(__builtin_amdgcn_ubfe(x, 0, k), en);
+        len = (en.B >> 24) + k;
     };
     // may_stage: false for a step whose t is known even (t - 2 is then never a tile's first
     // step in backward order, and for t = 0 the value read is a harmless, unused one)
@@ -370,7 +381,9 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
         }
         const uint32_t incl = escan16(lp);
         fpos -= erow_last(incl);
-        uint32_t at = fpos + incl - lp;
+        // the lane's position: the previous lane's inclusive sum above fpos (a DPP row shift,
+        // zero for lane 0, in the add)
+        uint32_t at = fpos + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x111, 0xF, 0xF, true);
 #pragma unroll
         for (int k = 0; k < P / 2; ++k) {
             ring_or2<G::kRingLog2>(ring_byte, at, fp[k]);
