@@ -211,6 +211,23 @@ def test_corruption_matches_oracle(torch_cuda, S):
     assert agree > 30
 
 
+@pytest.mark.parametrize("S_enc,S_dec", [(32, 64), (64, 32), (64, 128), (128, 32)])
+def test_other_stream_count_than_the_container_is_reported(torch_cuda, S_enc, S_dec):
+    """A container decoded with another stream count than the one it was written with: the
+    header names the count, so the decode reports a corrupt stream (every read and write of
+    the mismatched launch stays inside its buffers); with the right count it decodes."""
+    torch = torch_cuda
+    print(f"case: streams {S_enc} decoded as {S_dec}", flush=True)
+    x = D.tiny(n=36000)
+    t, lo, f = _table(x, 16, 7)
+    ref, _ = O.encode(x, lo, f, 7, 4096, S_enc)
+    cd = torch.from_numpy(ref).cuda()
+    y, st = _gpu_decode(torch, cd, x.size, t, codec.Params(streams=S_dec))
+    assert st == codec.SH_ERR_CORRUPT_STREAM
+    y, st = _gpu_decode(torch, cd, x.size, t, codec.Params(streams=S_enc))
+    assert st == 0 and np.array_equal(y.cpu().numpy(), x)
+
+
 def _sampled_chunk_parity(torch, x, t, lo, f, cont, p, samples=64, seed=0):
     """Compare sampled chunks of a GPU container with the oracle's encoding of them."""
     C_ = p.chunk_symbols
