@@ -11,17 +11,16 @@ namespace shn {
 // ------------------------------------------------------------------------------------
 // encode, kernel 1: every chunk into a worst-case slot of the workspace
 // ------------------------------------------------------------------------------------
-// The decoder's mapping run backwards: one chunk per 16-lane DPP row, lane j of a row runs P
-// adjacent streams, P j to P j + P - 1 (P = 2 for chunks of 32 streams, 4 for chunks of 64),
-// whose fields are adjacent in every step.  tANS encodes backwards, so each stream walks its
+// The decoder's mapping run backwards: one chunk per row of W lanes (a 16-lane DPP row, or a
+// half wavefront), lane j of a row runs P adjacent streams, P j to P j + P - 1 (16 x 2 for
+// chunks of 32 streams, 16 x 4 for 64, 16 x 8 for 128; 32 x 2 for launches of few chunks of
+// 64 streams, which it gives twice the wavefronts), whose fields are adjacent in every step.  tANS encodes backwards, so each stream walks its
 // values from the last step to the first and every step's fields are placed right to left:
-// the step's fields end where the later steps' fields begin, and a 16-lane prefix sum of the
+// the step's fields end where the later steps' fields begin, and a W-lane prefix sum of the
 // lanes' field lengths gives every lane's bit position.  A lane's fields are OR-ed, a pair
 // at a time, into a 128-dword LDS ring per chunk that is flushed to the chunk's slot 64
 // dwords at a time, highest first; the chunk ends up right-aligned in its slot with the
 // streams' final states (the decoder's initial states) in front.
-constexpr int kEncRowsBlock = 256;                 // 4 wavefronts, 16 rows = 16 chunks
-static_assert(kEncodeChunksPerBlock == kEncRowsBlock / 16, "one chunk per 16-lane row");
 constexpr uint32_t kEFlush = 64;                   // dwords per flush
 // LDS (dynamic; the kernel's only LDS, so it starts at LDS byte 0): the value entries (two
 // dwords per value, at a 2 KB boundary so that an entry's address is one AND-OR), the
@@ -30,31 +29,34 @@ constexpr uint32_t kEFlush = 64;                   // dwords per flush
 // the block's two totals
 constexpr uint32_t kEVtByte = 0;
 constexpr uint32_t kERingsByte = kEVtByte + 256 * 8;                                 // 2 KB
-template <int P>
+template <int W, int P>
 struct EncGeom {
-    static_assert(P == 2 || P == 4 || P == 8, "two, four or eight streams a lane");
-    static constexpr uint32_t kS = 16 * P;                  // streams of a chunk
+    static_assert((W == 16 && (P == 2 || P == 4 || P == 8)) || (W == 32 && P == 2),
+                  "16 x 2, 16 x 4, 16 x 8, 32 x 2");
+    static constexpr uint32_t kS = W * P;                   // streams of a chunk
+    static constexpr uint32_t kRowsPerWave = 64 / W;
+    static constexpr uint32_t kBlock = kEncodeChunksPerBlock * W;  // threads: one row a chunk
     // The ring holds every dword not yet flushed.  After a flush check the fields reach no
     // lower than 64 dwords below the flush mark; checks come at least every other step, and
     // a step places at most kS fields of 16 bits, kS / 2 dwords; so the unflushed dwords span
     // at most 64 + kS dwords: 128 dwords (the ring exactly at P = 4; the mark's own dword,
     // the lowest one's twin in the ring, is flushed and zero), 256 at P = 8.
-    static constexpr uint32_t kRingLog2 = P == 8 ? 8 : 7;
+    static constexpr uint32_t kRingLog2 = kS == 128 ? 8 : 7;
     static constexpr uint32_t kRing = 1u << kRingLog2;
     static_assert(kEFlush + kS <= kRing, "two steps fit in the ring");
     // a ring's LDS: its kRing dwords, the spill dword (ring_or2), padding to 16 bytes
     static constexpr uint32_t kRingStride = kRing + 4;
-    static constexpr uint32_t kTileSteps = P == 8 ? 8 : 16;  // input steps staged at a time
+    static constexpr uint32_t kTileSteps = kS == 128 ? 8 : 16;  // input steps staged at a time
     static constexpr uint32_t kTileBytes = kTileSteps * kS;
-    static constexpr uint32_t kLaneStage = kTileBytes / 16;  // bytes a lane stages
+    static constexpr uint32_t kLaneStage = kTileBytes / W;   // bytes a lane stages
     static constexpr uint32_t kTileVecs = kLaneStage / 16;   // 16-byte loads a lane stages
-    // The four rows of a wavefront write their rings and read their tiles at similar offsets
-    // in the same steps.  A row reads P bytes a lane of a tile step (16 P bytes, 4 P banks)
-    // and ORs about 16 P x 6.5 bits of fields a step into its ring (some 3 P dwords), so the
-    // tiles sit 16 P bytes apart beyond their size and the ring origins 4 P dwords apart (ring
-    // dword (d + 4 P row) mod kRing holds slot dword d): the rows use different LDS banks.
-    static constexpr uint32_t kTileStride = kTileBytes + 16 * P;
-    static constexpr uint32_t kRowTurn = 4 * P;             // ring dwords per row of the wavefront
+    // The rows of a wavefront write their rings and read their tiles at similar offsets in
+    // the same steps.  A row reads kS bytes of a tile step (kS / 4 banks) and ORs about kS x
+    // 6.5 bits of fields a step into its ring (some kS / 5 dwords), so the tiles sit kS bytes
+    // apart beyond their size and the ring origins kS / 4 dwords apart (ring dword (d + kS / 4
+    // row) mod kRing holds slot dword d): the rows use different LDS banks.
+    static constexpr uint32_t kTileStride = kTileBytes + kS;
+    static constexpr uint32_t kRowTurn = kS / 4;            // ring dwords per row of the wavefront
     static constexpr uint32_t kEsByte = kERingsByte + kEncodeChunksPerBlock * kRingStride * 4;
     static_assert(kEsByte >= 4 * kMaxLGpu && kEsByte + 4 * kMaxLGpu < 32768,
                   "encTable addresses stay positive and below bit 15 of an entry");
@@ -153,21 +155,22 @@ __device__ __forceinline__ uint32_t field_of(uint32_t s, const EEnt& en) {
     return f;
 }
 
-template <class A, int P>
-__global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
-    using G = EncGeom<P>;
+template <class A, int W, int P>
+__global__ __launch_bounds__(kEncodeChunksPerBlock * W) void k_encode_chunks(const A a) {
+    using G = EncGeom<W, P>;
+    constexpr uint32_t kBlock = G::kBlock, kRowsPerWave = G::kRowsPerWave;
     constexpr uint32_t kS = G::kS, kERing = G::kRing, kETileSteps = G::kTileSteps;
     constexpr uint32_t kEEsByte = G::kEsByte;
     using VT = std::conditional_t<P == 8, uint64_t, uint32_t>;  // a lane's P values, a byte each
     // the entry addresses below are formed with AND-OR, so the LDS block must start on a
     // 2 KB boundary (it is the kernel's only LDS, at byte 0)
     extern __shared__ __align__(2048) uint32_t esm[];
-    const uint32_t tid = threadIdx.x, lane = tid & 63, j = lane & 15, row = lane >> 4;
+    const uint32_t tid = threadIdx.x, lane = tid & 63, j = lane % W, row = lane / W;
     const uint32_t block = __builtin_amdgcn_readfirstlane(blockIdx.x);
     const SegDesc* sg = codec_seg(a, block, false);
     const uint32_t bseg = block - sg->first_block;
-    const uint32_t wid = __builtin_amdgcn_readfirstlane(bseg * (kEncRowsBlock / 64) + (tid >> 6));
-    const uint32_t rowi = (wid & (kEncRowsBlock / 64 - 1)) * 4 + row;  // row in the block
+    const uint32_t wid = __builtin_amdgcn_readfirstlane(bseg * (kBlock / 64) + (tid >> 6));
+    const uint32_t rowi = (wid & (kBlock / 64 - 1)) * kRowsPerWave + row;  // row in the block
     const uint32_t n_chunks = sg->n_chunks;
     const uint64_t n = sg->n;
     const uint32_t L = a.h.L, R = a.h.R, R1 = a.h.R + 1;
@@ -183,26 +186,26 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
     const uint32_t* vt = sg->tab ? sg->tab + kDTVt : inline_tab(a);
     const uint16_t* es_src = sg->tab ? reinterpret_cast<const uint16_t*>(sg->tab + kDTEs)
                                     : inline_es(a);
-    {
-        const uint32_t v0 = vt[2 * tid], v1 = vt[2 * tid + 1];  // value tid (256 threads)
+    if (tid < 256) {
+        const uint32_t v0 = vt[2 * tid], v1 = vt[2 * tid + 1];  // value tid
         const uint32_t start4 = es_byte + 4 * ((v1 >> 16) - kMaxLGpu);
         esm[kEVtByte / 4 + 2 * tid] = (v0 & 0xFFFFFFu) | (((v1 >> 8) & 15u) << 24);
         esm[kEVtByte / 4 + 2 * tid + 1] = (v1 & 0xFFu) | (start4 << 16) | ((v1 & 0x8000u) << 16);
     }
-    for (uint32_t i = tid; i < L; i += kEncRowsBlock) esm[kEEsByte / 4 + i] = L + es_src[i];
-    for (uint32_t i = j; i < G::kRingStride; i += 16) esm[kERingsByte / 4 + G::kRingStride * rowi + i] = 0;
+    for (uint32_t i = tid; i < L; i += kBlock) esm[kEEsByte / 4 + i] = L + es_src[i];
+    for (uint32_t i = j; i < G::kRingStride; i += W) esm[kERingsByte / 4 + G::kRingStride * rowi + i] = 0;
     if (tid < 2) agg_s[tid] = 0;
 
-    // the wavefront's four chunks, one per row
-    const uint32_t group = 4 * wid;
+    // the wavefront's chunks, one per row
+    const uint32_t group = kRowsPerWave * wid;
     const uint32_t chunk = group + row;
     const uint64_t grp_first = (uint64_t)group * a.h.C;
     const uint64_t grp_len = grp_first < n ? n - grp_first : 0;
     const rsrc_t rin = make_rsrc(sg->x + (grp_first < n ? grp_first : 0),
-                                 (uint32_t)(grp_len < 4ull * a.h.C ? grp_len : 4ull * a.h.C));
+                                 (uint32_t)(grp_len < kRowsPerWave * (uint64_t)a.h.C ? grp_len : kRowsPerWave * (uint64_t)a.h.C));
     const uint32_t slot0 = sg->slot_base + (group < n_chunks ? group : 0);
     const rsrc_t rslot = make_rsrc(a.h.slots + (uint64_t)slot0 * a.h.slot_dwords,
-                                   16u * a.h.slot_dwords);
+                                   4 * kRowsPerWave * a.h.slot_dwords);
     const uint32_t in_row = row * a.h.C;                   // byte of this row's chunk in rin
     const uint32_t slot_row = row * a.h.slot_dwords * 4;   // byte of its slot in rslot
     // a device table built for other parameters than the launch's, or one whose build
@@ -218,19 +221,18 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
     const uint32_t lanes = nc < kS ? nc : kS;
     uint32_t nc_min = 0xFFFFFFFFu, nc_max = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint32_t v = __builtin_amdgcn_readlane(nc, 16 * k);
+    for (uint32_t k = 0; k < kRowsPerWave; ++k) {
+        const uint32_t v = __builtin_amdgcn_readlane(nc, W * k);
         nc_min = nc_min < v ? nc_min : v;
         nc_max = nc_max > v ? nc_max : v;
     }
     const uint32_t steps = (nc_max + kS - 1) / kS;
 
-    // Lane j stages bytes [kLaneStage j, kLaneStage (j + 1)) of tile T (step 16 T + j when a
-    // tile is 16 steps).  Past a short chunk's end lies the end of the wavefront's range (a
+    // Lane j stages bytes [kLaneStage j, kLaneStage (j + 1)) of tile T.  Past a short chunk's end lies the end of the wavefront's range (a
     // 16-byte load reaching past it reads 0 as a whole, so the lanes at the end read byte by
     // byte) or the next chunk, whose values go unused.
     constexpr uint32_t kLaneStage = G::kLaneStage;
-    const uint32_t in_len = (uint32_t)(grp_len < 4ull * a.h.C ? grp_len : 4ull * a.h.C);
+    const uint32_t in_len = (uint32_t)(grp_len < kRowsPerWave * (uint64_t)a.h.C ? grp_len : kRowsPerWave * (uint64_t)a.h.C);
     auto load_tile = [&](uint32_t T, v4u* pv) {
         const uint32_t b = in_row + G::kTileBytes * T + kLaneStage * j;
         if (b + kLaneStage <= in_len) {
@@ -261,7 +263,8 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
     uint32_t flush_at = (fmark - kEFlush) * 32 + turn;  // once fpos is below this, flush a block
     uint32_t bad = 0;                    // entries OR-ed in: bit 31 marks a range without states
 
-    auto flush_block = [&](uint32_t blk) {  // ring dwords [blk, blk + 64) -> slot
+    auto flush_block = [&](uint32_t blk) {  // ring dwords [blk, blk + 64) -> slot, 16 lanes
+        if (j >= kEFlush / 4) return;
         typedef __attribute__((address_space(3))) v4u lds_v4;
         const uint32_t idx = (blk + G::kRowTurn * row + 4 * j) & (kERing - 1);
         lds_v4* r = (lds_v4*)(uintptr_t)(ring_byte + 4 * idx);
@@ -379,11 +382,18 @@ __global__ __launch_bounds__(kEncRowsBlock) void k_encode_chunks(const A a) {
             lq[k] = l[2 * k] + l[2 * k + 1];
             lp += lq[k];
         }
-        const uint32_t incl = escan16(lp);
-        fpos -= erow_last(incl);
-        // the lane's position: the previous lane's inclusive sum above fpos (a DPP row shift,
-        // zero for lane 0, in the add)
-        uint32_t at = fpos + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x111, 0xF, 0xF, true);
+        uint32_t at;
+        if constexpr (W == 16) {
+            const uint32_t incl = escan16(lp);
+            fpos -= erow_last(incl);
+            // the lane's position: the previous lane's inclusive sum above fpos (a DPP row
+            // shift, zero for lane 0, in the add)
+            at = fpos + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x111, 0xF, 0xF, true);
+        } else {  // a half wavefront: the row total from lane 31
+            const uint32_t incl = scan32(lp);
+            fpos -= bcast31(incl);
+            at = fpos + incl - lp;
+        }
 #pragma unroll
         for (int k = 0; k < P / 2; ++k) {
             ring_or2<G::kRingLog2>(ring_byte, at, fp[k]);
@@ -677,6 +687,17 @@ __global__ __launch_bounds__(256) void k_encode_place(const A a) {
     }
 }
 
+// Launches of fewer chunks than this take half-wavefront rows for 64-stream chunks (the
+// decoder's launch planner draws the same line for its row mappings).
+constexpr uint64_t kEncodeFewChunks = 16384;
+
+template <class K, int W, int P>
+void launch_chunks(const K& k, uint32_t blocks, uint32_t L, hipStream_t s) {
+    using G = EncGeom<W, P>;
+    const uint32_t lds = G::lds_bytes(L);
+    hipLaunchKernelGGL((k_encode_chunks<K, W, P>), dim3(blocks), dim3(G::kBlock), lds, s, k);
+}
+
 sh_status launch_encode(const CodecArgs& a, uint32_t total_blocks, uint32_t total_blocks_c,
                         bool place, void* stream) {
     if (a.S != kStreamsNarrow && a.S != kStreamsWide && a.S != kStreamsWidest)
@@ -685,15 +706,13 @@ sh_status launch_encode(const CodecArgs& a, uint32_t total_blocks, uint32_t tota
     with_kernel_args(a, [&](const auto& k) {
         using K = std::decay_t<decltype(k)>;
         if (total_blocks > 0) {
-            if (a.S == kStreamsWidest)
-                hipLaunchKernelGGL((k_encode_chunks<K, 8>), dim3(total_blocks), dim3(kEncRowsBlock),
-                                   EncGeom<8>::lds_bytes(a.L), s, k);
-            else if (a.S == kStreamsWide)
-                hipLaunchKernelGGL((k_encode_chunks<K, 4>), dim3(total_blocks), dim3(kEncRowsBlock),
-                                   EncGeom<4>::lds_bytes(a.L), s, k);
-            else
-                hipLaunchKernelGGL((k_encode_chunks<K, 2>), dim3(total_blocks), dim3(kEncRowsBlock),
-                                   EncGeom<2>::lds_bytes(a.L), s, k);
+            // 64-stream chunks of a launch too small to fill the GPU with 16-lane rows go to
+            // half-wavefront rows (twice the wavefronts), as in the decoder
+            const bool few = (uint64_t)total_blocks * kEncodeChunksPerBlock < kEncodeFewChunks;
+            if (a.S == kStreamsWidest) launch_chunks<K, 16, 8>(k, total_blocks, a.L, s);
+            else if (a.S == kStreamsWide && few) launch_chunks<K, 32, 2>(k, total_blocks, a.L, s);
+            else if (a.S == kStreamsWide) launch_chunks<K, 16, 4>(k, total_blocks, a.L, s);
+            else launch_chunks<K, 16, 2>(k, total_blocks, a.L, s);
         }
         if (place) {
             hipLaunchKernelGGL(k_encode_place<K>, dim3(total_blocks_c), dim3(256), 0, s, k);
