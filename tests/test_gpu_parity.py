@@ -89,15 +89,17 @@ def test_ragged_sizes(torch_cuda, n, S):
 
 @pytest.mark.parametrize("n,C_,S", [(16383 * 64, 64, 32), (16384 * 64, 64, 32),
                                     (16384 * 64 + 64, 64, 32), (20000 * 32 + 5, 32, 32),
-                                    (16384 * 64, 64, 64), (16384 * 64 + 64, 64, 64),
+                                    (16383 * 64, 64, 64), (16384 * 64, 64, 64),
+                                    (16384 * 64 + 64, 64, 64),
                                     (20000 * 64 + 5, 64, 64), (16384 * 128 + 128, 128, 128),
                                     (1000 * 128 + 77, 128, 128)])
 def test_chunk_counts_around_the_one_kernel_placement(torch_cuda, n, C_, S):
     """Up to 16384 chunks a tensor the encoder indexes and compacts in one kernel, beyond it
     the index comes first from its own kernel: both give the oracle's container.  The decode
     of 32-stream chunks switches kernels at the same count (half-wavefront chunks below
-    16384, 16-lane rows from there on): both decode the oracle's container.  Chunks of C = S
-    values hold one value a stream."""
+    16384, 16-lane rows from there on), and so do the encode and the decode of 64-stream
+    chunks (32 x 2 rows below, 16 x 4 from there on): every side gives or decodes the
+    oracle's container.  Chunks of C = S values hold one value a stream."""
     print(f"case: chunks n={n} C={C_} S={S} ({(n + C_ - 1) // C_} chunks)", flush=True)
     x = D.quantize(np.random.default_rng(n).laplace(0, 10, size=n))
     _case(torch_cuda, x, C_=C_, S=S)
