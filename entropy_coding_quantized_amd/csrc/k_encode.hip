@@ -14,19 +14,20 @@ namespace shn {
 // The decoder's mapping run backwards: one chunk per row of W lanes (a 16-lane DPP row, or a
 // half wavefront), lane j of a row runs P adjacent streams, P j to P j + P - 1 (16 x 2 for
 // chunks of 32 streams, 16 x 4 for 64, 16 x 8 for 128; 32 x 2 for launches of few chunks of
-// 64 streams, which it gives twice the wavefronts), whose fields are adjacent in every step.  tANS encodes backwards, so each stream walks its
-// values from the last step to the first and every step's fields are placed right to left:
-// the step's fields end where the later steps' fields begin, and a W-lane prefix sum of the
-// lanes' field lengths gives every lane's bit position.  A lane's fields are OR-ed, a pair
-// at a time, into a 128-dword LDS ring per chunk that is flushed to the chunk's slot 64
-// dwords at a time, highest first; the chunk ends up right-aligned in its slot with the
-// streams' final states (the decoder's initial states) in front.
+// 64 streams, which it gives twice the wavefronts), whose fields are adjacent in every
+// step.  tANS encodes backwards, so each stream walks its values from the last step to the
+// first and every step's fields are placed right to left: the step's fields end where the
+// later steps' fields begin, and a W-lane prefix sum of the lanes' field lengths gives every
+// lane's bit position.  A lane's fields are OR-ed, a pair at a time, into an LDS ring per
+// chunk (128 dwords, 256 for 128 streams) that is flushed to the chunk's slot 64 dwords at a
+// time, highest first; the chunk ends up right-aligned in its slot with the streams' final
+// states (the decoder's initial states) in front.
 constexpr uint32_t kEFlush = 64;                   // dwords per flush
 // LDS (dynamic; the kernel's only LDS, so it starts at LDS byte 0): the value entries (two
 // dwords per value, at a 2 KB boundary so that an entry's address is one AND-OR), the
-// rings (one per chunk, each followed by its spill dword), the encTable (a dword per slot, holding the
-// next state L + slot), the input tiles (u = x + 128 of kTileSteps steps of a chunk), then
-// the block's two totals
+// rings (one per chunk, each followed by its spill dword), the encTable (a dword per slot,
+// holding the next state L + slot), the input tiles (u = x + 128 of kTileSteps steps of a
+// chunk), then the block's two totals
 constexpr uint32_t kEVtByte = 0;
 constexpr uint32_t kERingsByte = kEVtByte + 256 * 8;                                 // 2 KB
 template <int W, int P>
@@ -39,8 +40,8 @@ struct EncGeom {
     // The ring holds every dword not yet flushed.  After a flush check the fields reach no
     // lower than 64 dwords below the flush mark; checks come at least every other step, and
     // a step places at most kS fields of 16 bits, kS / 2 dwords; so the unflushed dwords span
-    // at most 64 + kS dwords: 128 dwords (the ring exactly at P = 4; the mark's own dword,
-    // the lowest one's twin in the ring, is flushed and zero), 256 at P = 8.
+    // at most 64 + kS dwords: 128 dwords (the ring exactly at 64 streams; the mark's own
+    // dword, the lowest one's twin in the ring, is flushed and zero), 256 at 128 streams.
     static constexpr uint32_t kRingLog2 = kS == 128 ? 8 : 7;
     static constexpr uint32_t kRing = 1u << kRingLog2;
     static_assert(kEFlush + kS <= kRing, "two steps fit in the ring");
