@@ -252,8 +252,9 @@ sh_status launch_decode_wide_halves(const CodecArgs& a, uint32_t total_blocks, v
 // this many values long
 constexpr uint32_t kMaxMatvecCols = 16384;
 sh_status launch_decode_matvec(const CodecArgs& a, uint32_t total_blocks, void* stream);
-// the encoder's chunk kernel: one chunk per 16-lane row (two, four or eight streams a
-// lane), 16 chunks a block
+// the encoder's chunk kernel: one chunk per row of 16 lanes (two, four or eight streams a
+// lane) or, for launches of few chunks of 64 streams, of 32 lanes (two streams a lane); 16
+// chunks a block
 constexpr uint32_t kEncodeChunksPerBlock = 16;
 // segments of at most this many chunks are indexed and compacted by one kernel
 // (k_encode_place: each block sums the sizes of the chunks before its own, so the work
