@@ -101,7 +101,8 @@ _EXPORTS = {
     "sh_encode_batch_workspace": (C.c_uint64, [C.c_void_p, C.c_uint32, C.POINTER(sh_params)]),
     "sh_encode_batch": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_uint32,
                                     C.POINTER(sh_params), C.c_void_p, C.c_void_p, C.c_void_p,
-                                    C.c_uint64, C.c_void_p, C.c_void_p, C.c_void_p]),
+                                    C.c_uint64, C.c_void_p, C.c_void_p, C.c_void_p,
+                                    C.c_void_p]),
     "sh_decode_batch": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                     C.c_uint32, C.POINTER(sh_params), C.c_void_p, C.c_void_p]),
     "sh_decode_matvec_batch": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
@@ -178,6 +179,11 @@ def _stream(stream) -> int:
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+def _opt_stream(stream):
+    """A stream argument that may be NULL: None stays None."""
+    return None if stream is None else _stream(stream)
 
 
 # ---- the C ABI, one to one -----------------------------------------------------------
@@ -354,11 +360,12 @@ def sh_encode_batch_workspace(n: list, params: Params) -> int:
 
 
 def sh_encode_batch(d_tables, d_x: list, n: list, params: Params, d_out: list, out_cap: list,
-                    d_ws, ws_bytes: int, d_info=None, d_status=None, stream=None) -> None:
+                    d_ws, ws_bytes: int, d_info=None, d_status=None, stream=None,
+                    place_stream=None) -> None:
     p = params.c()
     st = lib().sh_encode_batch(_ptr(d_tables), _ptrs(d_x), _u64s(n), len(n), C.byref(p),
                                _ptrs(d_out), _u64s(out_cap), _ptr(d_ws), ws_bytes, _ptr(d_info),
-                               _ptr(d_status), _stream(stream))
+                               _ptr(d_status), _stream(stream), _opt_stream(place_stream))
     _check(st, "sh_encode_batch")
 
 
@@ -466,10 +473,10 @@ def tables_to_device(tables: list, params: Params, device, stream=None):
     return d
 
 
-def encode_tensors(d_tables, xs: list, params: Params, stream=None):
-    """Encode a list of device int8 tensors with their device tables.  Returns
-    (buffer, offsets, caps, info (nseg x 2 int64, device), status (device)); container i
-    starts at buffer[offsets[i]]."""
+def encode_tensors(d_tables, xs: list, params: Params, stream=None, place_stream=None):
+    """Encode a list of device int8 tensors with their device tables (place_stream: see
+    sh_encode_batch).  Returns (buffer, offsets, caps, info (nseg x 2 int64, device), status
+    (device)); container i starts at buffer[offsets[i]]."""
     import torch
     dev = xs[0].device
     xs = [x.contiguous().view(-1) for x in xs]
@@ -486,7 +493,7 @@ def encode_tensors(d_tables, xs: list, params: Params, stream=None):
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     base = buf.data_ptr()
     sh_encode_batch(d_tables, xs, ns, params, [base + o for o in offs], caps, ws, wsb, info,
-                    status, stream)
+                    status, stream, place_stream)
     return buf, offs, caps, info, status
 
 

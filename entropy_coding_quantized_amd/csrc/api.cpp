@@ -119,7 +119,8 @@ std::vector<std::pair<uint32_t, uint32_t>> groups_of(uint32_t nseg) {
     return g;
 }
 
-uint64_t encode_batch_ws(const uint64_t* n, uint32_t nseg, const sh_params* p) {
+// one launch group's workspace region: the largest group's layout (a multiple of 256 bytes)
+uint64_t encode_group_ws(const uint64_t* n, uint32_t nseg, const sh_params* p) {
     uint64_t best = 256;
     for (auto [b, e] : groups_of(nseg)) {
         uint64_t slots = 0;
@@ -127,6 +128,13 @@ uint64_t encode_batch_ws(const uint64_t* n, uint32_t nseg, const sh_params* p) {
         best = std::max(best, enc_layout(slots, p).bytes);
     }
     return best;
+}
+
+// the batch workspace: two group regions when the batch takes more than one launch group
+// (with a placement stream, group g's placement reads region g mod 2 while group g + 1's
+// chunk kernel writes the other), else one
+uint64_t encode_batch_ws(const uint64_t* n, uint32_t nseg, const sh_params* p) {
+    return encode_group_ws(n, nseg, p) * (nseg > kMaxInlineSegs ? 2 : 1);
 }
 
 void fill_codec_common(CodecArgs& a, const sh_params* p, int32_t* d_status) {
@@ -421,13 +429,17 @@ uint64_t sh_encode_batch_workspace(const uint64_t* n, uint32_t nseg, const sh_pa
 sh_status sh_encode_batch(const void* d_tables, const int8_t* const* d_x, const uint64_t* n,
                           uint32_t nseg, const sh_params* params, uint8_t* const* d_out,
                           const uint64_t* out_cap, void* d_ws, uint64_t ws_bytes,
-                          sh_encode_info* d_info, int32_t* d_status, void* stream) {
+                          sh_encode_info* d_info, int32_t* d_status, void* stream,
+                          void* place_stream) {
     if (nseg == 0) return SH_OK;
     if (!d_tables || !d_x || !n || !d_out || !out_cap || !aligned(d_tables, 16))
         return SH_ERR_INVALID_ARG;
     sh_status st = check_params(params);
     if (st != SH_OK) return st;
-    if (!d_ws || !aligned(d_ws, 256) || ws_bytes < encode_batch_ws(n, nseg, params))
+    const auto groups = groups_of(nseg);
+    const bool overlap = place_stream != nullptr && place_stream != stream && groups.size() > 1;
+    const uint64_t region = encode_group_ws(n, nseg, params);
+    if (!d_ws || !aligned(d_ws, 256) || ws_bytes < region * (overlap ? 2 : 1))
         return SH_ERR_BUFFER_TOO_SMALL;
     if (!aligned(d_info, 8) || !aligned(d_status, 4)) return SH_ERR_INVALID_ARG;
     for (uint32_t i = 0; i < nseg; ++i) {
@@ -436,7 +448,27 @@ sh_status sh_encode_batch(const void* d_tables, const int8_t* const* d_x, const 
         if (n[i] >= (1ull << 32) || bound_of(n[i], params) > 0xFFFFFFFFull) return SH_ERR_UNSUPPORTED;
         if (out_cap[i] < bound_of(n[i], params)) return SH_ERR_BUFFER_TOO_SMALL;
     }
-    for (auto [b, e] : groups_of(nseg)) {
+    // With overlap, group g's chunk kernel runs on stream in region g mod 2 and its
+    // placement on place_stream once the chunk kernel is done, beside group g + 1's chunk
+    // kernel; group g + 2's chunk kernel waits for group g's placement (it reuses the
+    // region), and stream waits for the last placement before the call returns.
+    std::vector<hipEvent_t> ready(overlap ? groups.size() : 0, nullptr);
+    std::vector<hipEvent_t> placed(ready.size(), nullptr);
+    auto release = [&]() {
+        for (hipEvent_t ev : ready)
+            if (ev) (void)hipEventDestroy(ev);
+        for (hipEvent_t ev : placed)
+            if (ev) (void)hipEventDestroy(ev);
+    };
+    for (size_t g = 0; g < ready.size(); ++g)
+        if (hipEventCreateWithFlags(&ready[g], hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&placed[g], hipEventDisableTiming) != hipSuccess) {
+            release();
+            return SH_ERR_HIP;
+        }
+    int last_placed = -1;
+    for (size_t g = 0; g < groups.size(); ++g) {
+        const auto [b, e] = groups[g];
         CodecArgs a;
         std::memset(&a, 0, sizeof(a));
         fill_codec_common(a, params, d_status);
@@ -464,13 +496,28 @@ sh_status sh_encode_batch(const void* d_tables, const int8_t* const* d_x, const 
             slots += slots_for(nch);
         }
         const EncLayout lay = enc_layout(slots, params);
-        a.slots = (uint32_t*)d_ws;
-        a.meta = (uint32_t*)((uint8_t*)d_ws + lay.meta_at);
-        a.agg = (uint32_t*)((uint8_t*)d_ws + lay.agg_at);
-        st = launch_encode(a, blocks, blocks_c, place, stream);
-        if (st != SH_OK) return st;
+        uint8_t* ws = (uint8_t*)d_ws + (overlap ? (g & 1) * region : 0);
+        a.slots = (uint32_t*)ws;
+        a.meta = (uint32_t*)(ws + lay.meta_at);
+        a.agg = (uint32_t*)(ws + lay.agg_at);
+        if (overlap && g >= 2 &&
+            hipStreamWaitEvent((hipStream_t)stream, placed[g - 2], 0) != hipSuccess) {
+            st = SH_ERR_HIP;
+            break;
+        }
+        st = overlap ? launch_encode(a, blocks, blocks_c, place, stream, place_stream, ready[g],
+                                     placed[g])
+                     : launch_encode(a, blocks, blocks_c, place, stream);
+        if (st != SH_OK) break;
+        last_placed = (int)g;
     }
-    return SH_OK;
+    // stream takes up after the last placement queued, also when a later launch failed
+    if (overlap && last_placed >= 0 &&
+        hipStreamWaitEvent((hipStream_t)stream, placed[last_placed], 0) != hipSuccess &&
+        st == SH_OK)
+        st = SH_ERR_HIP;
+    release();
+    return st;
 }
 
 sh_status sh_decode_batch(const void* d_tables, const uint8_t* const* d_in,

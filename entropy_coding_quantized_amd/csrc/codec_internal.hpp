@@ -260,9 +260,12 @@ constexpr uint32_t kEncodeChunksPerBlock = 16;
 // (k_encode_place: each block sums the sizes of the chunks before its own, so the work
 // grows with the square of the chunk count); longer ones take the index kernel first
 constexpr uint32_t kPlaceMaxChunks = 16384;
+// The chunk kernel runs on stream.  With place_stream non-null the placement kernels run
+// there instead: ready (an event) is recorded on stream after the chunk kernel, place_stream
+// waits for it, and placed is recorded on place_stream after the placement.
 sh_status launch_encode(const CodecArgs& a, uint32_t total_blocks, uint32_t total_blocks_c,
-                        bool place,
-                        void* stream);
+                        bool place, void* stream, void* place_stream = nullptr,
+                        void* ready = nullptr, void* placed = nullptr);
 
 // encode workspace layout
 inline uint32_t encode_slot_dwords(uint32_t C, uint32_t R, uint32_t S) {

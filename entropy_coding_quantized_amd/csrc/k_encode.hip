@@ -700,10 +700,12 @@ void launch_chunks(const K& k, uint32_t blocks, uint32_t L, hipStream_t s) {
 }
 
 sh_status launch_encode(const CodecArgs& a, uint32_t total_blocks, uint32_t total_blocks_c,
-                        bool place, void* stream) {
+                        bool place, void* stream, void* place_stream, void* ready,
+                        void* placed) {
     if (a.S != kStreamsNarrow && a.S != kStreamsWide && a.S != kStreamsWidest)
         return SH_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
+    hipError_t ev = hipSuccess;
     with_kernel_args(a, [&](const auto& k) {
         using K = std::decay_t<decltype(k)>;
         if (total_blocks > 0) {
@@ -715,6 +717,12 @@ sh_status launch_encode(const CodecArgs& a, uint32_t total_blocks, uint32_t tota
             else if (a.S == kStreamsWide) launch_chunks<K, 16, 4>(k, total_blocks, a.L, s);
             else launch_chunks<K, 16, 2>(k, total_blocks, a.L, s);
         }
+        if (place_stream) {
+            ev = hipEventRecord((hipEvent_t)ready, s);
+            if (ev == hipSuccess) ev = hipStreamWaitEvent((hipStream_t)place_stream, (hipEvent_t)ready, 0);
+            if (ev != hipSuccess) return;
+            s = (hipStream_t)place_stream;
+        }
         if (place) {
             hipLaunchKernelGGL(k_encode_place<K>, dim3(total_blocks_c), dim3(256), 0, s, k);
             return;
@@ -723,7 +731,8 @@ sh_status launch_encode(const CodecArgs& a, uint32_t total_blocks, uint32_t tota
         if (total_blocks_c > 0)
             hipLaunchKernelGGL(k_encode_compact<K>, dim3(total_blocks_c), dim3(256), 0, s, k);
     });
-    return hipGetLastError() == hipSuccess ? SH_OK : SH_ERR_HIP;
+    if (ev == hipSuccess && place_stream) ev = hipEventRecord((hipEvent_t)placed, s);
+    return hipGetLastError() == hipSuccess && ev == hipSuccess ? SH_OK : SH_ERR_HIP;
 }
 
 }  // namespace shn

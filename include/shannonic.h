@@ -282,12 +282,23 @@ sh_status sh_build_tables_batch(const int8_t* const* d_x, const uint64_t* n, uin
  * outside its table (SH_ERR_SYMBOL_NOT_IN_TABLE), a table whose build failed
  * (SH_ERR_UNSUPPORTED), or a device table built for another K or log2_L than params
  * (SH_ERR_INVALID_ARG; that tensor's chunks are then coded empty).  Asynchronous on stream.
+ * The batch is encoded in launches of up to 48 tensors, each a chunk kernel and then a
+ * placement that moves the chunks to their offsets.  place_stream (may be NULL) is a second
+ * stream of the caller's: when it is given, differs from stream and the batch takes more than
+ * one launch, each launch's placement runs on it, beside the next launch's chunk kernel, and
+ * the workspace holds two launch regions that the launches take in turn (the size
+ * sh_encode_batch_workspace returns covers this; one region, half of it, suffices without
+ * place_stream).  place_stream first waits for the work queued on stream before the call,
+ * and stream waits for the last placement, so work queued on stream after the call sees
+ * every container; work queued on place_stream after the call runs after the placements.
+ * The call creates and releases its own events.
  */
 uint64_t sh_encode_batch_workspace(const uint64_t* n, uint32_t nseg, const sh_params* params);
 sh_status sh_encode_batch(const void* d_tables, const int8_t* const* d_x, const uint64_t* n,
                           uint32_t nseg, const sh_params* params, uint8_t* const* d_out,
                           const uint64_t* out_cap, void* d_ws, uint64_t ws_bytes,
-                          sh_encode_info* d_info, int32_t* d_status, void* stream);
+                          sh_encode_info* d_info, int32_t* d_status, void* stream,
+                          void* place_stream);
 
 /*
  * The decoder of "Runtime encoding/decoding" (paper section 4.2) for nseg containers with

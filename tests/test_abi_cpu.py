@@ -165,18 +165,32 @@ def test_batch_argument_checks_are_synchronous():
     assert ws >= max(codec.sh_encode_workspace(n, p) for n in ns)
     # nothing to do
     assert lib.sh_encode_batch(fake, ptrs, n_arr, 0, C.byref(pc), ptrs, caps, fake, 0, None,
-                               None, None) == codec.SH_OK
+                               None, None, None) == codec.SH_OK
     # workspace, capacity, alignment
     assert lib.sh_encode_batch(fake, ptrs, n_arr, 3, C.byref(pc), ptrs, caps, fake, ws - 1,
-                               None, None, None) == codec.SH_ERR_BUFFER_TOO_SMALL
+                               None, None, None, None) == codec.SH_ERR_BUFFER_TOO_SMALL
     small = codec._u64s([codec.sh_encode_bound(n, p) - (i == 2) for i, n in enumerate(ns)])
     assert lib.sh_encode_batch(fake, ptrs, n_arr, 3, C.byref(pc), ptrs, small, fake, ws,
-                               None, None, None) == codec.SH_ERR_BUFFER_TOO_SMALL
+                               None, None, None, None) == codec.SH_ERR_BUFFER_TOO_SMALL
     assert lib.sh_encode_batch(fake + 4, ptrs, n_arr, 3, C.byref(pc), ptrs, caps, fake, ws,
-                               None, None, None) == codec.SH_ERR_INVALID_ARG
+                               None, None, None, None) == codec.SH_ERR_INVALID_ARG
     bad = codec.Params(streams=16).c()
     assert lib.sh_encode_batch(fake, ptrs, n_arr, 3, C.byref(bad), ptrs, caps, fake, ws,
-                               None, None, None) == codec.SH_ERR_UNSUPPORTED
+                               None, None, None, None) == codec.SH_ERR_UNSUPPORTED
+    # more than one launch (48 tensors each): two launch regions, so that a placement
+    # stream can take each launch's placement while the next launch encodes; without a
+    # placement stream one region is enough
+    many = [100000 + 4096 * i for i in range(50)]
+    one = max(codec.sh_encode_batch_workspace(many[:48], p),
+              codec.sh_encode_batch_workspace(many[48:], p))
+    ws_many = codec.sh_encode_batch_workspace(many, p)
+    assert ws_many == 2 * one
+    ptrs50, n50 = codec._ptrs([fake] * 50), codec._u64s(many)
+    caps50 = codec._u64s([codec.sh_encode_bound(n, p) for n in many])
+    assert lib.sh_encode_batch(fake, ptrs50, n50, 50, C.byref(pc), ptrs50, caps50, fake,
+                               ws_many - 1, None, None, None, fake) == codec.SH_ERR_BUFFER_TOO_SMALL
+    assert lib.sh_encode_batch(fake, ptrs50, n50, 50, C.byref(pc), ptrs50, caps50, fake,
+                               one - 1, None, None, None, None) == codec.SH_ERR_BUFFER_TOO_SMALL
     # a container shorter than its own index
     short = codec._u64s([codec.sh_encode_bound(n, p) for n in ns[:2]] + [40])
     assert lib.sh_decode_batch(fake, ptrs, short, ptrs, n_arr, 3, C.byref(pc), None,

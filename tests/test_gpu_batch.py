@@ -174,6 +174,73 @@ def test_batch_model_tensors(torch_cuda):
     assert int(info[0, 1].item()) == 0  # all-zero tensor: no field bits
 
 
+@pytest.mark.parametrize("count,C_,S,n_max", [(61, 4096, 32, 120000), (150, 16384, 64, 400000)])
+def test_batch_placement_on_a_second_stream(torch_cuda, count, C_, S, n_max):
+    """Batches of two and four launches with a placement stream: every launch's placement
+    runs there beside the next launch's chunk kernel, the launches take the workspace's two
+    regions in turn, and a decode queued on the main stream after the call reads finished
+    containers.  The containers and totals equal the one-stream encode's, byte for byte, and
+    the oracle's."""
+    torch = torch_cuda
+    p = codec.Params(chunk_symbols=C_, streams=S)
+    print(f"case: {count} tensors C={C_} S={S} with a placement stream", flush=True)
+    xs = _mixed_tensors(1000 + count, count, n_max)
+    ns = [x.size for x in xs]
+    dx = _to_dev(torch, xs)
+    tables, _ = codec.build_tables_tensors(dx, p)
+    side = torch.cuda.Stream()
+    buf, offs, caps, info, st = codec.encode_tensors(tables, dx, p, place_stream=side)
+    y, starts, st2 = codec.decode_tensors(tables, buf, offs, caps, ns, p)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0 and int(st2.item()) == 0
+    for i, x in enumerate(dx):
+        assert torch.equal(y[starts[i]: starts[i] + ns[i]], x[:ns[i]]), f"tensor {i}"
+    buf1, offs1, _, info1, st1 = codec.encode_tensors(tables, dx, p)
+    torch.cuda.synchronize()
+    assert int(st1.item()) == 0
+    assert torch.equal(info, info1)
+    b, b1 = buf.cpu().numpy(), buf1.cpu().numpy()
+    for i in range(count):
+        nb = int(info[i, 0].item())
+        assert np.array_equal(b[offs[i]: offs[i] + nb], b1[offs1[i]: offs1[i] + nb]), i
+    tabs = [O.build_table(O.histogram(x), p.K, p.log2_L) for x in xs]
+    _check_containers(buf, offs, info, xs, tabs, p, whole=set(range(0, count, 10)))
+
+
+def test_model_first_launch_as_the_bench_runs_it(torch_cuda):
+    """The model workload's first launch in the form the bench times it: the first 48
+    tensors (the decode and encode batches' launch size), drawn on the GPU by the same
+    generator, at C = 16,384 and 64 streams a chunk.  The launch holds about 91,000 chunks,
+    so it goes through the 16-lane rows with four streams a lane.  Every GPU-built table
+    equals the oracle's, three chunks of every container equal the oracle's encoding of
+    them, and every tensor decodes back whole."""
+    torch = torch_cuda
+    cfg = D.CONFIGS["model"]
+    p = codec.Params(K=cfg["K"], log2_L=cfg["log2_L"], chunk_symbols=cfg["chunk"],
+                     streams=cfg["streams"])
+    print("case: model tensors 0..47 drawn on the GPU, one launch", flush=True)
+    dx = [D.model_tensor_torch(i, "cuda").view(-1) for i in range(48)]
+    ns = [x.numel() for x in dx]
+    assert sum((n + p.chunk_symbols - 1) // p.chunk_symbols for n in ns) >= 16384
+    tables, _ = codec.build_tables_tensors(dx, p)
+    buf, offs, caps, info, st = codec.encode_tensors(tables, dx, p)
+    y, starts, st2 = codec.decode_tensors(tables, buf, offs, caps, ns, p)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0 and int(st2.item()) == 0
+    for i, x in enumerate(dx):
+        assert torch.equal(y[starts[i]: starts[i] + ns[i]], x), f"tensor {i}"
+    del y
+    xs = [x.cpu().numpy() for x in dx]
+    tb = codec.sh_device_table_bytes()
+    tabs = []
+    for i, x in enumerate(xs):
+        lo, f = O.build_table(O.histogram(x), p.K, p.log2_L)
+        t = codec.table_from_device(tables[i * tb:(i + 1) * tb])
+        assert (t.lo_array == lo).all() and (t.freq_array == f).all(), i
+        tabs.append((lo, f))
+    _check_containers(buf, offs, info, xs, tabs, p, whole=set())
+
+
 def test_batch_errors(torch_cuda):
     torch = torch_cuda
     p = codec.Params()
