@@ -18,7 +18,9 @@ sh_status launch_decode(const CodecArgs&, uint32_t, void*) { return SH_ERR_HIP; 
 sh_status launch_decode_halves(const CodecArgs&, uint32_t, void*) { return SH_ERR_HIP; }
 sh_status launch_decode_wide_halves(const CodecArgs&, uint32_t, void*) { return SH_ERR_HIP; }
 sh_status launch_decode_matvec(const CodecArgs&, uint32_t, void*) { return SH_ERR_HIP; }
-sh_status launch_encode(const CodecArgs&, uint32_t, uint32_t, bool, void*) { return SH_ERR_HIP; }
+sh_status launch_encode(const CodecArgs&, uint32_t, uint32_t, bool, void*, void*, void*, void*) {
+    return SH_ERR_HIP;
+}
 }  // namespace shn
 
 static uint64_t rng_state = 0x2545F4914F6CDD1Dull;
