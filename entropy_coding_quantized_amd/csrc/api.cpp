@@ -574,9 +574,11 @@ sh_status sh_decode_matvec_batch(const void* d_tables, const uint8_t* const* d_i
         return SH_ERR_INVALID_ARG;
     sh_status st = check_params(params);
     if (st != SH_OK) return st;
-    if (cols % 32 != 0 || cols > kMaxMatvecCols) return SH_ERR_UNSUPPORTED;
-    if (params->streams != kStreamsNarrow) return SH_ERR_UNSUPPORTED;  // half-wavefront kernel
-    if (params->log2_L > (uint32_t)kInlineMaxLog2L) return SH_ERR_UNSUPPORTED;  // one slot a thread
+    // chunks of 32 streams: the half-wavefront kernel (one slot a thread: L <= 256); of 64 or
+    // 128: the row decoder; a matrix row holds whole steps of the chunks' streams
+    const bool narrow = params->streams == kStreamsNarrow;
+    if (cols % params->streams != 0 || cols > kMaxMatvecCols) return SH_ERR_UNSUPPORTED;
+    if (narrow && params->log2_L > (uint32_t)kInlineMaxLog2L) return SH_ERR_UNSUPPORTED;
     if (!aligned(d_status, 4)) return SH_ERR_INVALID_ARG;
     for (uint32_t i = 0; i < nseg; ++i) {
         if (!d_in[i] || !aligned(d_in[i], 4) || n[i] % cols != 0) return SH_ERR_INVALID_ARG;
@@ -592,6 +594,9 @@ sh_status sh_decode_matvec_batch(const void* d_tables, const uint8_t* const* d_i
         fill_codec_common(a, params, d_status);
         a.cols = cols;
         a.nseg = e - b;
+        uint64_t total_chunks = 0;
+        for (uint32_t i = b; i < e; ++i) total_chunks += n_chunks_of(n[i], params->chunk_symbols);
+        const uint32_t per_block = narrow ? kChunksPerBlock : decode_path(total_chunks, params).per_block;
         uint32_t blocks = 0;
         for (uint32_t i = b; i < e; ++i) {
             SegDesc& sd = a.many[i - b];
@@ -604,9 +609,10 @@ sh_status sh_decode_matvec_batch(const void* d_tables, const uint8_t* const* d_i
             sd.tab = (const uint32_t*)((const uint8_t*)d_tables + (uint64_t)i * kDTBytes);
             sd.first_block = blocks;
             sd.n_chunks = (uint32_t)nch;
-            blocks += blocks_for(nch, kChunksPerBlock);
+            blocks += blocks_for(nch, per_block);
         }
-        st = launch_decode_matvec(a, blocks, stream);
+        st = narrow ? launch_decode_matvec(a, blocks, stream)
+                    : launch_decode_matvec_rows(a, blocks, total_chunks < kHalfDecodeMaxChunks, stream);
         if (st != SH_OK) return st;
     }
     return SH_OK;

@@ -252,6 +252,10 @@ sh_status launch_decode_wide_halves(const CodecArgs& a, uint32_t total_blocks, v
 // this many values long
 constexpr uint32_t kMaxMatvecCols = 16384;
 sh_status launch_decode_matvec(const CodecArgs& a, uint32_t total_blocks, void* stream);
+// the matrix-vector decode of chunks of 64 or 128 streams (the row decoder with a consumer
+// sink); few: a launch of fewer than 16,384 chunks (rows of 32 lanes)
+sh_status launch_decode_matvec_rows(const CodecArgs& a, uint32_t total_blocks, bool few,
+                                    void* stream);
 // the encoder's chunk kernel: one chunk per row of 16 lanes (two, four or eight streams a
 // lane) or, for launches of few chunks of 64 streams, of 32 lanes (two streams a lane); 16
 // chunks a block

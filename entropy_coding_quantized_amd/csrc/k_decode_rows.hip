@@ -181,6 +181,65 @@ __device__ __forceinline__ uint32_t put_byte(uint32_t x, uint32_t o, uint32_t A)
     return x;
 }
 
+// Where the decoded values go.  RowBytes: to the output tensor, through the LDS tiles.
+// RowMatvec: into y += W a for a row-major int8 matrix W of cols values a row (the
+// container's values) and an int8 vector a of cols values staged in LDS, int32 sums; the
+// values are never written.  Chunks and rows are multiples of the W P streams (C and cols),
+// so a step's values are W P adjacent columns of one matrix row and lane j's P values are
+// columns c .. c + P - 1: one dot product of the lane's packed bytes with P vector bytes
+// (v_dot4_i32_i8) takes them.  A chunk row's sum of a matrix row goes to y with one atomic
+// add by the row's last lane when the step reaches the matrix row's end, and at the chunk's
+// end (a matrix row may span chunks).
+struct RowBytes {
+    static constexpr bool kBytes = true;
+};
+template <int W, int P>
+struct RowMatvec {
+    static constexpr bool kBytes = false;
+    static constexpr uint32_t kS = W * P;
+    int32_t acc;
+    uint32_t a_cur;                // the vector bytes of this lane's columns in the step
+    uint32_t abyte, abase, aend;   // LDS byte addresses, each + P j: the next step's
+                                   // columns, column 0, column cols
+    uint32_t mrow;                 // the matrix row of the step
+    int32_t* y;
+    __device__ __forceinline__ uint32_t read_vec(uint32_t addr) const {
+        if constexpr (P == 4) return *(const __attribute__((address_space(3))) uint32_t*)(uintptr_t)addr;
+        else return *(const __attribute__((address_space(3))) uint16_t*)(uintptr_t)addr;
+    }
+    // chunk: the chunk index in its tensor; vec_byte: the staged vector's LDS byte address
+    __device__ __forceinline__ void init(uint32_t chunk, uint32_t C, uint32_t cols, uint32_t j,
+                                         uint32_t vec_byte, int32_t* y_) {
+        const uint32_t first = chunk * C;  // below 2^32: n is
+        acc = 0;
+        mrow = first / cols;
+        abase = vec_byte + P * j;
+        aend = abase + cols;
+        abyte = abase + first % cols;
+        y = y_;
+        a_cur = read_vec(abyte);
+    }
+    // the row sums of the chunk rows whose lanes have mine set go to y
+    __device__ __forceinline__ void flush(bool mine, uint32_t j) {
+        const uint32_t tot = scan_row<W>((uint32_t)acc);
+        if (mine) {
+            if (j == W - 1 && tot != 0) atomicAdd(y + mrow, (int32_t)tot);
+            acc = 0;
+            ++mrow;
+        }
+    }
+    // a step's packed values (byte i: stream P j + i, zero for streams without a value)
+    __device__ __forceinline__ void put(uint32_t packed, uint32_t j) {
+        acc = __builtin_amdgcn_sdot4((int)packed, (int)a_cur, acc, false);
+        abyte += kS;
+        const bool wrap = abyte == aend;
+        if (wrap) abyte = abase;
+        a_cur = read_vec(abyte);
+        if (__builtin_amdgcn_ballot_w64(wrap) != 0) flush(wrap, j);
+    }
+    __device__ __forceinline__ void finish(uint32_t j) { flush(true, j); }
+};
+
 // One chunk row's decoder state (every lane of the row holds the same values, except the
 // states).
 template <int W, int P>
@@ -193,7 +252,7 @@ struct Row {
     v4u pf[RowGeom<W, P>::kFillVecs]; // the next refill, in flight
 };
 
-template <class A, int W, int P>
+template <class A, int W, int P, class Sink>
 __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
     using G = RowGeom<W, P>;
     constexpr uint32_t kS = G::kS, kRowsPerWave = G::kRowsPerWave, kFillVecs = G::kFillVecs;
@@ -326,7 +385,18 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
             rg[kRRing + 1] = f0[0][1];
         }
     }
+    // the matrix-vector sink's vector, where the tiles would be: cols values (a multiple of
+    // the chunk's streams, 16-byte aligned source)
+    const uint32_t vec_dw = rings + G::kRowsPerBlock * kRRingStride;
+    if constexpr (!Sink::kBytes) {
+        const v4u* src = reinterpret_cast<const v4u*>(sg->vec);
+        for (uint32_t i = tid; i < a.h.cols / 16; i += kRowsBlock)
+            *reinterpret_cast<v4u*>(&dsm[vec_dw + 4 * i]) = src[i];
+    }
     __syncthreads();
+    Sink sink;
+    if constexpr (!Sink::kBytes)
+        sink.init(chunk, a.h.C, a.h.cols, j, tab_byte + 4 * vec_dw, reinterpret_cast<int32_t*>(sg->x));
 
     // initial slots: stream s's R bits at bit0 + s * R (at most 24 + 127 * 11 + 11 bits: within
     // the first ring words, no wrap)
@@ -419,8 +489,10 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
             }
         }
         // the lane's bytes into the tile, packed by the byte-destination adds above: one
-        // 16-bit write for two, one dword for four
-        if constexpr (P == 2) {
+        // 16-bit write for two, one dword for four (or into the consumer's sums)
+        if constexpr (!Sink::kBytes) {
+            sink.put(packed, j);
+        } else if constexpr (P == 2) {
             typedef __attribute__((address_space(3))) uint16_t lds_w2b;
             *(lds_w2b*)(uintptr_t)(r.tile + kS * k) = (uint16_t)packed;
         } else {
@@ -464,7 +536,7 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
                 full_step(eb, ea, k + 1);
                 refill();
             }
-            flush_tile(t);
+            if constexpr (Sink::kBytes) flush_tile(t);
         }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -488,7 +560,7 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
             for (int i = 0; i < P; ++i) ea[i] = eb[i];
         }
         refill();
-        if (kLaneBytes * j < left * kS) {
+        if (Sink::kBytes && kLaneBytes * j < left * kS) {
             const uint32_t at = row * a.h.C + kLaneBytes * j;
             if constexpr (kLaneBytes == 16) {
                 const v4u w = *(const __attribute__((address_space(3))) v4u*)(uintptr_t)(tile_base + 16 * j);
@@ -519,16 +591,21 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
 #pragma unroll
         for (uint32_t i = 0; i < G::kWin; ++i) w[i] = rp[i];
         split_fields<P>(w, start, nd, f, nd[0] + nd[1]);
+        uint32_t pk = 0;  // the matrix-vector sink's packed values
 #pragma unroll
         for (int i = 0; i < P; ++i) {
             const uint32_t o = __builtin_amdgcn_ubfe(f[i], 0, act[i] ? ea[i].B : 0u);
             if (act[i]) {
                 err |= o > maxo_of(ea[i]);
                 r.s[i] = ((f[i] >> (ea[i].B & 31)) << 3) + next_of(ea[i]);
-                __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(o + base_of(ea[i])), rout,
-                                                     (int)(r.vout + i), (int)(t * kS), 0);
+                if constexpr (Sink::kBytes)
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(o + base_of(ea[i])), rout,
+                                                         (int)(r.vout + i), (int)(t * kS), 0);
+                else
+                    pk |= ((o + base_of(ea[i])) & 0xFFu) << (8 * i);
             }
         }
+        if constexpr (!Sink::kBytes) sink.put(pk, j);
         r.pos += row_last<W>(incl);
 #pragma unroll
         for (int i = 0; i < P; ++i) ea[i] = read_ent(r.s[i]);
@@ -550,6 +627,7 @@ __global__ __launch_bounds__(kRowsBlock) void k_decode_rows(const A a) {
             if ((gap < 32 ? pad & ((1u << gap) - 1) : pad) != 0) err = 1;
         }
     }
+    if constexpr (!Sink::kBytes) sink.finish(j);
     report(a.h.status, SH_ERR_CORRUPT_STREAM, err != 0 || bad_offsets != 0);
 }
 
@@ -558,14 +636,24 @@ uint32_t rows_lds_bytes(uint32_t L) {
     using G = RowGeom<W, P>;
     return 4 * (2 * L + G::kRowsPerBlock * (G::kRingStride + G::kTileStride));
 }
-
+// the matrix-vector form: the vector (cols bytes, 16-byte multiples) in place of the tiles
 template <int W, int P>
+uint32_t rows_matvec_lds_bytes(uint32_t L, uint32_t cols) {
+    using G = RowGeom<W, P>;
+    return 4 * (2 * L + G::kRowsPerBlock * G::kRingStride) + (cols + 15) / 16 * 16;
+}
+
+template <int W, int P, class Sink = RowBytes>
 sh_status launch_rows(const CodecArgs& a, uint32_t total_blocks, void* stream) {
     if (total_blocks == 0) return SH_OK;
-    const uint32_t lds = rows_lds_bytes<W, P>(a.L);
+    const uint32_t lds = Sink::kBytes ? rows_lds_bytes<W, P>(a.L)
+                                      : rows_matvec_lds_bytes<W, P>(a.L, a.cols);
     with_kernel_args(a, [&](const auto& k) {
-        hipLaunchKernelGGL((k_decode_rows<std::decay_t<decltype(k)>, W, P>), dim3(total_blocks),
-                           dim3(kRowsBlock), lds, (hipStream_t)stream, k);
+        using K = std::decay_t<decltype(k)>;
+        // the matrix-vector form takes device tables only
+        if constexpr (Sink::kBytes || !std::is_same_v<K, KOne>)
+            hipLaunchKernelGGL((k_decode_rows<K, W, P, Sink>), dim3(total_blocks),
+                               dim3(kRowsBlock), lds, (hipStream_t)stream, k);
     });
     return hipGetLastError() == hipSuccess ? SH_OK : SH_ERR_HIP;
 }
@@ -581,6 +669,15 @@ sh_status launch_decode(const CodecArgs& a, uint32_t total_blocks, void* stream)
 sh_status launch_decode_wide_halves(const CodecArgs& a, uint32_t total_blocks, void* stream) {
     if (a.S == kStreamsWide) return launch_rows<32, 2>(a, total_blocks, stream);
     if (a.S == kStreamsWidest) return launch_rows<32, 4>(a, total_blocks, stream);
+    return SH_ERR_UNSUPPORTED;
+}
+
+sh_status launch_decode_matvec_rows(const CodecArgs& a, uint32_t total_blocks, bool few,
+                                    void* stream) {
+    if (a.nseg == 0) return SH_ERR_INVALID_ARG;  // device tables only
+    if (a.S == kStreamsWide && !few) return launch_rows<16, 4, RowMatvec<16, 4>>(a, total_blocks, stream);
+    if (a.S == kStreamsWide) return launch_rows<32, 2, RowMatvec<32, 2>>(a, total_blocks, stream);
+    if (a.S == kStreamsWidest) return launch_rows<32, 4, RowMatvec<32, 4>>(a, total_blocks, stream);
     return SH_ERR_UNSUPPORTED;
 }
 

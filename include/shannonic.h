@@ -324,12 +324,15 @@ sh_status sh_decode_batch(const void* d_tables, const uint8_t* const* d_in,
  * decompression inside the kernels that consume the data, applied to this container with
  * a matrix-vector product as the consumer (an int8 weight matrix times an int8 activation
  * vector, or int8 keys times a query).
- * params->streams must be 32 (SH_ERR_UNSUPPORTED otherwise).
- * cols: a multiple of 32, at most 16384 (SH_ERR_UNSUPPORTED otherwise; 0 is
+ * params->streams may be 32, 64 or 128: chunks of 32 streams go through the half-wavefront
+ * decoder (log2_L <= 8), chunks of 64 or 128 through the row decoder, whose lanes take the
+ * dot product of their packed values with the vector's bytes.
+ * cols: a multiple of params->streams, at most 16384 (SH_ERR_UNSUPPORTED otherwise; 0 is
  * SH_ERR_INVALID_ARG); every n[i] a multiple of cols (SH_ERR_INVALID_ARG).  d_a[i]: device,
  * cols int8 values, 16-byte aligned; d_y[i]: device, n[i] / cols int32, 4-byte aligned, read
  * and written (zero it first for y = W a).  Rows may span chunks: each chunk adds its part
- * of a row with one atomic add per row and half wavefront, so y[i] is exact in any order.
+ * of a row with one atomic add per row (per half wavefront or row of lanes), so y[i] is exact
+ * in any order.
  * Every check of sh_decode applies and the first error goes to *d_status; y[i] of a
  * container that fails them is unspecified.  Asynchronous on stream.
  */

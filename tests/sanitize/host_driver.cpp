@@ -18,6 +18,7 @@ sh_status launch_decode(const CodecArgs&, uint32_t, void*) { return SH_ERR_HIP; 
 sh_status launch_decode_halves(const CodecArgs&, uint32_t, void*) { return SH_ERR_HIP; }
 sh_status launch_decode_wide_halves(const CodecArgs&, uint32_t, void*) { return SH_ERR_HIP; }
 sh_status launch_decode_matvec(const CodecArgs&, uint32_t, void*) { return SH_ERR_HIP; }
+sh_status launch_decode_matvec_rows(const CodecArgs&, uint32_t, bool, void*) { return SH_ERR_HIP; }
 sh_status launch_encode(const CodecArgs&, uint32_t, uint32_t, bool, void*, void*, void*, void*) {
     return SH_ERR_HIP;
 }

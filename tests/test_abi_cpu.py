@@ -228,10 +228,13 @@ def test_matvec_argument_checks_are_synchronous():
     misaligned = codec._ptrs([fake + 4])
     assert lib.sh_decode_matvec_batch(fake, ptrs, caps, misaligned, ptrs, codec._u64s([1024]),
                                       32, 1, C.byref(pc), None, None) == codec.SH_ERR_INVALID_ARG
-    # the fused decode runs one stream a lane of a half wavefront: chunks of 32 streams only
-    wide = codec.Params(K=16, log2_L=7, chunk_symbols=4096, streams=64).c()
-    assert lib.sh_decode_matvec_batch(fake, ptrs, caps, ptrs, ptrs, codec._u64s([1024]), 32,
-                                      1, C.byref(wide), None, None) == codec.SH_ERR_UNSUPPORTED
+    # with chunks of 64 or 128 streams a matrix row must hold whole steps: cols a multiple of
+    # the streams
+    for S, cols in [(64, 32), (64, 96), (128, 64)]:
+        wide = codec.Params(K=16, log2_L=7, chunk_symbols=4096, streams=S).c()
+        assert lib.sh_decode_matvec_batch(fake, ptrs, caps, ptrs, ptrs, codec._u64s([cols * 32]),
+                                          cols, 1, C.byref(wide), None, None) == \
+            codec.SH_ERR_UNSUPPORTED
 
 
 def test_tables_from_bytes_rejects_garbage():

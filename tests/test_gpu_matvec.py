@@ -69,11 +69,37 @@ def test_matvec_matches_oracle(torch_cuda, rows, cols, C):
     assert np.array_equal(y, expect)
 
 
-def test_matvec_batch_accumulates_per_tensor(torch_cuda):
+@pytest.mark.parametrize("rows,cols,C,S", [
+    (1024, 4096, 16384, 64),   # the model's q/k/v/o/gate/up rows: four a chunk, aligned
+    (700, 14336, 16384, 64),   # the model's down_proj rows: they straddle chunks
+    (333, 192, 4096, 64),      # ragged last chunk
+    (3, 16384, 4096, 64),      # the widest rows
+    (37, 128, 1024, 128),      # 128 streams a chunk
+    (129, 640, 2048, 128),     # 128 streams, rows straddling chunks
+    (16400, 128, 128, 64),     # 16,400 chunks: the 16-lane rows with four streams a lane
+    (24576, 128, 192, 64),     # ... with rows straddling chunks
+])
+def test_matvec_wide_chunks_match_oracle(torch_cuda, rows, cols, C, S):
+    """Chunks of 64 and 128 streams go through the row decoder with a matrix-vector sink:
+    launches of fewer than 16,384 chunks in rows of 32 lanes, larger ones (64 streams) in
+    rows of 16 lanes with four streams a lane."""
+    torch = torch_cuda
+    print(f"case: matvec rows={rows} cols={cols} C={C} S={S}", flush=True)
+    rng = np.random.default_rng(rows * 11 + cols + S)
+    x = D.quantize(rng.laplace(0, 12, size=rows * cols))
+    a = rng.integers(-128, 128, size=cols).astype(np.int8)
+    p = codec.Params(K=16, log2_L=7, chunk_symbols=C, streams=S)
+    (y,), st = _matvec_gpu(torch, [x], [a], cols, p)
+    assert st == 0
+    assert np.array_equal(y, O.matvec_i8(x, cols, a))
+
+
+@pytest.mark.parametrize("S", [32, 64, 128])
+def test_matvec_batch_accumulates_per_tensor(torch_cuda, S):
     """Several matrices with their own tables, vectors and starting y (y += W a), and the
     degenerate tensors: all zero, every value once, an empty matrix."""
     torch = torch_cuda
-    print("case: matvec batch", flush=True)
+    print(f"case: matvec batch S={S}", flush=True)
     rng = np.random.default_rng(5)
     cols = 256
     xs = [D.quantize(rng.normal(0, s, size=r * cols)) for s, r in [(3.0, 40), (30.0, 129), (9.0, 7)]]
@@ -81,35 +107,37 @@ def test_matvec_batch_accumulates_per_tensor(torch_cuda):
            np.zeros(0, np.int8)]
     avs = [rng.integers(-128, 128, size=cols).astype(np.int8) for _ in xs]
     y0 = [rng.integers(-2**30, 2**30, size=x.size // cols) for x in xs]
-    p = codec.Params(K=16, log2_L=7, chunk_symbols=1024)
+    p = codec.Params(K=16, log2_L=7, chunk_symbols=1024, streams=S)
     ys, st = _matvec_gpu(torch, xs, avs, cols, p, y0=y0)
     assert st == 0
     for x, a, y, y_0 in zip(xs, avs, ys, y0):
         assert np.array_equal(y, O.matvec_i8(x, cols, a, y_0))
 
 
-def test_matvec_reports_a_corrupt_container(torch_cuda):
+@pytest.mark.parametrize("S", [32, 64, 128])
+def test_matvec_reports_a_corrupt_container(torch_cuda, S):
     torch = torch_cuda
-    print("case: matvec corrupt", flush=True)
+    print(f"case: matvec corrupt S={S}", flush=True)
     rng = np.random.default_rng(8)
     cols = 512
     x = D.quantize(rng.laplace(0, 10, size=64 * cols))
     a = rng.integers(-128, 128, size=cols).astype(np.int8)
-    p = codec.Params(K=16, log2_L=7, chunk_symbols=4096)
+    p = codec.Params(K=16, log2_L=7, chunk_symbols=4096, streams=S)
     _, st = _matvec_gpu(torch, [x], [a], cols, p, corrupt=(0, 0))
     assert st == codec.SH_ERR_CORRUPT_STREAM
 
 
-def test_matvec_many_tensors_span_launches(torch_cuda):
+@pytest.mark.parametrize("S", [32, 64])
+def test_matvec_many_tensors_span_launches(torch_cuda, S):
     """More tensors than one launch carries (48): the batch is split over launches."""
     torch = torch_cuda
-    print("case: matvec 50 tensors", flush=True)
+    print(f"case: matvec 50 tensors S={S}", flush=True)
     rng = np.random.default_rng(12)
     cols = 64
     xs = [D.quantize(rng.laplace(0, rng.choice([2.0, 8.0, 20.0]), size=int(r) * cols))
           for r in rng.integers(1, 300, size=50)]
     avs = [rng.integers(-128, 128, size=cols).astype(np.int8) for _ in xs]
-    p = codec.Params(K=16, log2_L=7, chunk_symbols=512)
+    p = codec.Params(K=16, log2_L=7, chunk_symbols=512, streams=S)
     ys, st = _matvec_gpu(torch, xs, avs, cols, p)
     assert st == 0
     for x, a, y in zip(xs, avs, ys):
