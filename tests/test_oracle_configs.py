@@ -24,11 +24,25 @@ def _check(x, cfg, pct=1.0):
 
 @pytest.mark.slow
 def test_kv_cache_every_head():
+    """Every head's payload within 1% of its H; the whole layer's container (framing
+    included, all 16 tables) within 1% of the layer's H."""
     cfg = D.CONFIGS["kv_cache"]
     x = D.kv_cache()
+    bits = hx = 0.0
     for a in range(x.shape[0]):
         for h in range(x.shape[1]):
-            _check(x[a, h], cfg)
+            st = _check(x[a, h], cfg)
+            bits += st["container_bps"] * x[a, h].size
+            hx += st["H"] * x[a, h].size
+    assert (bits - hx) / hx * 100.0 < 1.0
+
+
+@pytest.mark.slow
+def test_weight_container_within_one_percent():
+    """The weight tensor's container, framing included, within 1% of H."""
+    cfg = D.CONFIGS["weight"]
+    st = _check(D.weight(), cfg)
+    assert 0.0 < st["pct_container_over_H"] < 1.0, st
 
 
 @pytest.mark.slow
@@ -42,6 +56,8 @@ def test_activations_slice_with_whole_tensor_table():
     assert (O.decode(buf, part.size) == part).all()
     st = O.stats(h, lo, f, cfg["log2_L"], bits, buf.size, part.size)
     assert st["pct_payload_over_H"] < 1.0
+    # the slice's 1,024 chunks carry the same framing per chunk as the whole tensor's
+    assert st["pct_container_over_H"] < 1.0, st
 
 
 @pytest.mark.slow
